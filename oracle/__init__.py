@@ -1,0 +1,189 @@
+"""CPU oracle for the KV-compressor hot path -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its binding in ``sparse_attention_kv_plan_amd``) never imports it, and the two
+share no code: the arithmetic lives in ``kvc_oracle.c`` (plain C, float64) and
+in ``brute.py`` (pure Python, tiny sizes only).
+
+Every function takes and returns numpy arrays.  bf16 tensors travel as
+``uint16`` bit patterns; plan records travel as ``uint8`` byte arrays of
+16 (C, D) or 8 (W) bytes per record.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kvc_oracle.c")
+_LIB = os.path.join(_HERE, "libkvc_oracle.so")
+
+C_BYTES, W_BYTES, D_BYTES = 16, 8, 16
+WINDOW = {4: 8, 128: 128}
+ROW_MULT = {4: 4, 128: 2}  # row width of a kv/score row, in units of head_dim
+
+
+def build(force: bool = True) -> str:
+    """Compile kvc_oracle.c with gcc (no fast-math) into libkvc_oracle.so."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        # KVC_ORACLE_LIB lets the mutation test load a deliberately broken copy
+        path = os.environ.get("KVC_ORACLE_LIB")
+        if path is None:
+            path = _LIB
+            if not os.path.exists(path):
+                build(force=True)
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        L = ctypes.c_int64
+        lib.oracle_plan_prefill.argtypes = [I, I, I, P, P, P, L, P, I, P, I, P]
+        lib.oracle_plan_decode.argtypes = [I, I, P, P, L, P, P]
+        lib.oracle_compress.argtypes = [I, I, I, P, L, P, I, P, P, I, P]
+        lib.oracle_write.argtypes = [I, I, I, P, L, P, I, P, I]
+        lib.oracle_decode.argtypes = [I, I, I, P, L, P, P, P, I, P]
+        for f in ("oracle_plan_prefill", "oracle_plan_decode", "oracle_compress", "oracle_write",
+                  "oracle_decode"):
+            getattr(lib, f).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _i32(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _elem(a):
+    """Return (contiguous array, is_bf16) for a bf16 (uint16 bits) or fp32 array."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return a, 1
+    if a.dtype == np.float32:
+        return a, 0
+    raise TypeError("oracle inputs are bf16 bit patterns (uint16) or float32, got %s" % a.dtype)
+
+
+class OracleError(ValueError):
+    pass
+
+
+def plan_prefill(cr, seq_lens, extend_lens, state_index, num_state_rows, num_q, cap_c, cap_w):
+    """Build the prefill plan.  Returns (plan_c bytes [cap_c,16], plan_w bytes [cap_w,8], counts[4])."""
+    s, e, idx = _i32(seq_lens), _i32(extend_lens), _i32(state_index)
+    pc = np.zeros((max(cap_c, 0), C_BYTES), np.uint8)
+    pw = np.zeros((max(cap_w, 0), W_BYTES), np.uint8)
+    counts = np.zeros(4, np.int32)
+    rc = _load().oracle_plan_prefill(cr, len(s), num_q, _ptr(s), _ptr(e), _ptr(idx), int(num_state_rows),
+                                     _ptr(pc), cap_c, _ptr(pw), cap_w, _ptr(counts))
+    if rc != 0:
+        raise OracleError("oracle_plan_prefill rejected its arguments")
+    return pc, pw, counts
+
+
+def plan_decode(cr, seq_lens, state_index, num_state_rows):
+    """Build the decode plan.  Returns (plan_d bytes [B,16], status)."""
+    s, idx = _i32(seq_lens), _i32(state_index)
+    pd = np.zeros((len(s), D_BYTES), np.uint8)
+    status = np.zeros(1, np.int32)
+    rc = _load().oracle_plan_decode(cr, len(s), _ptr(s), _ptr(idx), int(num_state_rows), _ptr(pd), _ptr(status))
+    if rc != 0:
+        raise OracleError("oracle_plan_decode rejected its arguments")
+    return pd, int(status[0])
+
+
+def compress(cr, hd, state, inp, ape, plan_c, num_c, out=None):
+    """Pool the first num_c C records.  state [rows, R], inp [num_q, R], ape [W, hd].
+
+    Returns (out float64 [len(plan_c), hd] -- rows not pooled are NaN unless
+    ``out`` is given --, error bits)."""
+    state, sb = _elem(state)
+    inp, ib = _elem(inp)
+    ape, ab = _elem(ape)
+    assert sb == ib == ab
+    pc = np.ascontiguousarray(plan_c, dtype=np.uint8)
+    if out is None:
+        out = np.full((max(pc.shape[0], 1), hd), np.nan, np.float64)
+    err = _load().oracle_compress(cr, ib, hd, _ptr(state), state.shape[0], _ptr(inp), inp.shape[0], _ptr(ape),
+                                  _ptr(pc), int(num_c), _ptr(out))
+    return out[: pc.shape[0]], err
+
+
+def write(cr, hd, state, inp, plan_w, num_w):
+    """Scatter the first num_w W records into ``state`` in place.  Returns error bits."""
+    inp, ib = _elem(inp)
+    assert state.flags.c_contiguous
+    _, sb = _elem(state)
+    assert sb == ib
+    pw = np.ascontiguousarray(plan_w, dtype=np.uint8)
+    return _load().oracle_write(cr, ib, hd, _ptr(state), state.shape[0], _ptr(inp), inp.shape[0], _ptr(pw),
+                                int(num_w))
+
+
+def decode(cr, hd, state, inp, ape, plan_d):
+    """Fused decode, in place on ``state``.  Returns (out float64 [B, hd], error bits)."""
+    inp, ib = _elem(inp)
+    ape, ab = _elem(ape)
+    assert state.flags.c_contiguous
+    _, sb = _elem(state)
+    assert sb == ib == ab
+    pd = np.ascontiguousarray(plan_d, dtype=np.uint8)
+    B = pd.shape[0]
+    out = np.zeros((B, hd), np.float64)
+    err = _load().oracle_decode(cr, ib, hd, _ptr(state), state.shape[0], _ptr(inp), _ptr(ape), _ptr(pd), B,
+                                _ptr(out))
+    return out, err
+
+
+# --------------------------------------------------------------------------
+# record helpers (byte layout as documented in kvc_oracle.c)
+# --------------------------------------------------------------------------
+
+def unpack_c(plan_c):
+    """Decode C records -> int64 array [n, 5]: seq_len, ragged_id, buffer_len, read_page_0, read_page_1."""
+    w = np.ascontiguousarray(plan_c, np.uint8).view("<u4").reshape(-1, 4).astype(np.int64)
+    out = np.empty((w.shape[0], 5), np.int64)
+    out[:, 0] = w[:, 0]
+    out[:, 1] = w[:, 1] & 0xFFFFFF
+    out[:, 2] = w[:, 1] >> 24
+    out[:, 3] = w[:, 2].astype(np.uint32).view(np.int32)
+    out[:, 4] = w[:, 3].astype(np.uint32).view(np.int32)
+    return out
+
+
+def unpack_w(plan_w):
+    """Decode W records -> int64 array [n, 2]: ragged_id, write_loc."""
+    w = np.ascontiguousarray(plan_w, np.uint8).view("<u4").reshape(-1, 2)
+    return np.stack([w[:, 0].astype(np.int64), w[:, 1].view(np.int32).astype(np.int64)], axis=1)
+
+
+def unpack_d(plan_d):
+    """Decode D records -> int64 array [n, 4]: seq_len, write_loc, read_page_0, read_page_1."""
+    w = np.ascontiguousarray(plan_d, np.uint8).view("<u4").reshape(-1, 4)
+    out = w.view(np.int32).astype(np.int64)
+    out[:, 0] = w[:, 0].astype(np.int64)
+    return out
+
+
+def capacities(cr, B, num_q):
+    """Capacities that always suffice: every C or W record fits."""
+    return min(num_q, num_q // cr + B), min(num_q, B * (WINDOW[cr] - 1))

@@ -1,0 +1,407 @@
+/*
+ * kvc_oracle.c - plain, slow CPU oracle for the KV-compressor hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check of the graft
+ * entry point and the cpu_baseline leg of bench.py may load this library.
+ * The product path (the HIP library and its Python binding) never calls it.
+ * It shares no source, header, table or helper with the HIP path.
+ *
+ * What it computes, and where the pages state it ("c_plan.cuh" = the page
+ * sglang/jit_kernel/csrc/deepseek_v4/c_plan.cuh, "c4.cuh" = the page
+ * .../deepseek_v4/c4.cuh, "compressor_v2.py" = the page
+ * sglang/srt/layers/attention/dsv4/compressor_v2.py):
+ *
+ *   plan prefill  - c_plan.cuh, plan_compress_prefill_legacy (host loop over
+ *                   requests and positions) followed by
+ *                   plan_compress_prefill_legacy_kernel (per-request ring /
+ *                   page translation).  Records are emitted in loop order:
+ *                   request-major, position ascending.
+ *   plan decode   - c_plan.cuh, plan_compress_decode_legacy_kernel.
+ *   compress      - c4.cuh, c4_forward (8-entry window, overlap halves,
+ *                   first-block mask) and compressor_v2.py,
+ *                   _compress_forward_c128_fallback (softmax over the 128
+ *                   window entries of score + ape, weighted sum of kv).
+ *                   Entries that precede the chunk come from the state buffer
+ *                   as it was BEFORE this chunk's write; the rest come from
+ *                   the ragged input (c4.cuh, flash_c4_prefill launches the
+ *                   compress kernel before the write kernel).
+ *   write         - c4.cuh, c4_write / flash_c4_prefill<kWrite=true>, and
+ *                   compressor_v2.py, _c128_compress_prefill_write_kernel:
+ *                   a whole input row copied into one state row.
+ *   decode        - c4.cuh, flash_c4_decode and compressor_v2.py,
+ *                   _c128_compress_decode_kernel: write the new token, then
+ *                   pool the window if the new length is a multiple of the
+ *                   ratio, else emit a zero row.
+ *
+ * All pooling arithmetic is float64: a two-pass softmax (max, then the sums
+ * of exp(t - max) and exp(t - max) * kv).  bf16 and fp32 inputs are widened
+ * exactly to double.  Record layouts (little endian, written byte by byte):
+ *   C record 16 B: u32 seq_len | u32 ragged_id (bits 0..23) + buffer_len
+ *                  (bits 24..31) | i32 read_page_0 | i32 read_page_1
+ *   W record  8 B: u32 ragged_id | i32 write_loc
+ *   D record 16 B: u32 seq_len | i32 write_loc | i32 read_page_0 | i32 read_page_1
+ *   invalid record: every byte 0xFF.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* device-data error bits, as the library documents them */
+#define ERR_EXTEND 1   /* some extend_len <= 0 or > seq_len (decode: seq_len <= 0) */
+#define ERR_NUMQ 2     /* sum of extend_len != num_q */
+#define ERR_INDEX 4    /* some state_index outside [0, num_state_rows / window) */
+#define ERR_CAPACITY 8 /* more C or W records than cap_c / cap_w */
+#define ERR_RECORD 16  /* a consumer met a record pointing outside its buffers */
+
+static void put_u32(uint8_t* p, uint32_t v) {
+  p[0] = (uint8_t)(v & 0xFF);
+  p[1] = (uint8_t)((v >> 8) & 0xFF);
+  p[2] = (uint8_t)((v >> 16) & 0xFF);
+  p[3] = (uint8_t)((v >> 24) & 0xFF);
+}
+
+static uint32_t get_u32(const uint8_t* p) {
+  return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+}
+
+static int32_t get_i32(const uint8_t* p) {
+  uint32_t u = get_u32(p);
+  int32_t s;
+  memcpy(&s, &u, 4);
+  return s;
+}
+
+static uint32_t as_u32(int32_t v) {
+  uint32_t u;
+  memcpy(&u, &v, 4);
+  return u;
+}
+
+/* window length: 8 for ratio 4 (two overlapping blocks), 128 for ratio 128 */
+static int window_of(int cr) { return cr == 4 ? 8 : 128; }
+
+/* Per-request state page of a position (c_plan.cuh, legacy_compute_page):
+ * ratio 4 owns two pages of 4 slots per request and alternates between them
+ * block by block; ratio 128 owns one page of 128 slots. */
+static int64_t page_of(int cr, int64_t idx, int64_t pos) {
+  if (cr == 4) return idx * 2 + ((pos / 4) & 1);
+  return idx;
+}
+
+/* state row of a position (c_plan.cuh, legacy_compute_loc) */
+static int64_t loc_of(int cr, int64_t idx, int64_t pos) { return page_of(cr, idx, pos) * cr + pos % cr; }
+
+static double widen(const void* base, int is_bf16, int64_t row, int64_t row_len, int64_t col) {
+  if (is_bf16) {
+    uint16_t h = ((const uint16_t*)base)[row * row_len + col];
+    uint32_t bits = (uint32_t)h << 16; /* bf16 is the top half of an fp32 */
+    float f;
+    memcpy(&f, &bits, 4);
+    return (double)f;
+  }
+  return (double)((const float*)base)[row * row_len + col];
+}
+
+static int bad_host_args(int cr, int B) {
+  if (cr != 4 && cr != 128) return 1;
+  if (B < 1 || B > 1024) return 1;
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* plan prefill                                                              */
+/* ------------------------------------------------------------------------ */
+
+int oracle_plan_prefill(int cr, int B, int num_q, const int32_t* seq_lens, const int32_t* extend_lens,
+                        const int32_t* state_index, int64_t num_state_rows, uint8_t* plan_c, int cap_c,
+                        uint8_t* plan_w, int cap_w, int32_t* counts) {
+  if (bad_host_args(cr, B)) return -1;
+  if (num_q < B || num_q >= (1 << 24)) return -1;
+  if (cap_c < 0 || cap_w < 0 || num_state_rows < 0 || num_state_rows > INT32_MAX) return -1;
+  if (!seq_lens || !extend_lens || !state_index || !counts) return -1;
+  if ((cap_c > 0 && !plan_c) || (cap_w > 0 && !plan_w)) return -1;
+
+  const int W = window_of(cr);
+  int err = 0;
+  int64_t total = 0;
+  for (int b = 0; b < B; ++b) {
+    const int64_t s = seq_lens[b], e = extend_lens[b], idx = state_index[b];
+    if (e <= 0 || e > s) err |= ERR_EXTEND;
+    total += e;
+    if (idx < 0 || idx >= num_state_rows / W) err |= ERR_INDEX;
+  }
+  if (total != num_q) err |= ERR_NUMQ;
+
+  int num_c = 0, num_w = 0;
+  uint8_t* tmp_c = NULL;
+  uint8_t* tmp_w = NULL;
+  if (!(err & (ERR_EXTEND | ERR_NUMQ))) {
+    tmp_c = (uint8_t*)malloc((size_t)num_q * 16);
+    tmp_w = (uint8_t*)malloc((size_t)num_q * 8);
+    int64_t ragged_base = 0;
+    for (int b = 0; b < B; ++b) {
+      const int64_t s = seq_lens[b], e = extend_lens[b], idx = state_index[b];
+      const int64_t p0 = s - e;
+      /* last block boundary at or before s; ratio 4 also keeps the block
+       * before it, which the next window overlaps */
+      const int64_t last_c = (s / cr) * cr;
+      const int64_t first_w = last_c - (cr == 4 ? 4 : 0);
+      for (int64_t j = 0; j < e; ++j) {
+        const int64_t pos = p0 + j;
+        const int64_t ragged = ragged_base + j;
+        if ((pos + 1) % cr == 0) {
+          const int64_t in_chunk = (j + 1 < W) ? j + 1 : W;
+          const int64_t blen = W - in_chunk; /* window entries taken from the state */
+          const int64_t pos0 = (pos - cr > 0) ? pos - cr : 0;
+          uint8_t* r = tmp_c + (size_t)num_c * 16;
+          put_u32(r + 0, (uint32_t)(pos + 1));
+          put_u32(r + 4, (uint32_t)ragged | ((uint32_t)blen << 24));
+          put_u32(r + 8, as_u32((int32_t)page_of(cr, idx, pos0)));
+          put_u32(r + 12, as_u32((int32_t)page_of(cr, idx, pos)));
+          ++num_c;
+        }
+        if (pos >= first_w) {
+          uint8_t* r = tmp_w + (size_t)num_w * 8;
+          put_u32(r + 0, (uint32_t)ragged);
+          put_u32(r + 4, as_u32((int32_t)loc_of(cr, idx, pos)));
+          ++num_w;
+        }
+      }
+      ragged_base += e;
+    }
+    if (num_c > cap_c || num_w > cap_w) err |= ERR_CAPACITY;
+  }
+
+  if (err) {
+    num_c = 0;
+    num_w = 0;
+  } else {
+    memcpy(plan_c, tmp_c, (size_t)num_c * 16);
+    memcpy(plan_w, tmp_w, (size_t)num_w * 8);
+  }
+  if (cap_c > num_c) memset(plan_c + (size_t)num_c * 16, 0xFF, (size_t)(cap_c - num_c) * 16);
+  if (cap_w > num_w) memset(plan_w + (size_t)num_w * 8, 0xFF, (size_t)(cap_w - num_w) * 8);
+  counts[0] = num_c;
+  counts[1] = num_w;
+  counts[2] = err;
+  counts[3] = 0;
+  free(tmp_c);
+  free(tmp_w);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* plan decode                                                               */
+/* ------------------------------------------------------------------------ */
+
+int oracle_plan_decode(int cr, int B, const int32_t* seq_lens, const int32_t* state_index, int64_t num_state_rows,
+                       uint8_t* plan_d, int32_t* status) {
+  if (bad_host_args(cr, B)) return -1;
+  if (num_state_rows < 0 || num_state_rows > INT32_MAX) return -1;
+  if (!seq_lens || !state_index || !plan_d) return -1;
+  const int W = window_of(cr);
+  int err = 0;
+  for (int b = 0; b < B; ++b) {
+    if (seq_lens[b] <= 0) err |= ERR_EXTEND;
+    if (state_index[b] < 0 || state_index[b] >= num_state_rows / W) err |= ERR_INDEX;
+  }
+  if (err) {
+    memset(plan_d, 0xFF, (size_t)B * 16);
+  } else {
+    for (int b = 0; b < B; ++b) {
+      const int64_t s = seq_lens[b], idx = state_index[b];
+      const int64_t pos1 = s - 1; /* the new token */
+      const int64_t pos0 = (pos1 - cr > 0) ? pos1 - cr : 0;
+      uint8_t* r = plan_d + (size_t)b * 16;
+      put_u32(r + 0, (uint32_t)s);
+      put_u32(r + 4, as_u32((int32_t)loc_of(cr, idx, pos1)));
+      put_u32(r + 8, as_u32((int32_t)page_of(cr, idx, pos0)));
+      put_u32(r + 12, as_u32((int32_t)page_of(cr, idx, pos1)));
+    }
+  }
+  if (status) status[0] = err;
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* pooling                                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* Softmax over the n kept entries of t[], applied to v[] (two passes).
+ * Returns sum_i exp(t_i - m) v_i / sum_i exp(t_i - m), m = max_i t_i. */
+static double softmax_pool(const double* t, const double* v, int n) {
+  double m = t[0];
+  for (int i = 1; i < n; ++i)
+    if (t[i] > m) m = t[i];
+  double num = 0.0, den = 0.0;
+  for (int i = 0; i < n; ++i) {
+    const double w = exp(t[i] - m);
+    num += w * v[i];
+    den += w;
+  }
+  return num / den;
+}
+
+/* Where window entry i of a compressed row comes from, and which columns of
+ * that row hold its kv and score.  For ratio 4 the row is laid out as
+ * |kv overlap|kv|score overlap|score| (c4.cuh, Compress4PrefillParams);
+ * entries 0..3 (the previous block) read the overlap halves, entries 4..7
+ * (the block being closed) the others.  For ratio 128 the row is |kv|score|. */
+typedef struct {
+  int from_state; /* 1: state buffer row; 0: ragged input row */
+  int64_t row;
+  int64_t kv_col;
+  int64_t sc_col;
+} entry_src;
+
+static entry_src c4_entry(int i, int64_t blen, int64_t ragged, int64_t rp0, int64_t rp1, int64_t hd) {
+  entry_src e;
+  if (i < blen) {
+    e.from_state = 1;
+    e.row = (i < 4) ? rp0 * 4 + i : rp1 * 4 + (i - 4);
+  } else {
+    e.from_state = 0;
+    e.row = ragged - 7 + i;
+  }
+  e.kv_col = (i < 4) ? 0 : hd;
+  e.sc_col = (i < 4) ? 2 * hd : 3 * hd;
+  return e;
+}
+
+static entry_src c128_entry(int i, int64_t blen, int64_t ragged, int64_t rp0, int64_t hd) {
+  entry_src e;
+  if (i < blen) {
+    e.from_state = 1;
+    e.row = rp0 * 128 + i;
+  } else {
+    e.from_state = 0;
+    e.row = ragged - 127 + i;
+  }
+  e.kv_col = 0;
+  e.sc_col = hd;
+  return e;
+}
+
+/* Pool one compressed row (all hd channels) from entries described by src[].
+ * For ratio 4, seq_len == 4 is block 0: entries 0..3 lie before the sequence
+ * and are dropped (c4.cuh, c4_forward sets their kv to 0 and score to -1e9,
+ * whose weight underflows to exactly zero). */
+static void pool_row(int cr, int is_bf16, int64_t hd, const entry_src* src, int64_t seq_len, const void* state,
+                     const void* input, const void* ape, double* out) {
+  const int W = window_of(cr);
+  const int64_t R = (cr == 4 ? 4 : 2) * hd;
+  double* t = (double*)malloc(sizeof(double) * (size_t)W);
+  double* v = (double*)malloc(sizeof(double) * (size_t)W);
+  const int first = (cr == 4 && seq_len == 4) ? 4 : 0;
+  for (int64_t d = 0; d < hd; ++d) {
+    int n = 0;
+    for (int i = first; i < W; ++i) {
+      const void* base = src[i].from_state ? state : input;
+      const double kv = widen(base, is_bf16, src[i].row, R, src[i].kv_col + d);
+      const double sc = widen(base, is_bf16, src[i].row, R, src[i].sc_col + d);
+      t[n] = sc + widen(ape, is_bf16, i, hd, d);
+      v[n] = kv;
+      ++n;
+    }
+    out[d] = softmax_pool(t, v, n);
+  }
+  free(t);
+  free(v);
+}
+
+/* Compress every C record in [0, num_c).  Invalid records are skipped (their
+ * output rows untouched).  A record that points outside the input or the
+ * state is skipped too and reported with ERR_RECORD.  Returns the error bits. */
+int oracle_compress(int cr, int is_bf16, int hd, const void* state, int64_t num_state_rows, const void* input,
+                    int num_q, const void* ape, const uint8_t* plan_c, int num_c, double* out) {
+  const int W = window_of(cr);
+  int err = 0;
+  entry_src* src = (entry_src*)malloc(sizeof(entry_src) * (size_t)W);
+  for (int k = 0; k < num_c; ++k) {
+    const uint8_t* r = plan_c + (size_t)k * 16;
+    const uint32_t seq_len = get_u32(r);
+    if (seq_len == 0xFFFFFFFFu) continue;
+    const uint32_t rb = get_u32(r + 4);
+    const int64_t ragged = rb & 0xFFFFFF;
+    const int64_t blen = rb >> 24;
+    const int64_t rp0 = get_i32(r + 8), rp1 = get_i32(r + 12);
+    const int first = (cr == 4 && seq_len == 4) ? 4 : 0;
+    int ok = 1;
+    for (int i = 0; i < W; ++i) {
+      src[i] = (cr == 4) ? c4_entry(i, blen, ragged, rp0, rp1, hd) : c128_entry(i, blen, ragged, rp0, hd);
+      if (i < first) continue;
+      const int64_t lim = src[i].from_state ? num_state_rows : num_q;
+      if (src[i].row < 0 || src[i].row >= lim) ok = 0;
+    }
+    if (!ok) {
+      err |= ERR_RECORD;
+      continue;
+    }
+    pool_row(cr, is_bf16, hd, src, seq_len, state, input, ape, out + (size_t)k * hd);
+  }
+  free(src);
+  return err;
+}
+
+/* Copy input row ragged_id into state row write_loc for every W record in
+ * [0, num_w).  Returns the error bits. */
+int oracle_write(int cr, int is_bf16, int hd, void* state, int64_t num_state_rows, const void* input, int num_q,
+                 const uint8_t* plan_w, int num_w) {
+  const int64_t R = (cr == 4 ? 4 : 2) * (int64_t)hd;
+  const int64_t esz = is_bf16 ? 2 : 4;
+  int err = 0;
+  for (int k = 0; k < num_w; ++k) {
+    const uint8_t* r = plan_w + (size_t)k * 8;
+    const uint32_t ragged = get_u32(r);
+    if (ragged == 0xFFFFFFFFu) continue;
+    const int64_t loc = get_i32(r + 4);
+    if ((int64_t)ragged >= num_q || loc < 0 || loc >= num_state_rows) {
+      err |= ERR_RECORD;
+      continue;
+    }
+    memcpy((uint8_t*)state + (size_t)(loc * R * esz), (const uint8_t*)input + (size_t)((int64_t)ragged * R * esz),
+           (size_t)(R * esz));
+  }
+  return err;
+}
+
+/* Decode: for every request b, write input row b into the state, then pool
+ * the window if seq_len is a multiple of the ratio (reading the state after
+ * the write), else emit a zero row.  Invalid records emit a zero row and
+ * leave the state alone.  Returns the error bits. */
+int oracle_decode(int cr, int is_bf16, int hd, void* state, int64_t num_state_rows, const void* input,
+                  const void* ape, const uint8_t* plan_d, int B, double* out) {
+  const int W = window_of(cr);
+  const int64_t R = (cr == 4 ? 4 : 2) * (int64_t)hd;
+  const int64_t esz = is_bf16 ? 2 : 4;
+  int err = 0;
+  entry_src* src = (entry_src*)malloc(sizeof(entry_src) * (size_t)W);
+  for (int b = 0; b < B; ++b) {
+    const uint8_t* r = plan_d + (size_t)b * 16;
+    double* o = out + (size_t)b * hd;
+    const uint32_t seq_len = get_u32(r);
+    for (int d = 0; d < hd; ++d) o[d] = 0.0;
+    if (seq_len == 0xFFFFFFFFu) continue;
+    const int64_t wl = get_i32(r + 4), rp0 = get_i32(r + 8), rp1 = get_i32(r + 12);
+    const int boundary = (seq_len % (uint32_t)cr) == 0;
+    int ok = (wl >= 0 && wl < num_state_rows);
+    if (boundary) {
+      for (int i = 0; i < W; ++i) {
+        /* every window entry is in the state once the token is written */
+        src[i] = (cr == 4) ? c4_entry(i, W, 0, rp0, rp1, hd) : c128_entry(i, W, 0, rp0, hd);
+        if (cr == 4 && seq_len == 4 && i < 4) continue;
+        if (src[i].row < 0 || src[i].row >= num_state_rows) ok = 0;
+      }
+    }
+    if (!ok) {
+      err |= ERR_RECORD;
+      continue;
+    }
+    memcpy((uint8_t*)state + (size_t)(wl * R * esz), (const uint8_t*)input + (size_t)((int64_t)b * R * esz),
+           (size_t)(R * esz));
+    if (boundary) pool_row(cr, is_bf16, hd, src, seq_len, state, input, ape, o);
+  }
+  free(src);
+  return err;
+}

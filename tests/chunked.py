@@ -1,0 +1,121 @@
+"""Drive a sequence of prefill chunks and decode steps through a back end.
+
+A back end is any object with the five calls (plan_prefill, compress, write,
+plan_decode, decode) in the oracle's numpy calling convention; the CPU
+oracle is one, the HIP library (wrapped for numpy) is the other.  The driver
+records every emitted compressed row as {(request, seq_len): row} so that a
+test can compare it with the brute-force window over the whole sequence.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+WINDOW = {4: 8, 128: 128}
+
+
+def nan_state(num_rows, R, dtype):
+    if dtype == "bf16":
+        return np.full((num_rows, R), 0x7FC0, np.uint16)
+    return np.full((num_rows, R), np.nan, np.float32)
+
+
+def run_chunked(backend, cr, hd, dtype, seqs, chunks, decode_steps, state_index, num_slots, ape, state=None):
+    """seqs[b]: the request's whole input sequence [L_b, R]; chunks[b]: list of extend lengths
+    (prefill rounds, request b takes part in round r if it has an r-th chunk); then
+    ``decode_steps`` single-token steps for every request.  Returns (emitted, state)."""
+    B = len(seqs)
+    R = seqs[0].shape[1]
+    W = WINDOW[cr]
+    if state is None:
+        state = nan_state(num_slots * W, R, dtype)
+    length = [0] * B
+    emitted = {}
+    rounds = max(len(c) for c in chunks)
+    for r in range(rounds):
+        active = [b for b in range(B) if r < len(chunks[b])]
+        if not active:
+            continue
+        e = np.array([chunks[b][r] for b in active], np.int32)
+        s = np.array([length[b] + chunks[b][r] for b in active], np.int32)
+        idx = np.array([state_index[b] for b in active], np.int32)
+        inp = np.concatenate([seqs[b][length[b]:length[b] + chunks[b][r]] for b in active])
+        num_q = int(e.sum())
+        cap_c = min(num_q, num_q // cr + len(active))
+        cap_w = min(num_q, len(active) * (W - 1))
+        pc, pw, counts = backend.plan_prefill(cr, s, e, idx, state.shape[0], num_q, cap_c, cap_w)
+        assert counts[2] == 0, counts
+        out, err = backend.compress(cr, hd, state, inp, ape, pc, int(counts[0]))
+        assert err == 0
+        state = backend.write(cr, hd, state, inp, pw, int(counts[1]))
+        # map each record back to its request through the ragged offsets
+        base = np.concatenate([[0], np.cumsum(e)])
+        recs = np.ascontiguousarray(pc[: counts[0]]).view("<u4").reshape(-1, 4)
+        for k in range(int(counts[0])):
+            seq_len = int(recs[k, 0])
+            ragged = int(recs[k, 1]) & 0xFFFFFF
+            a = int(np.searchsorted(base, ragged, side="right") - 1)
+            key = (active[a], seq_len)
+            assert key not in emitted, key
+            emitted[key] = out[k].copy()
+        for b in active:
+            length[b] += chunks[b][r]
+    for _ in range(decode_steps):
+        s = np.array([length[b] + 1 for b in range(B)], np.int32)
+        idx = np.asarray(state_index, np.int32)
+        inp = np.stack([seqs[b][length[b]] for b in range(B)])
+        pd, status = backend.plan_decode(cr, s, idx, state.shape[0])
+        assert status == 0
+        out, state, err = backend.decode(cr, hd, state, inp, ape, pd)
+        assert err == 0
+        for b in range(B):
+            if s[b] % cr == 0:
+                key = (b, int(s[b]))
+                assert key not in emitted, key
+                emitted[key] = out[b].copy()
+            else:
+                assert np.all(out[b] == 0), "non-boundary decode row must be zero"
+            length[b] += 1
+    return emitted, state
+
+
+class OracleBackend:
+    """The CPU oracle in the driver's calling convention."""
+
+    def __init__(self, oracle):
+        self.o = oracle
+
+    def plan_prefill(self, cr, s, e, idx, rows, num_q, cap_c, cap_w):
+        return self.o.plan_prefill(cr, s, e, idx, rows, num_q, cap_c, cap_w)
+
+    def compress(self, cr, hd, state, inp, ape, pc, num_c):
+        return self.o.compress(cr, hd, state, inp, ape, pc, num_c)
+
+    def write(self, cr, hd, state, inp, pw, num_w):
+        state = state.copy()
+        assert self.o.write(cr, hd, state, inp, pw, num_w) == 0
+        return state
+
+    def plan_decode(self, cr, s, idx, rows):
+        return self.o.plan_decode(cr, s, idx, rows)
+
+    def decode(self, cr, hd, state, inp, ape, pd):
+        state = state.copy()
+        out, err = self.o.decode(cr, hd, state, inp, ape, pd)
+        return out, state, err
+
+
+def as_float(a, dtype):
+    if dtype == "bf16":
+        return (np.asarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.asarray(a, np.float32).astype(np.float64)
+
+
+def random_split(rng, L, max_chunks, min_len=1):
+    """Split L tokens into at most max_chunks positive pieces."""
+    n = int(rng.integers(1, max_chunks, endpoint=True))
+    n = min(n, L)
+    if n == 1:
+        return [L]
+    cuts = np.sort(rng.choice(np.arange(1, L), size=n - 1, replace=False))
+    pieces = np.diff(np.concatenate([[0], cuts, [L]]))
+    return [int(x) for x in pieces]

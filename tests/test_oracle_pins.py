@@ -1,0 +1,378 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+* closed-form plan counts and record fields written in a second, independent
+  form (ring-slot view, "positions the next window needs");
+* worked examples derived by hand from the pages (tests/golden/);
+* pooling identities: equal scores give the mean, a dominant score selects
+  its kv row, a two-value closed form, convexity, and agreement with a
+  library softmax (torch, float64, CPU);
+* chunking invariance: any split of a request into prefill chunks and decode
+  steps emits exactly the rows that the brute-force window definition gives
+  over the whole sequence, from a NaN-filled state (a read of a slot that was
+  never written shows up as NaN);
+* decode at length s equals a one-token prefill at the same length;
+* error words and padding.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import brute
+from sparse_attention_kv_plan_amd import workloads as wl
+from tests.chunked import OracleBackend, as_float, nan_state, random_split, run_chunked
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+W = {4: 8, 128: 128}
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------
+# plans
+# --------------------------------------------------------------------------
+
+def _single(cr, p0, e, idx=0, slots=1):
+    s = p0 + e
+    cap_c, cap_w = oracle.capacities(cr, 1, e)
+    pc, pw, counts = oracle.plan_prefill(cr, [s], [e], [idx], slots * W[cr], e, cap_c, cap_w)
+    assert counts[2] == 0
+    return pc, pw, counts
+
+
+@pytest.mark.parametrize("cr,limit,step", [(4, 40, 1), (128, 400, 7)])
+def test_plan_counts_closed_form(cr, limit, step):
+    """num_c = multiples of cr in (p0, s]; W records = the chunk's positions that the first
+    window closing after s needs (that window covers [s' - W, s'), s' = next multiple of cr above s)."""
+    for p0 in range(0, limit, step):
+        for e in range(1, limit - p0 + 1, step):
+            s = p0 + e
+            _, pw, counts = _single(cr, p0, e)
+            assert counts[0] == s // cr - p0 // cr
+            nxt = (s // cr + 1) * cr
+            need = [p for p in range(p0, s) if p >= nxt - W[cr]]
+            got = [p0 + int(r) for r in oracle.unpack_w(pw[: counts[1]])[:, 0]]
+            assert got == need, (p0, e)
+
+
+@pytest.mark.parametrize("cr", [4, 128])
+def test_plan_record_fields_ring_view(cr):
+    """Every record, checked against the ring-slot view of the state: a request's ring holds
+    position p at row index*W + p % W (W = 8 for ratio 4, 128 for ratio 128)."""
+    rng = np.random.default_rng(7)
+    for _ in range(30):
+        B = int(rng.integers(1, 9))
+        p0 = rng.integers(0, 3 * W[cr], size=B)
+        e = rng.integers(1, 3 * W[cr], size=B)
+        s = p0 + e
+        idx = rng.permutation(16)[:B]
+        num_q = int(e.sum())
+        cap_c, cap_w = oracle.capacities(cr, B, num_q)
+        pc, pw, counts = oracle.plan_prefill(cr, s, e, idx, 16 * W[cr], num_q, cap_c, cap_w)
+        assert counts[2] == 0
+        base = np.concatenate([[0], np.cumsum(e)])
+        C = oracle.unpack_c(pc[: counts[0]])
+        for seq_len, ragged, blen, rp0, rp1 in C:
+            b = int(np.searchsorted(base, ragged, side="right") - 1)
+            pos = seq_len - 1
+            assert seq_len % cr == 0 and p0[b] <= pos < s[b] and ragged - base[b] == pos - p0[b]
+            # entries of the window [seq_len - W, seq_len) that precede the chunk
+            assert blen == max(0, p0[b] - (seq_len - W[cr]))
+            if cr == 4:
+                # the 4 entries after the overlap live in page rp1, the overlap block in rp0
+                for q in range(max(seq_len - 4, 0), seq_len):
+                    assert rp1 * 4 + q % 4 == idx[b] * 8 + q % 8
+                for q in range(max(seq_len - 8, 0), seq_len - 4):
+                    assert rp0 * 4 + q % 4 == idx[b] * 8 + q % 8
+            else:
+                assert rp0 == rp1 == idx[b]
+        # records come request by request, positions ascending
+        assert np.all(np.diff(C[:, 1]) > 0)
+        Wr = oracle.unpack_w(pw[: counts[1]])
+        assert np.all(np.diff(Wr[:, 0]) > 0)
+        for ragged, loc in Wr:
+            b = int(np.searchsorted(base, ragged, side="right") - 1)
+            pos = p0[b] + ragged - base[b]
+            assert loc == idx[b] * W[cr] + pos % W[cr]
+
+
+def test_golden_c4_prefill():
+    g = _golden("plan_c4_prefill_two_requests.json")
+    pc, pw, counts = oracle.plan_prefill(4, g["seq_lens"], g["extend_lens"], g["state_index"], 4 * 8, g["num_q"],
+                                         16, 16)
+    assert counts.tolist() == [len(g["plan_c"]), len(g["plan_w"]), 0, 0]
+    assert oracle.unpack_c(pc[: counts[0]]).tolist() == g["plan_c"]
+    assert oracle.unpack_w(pw[: counts[1]]).tolist() == g["plan_w"]
+    assert np.all(pc[counts[0]:] == 0xFF) and np.all(pw[counts[1]:] == 0xFF)
+
+
+def test_golden_c128_prefill():
+    g = _golden("plan_c128_prefill_two_requests.json")
+    pc, pw, counts = oracle.plan_prefill(128, g["seq_lens"], g["extend_lens"], g["state_index"], 2 * 128,
+                                         g["num_q"], 8, 256)
+    assert oracle.unpack_c(pc[: counts[0]]).tolist() == g["plan_c"]
+    Wr = oracle.unpack_w(pw[: counts[1]]).tolist()
+    first, last, n = g["plan_w_first_last_count"]
+    assert Wr[0] == first and Wr[-1] == last and len(Wr) == n
+    assert Wr[-2:] == g["plan_w_request1"]
+
+
+def test_golden_decode():
+    g = _golden("plan_decode_examples.json")
+    for c in g["cases"]:
+        cr = c["compress_ratio"]
+        pd, status = oracle.plan_decode(cr, [c["seq_len"]], [c["state_index"]], 16 * W[cr])
+        assert status == 0
+        assert oracle.unpack_d(pd).tolist()[0] == c["record"], c
+
+
+def test_plan_errors_and_padding():
+    # extend > seq_len
+    pc, pw, counts = oracle.plan_prefill(4, [3, 8], [4, 4], [0, 1], 16, 8, 6, 8)
+    assert counts.tolist() == [0, 0, 1, 0] and np.all(pc == 0xFF) and np.all(pw == 0xFF)
+    # sum of extends != num_q
+    _, _, counts = oracle.plan_prefill(4, [8, 8], [4, 4], [0, 1], 16, 9, 6, 8)
+    assert counts.tolist() == [0, 0, 2, 0]
+    # state index outside the buffer (2 rings of 8 rows)
+    _, _, counts = oracle.plan_prefill(4, [8, 8], [4, 4], [0, 2], 16, 8, 6, 8)
+    assert counts.tolist() == [0, 0, 4, 0]
+    # capacity too small
+    _, _, counts = oracle.plan_prefill(4, [64], [64], [0], 8, 64, 15, 8)
+    assert counts.tolist() == [0, 0, 8, 0]
+    # host-checkable argument errors are rejected outright
+    with pytest.raises(oracle.OracleError):
+        oracle.plan_prefill(5, [8], [8], [0], 8, 8, 4, 4)
+    with pytest.raises(oracle.OracleError):
+        oracle.plan_prefill(4, [8], [8], [0], 8, 0, 4, 4)
+    pd, status = oracle.plan_decode(4, [0, 5], [0, 1], 16)
+    assert status == 1 and np.all(pd == 0xFF)
+
+
+# --------------------------------------------------------------------------
+# pooling identities
+# --------------------------------------------------------------------------
+
+def _one_row_prefill(cr, hd, inp, ape, state=None):
+    """Prefill one request from position 0 with the given rows; return every pooled row."""
+    L = inp.shape[0]
+    cap_c, cap_w = oracle.capacities(cr, 1, L)
+    pc, pw, counts = oracle.plan_prefill(cr, [L], [L], [0], W[cr], L, cap_c, cap_w)
+    if state is None:
+        state = nan_state(W[cr], inp.shape[1], "f32")
+    out, err = oracle.compress(cr, hd, state, inp, ape, pc, counts[0])
+    assert err == 0
+    return out[: counts[0]], oracle.unpack_c(pc[: counts[0]])
+
+
+@pytest.mark.parametrize("cr", [4, 128])
+def test_equal_scores_give_mean(cr):
+    hd = 3
+    rng = np.random.default_rng(1)
+    L = 3 * cr
+    R = wl.ROW_MULT[cr] * hd
+    inp = rng.standard_normal((L, R)).astype(np.float32)
+    score_cols = slice(2 * hd, 4 * hd) if cr == 4 else slice(hd, 2 * hd)
+    inp[:, score_cols] = 0.75
+    ape = np.zeros((W[cr], hd), np.float32)
+    out, C = _one_row_prefill(cr, hd, inp, ape)
+    for k, (seq_len, *_rest) in enumerate(C):
+        if cr == 4:
+            cur = inp[seq_len - 4:seq_len, hd:2 * hd].astype(np.float64)
+            if seq_len == 4:
+                mean = cur.mean(axis=0)
+            else:
+                prev = inp[seq_len - 8:seq_len - 4, 0:hd].astype(np.float64)
+                mean = np.concatenate([prev, cur]).mean(axis=0)
+        else:
+            mean = inp[seq_len - 128:seq_len, 0:hd].astype(np.float64).mean(axis=0)
+        np.testing.assert_allclose(out[k], mean, rtol=1e-14, atol=1e-14)
+
+
+@pytest.mark.parametrize("cr", [4, 128])
+def test_dominant_score_selects_its_row(cr):
+    hd = 2
+    rng = np.random.default_rng(2)
+    L = 2 * cr
+    R = wl.ROW_MULT[cr] * hd
+    inp = rng.standard_normal((L, R)).astype(np.float32)
+    ape = (0.1 * rng.standard_normal((W[cr], hd))).astype(np.float32)
+    # position 2*cr - 3 dominates the row closing at 2*cr (exp(-1000) is exactly 0 in float64)
+    p = 2 * cr - 3
+    if cr == 4:
+        inp[p, 3 * hd:4 * hd] = 1000.0  # current-block score quarter
+    else:
+        inp[p, hd:2 * hd] = 1000.0
+    out, C = _one_row_prefill(cr, hd, inp, ape)
+    k = [int(x) for x in C[:, 0]].index(2 * cr)
+    kv = inp[p, hd:2 * hd] if cr == 4 else inp[p, 0:hd]
+    assert np.array_equal(out[k], kv.astype(np.float64))
+
+
+def test_two_value_closed_form():
+    g = _golden("pool_two_value.json")
+    hd = 1
+    inp = np.zeros((4, 4), np.float32)
+    inp[:, 1] = g["kv"]       # kv quarter of the current block
+    inp[:, 3] = g["scores"]   # score quarter
+    inp[:, 0] = 1e6           # overlap quarters must not matter at seq_len 4
+    inp[:, 2] = 50.0
+    ape = np.zeros((8, 1), np.float32)
+    out, _ = _one_row_prefill(4, hd, inp, ape)
+    assert abs(out[0, 0] - g["expected"]) < 1e-6
+
+
+@pytest.mark.parametrize("cr", [4, 128])
+def test_convexity(cr):
+    hd = 4
+    rng = np.random.default_rng(3)
+    L = 4 * cr
+    R = wl.ROW_MULT[cr] * hd
+    inp = (3 * rng.standard_normal((L, R))).astype(np.float32)
+    ape = rng.standard_normal((W[cr], hd)).astype(np.float32)
+    out, C = _one_row_prefill(cr, hd, inp, ape)
+    for k, row in enumerate(C):
+        s = int(row[0])
+        if cr == 4:
+            kv = [inp[q, hd:2 * hd] for q in range(s - 4, s)]
+            if s > 4:
+                kv += [inp[q, 0:hd] for q in range(s - 8, s - 4)]
+        else:
+            kv = [inp[q, 0:hd] for q in range(s - 128, s)]
+        kv = np.array(kv, np.float64)
+        assert np.all(out[k] >= kv.min(axis=0) - 1e-12) and np.all(out[k] <= kv.max(axis=0) + 1e-12)
+
+
+def test_c128_matches_library_softmax():
+    """The c128 pool equals torch.softmax over the window (float64, CPU) applied to kv."""
+    torch = pytest.importorskip("torch")
+    hd = 16
+    rng = np.random.default_rng(4)
+    L = 3 * 128 + 17
+    inp_f = rng.standard_normal((L, 2 * hd)).astype(np.float32)
+    inp_f[:, hd:] *= 2
+    inp = wl.to_bf16_bits(inp_f)
+    ape = wl.to_bf16_bits(0.1 * rng.standard_normal((128, hd)).astype(np.float32))
+    out, C = _one_row_prefill(128, hd, inp, ape, state=nan_state(128, 2 * hd, "bf16"))
+    x = torch.from_numpy(as_float(inp, "bf16"))
+    a = torch.from_numpy(as_float(ape, "bf16"))
+    for k, row in enumerate(C):
+        s = int(row[0])
+        win = x[s - 128:s]
+        wts = torch.softmax(win[:, hd:] + a, dim=0)
+        ref = (wts * win[:, :hd]).sum(dim=0).numpy()
+        np.testing.assert_allclose(out[k], ref, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# chunking invariance against the brute-force definition
+# --------------------------------------------------------------------------
+
+def _check_against_brute(cr, hd, dtype, seqs, emitted, ape):
+    apef = as_float(ape, dtype).tolist()
+    seen = set()
+    for b, seq in enumerate(seqs):
+        seqf = as_float(seq, dtype).tolist()
+        for s in range(cr, len(seq) + 1, cr):
+            assert (b, s) in emitted, ("missing row", b, s)
+            seen.add((b, s))
+            ref = brute.pooled_row(cr, hd, seqf, apef, s)
+            np.testing.assert_allclose(emitted[(b, s)], ref, rtol=1e-12, atol=1e-12, err_msg=str((b, s)))
+    assert set(emitted) == seen
+
+
+@pytest.mark.parametrize("cr,dtype,trial", [(4, "f32", 0), (4, "bf16", 1), (4, "f32", 2), (128, "bf16", 3),
+                                            (128, "f32", 4)])
+def test_chunking_invariance(cr, dtype, trial):
+    rng = np.random.default_rng(100 + trial)
+    hd = 2
+    B = 3
+    R = wl.ROW_MULT[cr] * hd
+    Wn = W[cr]
+    seqs, chunks = [], []
+    decode_steps = 3 * cr // 2 if cr == 4 else 140
+    for b in range(B):
+        L = int(rng.integers(1, 5 * Wn))
+        x = rng.standard_normal((L + decode_steps, R)).astype(np.float32)
+        seqs.append(wl.to_bf16_bits(x) if dtype == "bf16" else x)
+        chunks.append(random_split(rng, L, 6))
+    ape_f = (0.1 * rng.standard_normal((Wn, hd))).astype(np.float32)
+    ape = wl.to_bf16_bits(ape_f) if dtype == "bf16" else ape_f
+    idx = rng.permutation(5)[:B]
+    emitted, _ = run_chunked(OracleBackend(oracle), cr, hd, dtype, seqs, chunks, decode_steps, idx, 5, ape)
+    _check_against_brute(cr, hd, dtype, seqs, emitted, ape)
+
+
+@pytest.mark.parametrize("cr", [4, 128])
+def test_decode_equals_one_token_prefill(cr):
+    rng = np.random.default_rng(5)
+    hd = 3
+    R = wl.ROW_MULT[cr] * hd
+    B = 6
+    idx = rng.permutation(B)
+    rows = B * W[cr]
+    state0 = rng.standard_normal((rows, R)).astype(np.float32)
+    ape = rng.standard_normal((W[cr], hd)).astype(np.float32)
+    s = np.array([cr, 2 * cr, 3 * cr - 1, 5 * cr, cr + 1, 7 * cr], np.int32)
+    inp = rng.standard_normal((B, R)).astype(np.float32)
+    # decode path
+    st_d = state0.copy()
+    pd, status = oracle.plan_decode(cr, s, idx, rows)
+    out_d, err = oracle.decode(cr, hd, st_d, inp, ape, pd)
+    assert status == 0 and err == 0
+    # prefill path: compress, then write
+    st_p = state0.copy()
+    pc, pw, counts = oracle.plan_prefill(cr, s, np.ones(B, np.int32), idx, rows, B, B, B)
+    out_p, err = oracle.compress(cr, hd, st_p, inp, ape, pc, counts[0])
+    assert err == 0 and oracle.write(cr, hd, st_p, inp, pw, counts[1]) == 0
+    # Decode always stores the new token.  Prefill stores only what a later window needs: at a
+    # ratio-128 boundary the closing token belongs to no later window, so that one row differs.
+    D = oracle.unpack_d(pd)
+    skipped = [int(D[b, 1]) for b in range(B) if cr == 128 and s[b] % cr == 0]
+    keep = np.setdiff1d(np.arange(rows), skipped)
+    assert np.array_equal(st_d[keep], st_p[keep])
+    assert np.array_equal(st_p[skipped], state0[skipped])
+    assert counts[1] == B - len(skipped)
+    C = oracle.unpack_c(pc[: counts[0]])
+    for k, row in enumerate(C):
+        b = int(row[1])
+        np.testing.assert_allclose(out_p[k], out_d[b], rtol=1e-14, atol=1e-14)
+    boundary = s % cr == 0
+    assert counts[0] == boundary.sum()
+    assert np.all(out_d[~boundary] == 0.0)
+
+
+def test_write_and_decode_touch_one_row():
+    rng = np.random.default_rng(6)
+    hd = 2
+    for cr in (4, 128):
+        R = wl.ROW_MULT[cr] * hd
+        rows = 3 * W[cr]
+        st = rng.standard_normal((rows, R)).astype(np.float32)
+        before = st.copy()
+        inp = rng.standard_normal((1, R)).astype(np.float32)
+        pd, _ = oracle.plan_decode(cr, [cr + 3], [1], rows)
+        oracle.decode(cr, hd, st, inp, np.zeros((W[cr], hd), np.float32), pd)
+        wloc = int(oracle.unpack_d(pd)[0, 1])
+        assert wloc == 1 * W[cr] + (cr + 2) % W[cr]
+        changed = np.nonzero(np.any(st != before, axis=1))[0].tolist()
+        assert changed == [wloc] and np.array_equal(st[wloc], inp[0])
+
+
+def test_consumer_record_errors():
+    hd = 2
+    R = 4 * hd
+    st = np.zeros((8, R), np.float32)
+    inp = np.zeros((4, R), np.float32)
+    bad_w = np.zeros((1, 8), np.uint8)
+    bad_w.view("<u4")[0, 0] = 9  # ragged id beyond the input
+    assert oracle.write(4, hd, st, inp, bad_w, 1) == 16
+    bad_c = np.zeros((1, 16), np.uint8)
+    bad_c.view("<u4")[0] = [8, 3 | (2 << 24), 0, 5]  # read page 5 lies outside 8 state rows
+    _, err = oracle.compress(4, hd, st, inp, np.zeros((8, hd), np.float32), bad_c, 1)
+    assert err == 16
