@@ -1,0 +1,269 @@
+"""Benchmark of the KV-compressor hot path on one MI355X.
+
+One step is one pass of the whole path over the named workloads, all through
+the C ABI on one HIP stream:
+  * ratio-4 mixed chunked prefill: 64 requests, prefixes in [0, 65536],
+    extends in [1, 4096] (~131k tokens), bf16, head_dim 512:
+    kvc_plan_prefill -> kvc_compress_c4 -> kvc_write;
+  * ratio-128 prefill over the same ragged batch:
+    kvc_plan_prefill -> kvc_compress_c128 -> kvc_write;
+  * ratio-4 decode, batch 256: kvc_plan_decode -> kvc_decode_c4;
+  * ratio-128 decode, batch 1024: kvc_plan_decode -> kvc_decode_c128.
+Inputs are synthetic (seeded normals), resident in HBM before timing starts.
+
+value = tokens consumed per second (each compressor pass counts its tokens,
+decode one token per request).  The roofline object reports the dominant
+kernel (kvc_compress_c4 on the prefill batch): algorithmic bytes per launch
+divided by its average duration, timed with HIP events on the launch stream
+over the timed region.  cpu_baseline times the float64 C oracle on one host
+core over the same step.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "compressed tokens/s and achieved HBM GB/s (% of peak), c4 & c128 prefill+decode"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=2)
+    return ap.parse_args()
+
+
+def algorithmic_bytes_compress(cr, hd, esize, seq_lens_of_rows):
+    """Bytes the pool must move: every kv and score element of the kept window entries once,
+    the fp32 output row, the 16-byte record; ape once per launch."""
+    W = 8 if cr == 4 else 128
+    kept = np.where((cr == 4) & (seq_lens_of_rows == 4), 4, W)
+    per_row = kept * 2 * hd * esize + hd * 4 + 16
+    return int(per_row.sum()) + W * hd * esize
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU: the compressor has no multi-GPU path in this library "
+              "(requests shard across GPUs with no exchange); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sparse_attention_kv_plan_amd import kvc
+    from sparse_attention_kv_plan_amd import workloads as wl
+
+    kvc.load(build_if_missing=True)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    t0 = time.time()
+    log("generating workloads ...")
+    p4, p128 = wl.config5(4), wl.config5(128)
+    d4, d128 = wl.config3(), wl.config4()
+    log("workloads ready in %.1f s: prefill num_q=%d, decode B=%d/%d" % (time.time() - t0, p4.num_q, d4.B, d128.B))
+
+    class Prefill:
+        def __init__(self, w):
+            self.w = w
+            self.s, self.e, self.idx = to_dev(w.seq_lens), to_dev(w.extend_lens), to_dev(w.state_index)
+            self.inp, self.ape, self.state = to_dev(w.input), to_dev(w.ape), to_dev(w.state)
+            self.plan_c, self.plan_w, self.counts = kvc.alloc_prefill_plan(w.cr, w.B, w.num_q, dev)
+            self.out = torch.empty((self.plan_c.shape[0], w.hd), dtype=torch.float32, device=dev)
+
+        def plan(self):
+            kvc.plan_prefill(self.w.cr, self.s, self.e, self.idx, self.w.num_state_rows, self.w.num_q,
+                             self.plan_c, self.plan_w, self.counts)
+
+        def compress(self):
+            kvc.compress(self.w.cr, self.w.hd, self.state, self.inp, self.ape, self.plan_c, self.counts, self.out)
+
+        def write(self):
+            kvc.write(self.w.cr, self.w.hd, self.state, self.inp, self.plan_w, self.counts)
+
+    class Decode:
+        def __init__(self, w):
+            self.w = w
+            self.s, self.idx = to_dev(w.seq_lens), to_dev(w.state_index)
+            self.inp, self.ape, self.state = to_dev(w.input), to_dev(w.ape), to_dev(w.state)
+            self.plan_d = torch.empty((w.B, kvc.D_BYTES), dtype=torch.uint8, device=dev)
+            self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+            self.out = torch.empty((w.B, w.hd), dtype=torch.float32, device=dev)
+
+        def plan(self):
+            kvc.plan_decode(self.w.cr, self.s, self.idx, self.w.num_state_rows, self.plan_d, self.status)
+
+        def decode(self):
+            kvc.decode(self.w.cr, self.w.hd, self.state, self.inp, self.ape, self.plan_d, self.out, self.status)
+
+    P4, P128, D4, D128 = Prefill(p4), Prefill(p128), Decode(d4), Decode(d128)
+    launches = [("plan_prefill c4", P4.plan), ("compress_c4", P4.compress), ("write c4", P4.write),
+                ("plan_prefill c128", P128.plan), ("compress_c128", P128.compress), ("write c128", P128.write),
+                ("plan_decode c4", D4.plan), ("decode_c4", D4.decode),
+                ("plan_decode c128", D128.plan), ("decode_c128", D128.decode)]
+    dominant = "compress_c4"
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        for name, f in launches:
+            if ev is not None and name == dominant:
+                ev[0].record(stream)
+                f()
+                ev[1].record(stream)
+            else:
+                f()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps ----
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for k in range(args.steps):
+        step(kev[k])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = start.elapsed_time(end)
+    ms_per_step = ms_total / args.steps
+    dom_us = float(np.mean([a.elapsed_time(b) for a, b in kev])) * 1e3
+
+    # per-kernel breakdown (separate, untimed pass; events around every launch)
+    bev = {name: [] for name, _ in launches}
+    for _ in range(5):
+        for name, f in launches:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            f()
+            b.record(stream)
+            bev[name].append((a, b))
+    torch.cuda.synchronize()
+    kernels_us = {n: round(float(np.median([a.elapsed_time(b) for a, b in v])) * 1e3, 2) for n, v in bev.items()}
+
+    # sanity: no device-side errors, plans as sized
+    for P in (P4, P128):
+        c = P.counts.cpu().tolist()
+        assert c[2] == 0 and c[3] == 0, ("device error", c)
+    for D in (D4, D128):
+        assert int(D.status.item()) == 0
+
+    n_c4 = int(P4.counts[0].item())
+    rows_seq = P4.plan_c[:n_c4].cpu().numpy().view("<u4").reshape(-1, 4)[:, 0].astype(np.int64)
+    dom_bytes = algorithmic_bytes_compress(4, p4.hd, p4.esize, rows_seq)
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+
+    tokens = p4.num_q + p128.num_q + d4.B + d128.B
+    value = tokens / (ms_per_step * 1e-3)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "c4+c128 mixed chunked prefill (64 req, prefix U[0,65536], extend U[1,4096], "
+                        "%d tokens, head_dim 512) + c4 decode B=256 + c128 decode B=1024" % p4.num_q,
+            "prefill_tokens": p4.num_q,
+            "decode_batch": [d4.B, d128.B],
+            "head_dim": 512,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": dominant,
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": dom_bytes,
+            "avg_launch_us": round(dom_us, 2),
+        },
+        "kernels_us": kernels_us,
+        "wall_s_timed": round(wall, 3),
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(p4, p128, d4, d128, tokens, args.cpu_reps)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(p4, p128, d4, d128, tokens, reps):
+    """The float64 C oracle over one whole step (same workloads, host copies), one core."""
+    import oracle
+
+    oracle.build(force=False)
+
+    def one_step():
+        for w in (p4, p128):
+            cap_c, cap_w = oracle.capacities(w.cr, w.B, w.num_q)
+            pc, pw, counts = oracle.plan_prefill(w.cr, w.seq_lens, w.extend_lens, w.state_index, w.num_state_rows,
+                                                 w.num_q, cap_c, cap_w)
+            oracle.compress(w.cr, w.hd, w.state, w.input, w.ape, pc, counts[0])
+            st = w.state.copy()
+            oracle.write(w.cr, w.hd, st, w.input, pw, counts[1])
+        for w in (d4, d128):
+            pd, _ = oracle.plan_decode(w.cr, w.seq_lens, w.state_index, w.num_state_rows)
+            st = w.state.copy()
+            oracle.decode(w.cr, w.hd, st, w.input, w.ape, pd)
+
+    times = []
+    for _ in range(reps):
+        t = time.perf_counter()
+        one_step()
+        times.append(time.perf_counter() - t)
+    sec = float(np.median(times))
+    cpu = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(tokens / sec, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "the whole step (both prefills, both decodes), median of %d runs, %.2f s each; %s"
+                      % (reps, sec, cpu)}
+
+
+if __name__ == "__main__":
+    main()

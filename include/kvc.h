@@ -1,0 +1,237 @@
+/*
+ * kvc.h - C ABI of the MI355X (gfx950) KV compressor.
+ *
+ * The compressor turns each block of `compress_ratio` tokens of a request
+ * into one compressed kv row.  Ratio 4 pools a window of 8 tokens (the block
+ * being closed plus the block before it); ratio 128 pools the 128 tokens of
+ * the block.  Every output channel d is
+ *
+ *     out[d] = sum_i exp(t_i[d]) kv_i[d] / sum_i exp(t_i[d]),
+ *     t_i[d] = score_i[d] + ape[i][d]
+ *
+ * over the window entries i (c4.cuh page, c4_forward; compressor_v2.py page,
+ * _c128_compress_prefill_compress_kernel and _compress_forward_c128_fallback).
+ *
+ * Pages cited below: "c_plan.cuh" is
+ * sgl-project--sglang/python/sglang/jit_kernel/csrc/deepseek_v4/c_plan.cuh,
+ * "c4.cuh" is .../jit_kernel/csrc/deepseek_v4/c4.cuh and "compressor_v2.py"
+ * is .../srt/layers/attention/dsv4/compressor_v2.py.
+ *
+ * Conventions for every call
+ * --------------------------
+ *  - Pointers to tensors, plans, counts and status words are DEVICE pointers
+ *    (HBM of the current HIP device), 16-byte aligned.  Sizes are host ints.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every call only enqueues work on `stream`: it never synchronises, never
+ *    allocates and keeps no pointer after it returns.  The caller owns every
+ *    buffer and must keep it alive until the stream has run the work.
+ *  - Return value: KVC_OK, or KVC_EINVAL when a host-visible argument is bad
+ *    (nothing is enqueued), or KVC_EHIP when the launch failed.
+ *  - Errors in DEVICE data (lengths, indices, records) cannot be seen on the
+ *    host without a sync.  They are reported as bits in a device error word
+ *    (KVC_DERR_*), and the offending work is skipped, never performed out of
+ *    bounds.
+ *
+ * Data layout
+ * -----------
+ *  - dtype KVC_BF16 (bf16 bit patterns) or KVC_F32; `ape`, input and state
+ *    share the dtype.  head_dim (hd) is 128, 256 or 512.
+ *  - A ratio-4 row holds 4*hd elements laid out |kv overlap|kv|score
+ *    overlap|score| (c4.cuh, Compress4PrefillParams).  Window entries 0..3
+ *    (the previous block) use the two overlap quarters, entries 4..7 the
+ *    others.  A ratio-128 row holds 2*hd elements laid out |kv|score|.
+ *  - The input is the ragged batch [num_q, row] (requests back to back, each
+ *    request's new tokens in position order); decode input is [B, row].
+ *  - The state buffer is [num_state_rows, row].  Ratio 4: request slot `idx`
+ *    owns rows idx*8 .. idx*8+7, two pages of 4 rows, position p at page
+ *    idx*2 + ((p/4) & 1), row page*4 + p%4.  Ratio 128: slot `idx` owns the
+ *    page of rows idx*128 .. idx*128+127, position p at row idx*128 + p%128
+ *    (c_plan.cuh, plan_compress_prefill_legacy_kernel).
+ *  - `ape` is [8, hd] (ratio 4) or [128, hd] (ratio 128).
+ *  - Compressed output is float32 [rows, hd].
+ *
+ * Call order
+ * ----------
+ *  prefill chunk: kvc_plan_prefill -> kvc_compress_c4 | kvc_compress_c128 ->
+ *                 kvc_write (compress must read the state as it was before
+ *                 this chunk's writes: c4.cuh, flash_c4_prefill launches the
+ *                 compress kernel before the write kernel);
+ *  decode step:   kvc_plan_decode -> kvc_decode_c4 | kvc_decode_c128.
+ *  Plans depend only on lengths and indices, so one plan serves every layer.
+ *  The state indices of one call must be distinct.
+ */
+#ifndef KVC_H_
+#define KVC_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* host return codes */
+#define KVC_OK 0
+#define KVC_EINVAL (-1)
+#define KVC_EHIP (-2)
+
+/* device error bits (counts[2], counts[3] or *status) */
+#define KVC_DERR_EXTEND 1   /* prefill: extend_len <= 0 or > seq_len; decode: seq_len <= 0 */
+#define KVC_DERR_NUMQ 2     /* prefill: sum of extend_len != num_q */
+#define KVC_DERR_INDEX 4    /* state_index outside [0, num_state_rows / window) */
+#define KVC_DERR_CAPACITY 8 /* prefill: more C or W records than cap_c or cap_w */
+#define KVC_DERR_RECORD 16  /* a consumer met a record that points outside its buffers */
+
+/* limits */
+#define KVC_MAX_PREFILL_BATCH 1024
+#define KVC_MAX_DECODE_BATCH 65536
+#define KVC_MAX_TOKENS (1 << 24)
+
+typedef enum { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
+
+/* Compress record, 16 bytes: one per compressed row of a prefill chunk
+ * (c_plan.cuh, CompressPlan as filled by plan_compress_prefill_legacy and
+ * its translation kernel).  The row closes the window ending at token
+ * seq_len - 1; ragged_id is that token's row in the ragged input;
+ * buffer_len (0..127) counts the window entries that precede the chunk and
+ * are read from the state; the others are input rows ragged_id - (W-1) + i.
+ * read_page_1 is the page of position seq_len - 1, read_page_0 the page of
+ * position max(seq_len - 1 - ratio, 0).  The page's ragged id is 16 bits
+ * wide; here it takes bits 0..23 and buffer_len bits 24..31. */
+typedef struct kvc_plan_c {
+  uint32_t seq_len;
+  uint32_t ragged_blen; /* ragged_id | buffer_len << 24 */
+  int32_t read_page_0;
+  int32_t read_page_1;
+} kvc_plan_c;
+
+/* Write record, 8 bytes: copy input row ragged_id to state row write_loc
+ * (c_plan.cuh, WritePlan). */
+typedef struct kvc_plan_w {
+  uint32_t ragged_id;
+  int32_t write_loc;
+} kvc_plan_w;
+
+/* Decode record, 16 bytes (c_plan.cuh, DecodePlan via
+ * plan_compress_decode_legacy_kernel): the new token is position
+ * seq_len - 1 and goes to state row write_loc; read pages as for kvc_plan_c. */
+typedef struct kvc_plan_d {
+  uint32_t seq_len;
+  int32_t write_loc;
+  int32_t read_page_0;
+  int32_t read_page_1;
+} kvc_plan_d;
+
+/* An invalid (padding) record has every byte 0xFF: seq_len == 0xFFFFFFFF
+ * for C and D records, ragged_id == 0xFFFFFFFF for W records. */
+
+/*
+ * kvc_plan_prefill - plan one ragged prefill chunk (c_plan.cuh,
+ * plan_compress_prefill_legacy and plan_compress_prefill_legacy_kernel;
+ * the device-built variant is plan_compress_prefill_kernel0).
+ *
+ * For request b (seq_len s, extend_len e, prefix p0 = s - e, new tokens at
+ * positions p0 .. s-1, ragged rows starting at the sum of earlier extends):
+ *  - position p emits a C record iff (p + 1) % ratio == 0;
+ *  - position p emits a W record iff p >= floor(s/ratio)*ratio - (ratio==4 ? 4 : 0),
+ *    i.e. the chunk's tokens that the next window still needs.
+ * Records are ordered request by request, positions ascending (the order of
+ * the pages' host loop); the build is deterministic.  Records [num_c, cap_c)
+ * and [num_w, cap_w) are filled with invalid records.
+ *
+ *  compress_ratio  4 or 128
+ *  batch           1 .. KVC_MAX_PREFILL_BATCH requests
+ *  num_q           batch .. KVC_MAX_TOKENS-1 rows in the ragged input
+ *  seq_lens, extend_lens, state_index   device int32 [batch]
+ *  num_state_rows  rows of the state buffer (0 .. INT32_MAX); a state index
+ *                  must lie in [0, num_state_rows / W), W = 8 or 128
+ *  plan_c, cap_c   device output, cap_c >= 0 records (never more than
+ *                  min(num_q, num_q/ratio + batch) are needed)
+ *  plan_w, cap_w   device output, cap_w >= 0 records (never more than
+ *                  min(num_q, batch*(W-1)) are needed)
+ *  counts          device int32 [4], written: num_c, num_w, device error
+ *                  bits of the plan, 0 (consumers OR their errors into
+ *                  counts[3]).  On any plan error num_c = num_w = 0 and every
+ *                  record is invalid, so the consumers do nothing.
+ */
+int kvc_plan_prefill(int compress_ratio, int batch, int num_q, const int32_t* seq_lens,
+                     const int32_t* extend_lens, const int32_t* state_index, int64_t num_state_rows,
+                     kvc_plan_c* plan_c, int cap_c, kvc_plan_w* plan_w, int cap_w, int32_t* counts,
+                     void* stream);
+
+/*
+ * kvc_plan_decode - plan one decode step, one record per request
+ * (c_plan.cuh, plan_compress_decode_legacy_kernel).  seq_lens are the
+ * lengths AFTER the new token.  A request with seq_len <= 0 or a state index
+ * out of range gets an invalid record; `status` (device int32 [1], may be
+ * NULL) receives the OR of the error bits.
+ *  batch 1 .. KVC_MAX_DECODE_BATCH.
+ */
+int kvc_plan_decode(int compress_ratio, int batch, const int32_t* seq_lens, const int32_t* state_index,
+                    int64_t num_state_rows, kvc_plan_d* plan_d, int32_t* status, void* stream);
+
+/*
+ * kvc_write - for each valid W record k < counts[1], copy input row
+ * ragged_id (all 4*hd or 2*hd elements, bit for bit) into state row
+ * write_loc (c4.cuh, c4_write; compressor_v2.py,
+ * _c128_compress_prefill_write_kernel).  Must run after the chunk's
+ * compress.  A record outside [0, num_q) x [0, num_state_rows) is skipped
+ * and sets KVC_DERR_RECORD in counts[3].
+ */
+int kvc_write(int compress_ratio, kvc_dtype dtype, int head_dim, void* state, int64_t num_state_rows,
+              const void* input, int num_q, const kvc_plan_w* plan_w, int cap_w, int32_t* counts, void* stream);
+
+/*
+ * kvc_compress_c4 - pool every valid C record k < counts[0] of a ratio-4
+ * plan into out[k] (float32 [cap_c, hd]; rows >= counts[0] are untouched).
+ * Window entry i (0..7) is state row (i < 4 ? read_page_0*4 + i :
+ * read_page_1*4 + i - 4) when i < buffer_len, else input row
+ * ragged_id - 7 + i.  When seq_len == 4 (the first block) entries 0..3 lie
+ * before the sequence and take no part (c4.cuh, c4_forward: kv 0,
+ * score -1e9, whose weight is exactly zero); their rows are not read.
+ * Reads the state as it was before this chunk's kvc_write.
+ * ape: [8, hd], same dtype as input and state.
+ */
+int kvc_compress_c4(kvc_dtype dtype, int head_dim, const void* state, int64_t num_state_rows, const void* input,
+                    int num_q, const void* ape, const kvc_plan_c* plan_c, int cap_c, int32_t* counts, float* out,
+                    void* stream);
+
+/*
+ * kvc_compress_c128 - as kvc_compress_c4 for ratio 128: entry i (0..127)
+ * is state row read_page_0*128 + i when i < buffer_len, else input row
+ * ragged_id - 127 + i (compressor_v2.py, _c128_compress_prefill_compress_kernel
+ * and _compress_forward_c128_fallback).  ape: [128, hd].
+ */
+int kvc_compress_c128(kvc_dtype dtype, int head_dim, const void* state, int64_t num_state_rows,
+                      const void* input, int num_q, const void* ape, const kvc_plan_c* plan_c, int cap_c,
+                      int32_t* counts, float* out, void* stream);
+
+/*
+ * kvc_decode_c4 - fused decode step for ratio 4 (c4.cuh, flash_c4_decode):
+ * for each request b, write input row b to state row write_loc; if
+ * seq_len % 4 == 0, pool the 8-entry window ending at the new token (read
+ * from the state after the write; first-block masking as in
+ * kvc_compress_c4) into out[b], else set out[b] to zeros.  An invalid
+ * record gives a zero row and no write.  A record pointing outside the state
+ * gives a zero row, no write, and KVC_DERR_RECORD in *status (status may be
+ * NULL; it is OR-ed, not cleared).  out: float32 [batch, hd].
+ */
+int kvc_decode_c4(kvc_dtype dtype, int head_dim, void* state, int64_t num_state_rows, const void* input,
+                  const void* ape, const kvc_plan_d* plan_d, int batch, int32_t* status, float* out, void* stream);
+
+/*
+ * kvc_decode_c128 - fused decode step for ratio 128 (compressor_v2.py,
+ * _c128_compress_decode_kernel): as kvc_decode_c4 with the 128-entry window
+ * of page read_page_0, pooled when seq_len % 128 == 0.
+ */
+int kvc_decode_c128(kvc_dtype dtype, int head_dim, void* state, int64_t num_state_rows, const void* input,
+                    const void* ape, const kvc_plan_d* plan_d, int batch, int32_t* status, float* out,
+                    void* stream);
+
+/* kvc_strerror - static text for a host return code or a device error bit. */
+const char* kvc_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H_ */

@@ -195,30 +195,34 @@ int oracle_plan_prefill(int cr, int B, int num_q, const int32_t* seq_lens, const
 /* plan decode                                                               */
 /* ------------------------------------------------------------------------ */
 
+/* Requests are independent in decode: a request with a bad length or index
+ * gets an invalid record, the others are planned as usual.  The error bits of
+ * the whole batch are OR-ed into status[0]. */
 int oracle_plan_decode(int cr, int B, const int32_t* seq_lens, const int32_t* state_index, int64_t num_state_rows,
                        uint8_t* plan_d, int32_t* status) {
-  if (bad_host_args(cr, B)) return -1;
+  if (cr != 4 && cr != 128) return -1;
+  if (B < 1 || B > 65536) return -1;
   if (num_state_rows < 0 || num_state_rows > INT32_MAX) return -1;
   if (!seq_lens || !state_index || !plan_d) return -1;
   const int W = window_of(cr);
   int err = 0;
   for (int b = 0; b < B; ++b) {
-    if (seq_lens[b] <= 0) err |= ERR_EXTEND;
-    if (state_index[b] < 0 || state_index[b] >= num_state_rows / W) err |= ERR_INDEX;
-  }
-  if (err) {
-    memset(plan_d, 0xFF, (size_t)B * 16);
-  } else {
-    for (int b = 0; b < B; ++b) {
-      const int64_t s = seq_lens[b], idx = state_index[b];
-      const int64_t pos1 = s - 1; /* the new token */
-      const int64_t pos0 = (pos1 - cr > 0) ? pos1 - cr : 0;
-      uint8_t* r = plan_d + (size_t)b * 16;
-      put_u32(r + 0, (uint32_t)s);
-      put_u32(r + 4, as_u32((int32_t)loc_of(cr, idx, pos1)));
-      put_u32(r + 8, as_u32((int32_t)page_of(cr, idx, pos0)));
-      put_u32(r + 12, as_u32((int32_t)page_of(cr, idx, pos1)));
+    const int64_t s = seq_lens[b], idx = state_index[b];
+    uint8_t* r = plan_d + (size_t)b * 16;
+    int bad = 0;
+    if (s <= 0) bad |= ERR_EXTEND;
+    if (idx < 0 || idx >= num_state_rows / W) bad |= ERR_INDEX;
+    err |= bad;
+    if (bad) {
+      memset(r, 0xFF, 16);
+      continue;
     }
+    const int64_t pos1 = s - 1; /* the new token */
+    const int64_t pos0 = (pos1 - cr > 0) ? pos1 - cr : 0;
+    put_u32(r + 0, (uint32_t)s);
+    put_u32(r + 4, as_u32((int32_t)loc_of(cr, idx, pos1)));
+    put_u32(r + 8, as_u32((int32_t)page_of(cr, idx, pos0)));
+    put_u32(r + 12, as_u32((int32_t)page_of(cr, idx, pos1)));
   }
   if (status) status[0] = err;
   return 0;

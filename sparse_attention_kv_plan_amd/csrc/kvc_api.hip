@@ -1,0 +1,142 @@
+// kvc_api.hip - the C entry points declared in include/kvc.h: host argument
+// checks, then one kernel launch each on the caller's stream.
+#include <stdint.h>
+
+#include "kvc.h"
+#include "kvc_launch.hpp"
+
+#define KVC_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool ratio_ok(int cr) { return cr == 4 || cr == 128; }
+bool dtype_ok(int dt) { return dt == KVC_F32 || dt == KVC_BF16; }
+bool hd_ok(int hd) { return hd == 128 || hd == 256 || hd == 512; }
+bool rows_ok(int64_t rows) { return rows >= 0 && rows <= INT32_MAX; }
+int status_of(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_EHIP; }
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+KVC_EXPORT int kvc_plan_prefill(int compress_ratio, int batch, int num_q, const int32_t* seq_lens,
+                                const int32_t* extend_lens, const int32_t* state_index, int64_t num_state_rows,
+                                kvc_plan_c* plan_c, int cap_c, kvc_plan_w* plan_w, int cap_w, int32_t* counts,
+                                void* stream) {
+  if (!ratio_ok(compress_ratio) || batch < 1 || batch > KVC_MAX_PREFILL_BATCH) return KVC_EINVAL;
+  if (num_q < batch || num_q >= KVC_MAX_TOKENS || cap_c < 0 || cap_w < 0 || !rows_ok(num_state_rows))
+    return KVC_EINVAL;
+  if (!aligned4(seq_lens) || !aligned4(extend_lens) || !aligned4(state_index) || !aligned4(counts))
+    return KVC_EINVAL;
+  if ((cap_c > 0 && !aligned16(plan_c)) || (cap_w > 0 && (plan_w == nullptr || (reinterpret_cast<uintptr_t>(plan_w) & 7u))))
+    return KVC_EINVAL;
+  kvc::PlanPrefillArgs a{seq_lens, extend_lens, state_index, num_state_rows, plan_c, plan_w, counts,
+                         batch,    num_q,       cap_c,       cap_w};
+  return status_of(kvc::launch_plan_prefill(compress_ratio, a, as_stream(stream)));
+}
+
+KVC_EXPORT int kvc_plan_decode(int compress_ratio, int batch, const int32_t* seq_lens, const int32_t* state_index,
+                               int64_t num_state_rows, kvc_plan_d* plan_d, int32_t* status, void* stream) {
+  if (!ratio_ok(compress_ratio) || batch < 1 || batch > KVC_MAX_DECODE_BATCH || !rows_ok(num_state_rows))
+    return KVC_EINVAL;
+  if (!aligned4(seq_lens) || !aligned4(state_index) || !aligned16(plan_d)) return KVC_EINVAL;
+  if (status != nullptr && !aligned4(status)) return KVC_EINVAL;
+  kvc::PlanDecodeArgs a{seq_lens, state_index, num_state_rows, plan_d, status, batch};
+  return status_of(kvc::launch_plan_decode(compress_ratio, a, as_stream(stream)));
+}
+
+KVC_EXPORT int kvc_write(int compress_ratio, kvc_dtype dtype, int head_dim, void* state, int64_t num_state_rows,
+                         const void* input, int num_q, const kvc_plan_w* plan_w, int cap_w, int32_t* counts,
+                         void* stream) {
+  if (!ratio_ok(compress_ratio) || !dtype_ok(dtype) || !hd_ok(head_dim) || !rows_ok(num_state_rows)) return KVC_EINVAL;
+  if (num_q < 0 || num_q >= KVC_MAX_TOKENS || cap_w < 0 || !aligned4(counts)) return KVC_EINVAL;
+  if (cap_w == 0) return KVC_OK;
+  if (!aligned16(state) || !aligned16(input) || plan_w == nullptr || (reinterpret_cast<uintptr_t>(plan_w) & 7u))
+    return KVC_EINVAL;
+  const int esize = dtype == KVC_BF16 ? 2 : 4;
+  const int row_vecs = (compress_ratio == 4 ? 4 : 2) * head_dim * esize / 16;
+  kvc::WriteArgs a{state, input, plan_w, counts, num_state_rows, num_q, cap_w, row_vecs};
+  return status_of(kvc::launch_write(a, as_stream(stream)));
+}
+
+namespace {
+
+int compress_common(bool c4, kvc_dtype dtype, int head_dim, const void* state, int64_t num_state_rows,
+                    const void* input, int num_q, const void* ape, const kvc_plan_c* plan_c, int cap_c,
+                    int32_t* counts, float* out, void* stream) {
+  if (!dtype_ok(dtype) || !hd_ok(head_dim) || !rows_ok(num_state_rows)) return KVC_EINVAL;
+  if (num_q < 0 || num_q >= KVC_MAX_TOKENS || cap_c < 0 || !aligned4(counts)) return KVC_EINVAL;
+  if (cap_c == 0) return KVC_OK;
+  if (!aligned16(input) || !aligned16(ape) || !aligned16(plan_c) || !aligned16(out)) return KVC_EINVAL;
+  if (num_state_rows > 0 && !aligned16(state)) return KVC_EINVAL;
+  kvc::CompressArgs a{state, input, ape, plan_c, counts, out, num_state_rows, num_q, cap_c};
+  const hipError_t e = c4 ? kvc::launch_compress_c4(dtype, head_dim, a, as_stream(stream))
+                          : kvc::launch_compress_c128(dtype, head_dim, a, as_stream(stream));
+  return status_of(e);
+}
+
+int decode_common(bool c4, kvc_dtype dtype, int head_dim, void* state, int64_t num_state_rows, const void* input,
+                  const void* ape, const kvc_plan_d* plan_d, int batch, int32_t* status, float* out, void* stream) {
+  if (!dtype_ok(dtype) || !hd_ok(head_dim) || !rows_ok(num_state_rows)) return KVC_EINVAL;
+  if (batch < 1 || batch > KVC_MAX_DECODE_BATCH) return KVC_EINVAL;
+  if (!aligned16(input) || !aligned16(ape) || !aligned16(plan_d) || !aligned16(out)) return KVC_EINVAL;
+  if (num_state_rows > 0 && !aligned16(state)) return KVC_EINVAL;
+  if (status != nullptr && !aligned4(status)) return KVC_EINVAL;
+  kvc::DecodeArgs a{state, input, ape, plan_d, status, out, num_state_rows, batch};
+  const hipError_t e = c4 ? kvc::launch_decode_c4(dtype, head_dim, a, as_stream(stream))
+                          : kvc::launch_decode_c128(dtype, head_dim, a, as_stream(stream));
+  return status_of(e);
+}
+
+}  // namespace
+
+KVC_EXPORT int kvc_compress_c4(kvc_dtype dtype, int head_dim, const void* state, int64_t num_state_rows,
+                               const void* input, int num_q, const void* ape, const kvc_plan_c* plan_c, int cap_c,
+                               int32_t* counts, float* out, void* stream) {
+  return compress_common(true, dtype, head_dim, state, num_state_rows, input, num_q, ape, plan_c, cap_c, counts, out,
+                         stream);
+}
+
+KVC_EXPORT int kvc_compress_c128(kvc_dtype dtype, int head_dim, const void* state, int64_t num_state_rows,
+                                 const void* input, int num_q, const void* ape, const kvc_plan_c* plan_c, int cap_c,
+                                 int32_t* counts, float* out, void* stream) {
+  return compress_common(false, dtype, head_dim, state, num_state_rows, input, num_q, ape, plan_c, cap_c, counts,
+                         out, stream);
+}
+
+KVC_EXPORT int kvc_decode_c4(kvc_dtype dtype, int head_dim, void* state, int64_t num_state_rows, const void* input,
+                             const void* ape, const kvc_plan_d* plan_d, int batch, int32_t* status, float* out,
+                             void* stream) {
+  return decode_common(true, dtype, head_dim, state, num_state_rows, input, ape, plan_d, batch, status, out, stream);
+}
+
+KVC_EXPORT int kvc_decode_c128(kvc_dtype dtype, int head_dim, void* state, int64_t num_state_rows, const void* input,
+                               const void* ape, const kvc_plan_d* plan_d, int batch, int32_t* status, float* out,
+                               void* stream) {
+  return decode_common(false, dtype, head_dim, state, num_state_rows, input, ape, plan_d, batch, status, out,
+                       stream);
+}
+
+KVC_EXPORT const char* kvc_strerror(int code) {
+  switch (code) {
+    case KVC_OK:
+      return "ok";
+    case KVC_EINVAL:
+      return "invalid argument (nothing was enqueued)";
+    case KVC_EHIP:
+      return "HIP launch failed";
+    case KVC_DERR_EXTEND:
+      return "device data: extend_len <= 0 or > seq_len (decode: seq_len <= 0)";
+    case KVC_DERR_NUMQ:
+      return "device data: sum of extend_len != num_q";
+    case KVC_DERR_INDEX:
+      return "device data: state index outside the state buffer";
+    case KVC_DERR_CAPACITY:
+      return "device data: plan needs more records than cap_c / cap_w";
+    case KVC_DERR_RECORD:
+      return "device data: record points outside the input or the state";
+    default:
+      return "unknown kvc code";
+  }
+}

@@ -1,0 +1,158 @@
+// kvc_compress.hip - prefill compress kernels (c4.cuh page, flash_c4_prefill
+// with kWrite = false; compressor_v2.py page,
+// _c128_compress_prefill_compress_kernel) and the state write (c4.cuh,
+// c4_write; compressor_v2.py, _c128_compress_prefill_write_kernel).
+//
+// All three are HBM-streaming kernels (no dense contraction, so no MFMA):
+//  - compress c4: 64 lanes x 16 B cover one half-row of hd 512 bf16, so a
+//    lane group reads each of its 8 window entries' kv and score quarters
+//    with one 16-byte load each, all 16 (+8 ape) loads in flight before the
+//    first use; 256-thread workgroups hold 256 / lanes-per-row rows.
+//  - compress c128: one workgroup per compressed row; its streams split the
+//    128 window entries and merge their online-softmax partials in LDS.
+//  - write: one wave per record, the whole row copied with 16-byte vectors.
+// Grids are sized from the host-known capacities; threads past counts[0]
+// (counts[1] for the write) return at once, so no host sync is needed.
+#include "kvc_device.hpp"
+#include "kvc_launch.hpp"
+#include "kvc_pool.hpp"
+
+namespace kvc {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename T, int HD>
+__global__ __launch_bounds__(kThreads) void compress_c4_kernel(CompressArgs a) {
+  typedef typename Elem<T>::storage E;
+  constexpr int V = Elem<T>::kVec;
+  constexpr int kLanes = HD / V;
+  constexpr int kRows = kThreads / kLanes;
+  const int64_t row = (int64_t)blockIdx.x * kRows + threadIdx.x / kLanes;
+  const int c = (threadIdx.x % kLanes) * V;
+  if (row >= a.counts[0] || row >= a.cap_c) return;
+  const kvc_plan_c rec = load_plan_c(a.plan_c + row);
+  if (plan_c_invalid(rec)) return;
+  const int64_t ragged = rec.ragged_blen & 0xFFFFFFu;
+  const int blen = (int)(rec.ragged_blen >> 24);
+  const int64_t rp0 = rec.read_page_0, rp1 = rec.read_page_1;
+  const bool first_block = rec.seq_len == 4u;
+  if (!c4_record_ok(ragged, blen, rp0, rp1, first_block ? 4 : 0, a.num_q, a.num_state_rows)) {
+    if (c == 0) atomicOr(a.counts + 3, KVC_DERR_RECORD);
+    return;
+  }
+  const E* state = static_cast<const E*>(a.state);
+  const E* input = static_cast<const E*>(a.input);
+  const E* ape = static_cast<const E*>(a.ape);
+  float res[V];
+  if (first_block) {
+    c4_pool<T, HD, 4>(state, input, ape, ragged, blen, rp0, rp1, c, res);
+  } else {
+    c4_pool<T, HD, 0>(state, input, ape, ragged, blen, rp0, rp1, c, res);
+  }
+  store_floats<V>(a.out + row * HD + c, res);
+}
+
+template <typename T, int HD>
+__global__ __launch_bounds__(kThreads) void compress_c128_kernel(CompressArgs a) {
+  typedef typename Elem<T>::storage E;
+  typedef C128Pool<T, HD, kThreads> Pool;
+  __shared__ float lds[Pool::kLdsFloats];
+  const int64_t row = blockIdx.x;
+  if (row >= a.counts[0] || row >= a.cap_c) return;
+  const kvc_plan_c rec = load_plan_c(a.plan_c + row);
+  if (plan_c_invalid(rec)) return;
+  const int64_t ragged = rec.ragged_blen & 0xFFFFFFu;
+  const int blen = (int)(rec.ragged_blen >> 24);
+  const int64_t rp0 = rec.read_page_0;
+  if (!c128_record_ok(ragged, blen, rp0, a.num_q, a.num_state_rows)) {
+    if (threadIdx.x == 0) atomicOr(a.counts + 3, KVC_DERR_RECORD);
+    return;
+  }
+  Pool::run(static_cast<const E*>(a.state), static_cast<const E*>(a.input), static_cast<const E*>(a.ape), ragged,
+            blen, rp0, a.out + row * HD, lds);
+}
+
+constexpr int kWriteRowsPerBlock = kThreads / kWave;
+constexpr int kWriteMaxVecPerLane = 8;  // rows up to 8 KiB (ratio 4, fp32, hd 512)
+
+__global__ __launch_bounds__(kThreads) void write_kernel(WriteArgs a) {
+  const int64_t k = (int64_t)blockIdx.x * kWriteRowsPerBlock + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  if (k >= a.counts[1] || k >= a.cap_w) return;
+  const uint2 rec = *reinterpret_cast<const uint2*>(a.plan_w + k);
+  if (rec.x == 0xFFFFFFFFu) return;
+  const int64_t ragged = rec.x;
+  const int64_t loc = (int32_t)rec.y;
+  if (ragged >= a.num_q || loc < 0 || loc >= a.num_state_rows) {
+    if (lane == 0) atomicOr(a.counts + 3, KVC_DERR_RECORD);
+    return;
+  }
+  const int64_t rb = (int64_t)a.row_vecs * 16;
+  const char* src = static_cast<const char*>(a.input) + ragged * rb;
+  char* dst = static_cast<char*>(a.state) + loc * rb;
+  u32x4 buf[kWriteMaxVecPerLane];
+#pragma unroll
+  for (int u = 0; u < kWriteMaxVecPerLane; ++u) {
+    const int v = lane + u * kWave;
+    if (v < a.row_vecs) buf[u] = load16(src + (int64_t)v * 16);
+  }
+#pragma unroll
+  for (int u = 0; u < kWriteMaxVecPerLane; ++u) {
+    const int v = lane + u * kWave;
+    if (v < a.row_vecs) store16(dst + (int64_t)v * 16, buf[u]);
+  }
+}
+
+template <typename T, int HD>
+hipError_t c4_launch(const CompressArgs& a, hipStream_t stream) {
+  constexpr int kRows = kThreads / (HD / Elem<T>::kVec);
+  const int grid = (a.cap_c + kRows - 1) / kRows;
+  compress_c4_kernel<T, HD><<<grid, kThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <typename T, int HD>
+hipError_t c128_launch(const CompressArgs& a, hipStream_t stream) {
+  compress_c128_kernel<T, HD><<<a.cap_c, kThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <template <typename, int> class F, typename Args>
+hipError_t dispatch(kvc_dtype dtype, int hd, const Args& a, hipStream_t stream) {
+  if (dtype == KVC_BF16) {
+    if (hd == 128) return F<Bf16, 128>::go(a, stream);
+    if (hd == 256) return F<Bf16, 256>::go(a, stream);
+    return F<Bf16, 512>::go(a, stream);
+  }
+  if (hd == 128) return F<float, 128>::go(a, stream);
+  if (hd == 256) return F<float, 256>::go(a, stream);
+  return F<float, 512>::go(a, stream);
+}
+
+template <typename T, int HD>
+struct C4Go {
+  static hipError_t go(const CompressArgs& a, hipStream_t s) { return c4_launch<T, HD>(a, s); }
+};
+template <typename T, int HD>
+struct C128Go {
+  static hipError_t go(const CompressArgs& a, hipStream_t s) { return c128_launch<T, HD>(a, s); }
+};
+
+}  // namespace
+
+hipError_t launch_compress_c4(kvc_dtype dtype, int head_dim, const CompressArgs& a, hipStream_t stream) {
+  return dispatch<C4Go>(dtype, head_dim, a, stream);
+}
+
+hipError_t launch_compress_c128(kvc_dtype dtype, int head_dim, const CompressArgs& a, hipStream_t stream) {
+  return dispatch<C128Go>(dtype, head_dim, a, stream);
+}
+
+hipError_t launch_write(const WriteArgs& a, hipStream_t stream) {
+  const int grid = (a.cap_w + kWriteRowsPerBlock - 1) / kWriteRowsPerBlock;
+  write_kernel<<<grid, kThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace kvc

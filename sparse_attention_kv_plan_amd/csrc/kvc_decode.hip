@@ -1,0 +1,140 @@
+// kvc_decode.hip - fused decode step: store the new token, pool on a block
+// boundary (c4.cuh page, flash_c4_decode; compressor_v2.py page,
+// _c128_compress_decode_kernel).
+//
+// The window's last entry is the new token itself.  Instead of reading it
+// back through the state (a read-after-write across lanes), the pool takes it
+// from the input row, which holds the same bits; the other entries are state
+// rows that this step does not write (indices are distinct per call).
+//  - ratio 4: one lane group (64 lanes for hd 512 bf16) per request; each lane
+//    copies its 16-byte slice of the 4 quarters, then pools 8 entries.
+//  - ratio 128: one workgroup per request; the first 2*hd*size/16 lanes copy
+//    the row, and on a boundary all streams pool the 128-entry page.
+#include "kvc_device.hpp"
+#include "kvc_launch.hpp"
+#include "kvc_pool.hpp"
+
+namespace kvc {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename T, int HD>
+__global__ __launch_bounds__(kThreads) void decode_c4_kernel(DecodeArgs a) {
+  typedef typename Elem<T>::storage E;
+  constexpr int V = Elem<T>::kVec;
+  constexpr int kLanes = HD / V;
+  constexpr int kReq = kThreads / kLanes;
+  constexpr int64_t R = 4 * HD;
+  const int64_t b = (int64_t)blockIdx.x * kReq + threadIdx.x / kLanes;
+  const int c = (threadIdx.x % kLanes) * V;
+  if (b >= a.batch) return;
+  float* out = a.out + b * HD + c;
+  const kvc_plan_d rec = load_plan_d(a.plan_d + b);
+  if (plan_d_invalid(rec)) {
+    store_zeros<V>(out);
+    return;
+  }
+  const bool boundary = (rec.seq_len & 3u) == 0u;
+  const bool first_block = rec.seq_len == 4u;
+  const int64_t wl = rec.write_loc, rp0 = rec.read_page_0, rp1 = rec.read_page_1;
+  bool ok = wl >= 0 && wl < a.num_state_rows;
+  // the pool reads entries 0..6 from the state (7 = the new token, from the input)
+  if (boundary) ok = ok && c4_record_ok(b, 7, rp0, rp1, first_block ? 4 : 0, a.batch, a.num_state_rows);
+  if (!ok) {
+    if (c == 0 && a.status) atomicOr(a.status, KVC_DERR_RECORD);
+    store_zeros<V>(out);
+    return;
+  }
+  E* state = static_cast<E*>(a.state);
+  const E* input = static_cast<const E*>(a.input);
+  u32x4 q[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = load16(input + b * R + i * HD + c);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) store16(state + wl * R + i * HD + c, q[i]);
+  if (!boundary) {
+    store_zeros<V>(out);
+    return;
+  }
+  float res[V];
+  const E* ape = static_cast<const E*>(a.ape);
+  if (first_block) {
+    c4_pool<T, HD, 4>(state, input, ape, b, 7, rp0, rp1, c, res);
+  } else {
+    c4_pool<T, HD, 0>(state, input, ape, b, 7, rp0, rp1, c, res);
+  }
+  store_floats<V>(out, res);
+}
+
+template <typename T, int HD>
+__global__ __launch_bounds__(kThreads) void decode_c128_kernel(DecodeArgs a) {
+  typedef typename Elem<T>::storage E;
+  typedef C128Pool<T, HD, kThreads> Pool;
+  constexpr int V = Elem<T>::kVec;
+  constexpr int64_t R = 2 * HD;
+  constexpr int kRowVecs = (int)(R / V);
+  __shared__ float lds[Pool::kLdsFloats];
+  const int64_t b = blockIdx.x;
+  float* out = a.out + b * HD;
+  const kvc_plan_d rec = load_plan_d(a.plan_d + b);
+  bool ok = !plan_d_invalid(rec);
+  const bool boundary = (rec.seq_len & 127u) == 0u;
+  const int64_t wl = rec.write_loc, rp0 = rec.read_page_0;
+  if (ok) {
+    ok = wl >= 0 && wl < a.num_state_rows;
+    if (boundary) ok = ok && c128_record_ok(b, 127, rp0, a.batch, a.num_state_rows);
+    if (!ok && threadIdx.x == 0 && a.status) atomicOr(a.status, KVC_DERR_RECORD);
+  }
+  if (!ok || !boundary) {
+    for (int d = threadIdx.x * 4; d < HD; d += kThreads * 4) store_zeros<4>(out + d);
+    if (!ok) return;
+  }
+  E* state = static_cast<E*>(a.state);
+  const E* input = static_cast<const E*>(a.input);
+  for (int v = threadIdx.x; v < kRowVecs; v += kThreads)
+    store16(state + wl * R + v * V, load16(input + b * R + v * V));
+  if (!boundary) return;
+  Pool::run(state, input, static_cast<const E*>(a.ape), b, 127, rp0, out, lds);
+}
+
+template <typename T, int HD>
+struct C4Go {
+  static hipError_t go(const DecodeArgs& a, hipStream_t s) {
+    constexpr int kReq = kThreads / (HD / Elem<T>::kVec);
+    decode_c4_kernel<T, HD><<<(a.batch + kReq - 1) / kReq, kThreads, 0, s>>>(a);
+    return hipGetLastError();
+  }
+};
+
+template <typename T, int HD>
+struct C128Go {
+  static hipError_t go(const DecodeArgs& a, hipStream_t s) {
+    decode_c128_kernel<T, HD><<<a.batch, kThreads, 0, s>>>(a);
+    return hipGetLastError();
+  }
+};
+
+template <template <typename, int> class F>
+hipError_t dispatch(kvc_dtype dtype, int hd, const DecodeArgs& a, hipStream_t stream) {
+  if (dtype == KVC_BF16) {
+    if (hd == 128) return F<Bf16, 128>::go(a, stream);
+    if (hd == 256) return F<Bf16, 256>::go(a, stream);
+    return F<Bf16, 512>::go(a, stream);
+  }
+  if (hd == 128) return F<float, 128>::go(a, stream);
+  if (hd == 256) return F<float, 256>::go(a, stream);
+  return F<float, 512>::go(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_decode_c4(kvc_dtype dtype, int head_dim, const DecodeArgs& a, hipStream_t stream) {
+  return dispatch<C4Go>(dtype, head_dim, a, stream);
+}
+
+hipError_t launch_decode_c128(kvc_dtype dtype, int head_dim, const DecodeArgs& a, hipStream_t stream) {
+  return dispatch<C128Go>(dtype, head_dim, a, stream);
+}
+
+}  // namespace kvc

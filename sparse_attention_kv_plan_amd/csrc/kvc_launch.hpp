@@ -1,0 +1,78 @@
+// kvc_launch.hpp - internal launchers, one per kernel family.  The C entry
+// points in kvc_api.hip check host arguments and call these; each launcher
+// only enqueues its kernel and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvc.h"
+
+namespace kvc {
+
+struct PlanPrefillArgs {
+  const int32_t* seq_lens;
+  const int32_t* extend_lens;
+  const int32_t* state_index;
+  int64_t num_state_rows;
+  kvc_plan_c* plan_c;
+  kvc_plan_w* plan_w;
+  int32_t* counts;
+  int batch;
+  int num_q;
+  int cap_c;
+  int cap_w;
+};
+
+struct PlanDecodeArgs {
+  const int32_t* seq_lens;
+  const int32_t* state_index;
+  int64_t num_state_rows;
+  kvc_plan_d* plan_d;
+  int32_t* status;
+  int batch;
+};
+
+struct WriteArgs {
+  void* state;
+  const void* input;
+  const kvc_plan_w* plan_w;
+  int32_t* counts;
+  int64_t num_state_rows;
+  int num_q;
+  int cap_w;
+  int row_vecs;  // 16-byte vectors per row
+};
+
+struct CompressArgs {
+  const void* state;
+  const void* input;
+  const void* ape;
+  const kvc_plan_c* plan_c;
+  int32_t* counts;
+  float* out;
+  int64_t num_state_rows;
+  int num_q;
+  int cap_c;
+};
+
+struct DecodeArgs {
+  void* state;
+  const void* input;
+  const void* ape;
+  const kvc_plan_d* plan_d;
+  int32_t* status;
+  float* out;
+  int64_t num_state_rows;
+  int batch;
+};
+
+hipError_t launch_plan_prefill(int compress_ratio, const PlanPrefillArgs& a, hipStream_t stream);
+hipError_t launch_plan_decode(int compress_ratio, const PlanDecodeArgs& a, hipStream_t stream);
+hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
+hipError_t launch_compress_c4(kvc_dtype dtype, int head_dim, const CompressArgs& a, hipStream_t stream);
+hipError_t launch_compress_c128(kvc_dtype dtype, int head_dim, const CompressArgs& a, hipStream_t stream);
+hipError_t launch_decode_c4(kvc_dtype dtype, int head_dim, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_c128(kvc_dtype dtype, int head_dim, const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace kvc

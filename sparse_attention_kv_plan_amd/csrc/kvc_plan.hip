@@ -1,0 +1,324 @@
+// kvc_plan.hip - prefill and decode planners (c_plan.cuh page:
+// plan_compress_prefill_kernel0 / plan_compress_prefill_legacy with the
+// per-request translation of plan_compress_prefill_legacy_kernel, and
+// plan_compress_decode_legacy_kernel).
+//
+// Prefill plan, one launch, no host sync, no scratch memory:
+//   stage A  every workgroup loads the <= 1024 requests (4 per thread), checks
+//            them, and forms per request e, num_c = s/r - p0/r and
+//            num_w = s - max(p0, floor(s/r)*r - overlap);
+//   stage B  64-lane wavefront scans (shuffles) + a 4-wave combine in LDS
+//            give exclusive offsets of the ragged rows, C records and W
+//            records, plus the sum / OR / min / max reductions;
+//   stage C  records are written in host-loop order (request-major,
+//            positions ascending), so the result is deterministic:
+//              general path  - one thread per output record; the owning
+//                              request comes from a binary search of the
+//                              offsets in LDS and the position from a
+//                              closed form;
+//              uniform path  - when every extend is the same E <= 32 (the
+//                              multi-token-prediction shape), one thread per
+//                              token: request k / E, offset k % E, no search;
+//   stage D  [num_c, cap_c) and [num_w, cap_w) are filled with 0xFF records.
+// Every workgroup repeats stages A/B (12 KiB of L2-resident loads), which is
+// cheaper than a second launch and needs no workspace; workgroup 0 writes
+// the counts.
+#include "kvc_device.hpp"
+#include "kvc_launch.hpp"
+
+namespace kvc {
+namespace {
+
+constexpr int kPlanThreads = 256;
+constexpr int kPlanWaves = kPlanThreads / kWave;
+constexpr int kPerThread = KVC_MAX_PREFILL_BATCH / kPlanThreads;  // 4 requests per thread
+constexpr int kUniformMaxExtend = 32;
+
+template <int CR>
+__device__ __forceinline__ int32_t page_of(int32_t idx, int32_t pos) {
+  if constexpr (CR == 4) {
+    return idx * 2 + ((pos >> 2) & 1);  // two 4-slot pages per request, alternating per block
+  } else {
+    return idx;  // one 128-slot page per request
+  }
+}
+
+template <int CR>
+__device__ __forceinline__ int32_t loc_of(int32_t idx, int32_t pos) {
+  return page_of<CR>(idx, pos) * CR + (pos & (CR - 1));
+}
+
+struct RequestTable {
+  int32_t s[KVC_MAX_PREFILL_BATCH];
+  int32_t p0[KVC_MAX_PREFILL_BATCH];
+  int32_t idx[KVC_MAX_PREFILL_BATCH];
+  int32_t roff[KVC_MAX_PREFILL_BATCH];  // first ragged row of the request
+  int32_t coff[KVC_MAX_PREFILL_BATCH];  // first C record of the request
+  int32_t woff[KVC_MAX_PREFILL_BATCH];  // first W record of the request
+};
+
+// C record for the compressed row closing at position pos of a request
+template <int CR>
+__device__ __forceinline__ void emit_c(kvc_plan_c* dst, int32_t pos, int32_t p0, int32_t idx, int32_t roff) {
+  constexpr int32_t W = CR == 4 ? 8 : 128;
+  const int32_t j = pos - p0;                                      // offset inside the chunk
+  const uint32_t blen = (j + 1 < W) ? (uint32_t)(W - 1 - j) : 0u;  // window entries before the chunk
+  const int32_t pos0 = pos - CR > 0 ? pos - CR : 0;
+  u32x4 v;
+  v.x = (uint32_t)(pos + 1);
+  v.y = (uint32_t)(roff + j) | (blen << 24);
+  v.z = (uint32_t)page_of<CR>(idx, pos0);
+  v.w = (uint32_t)page_of<CR>(idx, pos);
+  store16(dst, v);
+}
+
+template <int CR>
+__device__ __forceinline__ void emit_w(kvc_plan_w* dst, int32_t pos, int32_t p0, int32_t idx, int32_t roff) {
+  uint2 v;
+  v.x = (uint32_t)(roff + (pos - p0));
+  v.y = (uint32_t)loc_of<CR>(idx, pos);
+  *reinterpret_cast<uint2*>(dst) = v;
+}
+
+// largest b in [0, n) with off[b] <= k; off[0] == 0 <= k
+__device__ __forceinline__ int find_owner(const int32_t* off, int n, int k) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= k) {
+      lo = mid;
+    } else {
+      hi = mid - 1;
+    }
+  }
+  return lo;
+}
+
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v, int lane) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const uint32_t n = __shfl_up(v, d, kWave);
+    if (lane >= d) v += n;
+  }
+  return v;
+}
+
+template <int CR>
+__global__ __launch_bounds__(kPlanThreads) void plan_prefill_kernel(PlanPrefillArgs a) {
+  constexpr int32_t W = CR == 4 ? 8 : 128;
+  constexpr int32_t OV = CR == 4 ? 4 : 0;  // ratio 4 keeps the block the next window overlaps
+  __shared__ RequestTable T;
+  __shared__ uint32_t w_incl[kPlanWaves][3];
+  __shared__ long long w_esum[kPlanWaves];
+  __shared__ int w_err[kPlanWaves];
+  __shared__ uint32_t w_min[kPlanWaves];
+  __shared__ uint32_t w_max[kPlanWaves];
+
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const int wave = t / kWave;
+  const int64_t max_idx = a.num_state_rows / W;
+
+  // ---- stage A: this thread's requests t*4 .. t*4+3 ----
+  uint32_t ve[kPerThread], vc[kPerThread], vw[kPerThread];
+  long long esum = 0;
+  int err = 0;
+  uint32_t emin = 0xFFFFFFFFu, emax = 0u;
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    const int b = t * kPerThread + k;
+    ve[k] = vc[k] = vw[k] = 0u;
+    if (b < a.batch) {
+      const int32_t s = a.seq_lens[b], e = a.extend_lens[b], idx = a.state_index[b];
+      const bool ok = e >= 1 && e <= s;
+      if (!ok) err |= KVC_DERR_EXTEND;
+      if (idx < 0 || (int64_t)idx >= max_idx) err |= KVC_DERR_INDEX;
+      esum += e;
+      const int32_t p0 = ok ? s - e : 0;
+      if (ok) {
+        const int32_t fw = (s / CR) * CR - OV;
+        ve[k] = (uint32_t)e;
+        vc[k] = (uint32_t)(s / CR - p0 / CR);
+        vw[k] = (uint32_t)(s - (p0 > fw ? p0 : fw));
+      }
+      emin = min(emin, (uint32_t)e);
+      emax = max(emax, (uint32_t)e);
+      T.s[b] = s;
+      T.p0[b] = p0;
+      T.idx[b] = idx;
+    }
+  }
+
+  // ---- stage B: scans and reductions ----
+  uint32_t te = 0, tc = 0, tw = 0;
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    te += ve[k];
+    tc += vc[k];
+    tw += vw[k];
+  }
+  const uint32_t ie = wave_inclusive_sum(te, lane);
+  const uint32_t ic = wave_inclusive_sum(tc, lane);
+  const uint32_t iw = wave_inclusive_sum(tw, lane);
+#pragma unroll
+  for (int m = kWave / 2; m > 0; m >>= 1) {
+    esum += __shfl_xor(esum, m, kWave);
+    err |= __shfl_xor(err, m, kWave);
+    emin = min(emin, (uint32_t)__shfl_xor(emin, m, kWave));
+    emax = max(emax, (uint32_t)__shfl_xor(emax, m, kWave));
+  }
+  if (lane == kWave - 1) {
+    w_incl[wave][0] = ie;
+    w_incl[wave][1] = ic;
+    w_incl[wave][2] = iw;
+  }
+  if (lane == 0) {
+    w_esum[wave] = esum;
+    w_err[wave] = err;
+    w_min[wave] = emin;
+    w_max[wave] = emax;
+  }
+  __syncthreads();
+
+  uint32_t oe = 0, oc = 0, ow = 0, tot_c = 0, tot_w = 0;
+  long long tot_e = 0;
+  int tot_err = 0;
+  uint32_t tmin = 0xFFFFFFFFu, tmax = 0u;
+#pragma unroll
+  for (int w = 0; w < kPlanWaves; ++w) {
+    if (w < wave) {
+      oe += w_incl[w][0];
+      oc += w_incl[w][1];
+      ow += w_incl[w][2];
+    }
+    tot_c += w_incl[w][1];
+    tot_w += w_incl[w][2];
+    tot_e += w_esum[w];
+    tot_err |= w_err[w];
+    tmin = min(tmin, w_min[w]);
+    tmax = max(tmax, w_max[w]);
+  }
+  uint32_t xe = oe + ie - te, xc = oc + ic - tc, xw = ow + iw - tw;  // exclusive offsets
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    const int b = t * kPerThread + k;
+    if (b < a.batch) {
+      T.roff[b] = (int32_t)xe;
+      T.coff[b] = (int32_t)xc;
+      T.woff[b] = (int32_t)xw;
+    }
+    xe += ve[k];
+    xc += vc[k];
+    xw += vw[k];
+  }
+  if (tot_e != (long long)a.num_q) tot_err |= KVC_DERR_NUMQ;
+  if (!(tot_err & (KVC_DERR_EXTEND | KVC_DERR_NUMQ)) &&
+      ((int64_t)tot_c > (int64_t)a.cap_c || (int64_t)tot_w > (int64_t)a.cap_w))
+    tot_err |= KVC_DERR_CAPACITY;
+  const int n_c = tot_err ? 0 : (int)tot_c;
+  const int n_w = tot_err ? 0 : (int)tot_w;
+  __syncthreads();
+
+  if (blockIdx.x == 0 && t == 0) {
+    a.counts[0] = n_c;
+    a.counts[1] = n_w;
+    a.counts[2] = tot_err;
+    a.counts[3] = 0;
+  }
+
+  // ---- stage C: records ----
+  const int gtid = blockIdx.x * kPlanThreads + t;
+  const int gstride = gridDim.x * kPlanThreads;
+  const bool uniform = !tot_err && tmin == tmax && tmax <= (uint32_t)kUniformMaxExtend;
+  if (uniform) {
+    const int E = (int)tmax;  // num_q == batch * E
+    for (int k = gtid; k < a.num_q; k += gstride) {
+      const int b = k / E;
+      const int32_t j = k - b * E;
+      const int32_t s = T.s[b], p0 = T.p0[b], idx = T.idx[b], roff = T.roff[b];
+      const int32_t pos = p0 + j;
+      if (((pos + 1) & (CR - 1)) == 0) emit_c<CR>(a.plan_c + (T.coff[b] + pos / CR - p0 / CR), pos, p0, idx, roff);
+      const int32_t fw = (s / CR) * CR - OV;
+      if (pos >= fw) emit_w<CR>(a.plan_w + (T.woff[b] + pos - (p0 > fw ? p0 : fw)), pos, p0, idx, roff);
+    }
+  } else {
+    for (int k = gtid; k < n_c; k += gstride) {
+      const int b = find_owner(T.coff, a.batch, k);
+      const int32_t p0 = T.p0[b];
+      const int32_t pos = (p0 / CR + 1 + (k - T.coff[b])) * CR - 1;  // (k - coff)-th boundary at or after p0
+      emit_c<CR>(a.plan_c + k, pos, p0, T.idx[b], T.roff[b]);
+    }
+    for (int k = gtid; k < n_w; k += gstride) {
+      const int b = find_owner(T.woff, a.batch, k);
+      const int32_t s = T.s[b], p0 = T.p0[b];
+      const int32_t fw = (s / CR) * CR - OV;
+      const int32_t first = p0 > fw ? p0 : fw;
+      emit_w<CR>(a.plan_w + k, first + (k - T.woff[b]), p0, T.idx[b], T.roff[b]);
+    }
+  }
+
+  // ---- stage D: invalid padding ----
+  const u32x4 ones = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+  for (int k = n_c + gtid; k < a.cap_c; k += gstride) store16(a.plan_c + k, ones);
+  const uint2 ones2 = {0xFFFFFFFFu, 0xFFFFFFFFu};
+  for (int k = n_w + gtid; k < a.cap_w; k += gstride) *reinterpret_cast<uint2*>(a.plan_w + k) = ones2;
+}
+
+constexpr int kDecodePlanThreads = 1024;
+
+// One workgroup; requests are independent, the error word needs the whole batch.
+template <int CR>
+__global__ __launch_bounds__(kDecodePlanThreads) void plan_decode_kernel(PlanDecodeArgs a) {
+  constexpr int32_t W = CR == 4 ? 8 : 128;
+  __shared__ int s_err;
+  if (threadIdx.x == 0) s_err = 0;
+  __syncthreads();
+  const int64_t max_idx = a.num_state_rows / W;
+  int err = 0;
+  for (int b = threadIdx.x; b < a.batch; b += kDecodePlanThreads) {
+    const int32_t s = a.seq_lens[b], idx = a.state_index[b];
+    int bad = 0;
+    if (s <= 0) bad |= KVC_DERR_EXTEND;
+    if (idx < 0 || (int64_t)idx >= max_idx) bad |= KVC_DERR_INDEX;
+    u32x4 v = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+    if (!bad) {
+      const int32_t pos1 = s - 1;  // the new token
+      const int32_t pos0 = pos1 - CR > 0 ? pos1 - CR : 0;
+      v.x = (uint32_t)s;
+      v.y = (uint32_t)loc_of<CR>(idx, pos1);
+      v.z = (uint32_t)page_of<CR>(idx, pos0);
+      v.w = (uint32_t)page_of<CR>(idx, pos1);
+    }
+    store16(a.plan_d + b, v);
+    err |= bad;
+  }
+  if (err) atomicOr(&s_err, err);
+  __syncthreads();
+  if (threadIdx.x == 0 && a.status) a.status[0] = s_err;
+}
+
+}  // namespace
+
+hipError_t launch_plan_prefill(int compress_ratio, const PlanPrefillArgs& a, hipStream_t stream) {
+  // enough workgroups that every record (or, on the uniform path, every
+  // token) has a thread; the loops are grid-strided, so any count is correct
+  const int64_t work = std::max<int64_t>((int64_t)a.cap_c + a.cap_w, std::min(a.num_q, a.batch * kUniformMaxExtend));
+  const int grid = (int)std::min<int64_t>(1024, std::max<int64_t>(1, (work + kPlanThreads - 1) / kPlanThreads));
+  if (compress_ratio == 4) {
+    plan_prefill_kernel<4><<<grid, kPlanThreads, 0, stream>>>(a);
+  } else {
+    plan_prefill_kernel<128><<<grid, kPlanThreads, 0, stream>>>(a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_decode(int compress_ratio, const PlanDecodeArgs& a, hipStream_t stream) {
+  if (compress_ratio == 4) {
+    plan_decode_kernel<4><<<1, kDecodePlanThreads, 0, stream>>>(a);
+  } else {
+    plan_decode_kernel<128><<<1, kDecodePlanThreads, 0, stream>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvc

@@ -1,0 +1,184 @@
+// kvc_pool.hpp - the softmax pool over a window (c4.cuh page, c4_forward;
+// compressor_v2.py page, _c128_compress_prefill_compress_kernel), shared by
+// the prefill compress and the fused decode kernels.
+//
+// For every channel d of a compressed row:
+//   t_i = score_i[d] + ape[i][d]          (fp32)
+//   out = sum_i 2^((t_i - m) log2 e) kv_i[d] / sum_i 2^((t_i - m) log2 e),
+//   m = max_i t_i
+// A lane owns one 16-byte group of channels (8 bf16 or 4 fp32) and keeps the
+// maximum, the sum of weights and the weighted sum in fp32 registers.
+#pragma once
+
+#include "kvc_device.hpp"
+
+namespace kvc {
+
+// ---------------------------------------------------------------------------
+// ratio 4: 8 window entries, one lane group per row
+// ---------------------------------------------------------------------------
+//
+// Entry i of the row closing at seq_len comes from the state when
+// i < blen (rows rp0*4 + i for i < 4, rp1*4 + i - 4 otherwise), else from
+// input row ragged - 7 + i.  Entries 0..3 (the previous block) use the
+// |kv overlap| and |score overlap| quarters of their row, entries 4..7 the
+// |kv| and |score| quarters.  FIRST = 4 drops the entries before the start of
+// the sequence (the first block); they are not loaded at all.
+template <typename T, int HD, int FIRST>
+__device__ __forceinline__ void c4_pool(const typename Elem<T>::storage* __restrict__ state,
+                                        const typename Elem<T>::storage* __restrict__ input,
+                                        const typename Elem<T>::storage* __restrict__ ape, int64_t ragged, int blen,
+                                        int64_t rp0, int64_t rp1, int c, float* res) {
+  constexpr int V = Elem<T>::kVec;
+  constexpr int64_t R = 4 * HD;
+  u32x4 kv_raw[8], sc_raw[8], ap_raw[8];
+#pragma unroll
+  for (int i = FIRST; i < 8; ++i) {
+    const int64_t srow = (i < 4) ? rp0 * 4 + i : rp1 * 4 + (i - 4);
+    const typename Elem<T>::storage* row = (i < blen) ? state + srow * R : input + (ragged - 7 + i) * R;
+    kv_raw[i] = load16(row + ((i < 4) ? 0 : HD) + c);
+    sc_raw[i] = load16(row + ((i < 4) ? 2 * HD : 3 * HD) + c);
+    ap_raw[i] = load16(ape + i * HD + c);
+  }
+  float kv[8][V], t[8][V];
+#pragma unroll
+  for (int i = FIRST; i < 8; ++i) {
+    float a[V];
+    widen16<T>(kv_raw[i], kv[i]);
+    widen16<T>(sc_raw[i], t[i]);
+    widen16<T>(ap_raw[i], a);
+#pragma unroll
+    for (int v = 0; v < V; ++v) t[i][v] += a[v];
+  }
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    float m = t[FIRST][v];
+#pragma unroll
+    for (int i = FIRST + 1; i < 8; ++i) m = fmaxf(m, t[i][v]);
+    float den = 0.f, num = 0.f;
+#pragma unroll
+    for (int i = FIRST; i < 8; ++i) {
+      const float w = exp2_hw((t[i][v] - m) * kLog2e);
+      den += w;
+      num = fmaf(w, kv[i][v], num);
+    }
+    res[v] = num / den;
+  }
+}
+
+// Rows the ratio-4 window of a record reads, checked against the buffers.
+__device__ __forceinline__ bool c4_record_ok(int64_t ragged, int blen, int64_t rp0, int64_t rp1, int first,
+                                             int64_t num_q, int64_t num_state_rows) {
+  const int s_hi = blen < 8 ? blen : 8;
+  const int lo0 = first, hi0 = s_hi < 4 ? s_hi : 4;
+  const int lo1 = first > 4 ? first : 4, hi1 = s_hi;
+  const int in_lo = first > s_hi ? first : s_hi;
+  bool ok = rows_ok(rp0 * 4 + lo0, rp0 * 4 + hi0, num_state_rows);
+  ok = ok && rows_ok(rp1 * 4 + (lo1 - 4), rp1 * 4 + (hi1 - 4), num_state_rows);
+  ok = ok && rows_ok(ragged - 7 + in_lo, ragged + 1, num_q);
+  return ok;
+}
+
+// ---------------------------------------------------------------------------
+// ratio 128: 128 window entries, one workgroup per row
+// ---------------------------------------------------------------------------
+//
+// The workgroup's NT threads form S = NT / (HD / V) streams; stream s owns
+// entries s, s + S, s + 2S, ... and runs an online softmax over them in
+// chunks of U entries (all loads of a chunk are issued before any use).  The
+// S partial (max, sum, weighted sum) triples are merged in LDS.  Entry i is
+// state row rp0*128 + i when i < blen, else input row ragged - 127 + i.
+template <typename T, int HD, int NT>
+struct C128Pool {
+  static constexpr int V = Elem<T>::kVec;
+  static constexpr int kLanes = HD / V;   // lanes per stream
+  static constexpr int S = NT / kLanes;   // streams per workgroup
+  static constexpr int PER = 128 / S;     // entries per stream
+  static constexpr int U = PER < 8 ? PER : 8;
+  static constexpr int kLdsFloats = 3 * S * HD;
+  static_assert(NT % kLanes == 0 && 128 % S == 0 && PER % U == 0, "bad c128 pool shape");
+
+  __device__ __forceinline__ static void run(const typename Elem<T>::storage* __restrict__ state,
+                                             const typename Elem<T>::storage* __restrict__ input,
+                                             const typename Elem<T>::storage* __restrict__ ape, int64_t ragged,
+                                             int blen, int64_t rp0, float* __restrict__ out_row, float* lds) {
+    constexpr int64_t R = 2 * HD;
+    const int sid = threadIdx.x / kLanes;
+    const int c = (threadIdx.x % kLanes) * V;
+    float m[V], l[V], acc[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      m[v] = -INFINITY;
+      l[v] = 0.f;
+      acc[v] = 0.f;
+    }
+    for (int k0 = 0; k0 < PER; k0 += U) {
+      u32x4 kv_raw[U], sc_raw[U], ap_raw[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = sid + S * (k0 + u);
+        const typename Elem<T>::storage* row =
+            (i < blen) ? state + (rp0 * 128 + i) * R : input + (ragged - 127 + i) * R;
+        kv_raw[u] = load16(row + c);
+        sc_raw[u] = load16(row + HD + c);
+        ap_raw[u] = load16(ape + (int64_t)i * HD + c);
+      }
+      float kv[U][V], t[U][V];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float a[V];
+        widen16<T>(kv_raw[u], kv[u]);
+        widen16<T>(sc_raw[u], t[u]);
+        widen16<T>(ap_raw[u], a);
+#pragma unroll
+        for (int v = 0; v < V; ++v) t[u][v] += a[v];
+      }
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        float cm = t[0][v];
+#pragma unroll
+        for (int u = 1; u < U; ++u) cm = fmaxf(cm, t[u][v]);
+        const float nm = fmaxf(m[v], cm);
+        const float scale = exp2_hw((m[v] - nm) * kLog2e);  // 0 on the first chunk (m = -inf)
+        float lv = l[v] * scale, av = acc[v] * scale;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float w = exp2_hw((t[u][v] - nm) * kLog2e);
+          lv += w;
+          av = fmaf(w, kv[u][v], av);
+        }
+        m[v] = nm;
+        l[v] = lv;
+        acc[v] = av;
+      }
+    }
+    float* lm = lds;
+    float* ll = lds + S * HD;
+    float* la = lds + 2 * S * HD;
+    store_floats<V>(lm + sid * HD + c, m);
+    store_floats<V>(ll + sid * HD + c, l);
+    store_floats<V>(la + sid * HD + c, acc);
+    __syncthreads();
+    for (int d = threadIdx.x; d < HD; d += NT) {
+      float M = lm[d];
+#pragma unroll
+      for (int s = 1; s < S; ++s) M = fmaxf(M, lm[s * HD + d]);
+      float Lsum = 0.f, Asum = 0.f;
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const float f = exp2_hw((lm[s * HD + d] - M) * kLog2e);
+        Lsum = fmaf(ll[s * HD + d], f, Lsum);
+        Asum = fmaf(la[s * HD + d], f, Asum);
+      }
+      out_row[d] = Asum / Lsum;
+    }
+  }
+};
+
+__device__ __forceinline__ bool c128_record_ok(int64_t ragged, int blen, int64_t rp0, int64_t num_q,
+                                               int64_t num_state_rows) {
+  const int s_hi = blen < 128 ? blen : 128;
+  return rows_ok(rp0 * 128, rp0 * 128 + s_hi, num_state_rows) && rows_ok(ragged - 127 + s_hi, ragged + 1, num_q);
+}
+
+}  // namespace kvc

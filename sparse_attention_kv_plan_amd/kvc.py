@@ -1,0 +1,240 @@
+"""ctypes binding of libkvc.so (include/kvc.h): argument marshalling only.
+
+Every call takes torch CUDA tensors, passes their device pointers and the
+current HIP stream to the C entry point of the same name, and raises
+``KvcError`` when the library returns a non-zero code.  All computation runs
+in the library's HIP kernels; there is no fallback: if libkvc.so is missing
+or cannot be loaded, ``load()`` raises.
+
+Plan records are carried as uint8 tensors of 16 (C, D) or 8 (W) bytes per
+record; bf16 tensors may be passed as torch.bfloat16 or as int16/uint16 bit
+patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+LIB_PATH = os.path.join(PKG, "libkvc.so")
+HEADER = os.path.join(ROOT, "include", "kvc.h")
+
+KVC_OK, KVC_EINVAL, KVC_EHIP = 0, -1, -2
+KVC_F32, KVC_BF16 = 0, 1
+DERR_EXTEND, DERR_NUMQ, DERR_INDEX, DERR_CAPACITY, DERR_RECORD = 1, 2, 4, 8, 16
+WINDOW = {4: 8, 128: 128}
+ROW_MULT = {4: 4, 128: 2}
+C_BYTES, W_BYTES, D_BYTES = 16, 8, 16
+
+_lib = None
+
+
+class KvcError(RuntimeError):
+    pass
+
+
+def load(build_if_missing: bool = False):
+    """Load libkvc.so.  With build_if_missing, compile it first when absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        if not build_if_missing:
+            raise KvcError("libkvc.so is not built (python -m sparse_attention_kv_plan_amd.build)")
+        from sparse_attention_kv_plan_amd import build as _build
+        _build.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, L = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    sig = {
+        "kvc_plan_prefill": [I, I, I, P, P, P, L, P, I, P, I, P, P],
+        "kvc_plan_decode": [I, I, P, P, L, P, P, P],
+        "kvc_write": [I, I, I, P, L, P, I, P, I, P, P],
+        "kvc_compress_c4": [I, I, P, L, P, I, P, P, I, P, P, P],
+        "kvc_compress_c128": [I, I, P, L, P, I, P, P, I, P, P, P],
+        "kvc_decode_c4": [I, I, P, L, P, P, P, I, P, P, P],
+        "kvc_decode_c128": [I, I, P, L, P, P, P, I, P, P, P],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    lib.kvc_strerror.argtypes = [ctypes.c_int]
+    lib.kvc_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def header_functions():
+    """Names of the functions declared in include/kvc.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kvc_\w+)\s*\(", text, re.M)))
+
+
+def strerror(code: int) -> str:
+    return load().kvc_strerror(code).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != KVC_OK:
+        raise KvcError("%s: %s (%d)" % (what, strerror(rc), rc))
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype(t) -> int:
+    if t.dtype == torch.float32:
+        return KVC_F32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return KVC_BF16
+    raise KvcError("unsupported element type %s" % t.dtype)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise KvcError("tensors must be contiguous CUDA tensors")
+
+
+def _shape(t, rows_at_least, cols, what):
+    """The library cannot see device buffer sizes: check them before handing pointers over."""
+    if t.dim() != 2 or t.shape[0] < rows_at_least or t.shape[1] != cols:
+        raise KvcError("%s must be [>= %d, %d], got %s" % (what, rows_at_least, cols, tuple(t.shape)))
+
+
+def _rows(cr, head_dim, state, inp):
+    R = ROW_MULT[cr] * head_dim
+    _shape(state, 0, R, "state")
+    _shape(inp, 0, R, "input")
+    if state.element_size() != inp.element_size():
+        raise KvcError("state and input must share a dtype")
+
+
+# --------------------------------------------------------------------------
+# allocation helpers (torch owns the memory)
+# --------------------------------------------------------------------------
+
+def capacities(cr: int, batch: int, num_q: int):
+    """Record capacities that always suffice for a prefill chunk."""
+    return min(num_q, num_q // cr + batch), min(num_q, batch * (WINDOW[cr] - 1))
+
+
+def alloc_prefill_plan(cr: int, batch: int, num_q: int, device="cuda", cap_c=None, cap_w=None):
+    cc, cw = capacities(cr, batch, num_q)
+    cap_c = cc if cap_c is None else cap_c
+    cap_w = cw if cap_w is None else cap_w
+    plan_c = torch.empty((cap_c, C_BYTES), dtype=torch.uint8, device=device)
+    plan_w = torch.empty((cap_w, W_BYTES), dtype=torch.uint8, device=device)
+    counts = torch.empty(4, dtype=torch.int32, device=device)
+    return plan_c, plan_w, counts
+
+
+# --------------------------------------------------------------------------
+# the C entry points
+# --------------------------------------------------------------------------
+
+def plan_prefill(cr, seq_lens, extend_lens, state_index, num_state_rows, num_q, plan_c, plan_w, counts,
+                 stream=None):
+    _dev(seq_lens, extend_lens, state_index, plan_c, plan_w, counts)
+    B = seq_lens.numel()
+    if extend_lens.numel() != B or state_index.numel() != B or counts.numel() < 4:
+        raise KvcError("seq_lens, extend_lens, state_index must have one entry per request; counts 4")
+    _shape(plan_c, 0, C_BYTES, "plan_c")
+    _shape(plan_w, 0, W_BYTES, "plan_w")
+    rc = load().kvc_plan_prefill(cr, seq_lens.numel(), num_q, _p(seq_lens), _p(extend_lens), _p(state_index),
+                                 num_state_rows, _p(plan_c), plan_c.shape[0], _p(plan_w), plan_w.shape[0],
+                                 _p(counts), _stream(stream))
+    _check(rc, "kvc_plan_prefill")
+
+
+def plan_decode(cr, seq_lens, state_index, num_state_rows, plan_d, status=None, stream=None):
+    _dev(seq_lens, state_index, plan_d, status)
+    if state_index.numel() != seq_lens.numel():
+        raise KvcError("seq_lens and state_index must have one entry per request")
+    _shape(plan_d, seq_lens.numel(), D_BYTES, "plan_d")
+    rc = load().kvc_plan_decode(cr, seq_lens.numel(), _p(seq_lens), _p(state_index), num_state_rows, _p(plan_d),
+                                _p(status), _stream(stream))
+    _check(rc, "kvc_plan_decode")
+
+
+def write(cr, head_dim, state, inp, plan_w, counts, stream=None):
+    _dev(state, inp, plan_w, counts)
+    _rows(cr, head_dim, state, inp)
+    _shape(plan_w, 0, W_BYTES, "plan_w")
+    rc = load().kvc_write(cr, _dtype(inp), head_dim, _p(state), state.shape[0], _p(inp), inp.shape[0], _p(plan_w),
+                          plan_w.shape[0], _p(counts), _stream(stream))
+    _check(rc, "kvc_write")
+
+
+def compress_c4(head_dim, state, inp, ape, plan_c, counts, out, stream=None):
+    _dev(state, inp, ape, plan_c, counts, out)
+    _rows(4, head_dim, state, inp)
+    _shape(ape, WINDOW[4], head_dim, "ape")
+    _shape(plan_c, 0, C_BYTES, "plan_c")
+    _shape(out, plan_c.shape[0], head_dim, "out")
+    if out.dtype != torch.float32 or ape.element_size() != inp.element_size():
+        raise KvcError("out must be float32 and ape share the input dtype")
+    rc = load().kvc_compress_c4(_dtype(inp), head_dim, _p(state), state.shape[0], _p(inp), inp.shape[0], _p(ape),
+                                _p(plan_c), plan_c.shape[0], _p(counts), _p(out), _stream(stream))
+    _check(rc, "kvc_compress_c4")
+
+
+def compress_c128(head_dim, state, inp, ape, plan_c, counts, out, stream=None):
+    _dev(state, inp, ape, plan_c, counts, out)
+    _rows(128, head_dim, state, inp)
+    _shape(ape, WINDOW[128], head_dim, "ape")
+    _shape(plan_c, 0, C_BYTES, "plan_c")
+    _shape(out, plan_c.shape[0], head_dim, "out")
+    if out.dtype != torch.float32 or ape.element_size() != inp.element_size():
+        raise KvcError("out must be float32 and ape share the input dtype")
+    rc = load().kvc_compress_c128(_dtype(inp), head_dim, _p(state), state.shape[0], _p(inp), inp.shape[0],
+                                  _p(ape), _p(plan_c), plan_c.shape[0], _p(counts), _p(out), _stream(stream))
+    _check(rc, "kvc_compress_c128")
+
+
+def compress(cr, head_dim, state, inp, ape, plan_c, counts, out, stream=None):
+    (compress_c4 if cr == 4 else compress_c128)(head_dim, state, inp, ape, plan_c, counts, out, stream)
+
+
+def decode_c4(head_dim, state, inp, ape, plan_d, out, status=None, stream=None):
+    _dev(state, inp, ape, plan_d, out, status)
+    _rows(4, head_dim, state, inp)
+    _shape(plan_d, 0, D_BYTES, "plan_d")
+    B = plan_d.shape[0]
+    _shape(inp, B, ROW_MULT[4] * head_dim, "input")
+    _shape(ape, WINDOW[4], head_dim, "ape")
+    _shape(out, B, head_dim, "out")
+    if out.dtype != torch.float32 or ape.element_size() != inp.element_size():
+        raise KvcError("out must be float32 and ape share the input dtype")
+    rc = load().kvc_decode_c4(_dtype(inp), head_dim, _p(state), state.shape[0], _p(inp), _p(ape), _p(plan_d),
+                              plan_d.shape[0], _p(status), _p(out), _stream(stream))
+    _check(rc, "kvc_decode_c4")
+
+
+def decode_c128(head_dim, state, inp, ape, plan_d, out, status=None, stream=None):
+    _dev(state, inp, ape, plan_d, out, status)
+    _rows(128, head_dim, state, inp)
+    _shape(plan_d, 0, D_BYTES, "plan_d")
+    B = plan_d.shape[0]
+    _shape(inp, B, ROW_MULT[128] * head_dim, "input")
+    _shape(ape, WINDOW[128], head_dim, "ape")
+    _shape(out, B, head_dim, "out")
+    if out.dtype != torch.float32 or ape.element_size() != inp.element_size():
+        raise KvcError("out must be float32 and ape share the input dtype")
+    rc = load().kvc_decode_c128(_dtype(inp), head_dim, _p(state), state.shape[0], _p(inp), _p(ape), _p(plan_d),
+                                plan_d.shape[0], _p(status), _p(out), _stream(stream))
+    _check(rc, "kvc_decode_c128")
+
+
+def decode(cr, head_dim, state, inp, ape, plan_d, out, status=None, stream=None):
+    (decode_c4 if cr == 4 else decode_c128)(head_dim, state, inp, ape, plan_d, out, status, stream)

@@ -11,7 +11,8 @@ Recipe (all draws from ``numpy.random.default_rng``):
     first B taken);
   * each compressor's tensors come from ``default_rng([seed, ratio])`` in the
     order input, ape, state; normals are float32 ``standard_normal`` scaled by
-    the stated standard deviation and drawn in chunks of 8192 rows;
+    the stated standard deviation; a tensor is drawn in chunks of 8192 rows,
+    chunk k from the k-th child seed that the tensor's generator spawns;
   * bf16 tensors are the float32 draws rounded to nearest-even bf16 and are
     carried as uint16 bit patterns; fp32 tensors are carried as float32.
   * "uniform in [a, b]" means integers with both ends included.
@@ -23,6 +24,8 @@ ratio 4 gives each ring 8 rows, ratio 128 gives each page 128 rows.
 """
 from __future__ import annotations
 
+import concurrent.futures
+import os
 from dataclasses import dataclass, field
 from typing import Optional
 
@@ -35,9 +38,17 @@ CHUNK_ROWS = 8192
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 (ties to even); return the uint16 bit patterns."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    r = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
-    return (r >> np.uint32(16)).astype(np.uint16)
+    u = np.array(x, dtype=np.float32, copy=True).view(np.uint32)
+    return _round_in_place(u)
+
+
+def _round_in_place(u: np.ndarray) -> np.ndarray:
+    """u: float32 bit patterns (modified).  Returns the bf16 patterns (nearest, ties to even)."""
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u >>= np.uint32(16)
+    return u.astype(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -45,13 +56,33 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def _normal_rows(rng, rows, cols, col_sigma, dtype):
-    """[rows, cols] normals, column c scaled by col_sigma[c]; float32 or bf16 bits."""
+    """[rows, cols] normals, column c scaled by col_sigma[c]; float32 or bf16 bits.
+
+    Row chunk k (CHUNK_ROWS rows) is drawn from its own child generator
+    ``default_rng(rng_seed.spawn)``: the values do not depend on how many
+    threads draw them."""
     out = np.empty((rows, cols), np.uint16 if dtype == "bf16" else np.float32)
-    for r0 in range(0, rows, CHUNK_ROWS):
-        r1 = min(rows, r0 + CHUNK_ROWS)
-        x = rng.standard_normal((r1 - r0, cols), dtype=np.float32)
-        x *= col_sigma
-        out[r0:r1] = to_bf16_bits(x) if dtype == "bf16" else x
+    sig = np.broadcast_to(np.asarray(col_sigma, np.float32), (cols,))
+    scale = None if np.all(sig == 1.0) else np.ascontiguousarray(sig)
+    nchunks = (rows + CHUNK_ROWS - 1) // CHUNK_ROWS
+    seeds = rng.bit_generator.seed_seq.spawn(max(nchunks, 1)) if hasattr(rng.bit_generator, "seed_seq") \
+        else rng.bit_generator._seed_seq.spawn(max(nchunks, 1))
+
+    def fill(k):
+        r0, r1 = k * CHUNK_ROWS, min(rows, (k + 1) * CHUNK_ROWS)
+        x = np.random.default_rng(seeds[k]).standard_normal((r1 - r0, cols), dtype=np.float32)
+        if scale is not None:
+            x *= scale
+        if dtype == "bf16":
+            out[r0:r1] = _round_in_place(x.view(np.uint32))
+        else:
+            out[r0:r1] = x
+
+    if nchunks > 1:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+            list(ex.map(fill, range(nchunks)))
+    elif nchunks == 1:
+        fill(0)
     return out
 
 

@@ -1,0 +1,354 @@
+"""GPU parity: every C-ABI call against the CPU oracle on the same seeded inputs.
+
+Bars: plans, counts, padding and state buffers bit-exact; pooled rows within
+|err| <= 1e-5 + 1e-5 |ref| for fp32 inputs and <= 2e-2 for bf16 inputs
+(fp32 accumulation on the GPU, float64 in the oracle).  Output rows past
+num_c must stay untouched (checked against a NaN fill, bitwise).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from sparse_attention_kv_plan_amd import kvc  # noqa: E402
+from sparse_attention_kv_plan_amd import workloads as wl  # noqa: E402
+from tests.chunked import OracleBackend, nan_state, random_split, run_chunked  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+W = {4: 8, 128: 128}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tests.gpu_backend import GpuBackend
+    return GpuBackend()
+
+
+def assert_pool_close(got, ref, dtype, what=""):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), what
+    err = np.abs(got - ref)
+    tol = (1e-5 + 1e-5 * np.abs(ref)) if dtype == "f32" else np.full_like(ref, 2e-2)
+    bad = err > tol
+    assert not bad.any(), "%s: %d elements out of tolerance, max err %.3g" % (what, bad.sum(), err.max())
+
+
+def _plans_equal(g, o):
+    gpc, gpw, gcounts = g
+    opc, opw, ocounts = o
+    assert gcounts.tolist() == ocounts.tolist()
+    assert np.array_equal(gpc, opc), "C records differ"
+    assert np.array_equal(gpw, opw), "W records differ"
+
+
+# --------------------------------------------------------------------------
+# planners
+# --------------------------------------------------------------------------
+
+def _random_plan_case(rng, cr):
+    B = int(np.exp(rng.uniform(0, np.log(1024.5))))
+    B = max(1, min(1024, B))
+    kind = rng.integers(0, 3)
+    prefix = rng.integers(0, 5000, size=B)
+    if kind == 0:      # general ragged batch
+        e = rng.integers(1, 600, size=B)
+    elif kind == 1:    # uniform extends (multi-token prediction shape)
+        e = np.full(B, int(rng.integers(1, 33)))
+    else:              # uniform but long: takes the general path
+        e = np.full(B, int(rng.integers(33, 300)))
+    idx = rng.permutation(1024)[:B]
+    return B, prefix + e, e, idx
+
+
+@pytest.mark.parametrize("cr", [4, 128])
+def test_plan_prefill_fuzz(gpu, cr):
+    rng = np.random.default_rng(11 + cr)
+    for case in range(60):
+        B, s, e, idx = _random_plan_case(rng, cr)
+        num_q = int(e.sum())
+        cap_c, cap_w = oracle.capacities(cr, B, num_q)
+        cap_c += int(rng.integers(0, 5))
+        cap_w += int(rng.integers(0, 5))
+        say("plan_prefill cr=%d case=%d B=%d num_q=%d" % (cr, case, B, num_q))
+        g = gpu.plan_prefill(cr, s, e, idx, 1024 * W[cr], num_q, cap_c, cap_w)
+        o = oracle.plan_prefill(cr, s, e, idx, 1024 * W[cr], num_q, cap_c, cap_w)
+        _plans_equal(g, o)
+
+
+@pytest.mark.parametrize("E", [1, 2, 3, 4, 5, 31, 32, 33])
+@pytest.mark.parametrize("cr", [4, 128])
+def test_plan_prefill_uniform_extend(gpu, cr, E):
+    s, e, idx = wl.config5_lens(uniform_extend=E)
+    num_q = int(e.sum())
+    cap_c, cap_w = oracle.capacities(cr, 64, num_q)
+    say("plan_prefill uniform cr=%d E=%d" % (cr, E))
+    _plans_equal(gpu.plan_prefill(cr, s, e, idx, 64 * W[cr], num_q, cap_c, cap_w),
+                 oracle.plan_prefill(cr, s, e, idx, 64 * W[cr], num_q, cap_c, cap_w))
+
+
+def test_plan_prefill_errors(gpu):
+    cases = [
+        (4, [3, 8], [4, 4], [0, 1], 16, 8, 6, 8),      # extend > seq_len
+        (4, [8, 8], [0, 8], [0, 1], 16, 8, 6, 8),      # extend == 0
+        (4, [8, 8], [4, 4], [0, 1], 16, 9, 6, 8),      # sum != num_q
+        (4, [8, 8], [4, 4], [0, 2], 16, 8, 6, 8),      # index out of range
+        (4, [8, 8], [4, 4], [-1, 0], 16, 8, 6, 8),     # negative index
+        (4, [64], [64], [0], 8, 64, 15, 8),            # C capacity
+        (4, [64], [64], [0], 8, 64, 16, 6),            # W capacity
+        (128, [300, 130], [300, 5], [1, 0], 256, 305, 2, 46),   # C capacity, ratio 128
+        (128, [300, 130], [300, 5], [1, 0], 256, 305, 3, 45),   # W capacity, ratio 128
+        (128, [300, 130], [300, 5], [1, 0], 256, 305, 0, 0),    # zero capacities
+        (128, [300, 130], [300, 5], [1, 0], 256, 305, 3, 46),   # exactly enough
+        (4, [2 ** 31 - 1], [5], [0], 8, 5, 5, 5),       # very long sequence
+    ]
+    for c in cases:
+        say("plan_prefill errors", c)
+        _plans_equal(gpu.plan_prefill(*c), oracle.plan_prefill(*c))
+
+
+@pytest.mark.parametrize("cr", [4, 128])
+def test_plan_prefill_golden(gpu, cr):
+    import json
+    import os
+    name = "plan_c4_prefill_two_requests.json" if cr == 4 else "plan_c128_prefill_two_requests.json"
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", name)))
+    pc, pw, counts = gpu.plan_prefill(cr, g["seq_lens"], g["extend_lens"], g["state_index"], 4 * W[cr],
+                                      g["num_q"], 16, 256)
+    assert oracle.unpack_c(pc[: counts[0]]).tolist() == g["plan_c"]
+    assert counts[2] == 0
+
+
+def test_plan_decode(gpu):
+    rng = np.random.default_rng(3)
+    for cr in (4, 128):
+        for B in (1, 7, 256, 1024, 1025, 4096, 65536):
+            s = rng.integers(1, 1 << 20, size=B)
+            idx = rng.permutation(max(B, 70000))[:B]
+            rows = max(B, 70000) * W[cr]
+            say("plan_decode cr=%d B=%d" % (cr, B))
+            g = gpu.plan_decode(cr, s, idx, rows)
+            o = oracle.plan_decode(cr, s, idx, rows)
+            assert g[1] == o[1] == 0 and np.array_equal(g[0], o[0])
+        # bad requests are invalid one by one
+        s = np.array([5, 0, 9, -3, 12], np.int32)
+        idx = np.array([0, 1, 2, 3, 9], np.int32)
+        g = gpu.plan_decode(cr, s, idx, 5 * W[cr])
+        o = oracle.plan_decode(cr, s, idx, 5 * W[cr])
+        assert g[1] == o[1] == (kvc.DERR_EXTEND | kvc.DERR_INDEX) and np.array_equal(g[0], o[0])
+
+
+# --------------------------------------------------------------------------
+# write / compress / decode on oracle-built plans
+# --------------------------------------------------------------------------
+
+SHAPES = [(4, 128, "f32"), (4, 512, "bf16"), (4, 256, "bf16"), (4, 128, "bf16"), (4, 512, "f32"),
+          (128, 512, "bf16"), (128, 128, "f32"), (128, 256, "f32"), (128, 128, "bf16"), (128, 512, "f32")]
+
+
+@pytest.mark.parametrize("cr,hd,dtype", SHAPES)
+def test_prefill_compress_and_write(gpu, cr, hd, dtype):
+    rng = np.random.default_rng(hd + cr + (dtype == "bf16"))
+    for trial in range(3):
+        B = int(rng.integers(1, 9))
+        w = wl.random_prefill(rng, cr, hd, dtype, B, prefix_hi=3 * W[cr], extend_lo=1,
+                              extend_hi=3 * W[cr] if trial < 2 else 700, num_slots=B + 3)
+        cap_c, cap_w = oracle.capacities(cr, B, w.num_q)
+        pc, pw, counts = oracle.plan_prefill(cr, w.seq_lens, w.extend_lens, w.state_index, w.num_state_rows,
+                                             w.num_q, cap_c + 2, cap_w + 2)
+        say("compress cr=%d hd=%d %s trial=%d B=%d num_q=%d num_c=%d" % (cr, hd, dtype, trial, B, w.num_q,
+                                                                         counts[0]))
+        ref, err = oracle.compress(cr, hd, w.state, w.input, w.ape, pc, counts[0])
+        got, gerr = gpu.compress(cr, hd, w.state, w.input, w.ape, pc, counts[0])
+        assert err == gerr == 0
+        n = int(counts[0])
+        assert_pool_close(got[:n], ref[:n], dtype, "compress")
+        assert np.all(np.isnan(got[n:])), "rows past num_c must be untouched"
+        st_o = w.state.copy()
+        assert oracle.write(cr, hd, st_o, w.input, pw, counts[1]) == 0
+        st_g = gpu.write(cr, hd, w.state, w.input, pw, counts[1])
+        assert np.array_equal(st_g.view(np.uint8), st_o.view(np.uint8)), "state differs after write"
+
+
+@pytest.mark.parametrize("cr,hd,dtype", SHAPES)
+def test_decode(gpu, cr, hd, dtype):
+    rng = np.random.default_rng(7 * hd + cr)
+    for trial in range(3):
+        B = int(rng.integers(1, 300))
+        w = wl.random_decode(rng, cr, hd, dtype, B, prefix_hi=3 * W[cr], num_slots=B + 2)
+        if trial == 2:  # every request on a boundary, including the first block
+            w.seq_lens = (rng.integers(1, 4, size=B) * cr).astype(np.int32)
+        pd, status = oracle.plan_decode(cr, w.seq_lens, w.state_index, w.num_state_rows)
+        say("decode cr=%d hd=%d %s trial=%d B=%d boundaries=%d" % (cr, hd, dtype, trial, B,
+                                                                   int((w.seq_lens % cr == 0).sum())))
+        st_o = w.state.copy()
+        ref, err = oracle.decode(cr, hd, st_o, w.input, w.ape, pd)
+        got, st_g, gerr = gpu.decode(cr, hd, w.state, w.input, w.ape, pd)
+        assert err == gerr == 0
+        assert_pool_close(got, ref, dtype, "decode")
+        nb = w.seq_lens % cr != 0
+        assert np.all(got[nb] == 0.0)
+        assert np.array_equal(st_g.view(np.uint8), st_o.view(np.uint8)), "state differs after decode"
+
+
+def test_first_block_never_reads_masked_rows(gpu):
+    """Block 0 of ratio 4: the overlap entries precede the sequence and must not be loaded.
+    The state is NaN and the ragged rows before the request hold +-inf; a read of either
+    would show up in the output."""
+    hd = 128
+    rng = np.random.default_rng(5)
+    # request 0 fills ragged rows 0..5 with infinities; request 1 starts a sequence at row 6
+    inp = rng.standard_normal((6 + 4, 4 * hd)).astype(np.float32)
+    inp[:6] = np.inf
+    s, e, idx = [6, 4], [6, 4], [1, 0]
+    pc, pw, counts = oracle.plan_prefill(4, s, e, idx, 16, 10, 4, 14)
+    C = oracle.unpack_c(pc[: counts[0]])
+    ape = rng.standard_normal((8, hd)).astype(np.float32)
+    state = nan_state(16, 4 * hd, "f32")
+    got, gerr = gpu.compress(4, hd, state, inp, ape, pc, counts[0])
+    ref, err = oracle.compress(4, hd, state, inp, ape, pc, counts[0])
+    k = [int(r[1]) for r in C].index(9)
+    assert gerr == err == 0 and np.all(np.isfinite(got[k]))
+    assert_pool_close(got[k:k + 1], ref[k:k + 1], "f32", "first block")
+    # decode of the first block too
+    pd, _ = oracle.plan_decode(4, [4], [0], 8)
+    st = nan_state(8, 4 * hd, "f32")
+    st[0:3] = inp[6:9]  # positions 0..2 already in the ring
+    out, st_g, gerr = gpu.decode(4, hd, st, inp[9:10], ape, pd)
+    ref, _ = oracle.decode(4, hd, st.copy(), inp[9:10], ape, pd)
+    assert gerr == 0 and np.all(np.isfinite(out))
+    assert_pool_close(out, ref, "f32", "first block decode")
+
+
+def test_consumer_record_errors(gpu):
+    hd = 128
+    inp = np.zeros((4, 4 * hd), np.float32)
+    st = np.zeros((8, 4 * hd), np.float32)
+    bad_w = np.zeros((1, 8), np.uint8)
+    bad_w.view("<u4")[0, 0] = 9
+    counts = torch.tensor([0, 1, 0, 0], dtype=torch.int32, device="cuda")
+    from tests.gpu_backend import to_dev
+    st_d = to_dev(st)
+    kvc.write(4, hd, st_d, to_dev(inp), to_dev(bad_w), counts)
+    assert int(counts[3].item()) == oracle.write(4, hd, st.copy(), inp, bad_w, 1) == kvc.DERR_RECORD
+    assert torch.count_nonzero(st_d).item() == 0
+    bad_c = np.zeros((1, 16), np.uint8)
+    bad_c.view("<u4")[0] = [8, 3 | (2 << 24), 0, 5]
+    got, gerr = gpu.compress(4, hd, st, inp, np.zeros((8, hd), np.float32), bad_c, 1)
+    _, err = oracle.compress(4, hd, st, inp, np.zeros((8, hd), np.float32), bad_c, 1)
+    assert gerr == err == kvc.DERR_RECORD and np.all(np.isnan(got))
+    bad_d = np.zeros((1, 16), np.uint8)
+    bad_d.view("<i4")[0] = [8, 99, 0, 1]
+    out, st_g, gerr = gpu.decode(4, hd, st, inp[:1], np.zeros((8, hd), np.float32), bad_d)
+    ref, oerr = oracle.decode(4, hd, st.copy(), inp[:1], np.zeros((8, hd), np.float32), bad_d)
+    assert gerr == oerr == kvc.DERR_RECORD and np.all(out == 0) and np.array_equal(st_g, st)
+
+
+# --------------------------------------------------------------------------
+# end to end: chunked prefill + decode, GPU against the oracle
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cr,dtype", [(4, "bf16"), (4, "f32"), (128, "bf16")])
+def test_chunked_prefill_then_decode(gpu, cr, dtype):
+    rng = np.random.default_rng(21 + cr)
+    hd = 128
+    B = 5
+    R = wl.ROW_MULT[cr] * hd
+    decode_steps = 12 if cr == 4 else 140
+    seqs, chunks = [], []
+    for b in range(B):
+        L = int(rng.integers(1, 5 * W[cr]))
+        x = rng.standard_normal((L + decode_steps, R)).astype(np.float32)
+        seqs.append(wl.to_bf16_bits(x) if dtype == "bf16" else x)
+        chunks.append(random_split(rng, L, 5))
+    ape_f = (0.1 * rng.standard_normal((W[cr], hd))).astype(np.float32)
+    ape = wl.to_bf16_bits(ape_f) if dtype == "bf16" else ape_f
+    idx = rng.permutation(7)[:B]
+    say("chunked cr=%d %s chunks=%s" % (cr, dtype, chunks))
+    em_o, st_o = run_chunked(OracleBackend(oracle), cr, hd, dtype, seqs, chunks, decode_steps, idx, 7, ape)
+    em_g, st_g = run_chunked(gpu, cr, hd, dtype, seqs, chunks, decode_steps, idx, 7, ape)
+    assert sorted(em_o) == sorted(em_g)
+    for k in em_o:
+        assert_pool_close(em_g[k][None], em_o[k][None], dtype, str(k))
+    assert np.array_equal(st_g.view(np.uint8), st_o.view(np.uint8))
+
+
+# --------------------------------------------------------------------------
+# the named workloads at full size, GPU plans feeding GPU kernels
+# --------------------------------------------------------------------------
+
+def _run_prefill_pipeline(w):
+    """GPU: plan -> compress -> write, all through the C ABI, in the launch order the bench uses."""
+    from tests.gpu_backend import to_dev
+    cr, hd = w.cr, w.hd
+    plan_c, plan_w, counts = kvc.alloc_prefill_plan(cr, w.B, w.num_q)
+    state = to_dev(w.state)
+    inp = to_dev(w.input)
+    ape = to_dev(w.ape)
+    out = torch.full((plan_c.shape[0], hd), float("nan"), dtype=torch.float32, device="cuda")
+    kvc.plan_prefill(cr, to_dev(w.seq_lens), to_dev(w.extend_lens), to_dev(w.state_index), w.num_state_rows,
+                     w.num_q, plan_c, plan_w, counts)
+    kvc.compress(cr, hd, state, inp, ape, plan_c, counts, out)
+    kvc.write(cr, hd, state, inp, plan_w, counts)
+    torch.cuda.synchronize()
+    return (plan_c.cpu().numpy(), plan_w.cpu().numpy(), counts.cpu().numpy(), out.cpu().numpy(),
+            state.cpu().numpy())
+
+
+@pytest.mark.parametrize("name", ["config1", "config2", "config5_c4", "config5_c128", "config5_c4_mtp",
+                                  "config5_c128_mtp"])
+def test_named_prefill_workloads(gpu, name):
+    w = {"config1": lambda: wl.config1(), "config2": lambda: wl.config2(),
+         "config5_c4": lambda: wl.config5(4), "config5_c128": lambda: wl.config5(128),
+         "config5_c4_mtp": lambda: wl.config5(4, uniform_extend=2),
+         "config5_c128_mtp": lambda: wl.config5(128, uniform_extend=2)}[name]()
+    say("workload %s: B=%d num_q=%d" % (w.name, w.B, w.num_q))
+    pc, pw, counts, out, state = _run_prefill_pipeline(w)
+    cap_c, cap_w = oracle.capacities(w.cr, w.B, w.num_q)
+    opc, opw, ocounts = oracle.plan_prefill(w.cr, w.seq_lens, w.extend_lens, w.state_index, w.num_state_rows,
+                                            w.num_q, cap_c, cap_w)
+    assert counts.tolist() == ocounts.tolist() and counts[2] == 0 and counts[3] == 0
+    assert np.array_equal(pc, opc) and np.array_equal(pw, opw)
+    n = int(counts[0])
+    ref, err = oracle.compress(w.cr, w.hd, w.state, w.input, w.ape, opc, n)
+    assert err == 0
+    assert_pool_close(out[:n], ref[:n], w.dtype, w.name)
+    st_o = w.state.copy()
+    oracle.write(w.cr, w.hd, st_o, w.input, opw, int(ocounts[1]))
+    assert np.array_equal(state.view(np.uint8), st_o.view(np.uint8))
+    if name == "config1":
+        assert n == 16 and counts[1] == 4
+
+
+@pytest.mark.parametrize("name", ["config3", "config4"])
+def test_named_decode_workloads(gpu, name):
+    from tests.gpu_backend import to_dev
+    w = wl.config3() if name == "config3" else wl.config4()
+    say("workload %s: B=%d boundaries=%d" % (w.name, w.B, int((w.seq_lens % w.cr == 0).sum())))
+    plan_d = torch.empty((w.B, kvc.D_BYTES), dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    state = to_dev(w.state)
+    out = torch.full((w.B, w.hd), float("nan"), dtype=torch.float32, device="cuda")
+    kvc.plan_decode(w.cr, to_dev(w.seq_lens), to_dev(w.state_index), w.num_state_rows, plan_d, status)
+    kvc.decode(w.cr, w.hd, state, to_dev(w.input), to_dev(w.ape), plan_d, out, status)
+    torch.cuda.synchronize()
+    opd, ostatus = oracle.plan_decode(w.cr, w.seq_lens, w.state_index, w.num_state_rows)
+    assert int(status.item()) == ostatus == 0
+    assert np.array_equal(plan_d.cpu().numpy(), opd)
+    st_o = w.state.copy()
+    ref, err = oracle.decode(w.cr, w.hd, st_o, w.input, w.ape, opd)
+    assert err == 0
+    assert_pool_close(out.cpu().numpy(), ref, w.dtype, w.name)
+    assert np.array_equal(state.cpu().numpy().view(np.uint8), st_o.view(np.uint8))

@@ -24,8 +24,8 @@ MUTANTS = [
      "put_u32(r + 4, (uint32_t)ragged | ((uint32_t)blen << 24));\n          put_u32(r + 8, as_u32((int32_t)page_of(cr, idx, pos0)));",
      "put_u32(r + 4, (uint32_t)ragged | ((uint32_t)blen << 24));\n          put_u32(r + 8, as_u32((int32_t)page_of(cr, idx, pos)));"),
     ("decode read page 0 taken at the new token",
-     "put_u32(r + 4, as_u32((int32_t)loc_of(cr, idx, pos1)));\n      put_u32(r + 8, as_u32((int32_t)page_of(cr, idx, pos0)));",
-     "put_u32(r + 4, as_u32((int32_t)loc_of(cr, idx, pos1)));\n      put_u32(r + 8, as_u32((int32_t)page_of(cr, idx, pos1)));"),
+     "put_u32(r + 4, as_u32((int32_t)loc_of(cr, idx, pos1)));\n    put_u32(r + 8, as_u32((int32_t)page_of(cr, idx, pos0)));",
+     "put_u32(r + 4, as_u32((int32_t)loc_of(cr, idx, pos1)));\n    put_u32(r + 8, as_u32((int32_t)page_of(cr, idx, pos1)));"),
     ("kv quarters swapped", "e.kv_col = (i < 4) ? 0 : hd;", "e.kv_col = (i < 4) ? hd : 0;"),
     ("score quarters swapped", "e.sc_col = (i < 4) ? 2 * hd : 3 * hd;", "e.sc_col = (i < 4) ? 3 * hd : 2 * hd;"),
     ("ragged window off by one", "e.row = ragged - 7 + i;", "e.row = ragged - 8 + i;"),

@@ -150,8 +150,12 @@ def test_plan_errors_and_padding():
         oracle.plan_prefill(5, [8], [8], [0], 8, 8, 4, 4)
     with pytest.raises(oracle.OracleError):
         oracle.plan_prefill(4, [8], [8], [0], 8, 0, 4, 4)
+    # decode validates request by request: only the bad one is invalid
     pd, status = oracle.plan_decode(4, [0, 5], [0, 1], 16)
-    assert status == 1 and np.all(pd == 0xFF)
+    assert status == 1 and np.all(pd[0] == 0xFF)
+    assert oracle.unpack_d(pd[1:]).tolist() == [[5, 12, 2, 3]]
+    pd, status = oracle.plan_decode(4, [5, 5], [0, 2], 16)
+    assert status == 4 and np.all(pd[1] == 0xFF) and oracle.unpack_d(pd[:1]).tolist() == [[5, 4, 0, 1]]
 
 
 # --------------------------------------------------------------------------
