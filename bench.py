@@ -46,11 +46,68 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=2)
+    ap.add_argument("--cpu-reps", type=int, default=5)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only copy 1 GiB device to device 5 times (calibrates the HBM byte counters)")
     return ap.parse_args()
+
+
+# Sources of the dominant kernel: the traffic figure is only reported while they are
+# unchanged since the counters in TRAFFIC_FILE were taken.
+KERNEL_SOURCES = ["sparse_attention_kv_plan_amd/csrc/kvc_compress.hip", "sparse_attention_kv_plan_amd/csrc/kvc_pool.hpp",
+                  "sparse_attention_kv_plan_amd/csrc/kvc_device.hpp"]
+TRAFFIC_FILE = "profiles/compress_c4_mixed_prefill_traffic.md"
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter summary, or None.
+
+    The summary holds lines "key: value"; it is used only if its source hash matches."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(("#", "|", "`")):
+                k, v = line.split(":", 1)
+                kv[k.strip().lstrip("-* ").strip()] = v.strip().strip("`")
+    if kv.get("kernel source hash") != kernel_source_hash():
+        return None
+    try:
+        return int(float(kv["HBM bytes per launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(5):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / 5
+    print(json.dumps({"copy_probe_bytes": n, "copies": 5, "ms_per_copy": round(ms, 4),
+                      "GBps_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def algorithmic_bytes_compress(cr, hd, esize, seq_lens_of_rows):
@@ -64,6 +121,9 @@ def algorithmic_bytes_compress(cr, hd, esize, seq_lens_of_rows):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe()
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU: the compressor has no multi-GPU path in this library "
               "(requests shard across GPUs with no exchange); run with --gpus 1", file=sys.stderr)
@@ -212,7 +272,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
             "bytes_per_launch": dom_bytes,
             "avg_launch_us": round(dom_us, 2),
         },
