@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kThreads) void compress_c128_kernel(CompressArgs a)
     return;
   }
   Pool::run(static_cast<const E*>(a.state), static_cast<const E*>(a.input), static_cast<const E*>(a.ape), ragged,
-            blen, rp0, a.out + row * HD, lds);
+            blen, rp0, 0, a.out + row * HD, lds);
 }
 
 constexpr int kWriteRowsPerBlock = kThreads / kWave;

@@ -8,8 +8,9 @@
 // rows that this step does not write (indices are distinct per call).
 //  - ratio 4: one lane group (64 lanes for hd 512 bf16) per request; each lane
 //    copies its 16-byte slice of the 4 quarters, then pools 8 entries.
-//  - ratio 128: one workgroup per request; the first 2*hd*size/16 lanes copy
-//    the row, and on a boundary all streams pool the 128-entry page.
+//  - ratio 128: a few workgroups per request, each owning a slice of the
+//    channels: it copies its slice of the row and, on a boundary, pools its
+//    channels over the 128-entry page.
 #include "kvc_device.hpp"
 #include "kvc_launch.hpp"
 #include "kvc_pool.hpp"
@@ -67,15 +68,30 @@ __global__ __launch_bounds__(kThreads) void decode_c4_kernel(DecodeArgs a) {
   store_floats<V>(out, res);
 }
 
+// Ratio 128: CS workgroups of 128 threads per request, each owning HD / CS
+// channels (8 lanes x 16 bytes per stream, 16 streams, 8 entries each).  A
+// boundary request's 256 KiB window is thus read by CS workgroups on different
+// CUs at once; the light requests copy their slice of the row and write zeros.
+constexpr int kDec128Threads = 128;
+
 template <typename T, int HD>
-__global__ __launch_bounds__(kThreads) void decode_c128_kernel(DecodeArgs a) {
+struct Dec128Shape {
+  static constexpr int V = Elem<T>::kVec;
+  static constexpr int CS = HD / (8 * V);  // channel slices per request
+};
+
+template <typename T, int HD>
+__global__ __launch_bounds__(kDec128Threads) void decode_c128_kernel(DecodeArgs a) {
   typedef typename Elem<T>::storage E;
-  typedef C128Pool<T, HD, kThreads> Pool;
   constexpr int V = Elem<T>::kVec;
+  constexpr int CS = Dec128Shape<T, HD>::CS;
+  typedef C128Pool<T, HD, kDec128Threads, CS> Pool;
   constexpr int64_t R = 2 * HD;
-  constexpr int kRowVecs = (int)(R / V);
+  constexpr int kSliceVecs = (int)(R / V) / CS;  // 16-byte vectors of the row this workgroup copies
+  constexpr int HDW = HD / CS;
   __shared__ float lds[Pool::kLdsFloats];
-  const int64_t b = blockIdx.x;
+  const int64_t b = blockIdx.x / CS;
+  const int cs = blockIdx.x % CS;
   float* out = a.out + b * HD;
   const kvc_plan_d rec = load_plan_d(a.plan_d + b);
   bool ok = !plan_d_invalid(rec);
@@ -84,18 +100,20 @@ __global__ __launch_bounds__(kThreads) void decode_c128_kernel(DecodeArgs a) {
   if (ok) {
     ok = wl >= 0 && wl < a.num_state_rows;
     if (boundary) ok = ok && c128_record_ok(b, 127, rp0, a.batch, a.num_state_rows);
-    if (!ok && threadIdx.x == 0 && a.status) atomicOr(a.status, KVC_DERR_RECORD);
+    if (!ok && cs == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, KVC_DERR_RECORD);
   }
   if (!ok || !boundary) {
-    for (int d = threadIdx.x * 4; d < HD; d += kThreads * 4) store_zeros<4>(out + d);
+    for (int d = threadIdx.x * 4; d < HDW; d += kDec128Threads * 4) store_zeros<4>(out + cs * HDW + d);
     if (!ok) return;
   }
   E* state = static_cast<E*>(a.state);
   const E* input = static_cast<const E*>(a.input);
-  for (int v = threadIdx.x; v < kRowVecs; v += kThreads)
-    store16(state + wl * R + v * V, load16(input + b * R + v * V));
+  for (int v = threadIdx.x; v < kSliceVecs; v += kDec128Threads) {
+    const int64_t off = (int64_t)(cs * kSliceVecs + v) * V;
+    store16(state + wl * R + off, load16(input + b * R + off));
+  }
   if (!boundary) return;
-  Pool::run(state, input, static_cast<const E*>(a.ape), b, 127, rp0, out, lds);
+  Pool::run(state, input, static_cast<const E*>(a.ape), b, 127, rp0, cs, out, lds);
 }
 
 template <typename T, int HD>
@@ -110,7 +128,8 @@ struct C4Go {
 template <typename T, int HD>
 struct C128Go {
   static hipError_t go(const DecodeArgs& a, hipStream_t s) {
-    decode_c128_kernel<T, HD><<<a.batch, kThreads, 0, s>>>(a);
+    const int64_t grid = (int64_t)a.batch * Dec128Shape<T, HD>::CS;
+    decode_c128_kernel<T, HD><<<(unsigned)grid, kDec128Threads, 0, s>>>(a);
     return hipGetLastError();
   }
 };

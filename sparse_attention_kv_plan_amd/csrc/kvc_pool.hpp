@@ -84,29 +84,33 @@ __device__ __forceinline__ bool c4_record_ok(int64_t ragged, int blen, int64_t r
 // ratio 128: 128 window entries, one workgroup per row
 // ---------------------------------------------------------------------------
 //
-// The workgroup's NT threads form S = NT / (HD / V) streams; stream s owns
-// entries s, s + S, s + 2S, ... (so at any moment the streams read adjacent
-// rows) and runs an online softmax over them in chunks of U entries (all loads
-// of a chunk are issued before any use).  U = 4 keeps a 256-thread workgroup
-// under 128 VGPRs, i.e. 4 waves per SIMD.  The S partial (max, sum, weighted
-// sum) triples are merged in LDS.  Entry i is state row rp0*128 + i when
-// i < blen, else input row ragged - 127 + i.
-template <typename T, int HD, int NT, int U = 4>
+// The workgroup's NT threads form S = NT / (HDW / V) streams over a slice of
+// HDW = HD / CS channels (CS workgroups share a row when CS > 1; the softmax is
+// per channel, so the slices need no merge).  Stream s owns entries s, s + S,
+// s + 2S, ... (at any moment the streams read adjacent rows) and runs an online
+// softmax over them in chunks of U entries, all loads of a chunk issued before
+// any use.  U = 4 keeps a 256-thread workgroup under 128 VGPRs (4 waves per
+// SIMD).  The S partial (max, sum, weighted sum) triples are merged in LDS.
+// Entry i is state row rp0*128 + i when i < blen, else input row
+// ragged - 127 + i.
+template <typename T, int HD, int NT, int CS = 1, int U = 4>
 struct C128Pool {
   static constexpr int V = Elem<T>::kVec;
-  static constexpr int kLanes = HD / V;   // lanes per stream
+  static constexpr int HDW = HD / CS;     // channels of this workgroup
+  static constexpr int kLanes = HDW / V;  // lanes per stream
   static constexpr int S = NT / kLanes;   // streams per workgroup
   static constexpr int PER = 128 / S;     // entries per stream
-  static constexpr int kLdsFloats = 3 * S * HD;
-  static_assert(NT % kLanes == 0 && 128 % S == 0 && PER % U == 0, "bad c128 pool shape");
+  static constexpr int kLdsFloats = 3 * S * HDW;
+  static_assert(HD % CS == 0 && NT % kLanes == 0 && 128 % S == 0 && PER % U == 0, "bad c128 pool shape");
 
   __device__ __forceinline__ static void run(const typename Elem<T>::storage* __restrict__ state,
                                              const typename Elem<T>::storage* __restrict__ input,
                                              const typename Elem<T>::storage* __restrict__ ape, int64_t ragged,
-                                             int blen, int64_t rp0, float* __restrict__ out_row, float* lds) {
+                                             int blen, int64_t rp0, int cs, float* __restrict__ out_row, float* lds) {
     constexpr int64_t R = 2 * HD;
     const int sid = threadIdx.x / kLanes;
-    const int c = (threadIdx.x % kLanes) * V;
+    const int cl = (threadIdx.x % kLanes) * V;  // channel inside the slice
+    const int c = cs * HDW + cl;
     float m[V], l[V], acc[V];
 #pragma unroll
     for (int v = 0; v < V; ++v) {
@@ -155,24 +159,24 @@ struct C128Pool {
       }
     }
     float* lm = lds;
-    float* ll = lds + S * HD;
-    float* la = lds + 2 * S * HD;
-    store_floats<V>(lm + sid * HD + c, m);
-    store_floats<V>(ll + sid * HD + c, l);
-    store_floats<V>(la + sid * HD + c, acc);
+    float* ll = lds + S * HDW;
+    float* la = lds + 2 * S * HDW;
+    store_floats<V>(lm + sid * HDW + cl, m);
+    store_floats<V>(ll + sid * HDW + cl, l);
+    store_floats<V>(la + sid * HDW + cl, acc);
     __syncthreads();
-    for (int d = threadIdx.x; d < HD; d += NT) {
+    for (int d = threadIdx.x; d < HDW; d += NT) {
       float M = lm[d];
 #pragma unroll
-      for (int s = 1; s < S; ++s) M = fmaxf(M, lm[s * HD + d]);
+      for (int s = 1; s < S; ++s) M = fmaxf(M, lm[s * HDW + d]);
       float Lsum = 0.f, Asum = 0.f;
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        const float f = exp2_hw((lm[s * HD + d] - M) * kLog2e);
-        Lsum = fmaf(ll[s * HD + d], f, Lsum);
-        Asum = fmaf(la[s * HD + d], f, Asum);
+        const float f = exp2_hw((lm[s * HDW + d] - M) * kLog2e);
+        Lsum = fmaf(ll[s * HDW + d], f, Lsum);
+        Asum = fmaf(la[s * HDW + d], f, Asum);
       }
-      out_row[d] = Asum / Lsum;
+      out_row[cs * HDW + d] = Asum / Lsum;
     }
   }
 };
