@@ -28,29 +28,47 @@ __global__ __launch_bounds__(kThreads) void compress_c4_kernel(CompressArgs a) {
   constexpr int V = Elem<T>::kVec;
   constexpr int kLanes = HD / V;
   constexpr int kRows = kThreads / kLanes;
+  __shared__ float stage[kThreads * V];  // the workgroup's output rows
   const int64_t row = (int64_t)blockIdx.x * kRows + threadIdx.x / kLanes;
-  const int c = (threadIdx.x % kLanes) * V;
-  if (row >= a.counts[0] || row >= a.cap_c) return;
-  const kvc_plan_c rec = load_plan_c(a.plan_c + row);
-  if (plan_c_invalid(rec)) return;
-  const int64_t ragged = rec.ragged_blen & 0xFFFFFFu;
-  const int blen = (int)(rec.ragged_blen >> 24);
-  const int64_t rp0 = rec.read_page_0, rp1 = rec.read_page_1;
-  const bool first_block = rec.seq_len == 4u;
-  if (!c4_record_ok(ragged, blen, rp0, rp1, first_block ? 4 : 0, a.num_q, a.num_state_rows)) {
-    if (c == 0) atomicOr(a.counts + 3, KVC_DERR_RECORD);
-    return;
-  }
-  const E* state = static_cast<const E*>(a.state);
-  const E* input = static_cast<const E*>(a.input);
-  const E* ape = static_cast<const E*>(a.ape);
+  const int lane = threadIdx.x % kLanes;
+  const int c = lane * V;
+  bool live = row < a.counts[0] && row < a.cap_c;
   float res[V];
-  if (first_block) {
-    c4_pool<T, HD, 4>(state, input, ape, ragged, blen, rp0, rp1, c, res);
-  } else {
-    c4_pool<T, HD, 0>(state, input, ape, ragged, blen, rp0, rp1, c, res);
+  if (live) {
+    const kvc_plan_c rec = load_plan_c(a.plan_c + row);
+    const int64_t ragged = rec.ragged_blen & 0xFFFFFFu;
+    const int blen = (int)(rec.ragged_blen >> 24);
+    const int64_t rp0 = rec.read_page_0, rp1 = rec.read_page_1;
+    const bool first_block = rec.seq_len == 4u;
+    live = !plan_c_invalid(rec);
+    if (live && !c4_record_ok(ragged, blen, rp0, rp1, first_block ? 4 : 0, a.num_q, a.num_state_rows)) {
+      if (c == 0) atomicOr(a.counts + 3, KVC_DERR_RECORD);
+      live = false;
+    }
+    if (live) {
+      const E* state = static_cast<const E*>(a.state);
+      const E* input = static_cast<const E*>(a.input);
+      const E* ape = static_cast<const E*>(a.ape);
+      if (first_block) {
+        c4_pool<T, HD, 4>(state, input, ape, ragged, blen, rp0, rp1, c, res);
+      } else {
+        c4_pool<T, HD, 0>(state, input, ape, ragged, blen, rp0, rp1, c, res);
+      }
+    }
   }
-  store_floats<V, true>(a.out + row * HD + c, res);  // written once, read by a later kernel
+  // A lane holds V adjacent channels, so storing them directly would write
+  // 16-byte pieces at a 4*V-byte stride.  Staging the row in LDS lets every
+  // store instruction write 64 x 16 contiguous bytes instead.
+  float* w = stage + (threadIdx.x / kLanes) * HD;
+  store_floats<V>(w + c, res);
+  __syncthreads();
+  if (live) {
+#pragma unroll
+    for (int k = 0; k < V / 4; ++k) {
+      const int ch = k * (kLanes * 4) + lane * 4;
+      store16_stream(a.out + row * HD + ch, load16(w + ch));  // written once, read by a later kernel
+    }
+  }
 }
 
 template <typename T, int HD>
@@ -99,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void write_kernel(WriteArgs a) {
 #pragma unroll
   for (int u = 0; u < PER; ++u) buf[u] = load16_stream(src + (int64_t)(lane + u * kWave) * 16);
 #pragma unroll
-  for (int u = 0; u < PER; ++u) store16(dst + (int64_t)(lane + u * kWave) * 16, buf[u]);
+  for (int u = 0; u < PER; ++u) store16_stream(dst + (int64_t)(lane + u * kWave) * 16, buf[u]);
 }
 
 template <typename T, int HD>

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void decode_c4_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) q[i] = load16(input + b * R + i * HD + c);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) store16(state + wl * R + i * HD + c, q[i]);
+  for (int i = 0; i < 4; ++i) store16_stream(state + wl * R + i * HD + c, q[i]);
   if (!boundary) {
     store_zeros<V>(out);
     return;
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kThreads) void decode_c4_kernel(DecodeArgs a) {
   } else {
     c4_pool<T, HD, 0>(state, input, ape, b, 7, rp0, rp1, c, res);
   }
-  store_floats<V>(out, res);
+  store_floats<V, true>(out, res);
 }
 
 // Ratio 128: CS workgroups of 128 threads per request, each owning HD / CS
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(kDec128Threads) void decode_c128_kernel(DecodeArgs 
   const E* input = static_cast<const E*>(a.input);
   for (int v = threadIdx.x; v < kSliceVecs; v += kDec128Threads) {
     const int64_t off = (int64_t)(cs * kSliceVecs + v) * V;
-    store16(state + wl * R + off, load16(input + b * R + off));
+    store16_stream(state + wl * R + off, load16(input + b * R + off));
   }
   if (!boundary) return;
   Pool::run(state, input, static_cast<const E*>(a.ape), b, 127, rp0, cs, out, lds);

@@ -40,7 +40,9 @@ __device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u3
 // line is not kept in L2 / the last-level cache, so a stream of kv/score rows
 // neither evicts the small reused operands (ape, plans) nor forces write-backs
 // of dirty lines left by earlier kernels.  On MI355X this lifts a plain read
-// stream from about 6.1 to about 6.9 TB/s.
+// stream from about 6.1 to about 6.9 TB/s.  Every row that a kernel writes for
+// a later kernel (state rows, compressed rows) is stored the same way: dirty
+// cached lines left by a write kernel slow the next streaming kernel by ~25%.
 __device__ __forceinline__ u32x4 load16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
@@ -97,7 +99,7 @@ template <int N>
 __device__ __forceinline__ void store_zeros(float* dst) {
   const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int i = 0; i < N; i += 4) store16(dst + i, z);
+  for (int i = 0; i < N; i += 4) store16_stream(dst + i, z);
 }
 
 __device__ __forceinline__ bool plan_c_invalid(const kvc_plan_c& r) { return r.seq_len == 0xFFFFFFFFu; }

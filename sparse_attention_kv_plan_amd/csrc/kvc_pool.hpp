@@ -176,7 +176,7 @@ struct C128Pool {
         Lsum = fmaf(ll[s * HDW + d], f, Lsum);
         Asum = fmaf(la[s * HDW + d], f, Asum);
       }
-      out_row[cs * HDW + d] = Asum / Lsum;
+      __builtin_nontemporal_store(Asum / Lsum, out_row + cs * HDW + d);
     }
   }
 };
