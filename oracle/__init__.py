@@ -58,8 +58,10 @@ def _load():
         lib.oracle_compress.argtypes = [I, I, I, P, L, P, I, P, P, I, P]
         lib.oracle_write.argtypes = [I, I, I, P, L, P, I, P, I]
         lib.oracle_decode.argtypes = [I, I, I, P, L, P, P, P, I, P]
+        lib.oracle_plan_prefill_swa.argtypes = [I, I, I, P, P, P, P, L, L, P, L, I, I, L, P, I, P, I, P, P]
+        lib.oracle_plan_decode_swa.argtypes = [I, I, P, P, P, L, L, P, L, I, I, L, P, P]
         for f in ("oracle_plan_prefill", "oracle_plan_decode", "oracle_compress", "oracle_write",
-                  "oracle_decode"):
+                  "oracle_decode", "oracle_plan_prefill_swa", "oracle_plan_decode_swa"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -152,6 +154,48 @@ def decode(cr, hd, state, inp, ape, plan_d):
     err = _load().oracle_decode(cr, ib, hd, _ptr(state), state.shape[0], _ptr(inp), _ptr(ape), _ptr(pd), B,
                                 _ptr(out))
     return out, err
+
+
+def plan_prefill_swa(cr, seq_lens, extend_lens, req_pool_indices, req_to_token, full_to_swa, swa_page_size,
+                     ring_size, num_state_rows, num_q, cap_c, cap_w):
+    """SWA-paged prefill plan.  req_to_token: int32 [num_reqs, stride]; full_to_swa: int32 [num_full].
+    Returns (plan_c, plan_w, counts[4], status)."""
+    s, e, rid = _i32(seq_lens), _i32(extend_lens), _i32(req_pool_indices)
+    r2t = _i32(req_to_token)
+    f2s = _i32(full_to_swa)
+    pc = np.zeros((max(cap_c, 0), C_BYTES), np.uint8)
+    pw = np.zeros((max(cap_w, 0), W_BYTES), np.uint8)
+    counts = np.zeros(4, np.int32)
+    status = np.zeros(1, np.int32)
+    rc = _load().oracle_plan_prefill_swa(cr, len(s), num_q, _ptr(s), _ptr(e), _ptr(rid), _ptr(r2t), r2t.shape[1],
+                                         r2t.shape[0], _ptr(f2s), f2s.shape[0], swa_page_size, ring_size,
+                                         int(num_state_rows), _ptr(pc), cap_c, _ptr(pw), cap_w, _ptr(counts),
+                                         _ptr(status))
+    if rc != 0:
+        raise OracleError("oracle_plan_prefill_swa rejected its arguments")
+    return pc, pw, counts, int(status[0])
+
+
+def plan_decode_swa(cr, seq_lens, req_pool_indices, req_to_token, full_to_swa, swa_page_size, ring_size,
+                    num_state_rows):
+    """SWA-paged decode plan.  Returns (plan_d, status)."""
+    s, rid = _i32(seq_lens), _i32(req_pool_indices)
+    r2t = _i32(req_to_token)
+    f2s = _i32(full_to_swa)
+    pd = np.zeros((len(s), D_BYTES), np.uint8)
+    status = np.zeros(1, np.int32)
+    rc = _load().oracle_plan_decode_swa(cr, len(s), _ptr(s), _ptr(rid), _ptr(r2t), r2t.shape[1], r2t.shape[0],
+                                        _ptr(f2s), f2s.shape[0], swa_page_size, ring_size, int(num_state_rows),
+                                        _ptr(pd), _ptr(status))
+    if rc != 0:
+        raise OracleError("oracle_plan_decode_swa rejected its arguments")
+    return pd, int(status[0])
+
+
+def capacities_swa(cr, B, num_q, swa_page_size):
+    """Capacities that always suffice for the SWA-paged plan (ratio 4 adds page-tail writes)."""
+    cap_w = B * (WINDOW[cr] - 1) + (4 * (num_q // swa_page_size + B) if cr == 4 else 0)
+    return min(num_q, num_q // cr + B), min(num_q, cap_w)
 
 
 # --------------------------------------------------------------------------

@@ -409,3 +409,196 @@ int oracle_decode(int cr, int is_bf16, int hd, void* state, int64_t num_state_ro
   free(src);
   return err;
 }
+
+/* ------------------------------------------------------------------------ */
+/* SWA-paged state mapping                                                   */
+/* ------------------------------------------------------------------------ */
+/*
+ * c_plan.cuh: plan_compress_prefill_kernel0 (records on the device),
+ * plan_compress_prefill_kernel_1 (translation) and plan_compress_decode_kernel.
+ * The state of ratio 4 is paged with the sliding-window (SWA) pool: a token's
+ * full-cache slot req_to_token[rid][pos] maps to an SWA slot full_to_swa[...];
+ * SWA page swa / swa_page_size owns a ring of ring_size state rows and the
+ * token lives at row (swa / swa_page_size) * ring_size + swa % ring_size.
+ * Ratio 128 keeps its request-scoped ring: row rid * ring_size + pos % ring_size
+ * (ring_size must be 128: the consumer pools page read_page_0).  A ratio-4 ring
+ * is a multiple of 8 rows, so the two 4-row pages of a window never coincide.
+ * The write rule adds, for ratio 4, the last `ratio` slots of every SWA page
+ * (the next page's first window overlaps them), and caps the first written
+ * position at seq_len - mtp_pad, mtp_pad = min(ring_size - ratio, 4).
+ * A C record whose window takes nothing from the state (buffer_len == 0) keeps
+ * read_page_0 = -1 and read_page_1 = its request's batch index, untranslated.
+ * A lookup that leaves its table makes that one record invalid and sets
+ * ERR_INDEX in *status (OR-ed; the caller clears it).
+ */
+
+static int64_t swa_row(int cr, int64_t rid, int64_t pos, const int32_t* r2t, int64_t stride, const int32_t* f2s,
+                       int64_t num_full, int sps, int ring, int64_t num_state_rows) {
+  int64_t row;
+  if (cr == 128) {
+    row = rid * ring + pos % ring;
+  } else {
+    const int64_t full = r2t[rid * stride + pos];
+    if (full < 0 || full >= num_full) return -1;
+    const int64_t swa = f2s[full];
+    if (swa < 0) return -1;
+    row = (swa / sps) * ring + swa % ring;
+  }
+  if (row < 0 || row >= num_state_rows) return -1;
+  return row;
+}
+
+/* The ratio-4 window spans two 4-row pages, which must be distinct rows of the
+ * ring: a ring of ratio-4 rows is a multiple of 8.  The ratio-128 ring is one
+ * page of 128 rows. */
+static int swa_host_args(int cr, int sps, int ring) {
+  if (sps <= 0 || ring <= 0 || sps % ring != 0 || ring % cr != 0) return 1;
+  if (cr == 4 && ring % 8 != 0) return 1;
+  if (cr == 128 && ring != 128) return 1;
+  return 0;
+}
+
+int oracle_plan_prefill_swa(int cr, int B, int num_q, const int32_t* seq_lens, const int32_t* extend_lens,
+                            const int32_t* req_pool_indices, const int32_t* req_to_token, int64_t r2t_stride,
+                            int64_t num_reqs, const int32_t* full_to_swa, int64_t num_full, int swa_page_size,
+                            int ring_size, int64_t num_state_rows, uint8_t* plan_c, int cap_c, uint8_t* plan_w,
+                            int cap_w, int32_t* counts, int32_t* status) {
+  if (bad_host_args(cr, B) || swa_host_args(cr, swa_page_size, ring_size)) return -1;
+  if (num_q < B || num_q >= (1 << 24)) return -1;
+  if (cap_c < 0 || cap_w < 0 || num_state_rows < 0 || num_state_rows > INT32_MAX) return -1;
+  if (r2t_stride <= 0 || num_reqs <= 0 || num_full < 0) return -1;
+  if (!seq_lens || !extend_lens || !req_pool_indices || !req_to_token || !full_to_swa || !counts) return -1;
+  if ((cap_c > 0 && !plan_c) || (cap_w > 0 && !plan_w)) return -1;
+
+  const int W = window_of(cr);
+  const int mtp_pad = (ring_size - cr < 4) ? ring_size - cr : 4;
+  int err = 0, rec_err = 0;
+  int64_t total = 0;
+  for (int b = 0; b < B; ++b) {
+    const int64_t s = seq_lens[b], e = extend_lens[b], rid = req_pool_indices[b];
+    if (e <= 0 || e > s) err |= ERR_EXTEND;
+    total += e;
+    if (rid < 0 || rid >= num_reqs || s > r2t_stride) err |= ERR_INDEX;
+  }
+  if (total != num_q) err |= ERR_NUMQ;
+
+  int num_c = 0, num_w = 0;
+  uint8_t* tmp_c = NULL;
+  uint8_t* tmp_w = NULL;
+  if (!(err & (ERR_EXTEND | ERR_NUMQ))) {
+    tmp_c = (uint8_t*)malloc((size_t)num_q * 16);
+    tmp_w = (uint8_t*)malloc((size_t)num_q * 8);
+    int64_t ragged_base = 0;
+    for (int b = 0; b < B; ++b) {
+      const int64_t s = seq_lens[b], e = extend_lens[b], rid = req_pool_indices[b];
+      const int64_t p0 = s - e;
+      const int64_t last_c = (s / cr) * cr;
+      int64_t first_w = last_c - (cr == 4 ? 4 : 0);
+      if (s - mtp_pad < first_w) first_w = s - mtp_pad;
+      for (int64_t j = 0; j < e; ++j) {
+        const int64_t pos = p0 + j;
+        const int64_t ragged = ragged_base + j;
+        if ((pos + 1) % cr == 0) {
+          const int64_t in_chunk = (j + 1 < W) ? j + 1 : W;
+          const int64_t blen = W - in_chunk;
+          uint8_t* r = tmp_c + (size_t)num_c * 16;
+          int64_t rp0 = -1, rp1 = b;
+          int ok = 1;
+          if (blen > 0 && !(err & ERR_INDEX)) {
+            const int64_t pos0 = (pos - cr > 0) ? pos - cr : 0;
+            const int64_t row0 = swa_row(cr, rid, pos0, req_to_token, r2t_stride, full_to_swa, num_full,
+                                         swa_page_size, ring_size, num_state_rows);
+            const int64_t row1 = swa_row(cr, rid, pos, req_to_token, r2t_stride, full_to_swa, num_full,
+                                         swa_page_size, ring_size, num_state_rows);
+            ok = row0 >= 0 && row1 >= 0;
+            rp0 = row0 / cr;
+            rp1 = row1 / cr;
+          }
+          if (ok) {
+            put_u32(r + 0, (uint32_t)(pos + 1));
+            put_u32(r + 4, (uint32_t)ragged | ((uint32_t)blen << 24));
+            put_u32(r + 8, as_u32((int32_t)rp0));
+            put_u32(r + 12, as_u32((int32_t)rp1));
+          } else {
+            memset(r, 0xFF, 16);
+            rec_err |= ERR_INDEX;
+          }
+          ++num_c;
+        }
+        const int page_tail = (cr == 4) && (pos % swa_page_size >= swa_page_size - cr);
+        if (pos >= first_w || page_tail) {
+          uint8_t* r = tmp_w + (size_t)num_w * 8;
+          const int64_t row = (err & ERR_INDEX) ? -1
+                                                : swa_row(cr, rid, pos, req_to_token, r2t_stride, full_to_swa,
+                                                          num_full, swa_page_size, ring_size, num_state_rows);
+          if (row >= 0) {
+            put_u32(r + 0, (uint32_t)ragged);
+            put_u32(r + 4, as_u32((int32_t)row));
+          } else {
+            memset(r, 0xFF, 8);
+            rec_err |= ERR_INDEX;
+          }
+          ++num_w;
+        }
+      }
+      ragged_base += e;
+    }
+    if (num_c > cap_c || num_w > cap_w) err |= ERR_CAPACITY;
+  }
+  if (err) {
+    num_c = 0;
+    num_w = 0;
+  } else {
+    memcpy(plan_c, tmp_c, (size_t)num_c * 16);
+    memcpy(plan_w, tmp_w, (size_t)num_w * 8);
+    if (status) status[0] |= rec_err;
+  }
+  if (cap_c > num_c) memset(plan_c + (size_t)num_c * 16, 0xFF, (size_t)(cap_c - num_c) * 16);
+  if (cap_w > num_w) memset(plan_w + (size_t)num_w * 8, 0xFF, (size_t)(cap_w - num_w) * 8);
+  counts[0] = num_c;
+  counts[1] = num_w;
+  counts[2] = err;
+  counts[3] = 0;
+  free(tmp_c);
+  free(tmp_w);
+  return 0;
+}
+
+int oracle_plan_decode_swa(int cr, int B, const int32_t* seq_lens, const int32_t* req_pool_indices,
+                           const int32_t* req_to_token, int64_t r2t_stride, int64_t num_reqs,
+                           const int32_t* full_to_swa, int64_t num_full, int swa_page_size, int ring_size,
+                           int64_t num_state_rows, uint8_t* plan_d, int32_t* status) {
+  if (cr != 4 && cr != 128) return -1;
+  if (B < 1 || B > 65536 || swa_host_args(cr, swa_page_size, ring_size)) return -1;
+  if (num_state_rows < 0 || num_state_rows > INT32_MAX || r2t_stride <= 0 || num_reqs <= 0 || num_full < 0) return -1;
+  if (!seq_lens || !req_pool_indices || !req_to_token || !full_to_swa || !plan_d) return -1;
+  int err = 0;
+  for (int b = 0; b < B; ++b) {
+    const int64_t s = seq_lens[b], rid = req_pool_indices[b];
+    uint8_t* r = plan_d + (size_t)b * 16;
+    int bad = 0;
+    if (s <= 0) bad |= ERR_EXTEND;
+    if (rid < 0 || rid >= num_reqs || s > r2t_stride) bad |= ERR_INDEX;
+    int64_t row0 = -1, row1 = -1;
+    if (!bad) {
+      const int64_t pos1 = s - 1;
+      const int64_t pos0 = (pos1 - cr > 0) ? pos1 - cr : 0;
+      row0 = swa_row(cr, rid, pos0, req_to_token, r2t_stride, full_to_swa, num_full, swa_page_size, ring_size,
+                     num_state_rows);
+      row1 = swa_row(cr, rid, pos1, req_to_token, r2t_stride, full_to_swa, num_full, swa_page_size, ring_size,
+                     num_state_rows);
+      if (row0 < 0 || row1 < 0) bad |= ERR_INDEX;
+    }
+    err |= bad;
+    if (bad) {
+      memset(r, 0xFF, 16);
+      continue;
+    }
+    put_u32(r + 0, (uint32_t)s);
+    put_u32(r + 4, as_u32((int32_t)row1));
+    put_u32(r + 8, as_u32((int32_t)(row0 / cr)));
+    put_u32(r + 12, as_u32((int32_t)(row1 / cr)));
+  }
+  if (status) status[0] = err;
+  return 0;
+}

@@ -241,3 +241,28 @@ def random_decode(rng, cr, hd, dtype, B, prefix_hi, num_slots=None, state_fill=N
     idx = rng.permutation(num_slots)[:B]
     w = decode_workload("random", cr, hd, dtype, prefix + 1, idx, num_slots, None, with_tensors=False)
     return fill_tensors(w, rng, state_fill=state_fill)
+
+
+# --------------------------------------------------------------------------
+# SWA-paged state: index tables (inputs of the SWA planners)
+# --------------------------------------------------------------------------
+
+def swa_tables(rng, max_len, num_reqs, swa_page_size, stride=None):
+    """Index tables of a paged sliding-window pool, as a serving system would hold them.
+
+    req_to_token[rid, pos] is the token's slot in the full KV cache (a random
+    permutation of all num_reqs * stride slots); full_to_swa[slot] is its slot
+    in the SWA pool: each (request, pos // swa_page_size) gets its own SWA page,
+    drawn from a shuffled pool, and the token sits at page * swa_page_size +
+    pos % swa_page_size.  Returns (req_to_token int32 [num_reqs, stride],
+    full_to_swa int32 [num_reqs * stride], number of SWA pages)."""
+    stride = stride or max_len
+    pages_per_req = (stride + swa_page_size - 1) // swa_page_size
+    num_pages = num_reqs * pages_per_req
+    page_of = rng.permutation(num_pages).reshape(num_reqs, pages_per_req)
+    full = rng.permutation(num_reqs * stride).astype(np.int64).reshape(num_reqs, stride)
+    pos = np.arange(stride)
+    swa = page_of[:, pos // swa_page_size] * swa_page_size + pos % swa_page_size
+    f2s = np.empty(num_reqs * stride, np.int64)
+    f2s[full.ravel()] = swa.ravel()
+    return full.astype(np.int32), f2s.astype(np.int32), int(num_pages)

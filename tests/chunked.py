@@ -19,16 +19,22 @@ def nan_state(num_rows, R, dtype):
     return np.full((num_rows, R), np.nan, np.float32)
 
 
-def run_chunked(backend, cr, hd, dtype, seqs, chunks, decode_steps, state_index, num_slots, ape, state=None):
+def run_chunked(backend, cr, hd, dtype, seqs, chunks, decode_steps, state_index, num_slots, ape, state=None,
+                swa=None, start=None):
     """seqs[b]: the request's whole input sequence [L_b, R]; chunks[b]: list of extend lengths
     (prefill rounds, request b takes part in round r if it has an r-th chunk); then
-    ``decode_steps`` single-token steps for every request.  Returns (emitted, state)."""
+    ``decode_steps`` single-token steps for every request.  Returns (emitted, state).
+
+    With ``swa`` = dict(req_to_token, full_to_swa, swa_page_size, ring_size, num_state_rows) the
+    plans come from the SWA-paged planners and state_index holds the request pool indices.
+    ``start[b]`` (default 0) is a prefix of request b already held in the state (prefix reuse)."""
     B = len(seqs)
     R = seqs[0].shape[1]
     W = WINDOW[cr]
     if state is None:
-        state = nan_state(num_slots * W, R, dtype)
-    length = [0] * B
+        rows = swa["num_state_rows"] if swa else num_slots * W
+        state = nan_state(rows, R, dtype)
+    length = list(start) if start is not None else [0] * B
     emitted = {}
     rounds = max(len(c) for c in chunks)
     for r in range(rounds):
@@ -41,8 +47,16 @@ def run_chunked(backend, cr, hd, dtype, seqs, chunks, decode_steps, state_index,
         inp = np.concatenate([seqs[b][length[b]:length[b] + chunks[b][r]] for b in active])
         num_q = int(e.sum())
         cap_c = min(num_q, num_q // cr + len(active))
-        cap_w = min(num_q, len(active) * (W - 1))
-        pc, pw, counts = backend.plan_prefill(cr, s, e, idx, state.shape[0], num_q, cap_c, cap_w)
+        if swa:
+            cap_w = min(num_q, len(active) * (W - 1) + (4 * (num_q // swa["swa_page_size"] + len(active))
+                                                        if cr == 4 else 0))
+            pc, pw, counts, st = backend.plan_prefill_swa(cr, s, e, idx, swa["req_to_token"], swa["full_to_swa"],
+                                                          swa["swa_page_size"], swa["ring_size"], state.shape[0],
+                                                          num_q, cap_c, cap_w)
+            assert st == 0, st
+        else:
+            cap_w = min(num_q, len(active) * (W - 1))
+            pc, pw, counts = backend.plan_prefill(cr, s, e, idx, state.shape[0], num_q, cap_c, cap_w)
         assert counts[2] == 0, counts
         out, err = backend.compress(cr, hd, state, inp, ape, pc, int(counts[0]))
         assert err == 0
@@ -63,7 +77,11 @@ def run_chunked(backend, cr, hd, dtype, seqs, chunks, decode_steps, state_index,
         s = np.array([length[b] + 1 for b in range(B)], np.int32)
         idx = np.asarray(state_index, np.int32)
         inp = np.stack([seqs[b][length[b]] for b in range(B)])
-        pd, status = backend.plan_decode(cr, s, idx, state.shape[0])
+        if swa:
+            pd, status = backend.plan_decode_swa(cr, s, idx, swa["req_to_token"], swa["full_to_swa"],
+                                                 swa["swa_page_size"], swa["ring_size"], state.shape[0])
+        else:
+            pd, status = backend.plan_decode(cr, s, idx, state.shape[0])
         assert status == 0
         out, state, err = backend.decode(cr, hd, state, inp, ape, pd)
         assert err == 0
@@ -97,6 +115,12 @@ class OracleBackend:
 
     def plan_decode(self, cr, s, idx, rows):
         return self.o.plan_decode(cr, s, idx, rows)
+
+    def plan_prefill_swa(self, *a):
+        return self.o.plan_prefill_swa(*a)
+
+    def plan_decode_swa(self, *a):
+        return self.o.plan_decode_swa(*a)
 
     def decode(self, cr, hd, state, inp, ape, pd):
         state = state.copy()

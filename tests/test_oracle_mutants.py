@@ -16,7 +16,9 @@ SRC = os.path.join(ROOT, "oracle", "kvc_oracle.c")
 
 MUTANTS = [
     ("buffer_len off by one", "const int64_t in_chunk = (j + 1 < W) ? j + 1 : W;",
-     "const int64_t in_chunk = (j < W) ? j : W;"),
+     "const int64_t in_chunk = (j < W) ? j : W;", 0),
+    ("SWA buffer_len off by one", "const int64_t in_chunk = (j + 1 < W) ? j + 1 : W;",
+     "const int64_t in_chunk = (j < W) ? j : W;", 1),
     ("page alternation dropped", "if (cr == 4) return idx * 2 + ((pos / 4) & 1);", "if (cr == 4) return idx * 2;"),
     ("overlap block not kept", "const int64_t first_w = last_c - (cr == 4 ? 4 : 0);",
      "const int64_t first_w = last_c;"),
@@ -36,7 +38,8 @@ MUTANTS = [
     ("first-block mask dropped", "  const int first = (cr == 4 && seq_len == 4) ? 4 : 0;\n  for (int64_t d",
      "  const int first = 0;\n  for (int64_t d"),
     ("softmax sign flipped", "const double w = exp(t[i] - m);", "const double w = exp(m - t[i]);"),
-    ("ragged base not advanced", "ragged_base += e;", "ragged_base += 0;"),
+    ("ragged base not advanced", "ragged_base += e;", "ragged_base += 0;", 0),
+    ("SWA ragged base not advanced", "ragged_base += e;", "ragged_base += 0;", 1),
     ("overlap page used for current block", "e.row = (i < 4) ? rp0 * 4 + i : rp1 * 4 + (i - 4);",
      "e.row = (i < 4) ? rp0 * 4 + i : rp0 * 4 + (i - 4);"),
     ("write location one position late", "put_u32(r + 4, as_u32((int32_t)loc_of(cr, idx, pos)));",
@@ -49,20 +52,41 @@ MUTANTS = [
      "    if (boundary) pool_row(cr, is_bf16, hd, src, seq_len, state, input, ape, o);\n"
      "    memcpy((uint8_t*)state + (size_t)(wl * R * esz), (const uint8_t*)input + (size_t)((int64_t)b * R * esz),\n"
      "           (size_t)(R * esz));"),
-    ("compress trigger shifted", "if ((pos + 1) % cr == 0) {", "if (pos % cr == 0) {"),
+    ("compress trigger shifted", "if ((pos + 1) % cr == 0) {", "if (pos % cr == 0) {", 0),
+    ("SWA compress trigger shifted", "if ((pos + 1) % cr == 0) {", "if (pos % cr == 0) {", 1),
+    ("SWA page-tail writes dropped", "const int page_tail = (cr == 4) && (pos % swa_page_size >= swa_page_size - cr);",
+     "const int page_tail = 0;"),
+    ("SWA ring slot taken modulo the page size", "row = (swa / sps) * ring + swa % ring;",
+     "row = (swa / sps) * ring + (swa % sps) % ring + ((swa % sps) >= ring ? 1 : 0);"),
+    ("SWA ring of the wrong page", "row = (swa / sps) * ring + swa % ring;", "row = (swa / ring) * ring + swa % ring;"),
+    ("SWA decode reads the overlap block from the new token's page",
+     "put_u32(r + 8, as_u32((int32_t)(row0 / cr)));", "put_u32(r + 8, as_u32((int32_t)(row1 / cr)));"),
 ]
 
 
-@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0].replace(" ", "_") for m in MUTANTS])
-def test_pins_catch_mutant(tmp_path, name, old, new):
+def _plant(src, old, new, nth):
+    """Replace the nth occurrence of old (or the only one when nth is None)."""
+    if nth is None:
+        assert src.count(old) == 1, "mutation site not found exactly once: %r" % old
+        return src.replace(old, new)
+    at = -1
+    for _ in range(nth + 1):
+        at = src.index(old, at + 1)
+    return src[:at] + new + src[at + len(old):]
+
+
+@pytest.mark.parametrize("mutant", MUTANTS, ids=[m[0].replace(" ", "_") for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, mutant):
+    name, old, new = mutant[:3]
+    nth = mutant[3] if len(mutant) > 3 else None
     src = open(SRC).read()
-    assert src.count(old) == 1, "mutation site not found exactly once: %r" % old
     mutated = tmp_path / "kvc_oracle_mutant.c"
-    mutated.write_text(src.replace(old, new))
+    mutated.write_text(_plant(src, old, new, nth))
     lib = tmp_path / "libkvc_oracle_mutant.so"
     subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", str(lib), str(mutated), "-lm"])
     env = dict(os.environ, KVC_ORACLE_LIB=str(lib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_swa_pins.py")],
                        cwd=ROOT, env=env, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, timeout=600)
     assert r.returncode != 0, "pins did not catch mutant '%s':\n%s" % (name, r.stdout.decode()[-2000:])

@@ -1,0 +1,216 @@
+"""Pins of the oracle's SWA-paged planners (c_plan.cuh page: plan_compress_prefill_kernel0,
+plan_compress_prefill_kernel_1, plan_compress_decode_kernel).
+
+* With one SWA page per request the SWA plan equals the per-request plan, except that a C
+  record whose window takes nothing from the state stays untranslated (-1, batch index).
+* The write set, characterised independently: what the next window needs, plus the 4
+  positions before every SWA page boundary (a request may resume at a page boundary, and its
+  first window then reads them from the state).
+* Chunking invariance through SWA pages against the brute-force window definition, from a
+  NaN-filled state, including a second request that reuses the first one's prefix pages and
+  resumes at a page boundary.
+* Decode equals a one-token prefill; lookup errors invalidate single records.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import brute
+from sparse_attention_kv_plan_amd import workloads as wl
+from tests.chunked import OracleBackend, as_float, random_split, run_chunked
+
+W = {4: 8, 128: 128}
+
+
+def _identity_tables(num_reqs, stride):
+    r2t = (np.arange(num_reqs)[:, None] * stride + np.arange(stride)[None, :]).astype(np.int32)
+    f2s = np.arange(num_reqs * stride, dtype=np.int32)
+    return r2t, f2s
+
+
+@pytest.mark.parametrize("cr", [4, 128])
+def test_one_page_per_request_is_the_per_request_plan(cr):
+    rng = np.random.default_rng(31)
+    stride = 1024
+    for _ in range(25):
+        B = int(rng.integers(1, 7))
+        p0 = rng.integers(0, 300, size=B)
+        e = rng.integers(1, 300, size=B)
+        s = p0 + e
+        rid = rng.permutation(8)[:B]
+        r2t, f2s = _identity_tables(8, stride)
+        num_q = int(e.sum())
+        cap_c, cap_w = oracle.capacities_swa(cr, B, num_q, stride)
+        rows = 8 * W[cr]
+        sc, sw, scounts, st = oracle.plan_prefill_swa(cr, s, e, rid, r2t, f2s, stride, W[cr], rows, num_q, cap_c,
+                                                      cap_w)
+        lc, lw, lcounts = oracle.plan_prefill(cr, s, e, rid, rows, num_q, cap_c, cap_w)
+        assert st == 0 and scounts.tolist() == lcounts.tolist()
+        assert np.array_equal(sw, lw)
+        SC, LC = oracle.unpack_c(sc[: scounts[0]]), oracle.unpack_c(lc[: lcounts[0]])
+        base = np.concatenate([[0], np.cumsum(e)])
+        for a, b in zip(SC, LC):
+            assert a[:3].tolist() == b[:3].tolist()
+            if a[2] > 0:
+                assert a[3:].tolist() == b[3:].tolist()
+            else:
+                req = int(np.searchsorted(base, a[1], side="right") - 1)
+                assert a[3:].tolist() == [-1, req]
+
+
+@pytest.mark.parametrize("sps", [8, 16, 24, 32])
+def test_write_set_next_window_and_page_tails(sps):
+    """W records of ratio 4 = positions the next window needs, plus the 4 positions before each
+    SWA page boundary inside the chunk."""
+    ring = 8
+    stride = 256
+    r2t, f2s = _identity_tables(1, stride)
+    for p0 in range(0, 70):
+        for e in range(1, 70):
+            s = p0 + e
+            cap_c, cap_w = oracle.capacities_swa(4, 1, e, sps)
+            _, pw, counts, st = oracle.plan_prefill_swa(4, [s], [e], [0], r2t, f2s, sps, ring,
+                                                        (stride // sps) * ring, e, cap_c, cap_w)
+            assert counts[2] == 0 and st == 0
+            nxt = (s // 4 + 1) * 4
+            need = {q for q in range(p0, s) if q >= nxt - 8}
+            need |= {q for q in range(p0, s) for boundary in range(sps, s + sps, sps) if boundary - 4 <= q < boundary}
+            got = [p0 + int(r) for r in oracle.unpack_w(pw[: counts[1]])[:, 0]]
+            assert got == sorted(need), (sps, p0, e)
+
+
+def _swa_case(rng, cr, hd, dtype, B, sps, ring, decode_steps, max_len):
+    R = wl.ROW_MULT[cr] * hd
+    seqs, chunks = [], []
+    for b in range(B):
+        L = int(rng.integers(1, max_len))
+        x = rng.standard_normal((L + decode_steps, R)).astype(np.float32)
+        seqs.append(wl.to_bf16_bits(x) if dtype == "bf16" else x)
+        chunks.append(random_split(rng, L, 6))
+    stride = max(len(x) for x in seqs) + 8
+    num_reqs = B + 2
+    r2t, f2s, num_pages = wl.swa_tables(rng, stride, num_reqs, sps, stride=stride)
+    rows = num_pages * ring if cr == 4 else num_reqs * 128
+    swa = dict(req_to_token=r2t, full_to_swa=f2s, swa_page_size=sps, ring_size=ring, num_state_rows=rows)
+    ape_f = (0.1 * rng.standard_normal((W[cr], hd))).astype(np.float32)
+    ape = wl.to_bf16_bits(ape_f) if dtype == "bf16" else ape_f
+    idx = rng.permutation(num_reqs)[:B]
+    return seqs, chunks, swa, ape, idx
+
+
+def _check(cr, hd, dtype, seqs, emitted, ape, first=None):
+    apef = as_float(ape, dtype).tolist()
+    for b, seq in enumerate(seqs):
+        seqf = as_float(seq, dtype).tolist()
+        lo = first[b] if first else 0
+        for s in range(cr, len(seq) + 1, cr):
+            if s <= lo:
+                continue
+            assert (b, s) in emitted, ("missing row", b, s)
+            np.testing.assert_allclose(emitted[(b, s)], brute.pooled_row(cr, hd, seqf, apef, s), rtol=1e-12,
+                                       atol=1e-12, err_msg=str((b, s)))
+
+
+@pytest.mark.parametrize("cr,sps,ring,dtype,trial", [(4, 8, 8, "f32", 0), (4, 16, 8, "bf16", 1), (4, 32, 8, "f32", 2),
+                                                     (4, 16, 16, "f32", 3), (4, 24, 8, "f32", 4),
+                                                     (128, 256, 128, "bf16", 5)])
+def test_swa_chunking_invariance(cr, sps, ring, dtype, trial):
+    rng = np.random.default_rng(200 + trial)
+    hd = 2
+    decode_steps = 9 if cr == 4 else 140
+    seqs, chunks, swa, ape, idx = _swa_case(rng, cr, hd, dtype, 3, sps, ring, decode_steps,
+                                            6 * sps if cr == 4 else 600)
+    emitted, _ = run_chunked(OracleBackend(oracle), cr, hd, dtype, seqs, chunks, decode_steps, idx, 0, ape, swa=swa)
+    _check(cr, hd, dtype, seqs, emitted, ape)
+
+
+@pytest.mark.parametrize("sps,ring", [(8, 8), (16, 8), (24, 8)])
+def test_swa_resume_at_page_boundary(sps, ring):
+    """Request 1 reuses request 0's first P tokens (P a multiple of the SWA page size): same
+    full-cache slots, hence the same SWA pages.  It starts its first chunk at p0 = P and its first
+    window reads the 4 positions before P from the state, which request 0 stored as page tails."""
+    rng = np.random.default_rng(7 + sps)
+    hd, cr = 2, 4
+    R = 4 * hd
+    P = 3 * sps
+    L0, L1 = P + 2 * sps + 5, P + 2 * sps + 3
+    x0 = rng.standard_normal((L0, R)).astype(np.float32)
+    x1 = x0.copy()[:L1]
+    x1[P:] = rng.standard_normal((L1 - P, R)).astype(np.float32)
+    stride = max(L0, L1) + 8
+    r2t, f2s, num_pages = wl.swa_tables(rng, stride, 2, sps, stride=stride)
+    # request 1 holds request 0's full-cache slots for the shared prefix; its own later slots are
+    # new ones (request 1's table row), mapped to request 1's own SWA pages
+    r2t[1, :P] = r2t[0, :P]
+    swa = dict(req_to_token=r2t, full_to_swa=f2s, swa_page_size=sps, ring_size=ring,
+               num_state_rows=num_pages * ring)
+    ape = (0.1 * rng.standard_normal((8, hd))).astype(np.float32)
+    be = OracleBackend(oracle)
+    # request 0 alone, chunked so that no chunk ends right after position P - 1
+    em0, state = run_chunked(be, cr, hd, "f32", [x0], [[P + 2, L0 - P - 2]], 0, [0], 0, ape, swa=swa)
+    _check(cr, hd, "f32", [x0], em0, ape)
+    # request 1 resumes at P on the same state buffer
+    em1, _ = run_chunked(be, cr, hd, "f32", [x1], [[L1 - P]], 0, [1], 0, ape, state=state, swa=swa, start=[P])
+    _check(cr, hd, "f32", [x1], em1, ape, first=[P])
+
+
+@pytest.mark.parametrize("cr", [4, 128])
+def test_swa_decode_equals_one_token_prefill(cr):
+    rng = np.random.default_rng(41)
+    hd = 3
+    R = wl.ROW_MULT[cr] * hd
+    B = 6
+    sps, ring = (16, 8) if cr == 4 else (128, 128)
+    stride = 7 * cr + 8
+    r2t, f2s, num_pages = wl.swa_tables(rng, stride, B, sps, stride=stride)
+    rows = num_pages * ring if cr == 4 else B * 128
+    rid = rng.permutation(B)
+    state0 = rng.standard_normal((rows, R)).astype(np.float32)
+    ape = rng.standard_normal((W[cr], hd)).astype(np.float32)
+    s = np.array([cr, 2 * cr, 3 * cr - 1, 5 * cr, cr + 1, 7 * cr], np.int32)
+    inp = rng.standard_normal((B, R)).astype(np.float32)
+    st_d = state0.copy()
+    pd, status = oracle.plan_decode_swa(cr, s, rid, r2t, f2s, sps, ring, rows)
+    out_d, err = oracle.decode(cr, hd, st_d, inp, ape, pd)
+    assert status == 0 and err == 0
+    st_p = state0.copy()
+    pc, pw, counts, st = oracle.plan_prefill_swa(cr, s, np.ones(B, np.int32), rid, r2t, f2s, sps, ring, rows, B,
+                                                 B, B)
+    assert st == 0 and counts[2] == 0
+    out_p, err = oracle.compress(cr, hd, st_p, inp, ape, pc, counts[0])
+    assert err == 0 and oracle.write(cr, hd, st_p, inp, pw, counts[1]) == 0
+    C = oracle.unpack_c(pc[: counts[0]])
+    for k, row in enumerate(C):
+        np.testing.assert_allclose(out_p[k], out_d[int(row[1])], rtol=1e-14, atol=1e-14)
+    D = oracle.unpack_d(pd)
+    skipped = [int(D[b, 1]) for b in range(B) if cr == 128 and s[b] % cr == 0]
+    keep = np.setdiff1d(np.arange(rows), skipped)
+    assert np.array_equal(st_d[keep], st_p[keep])
+
+
+def test_swa_errors():
+    stride = 64
+    r2t, f2s = _identity_tables(2, stride)
+    # request pool index outside req_to_token, and seq_len beyond its row
+    _, _, counts, _ = oracle.plan_prefill_swa(4, [8, 8], [4, 4], [0, 2], r2t, f2s, 64, 8, 16, 8, 6, 16)
+    assert counts.tolist() == [0, 0, 4, 0]
+    _, _, counts, _ = oracle.plan_prefill_swa(4, [70], [4], [0], r2t, f2s, 64, 8, 16, 4, 6, 16)
+    assert counts.tolist() == [0, 0, 4, 0]
+    # a full-cache slot with no SWA slot invalidates just the records that need it
+    bad = f2s.copy()
+    bad[9] = -1  # position 9 is written by this chunk
+    pc, pw, counts, st = oracle.plan_prefill_swa(4, [12], [12], [0], r2t, bad, 64, 8, 8, 12, 8, 16)
+    assert counts[2] == 0 and st == 4
+    Wr = oracle.unpack_w(pw[: counts[1]])
+    assert np.all(pw[: counts[1]][Wr[:, 0] == 0xFFFFFFFF] == 0xFF)
+    assert (Wr[:, 0] == 0xFFFFFFFF).sum() == 1
+    pd, st = oracle.plan_decode_swa(4, [10, 12], [0, 1], r2t, bad, 64, 8, 16)  # request 0 adds position 9
+    assert st == 4 and np.all(pd[0] == 0xFF) and not np.all(pd[1] == 0xFF)
+    # host-checkable: page size not a multiple of the ring, a ratio-4 ring of 4 rows (both blocks
+    # of a window would share them), ratio-128 ring not 128
+    with pytest.raises(oracle.OracleError):
+        oracle.plan_prefill_swa(4, [8], [8], [0], r2t, f2s, 12, 8, 16, 8, 4, 8)
+    with pytest.raises(oracle.OracleError):
+        oracle.plan_prefill_swa(4, [8], [8], [0], r2t, f2s, 12, 4, 16, 8, 4, 8)
+    with pytest.raises(oracle.OracleError):
+        oracle.plan_prefill_swa(128, [8], [8], [0], r2t, f2s, 256, 256, 512, 8, 4, 8)
