@@ -182,6 +182,46 @@ def main():
             kvc.decode(self.w.cr, self.w.hd, self.state, self.inp, self.ape, self.plan_d, self.out, self.status)
 
     P4, P128, D4, D128 = Prefill(p4), Prefill(p128), Decode(d4), Decode(d128)
+
+    # SWA-paged planners over the same requests (timed in the breakdown pass only): SWA pages of
+    # 128 tokens, ratio-4 rings of 8 rows, ratio-128 rings of 128 rows; each workload gets index
+    # tables sized to its own requests
+    def swa_tables_dev(w, seed):
+        rng = np.random.default_rng(seed)
+        r2t, f2s, npages = wl.swa_tables(rng, int(w.seq_lens.max()), w.B, 128)
+        rows = npages * 8 if w.cr == 4 else w.B * 128
+        return to_dev(r2t), to_dev(f2s), rows, to_dev(rng.permutation(w.B).astype(np.int32))
+
+    class SwaPrefill:
+        def __init__(self, w, seed):
+            self.w = w
+            self.r2t, self.f2s, self.rows, self.rid = swa_tables_dev(w, seed)
+            self.s, self.e = to_dev(w.seq_lens), to_dev(w.extend_lens)
+            cc, cw = kvc.capacities_swa(w.cr, w.B, w.num_q, 128)
+            self.pc, self.pw, self.counts = kvc.alloc_prefill_plan(w.cr, w.B, w.num_q, dev, cap_c=cc, cap_w=cw)
+            self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+        def plan(self):
+            kvc.plan_prefill_swa(self.w.cr, self.s, self.e, self.rid, self.r2t, self.f2s, 128,
+                                 8 if self.w.cr == 4 else 128, self.rows, self.w.num_q, self.pc, self.pw,
+                                 self.counts, self.status)
+
+    class SwaDecode:
+        def __init__(self, w, seed):
+            self.w = w
+            self.r2t, self.f2s, self.rows, self.rid = swa_tables_dev(w, seed)
+            self.s = to_dev(w.seq_lens)
+            self.pd = torch.empty((w.B, kvc.D_BYTES), dtype=torch.uint8, device=dev)
+            self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+        def plan(self):
+            kvc.plan_decode_swa(self.w.cr, self.s, self.rid, self.r2t, self.f2s, 128, 8 if self.w.cr == 4 else 128,
+                                self.rows, self.pd, self.status)
+
+    SP4, SP128, SD4 = SwaPrefill(p4, 2004), SwaPrefill(p128, 2128), SwaDecode(d4, 2003)
+    swa_launches = [("plan_prefill_swa c4", SP4.plan), ("plan_prefill_swa c128", SP128.plan),
+                    ("plan_decode_swa c4", SD4.plan)]
+
     launches = [("plan_prefill c4", P4.plan), ("compress_c4", P4.compress), ("write c4", P4.write),
                 ("plan_prefill c128", P128.plan), ("compress_c128", P128.compress), ("write c128", P128.write),
                 ("plan_decode c4", D4.plan), ("decode_c4", D4.decode),
@@ -217,10 +257,11 @@ def main():
     ms_per_step = ms_total / args.steps
     dom_us = float(np.mean([a.elapsed_time(b) for a, b in kev])) * 1e3
 
-    # per-kernel breakdown (separate, untimed pass; events around every launch)
-    bev = {name: [] for name, _ in launches}
+    # per-kernel breakdown (separate, untimed pass; events around every launch), with the
+    # SWA-paged planners of the same requests
+    bev = {name: [] for name, _ in launches + swa_launches}
     for _ in range(5):
-        for name, f in launches:
+        for name, f in launches + swa_launches:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             f()
@@ -235,6 +276,10 @@ def main():
         assert c[2] == 0 and c[3] == 0, ("device error", c)
     for D in (D4, D128):
         assert int(D.status.item()) == 0
+    for S in (SP4, SP128):
+        c = S.counts.cpu().tolist()
+        assert c[2] == 0 and int(S.status.item()) == 0, ("SWA plan error", c)
+    assert int(SD4.status.item()) == 0
 
     n_c4 = int(P4.counts[0].item())
     rows_seq = P4.plan_c[:n_c4].cpu().numpy().view("<u4").reshape(-1, 4)[:, 0].astype(np.int64)

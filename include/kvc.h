@@ -170,6 +170,53 @@ int kvc_plan_decode(int compress_ratio, int batch, const int32_t* seq_lens, cons
                     int64_t num_state_rows, kvc_plan_d* plan_d, int32_t* status, void* stream);
 
 /*
+ * SWA-paged state mapping (c_plan.cuh page: plan_compress_prefill_kernel0,
+ * plan_compress_prefill_kernel_1, plan_compress_decode_kernel).
+ *
+ * A serving system that keeps the ratio-4 state in its sliding-window (SWA)
+ * page pool plans with these two calls instead of the per-request ones; the
+ * records have the same layout and feed the same compress / write / decode
+ * calls.  Tables (device int32):
+ *   req_to_token [num_reqs, r2t_stride]: full-cache slot of token pos of
+ *                 request slot rid (row rid = req_pool_indices[b]);
+ *   full_to_swa  [num_full]: SWA slot of a full-cache slot (< 0: none).
+ * Ratio 4: the token lives at state row (swa / swa_page_size) * ring_size +
+ * swa % ring_size, swa = full_to_swa[req_to_token[rid][pos]]: every SWA page
+ * owns a ring of ring_size rows.  Ratio 128 keeps its request-scoped ring:
+ * row rid * ring_size + pos % ring_size.
+ * Write rule: as kvc_plan_prefill, but the first unconditionally written
+ * position is capped at seq_len - min(ring_size - ratio, 4), and ratio 4 also
+ * writes the last 4 positions of every SWA page (a request that resumes at a
+ * page boundary reads them as its first window's overlap block).
+ * A C record with buffer_len 0 reads nothing from the state and keeps
+ * read_page_0 = -1, read_page_1 = its batch index (untranslated).
+ * Requirements (else KVC_EINVAL): swa_page_size % ring_size == 0; ratio 4:
+ * ring_size a multiple of 8; ratio 128: ring_size == 128.
+ * Errors: seq_len > r2t_stride or a request slot outside [0, num_reqs) is a
+ * plan error (KVC_DERR_INDEX in counts[2], no records).  A lookup that leaves
+ * its table, a missing SWA slot or a row outside the state buffer makes just
+ * that record invalid and ORs KVC_DERR_INDEX into *status (device int32,
+ * may be NULL; the caller clears it).
+ */
+int kvc_plan_prefill_swa(int compress_ratio, int batch, int num_q, const int32_t* seq_lens,
+                         const int32_t* extend_lens, const int32_t* req_pool_indices, const int32_t* req_to_token,
+                         int64_t r2t_stride, int64_t num_reqs, const int32_t* full_to_swa, int64_t num_full,
+                         int swa_page_size, int ring_size, int64_t num_state_rows, kvc_plan_c* plan_c, int cap_c,
+                         kvc_plan_w* plan_w, int cap_w, int32_t* counts, int32_t* status, void* stream);
+
+/*
+ * kvc_plan_decode_swa - one decode record per request under the SWA-paged
+ * mapping: write_loc = row of position seq_len - 1, read pages = rows of
+ * positions max(seq_len - 1 - ratio, 0) and seq_len - 1 divided by the ratio.
+ * A request with seq_len <= 0, a bad slot or a failed lookup gets an invalid
+ * record; *status (may be NULL) receives the OR of the error bits.
+ */
+int kvc_plan_decode_swa(int compress_ratio, int batch, const int32_t* seq_lens, const int32_t* req_pool_indices,
+                        const int32_t* req_to_token, int64_t r2t_stride, int64_t num_reqs, const int32_t* full_to_swa,
+                        int64_t num_full, int swa_page_size, int ring_size, int64_t num_state_rows,
+                        kvc_plan_d* plan_d, int32_t* status, void* stream);
+
+/*
  * kvc_write - for each valid W record k < counts[1], copy input row
  * ragged_id (all 4*hd or 2*hd elements, bit for bit) into state row
  * write_loc (c4.cuh, c4_write; compressor_v2.py,

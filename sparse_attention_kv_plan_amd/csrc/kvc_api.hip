@@ -2,6 +2,8 @@
 // checks, then one kernel launch each on the caller's stream.
 #include <stdint.h>
 
+#include <climits>
+
 #include "kvc.h"
 #include "kvc_launch.hpp"
 
@@ -31,9 +33,19 @@ KVC_EXPORT int kvc_plan_prefill(int compress_ratio, int batch, int num_q, const 
     return KVC_EINVAL;
   if ((cap_c > 0 && !aligned16(plan_c)) || (cap_w > 0 && (plan_w == nullptr || (reinterpret_cast<uintptr_t>(plan_w) & 7u))))
     return KVC_EINVAL;
-  kvc::PlanPrefillArgs a{seq_lens, extend_lens, state_index, num_state_rows, plan_c, plan_w, counts,
-                         batch,    num_q,       cap_c,       cap_w};
-  return status_of(kvc::launch_plan_prefill(compress_ratio, a, as_stream(stream)));
+  kvc::PlanPrefillArgs a{};
+  a.seq_lens = seq_lens;
+  a.extend_lens = extend_lens;
+  a.state_index = state_index;
+  a.num_state_rows = num_state_rows;
+  a.plan_c = plan_c;
+  a.plan_w = plan_w;
+  a.counts = counts;
+  a.batch = batch;
+  a.num_q = num_q;
+  a.cap_c = cap_c;
+  a.cap_w = cap_w;
+  return status_of(kvc::launch_plan_prefill(compress_ratio, false, a, as_stream(stream)));
 }
 
 KVC_EXPORT int kvc_plan_decode(int compress_ratio, int batch, const int32_t* seq_lens, const int32_t* state_index,
@@ -42,8 +54,86 @@ KVC_EXPORT int kvc_plan_decode(int compress_ratio, int batch, const int32_t* seq
     return KVC_EINVAL;
   if (!aligned4(seq_lens) || !aligned4(state_index) || !aligned16(plan_d)) return KVC_EINVAL;
   if (status != nullptr && !aligned4(status)) return KVC_EINVAL;
-  kvc::PlanDecodeArgs a{seq_lens, state_index, num_state_rows, plan_d, status, batch};
-  return status_of(kvc::launch_plan_decode(compress_ratio, a, as_stream(stream)));
+  kvc::PlanDecodeArgs a{};
+  a.seq_lens = seq_lens;
+  a.state_index = state_index;
+  a.num_state_rows = num_state_rows;
+  a.plan_d = plan_d;
+  a.status = status;
+  a.batch = batch;
+  return status_of(kvc::launch_plan_decode(compress_ratio, false, a, as_stream(stream)));
+}
+
+namespace {
+
+// Host checks of the SWA tables; fills t on success.
+bool swa_args_ok(int cr, const int32_t* req_to_token, int64_t r2t_stride, int64_t num_reqs,
+                 const int32_t* full_to_swa, int64_t num_full, int swa_page_size, int ring_size, kvc::SwaTables* t) {
+  if (swa_page_size <= 0 || ring_size <= 0 || swa_page_size % ring_size != 0 || ring_size % cr != 0) return false;
+  if (cr == 4 && ring_size % 8 != 0) return false;  // both 4-row pages of a window must be distinct rows
+  if (cr == 128 && ring_size != 128) return false;  // the ratio-128 consumer pools one 128-row page
+  if (r2t_stride <= 0 || num_reqs <= 0 || num_full < 0 || num_full > INT32_MAX) return false;
+  if (r2t_stride > INT64_MAX / num_reqs) return false;
+  if (!aligned4(req_to_token) || (num_full > 0 && !aligned4(full_to_swa))) return false;
+  *t = kvc::SwaTables{req_to_token, full_to_swa, r2t_stride, num_reqs, num_full, swa_page_size, ring_size};
+  return true;
+}
+
+}  // namespace
+
+KVC_EXPORT int kvc_plan_prefill_swa(int compress_ratio, int batch, int num_q, const int32_t* seq_lens,
+                                    const int32_t* extend_lens, const int32_t* req_pool_indices,
+                                    const int32_t* req_to_token, int64_t r2t_stride, int64_t num_reqs,
+                                    const int32_t* full_to_swa, int64_t num_full, int swa_page_size, int ring_size,
+                                    int64_t num_state_rows, kvc_plan_c* plan_c, int cap_c, kvc_plan_w* plan_w,
+                                    int cap_w, int32_t* counts, int32_t* status, void* stream) {
+  if (!ratio_ok(compress_ratio) || batch < 1 || batch > KVC_MAX_PREFILL_BATCH) return KVC_EINVAL;
+  if (num_q < batch || num_q >= KVC_MAX_TOKENS || cap_c < 0 || cap_w < 0 || !rows_ok(num_state_rows))
+    return KVC_EINVAL;
+  if (!aligned4(seq_lens) || !aligned4(extend_lens) || !aligned4(req_pool_indices) || !aligned4(counts))
+    return KVC_EINVAL;
+  if ((cap_c > 0 && !aligned16(plan_c)) || (cap_w > 0 && (plan_w == nullptr || (reinterpret_cast<uintptr_t>(plan_w) & 7u))))
+    return KVC_EINVAL;
+  if (status != nullptr && !aligned4(status)) return KVC_EINVAL;
+  kvc::PlanPrefillArgs a{};
+  if (!swa_args_ok(compress_ratio, req_to_token, r2t_stride, num_reqs, full_to_swa, num_full, swa_page_size,
+                   ring_size, &a.swa))
+    return KVC_EINVAL;
+  a.seq_lens = seq_lens;
+  a.extend_lens = extend_lens;
+  a.state_index = req_pool_indices;
+  a.num_state_rows = num_state_rows;
+  a.plan_c = plan_c;
+  a.plan_w = plan_w;
+  a.counts = counts;
+  a.status = status;
+  a.batch = batch;
+  a.num_q = num_q;
+  a.cap_c = cap_c;
+  a.cap_w = cap_w;
+  return status_of(kvc::launch_plan_prefill(compress_ratio, true, a, as_stream(stream)));
+}
+
+KVC_EXPORT int kvc_plan_decode_swa(int compress_ratio, int batch, const int32_t* seq_lens,
+                                   const int32_t* req_pool_indices, const int32_t* req_to_token, int64_t r2t_stride,
+                                   int64_t num_reqs, const int32_t* full_to_swa, int64_t num_full, int swa_page_size,
+                                   int ring_size, int64_t num_state_rows, kvc_plan_d* plan_d, int32_t* status,
+                                   void* stream) {
+  if (!ratio_ok(compress_ratio) || batch < 1 || batch > KVC_MAX_DECODE_BATCH || !rows_ok(num_state_rows))
+    return KVC_EINVAL;
+  if (!aligned4(seq_lens) || !aligned4(req_pool_indices) || !aligned16(plan_d)) return KVC_EINVAL;
+  if (status != nullptr && !aligned4(status)) return KVC_EINVAL;
+  kvc::PlanDecodeArgs a{};
+  if (!swa_args_ok(compress_ratio, req_to_token, r2t_stride, num_reqs, full_to_swa, num_full, swa_page_size,
+                   ring_size, &a.swa))
+    return KVC_EINVAL;
+  a.seq_lens = seq_lens;
+  a.state_index = req_pool_indices;
+  a.num_state_rows = num_state_rows;
+  a.plan_d = plan_d;
+  a.status = status;
+  a.batch = batch;
+  return status_of(kvc::launch_plan_decode(compress_ratio, true, a, as_stream(stream)));
 }
 
 KVC_EXPORT int kvc_write(int compress_ratio, kvc_dtype dtype, int head_dim, void* state, int64_t num_state_rows,

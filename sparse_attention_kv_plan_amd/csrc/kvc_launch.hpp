@@ -10,18 +10,31 @@
 
 namespace kvc {
 
+// SWA-paged state tables (used by the *_swa planners only)
+struct SwaTables {
+  const int32_t* req_to_token;  // [num_reqs, stride]
+  const int32_t* full_to_swa;   // [num_full]
+  int64_t stride;
+  int64_t num_reqs;
+  int64_t num_full;
+  int swa_page_size;
+  int ring_size;
+};
+
 struct PlanPrefillArgs {
   const int32_t* seq_lens;
   const int32_t* extend_lens;
-  const int32_t* state_index;
+  const int32_t* state_index;  // request pool indices in SWA mode
   int64_t num_state_rows;
   kvc_plan_c* plan_c;
   kvc_plan_w* plan_w;
   int32_t* counts;
+  int32_t* status;  // SWA mode: OR of record lookup errors (may be null)
   int batch;
   int num_q;
   int cap_c;
   int cap_w;
+  SwaTables swa;
 };
 
 struct PlanDecodeArgs {
@@ -31,6 +44,7 @@ struct PlanDecodeArgs {
   kvc_plan_d* plan_d;
   int32_t* status;
   int batch;
+  SwaTables swa;
 };
 
 struct WriteArgs {
@@ -67,8 +81,8 @@ struct DecodeArgs {
   int batch;
 };
 
-hipError_t launch_plan_prefill(int compress_ratio, const PlanPrefillArgs& a, hipStream_t stream);
-hipError_t launch_plan_decode(int compress_ratio, const PlanDecodeArgs& a, hipStream_t stream);
+hipError_t launch_plan_prefill(int compress_ratio, bool swa, const PlanPrefillArgs& a, hipStream_t stream);
+hipError_t launch_plan_decode(int compress_ratio, bool swa, const PlanDecodeArgs& a, hipStream_t stream);
 hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
 hipError_t launch_compress_c4(kvc_dtype dtype, int head_dim, const CompressArgs& a, hipStream_t stream);
 hipError_t launch_compress_c128(kvc_dtype dtype, int head_dim, const CompressArgs& a, hipStream_t stream);

@@ -1,12 +1,14 @@
 // kvc_plan.hip - prefill and decode planners (c_plan.cuh page:
 // plan_compress_prefill_kernel0 / plan_compress_prefill_legacy with the
-// per-request translation of plan_compress_prefill_legacy_kernel, and
-// plan_compress_decode_legacy_kernel).
+// per-request translation of plan_compress_prefill_legacy_kernel, the
+// SWA-paged translation of plan_compress_prefill_kernel_1, and
+// plan_compress_decode_legacy_kernel / plan_compress_decode_kernel).
 //
 // Prefill plan, one launch, no host sync, no scratch memory:
 //   stage A  every workgroup loads the <= 1024 requests (4 per thread), checks
-//            them, and forms per request e, num_c = s/r - p0/r and
-//            num_w = s - max(p0, floor(s/r)*r - overlap);
+//            them, and forms per request e, num_c = s/r - p0/r and num_w (the
+//            chunk's positions the next window needs; in SWA mode also the
+//            last 4 slots of every SWA page, counted in closed form);
 //   stage B  64-lane wavefront scans (shuffles) + a 4-wave combine in LDS
 //            give exclusive offsets of the ragged rows, C records and W
 //            records, plus the sum / OR / min / max reductions;
@@ -19,10 +21,14 @@
 //              uniform path  - when every extend is the same E <= 32 (the
 //                              multi-token-prediction shape), one thread per
 //                              token: request k / E, offset k % E, no search;
+//            in SWA mode each record's rows are looked up through
+//            req_to_token and full_to_swa as it is written;
 //   stage D  [num_c, cap_c) and [num_w, cap_w) are filled with 0xFF records.
 // Every workgroup repeats stages A/B (12 KiB of L2-resident loads), which is
 // cheaper than a second launch and needs no workspace; workgroup 0 writes
 // the counts.
+#include <algorithm>
+
 #include "kvc_device.hpp"
 #include "kvc_launch.hpp"
 
@@ -48,6 +54,37 @@ __device__ __forceinline__ int32_t loc_of(int32_t idx, int32_t pos) {
   return page_of<CR>(idx, pos) * CR + (pos & (CR - 1));
 }
 
+// State row of position pos of request rid under the SWA-paged mapping, or -1
+// when a lookup leaves its table or the row leaves the state buffer.
+template <int CR>
+__device__ __forceinline__ int64_t swa_row(const SwaTables& t, int64_t rid, int32_t pos, int64_t num_state_rows) {
+  int64_t row;
+  if constexpr (CR == 128) {
+    row = rid * t.ring_size + pos % t.ring_size;  // request-scoped ring
+  } else {
+    const int64_t full = t.req_to_token[rid * t.stride + pos];
+    if (full < 0 || full >= t.num_full) return -1;
+    const int64_t swa = t.full_to_swa[full];
+    if (swa < 0) return -1;
+    row = (swa / t.swa_page_size) * t.ring_size + swa % t.ring_size;  // the SWA page's ring
+  }
+  return (row >= 0 && row < num_state_rows) ? row : -1;
+}
+
+// Ratio-4 SWA page tails: positions p with p % sps >= sps - 4.  Count in [0, x):
+__device__ __forceinline__ int64_t tails_before(int64_t x, int sps) {
+  const int64_t r = x % sps - (sps - 4);
+  return (x / sps) * 4 + (r > 0 ? r : 0);
+}
+__device__ __forceinline__ int64_t tails_in(int64_t lo, int64_t hi, int sps) {
+  return hi > lo ? tails_before(hi, sps) - tails_before(lo, sps) : 0;
+}
+// the t-th page-tail position at or after lo
+__device__ __forceinline__ int32_t tail_pos(int64_t lo, int64_t t, int sps) {
+  const int64_t n = tails_before(lo, sps) + t;
+  return (int32_t)((n / 4) * sps + sps - 4 + n % 4);
+}
+
 struct RequestTable {
   int32_t s[KVC_MAX_PREFILL_BATCH];
   int32_t p0[KVC_MAX_PREFILL_BATCH];
@@ -57,9 +94,19 @@ struct RequestTable {
   int32_t woff[KVC_MAX_PREFILL_BATCH];  // first W record of the request
 };
 
-// C record for the compressed row closing at position pos of a request
-template <int CR>
-__device__ __forceinline__ void emit_c(kvc_plan_c* dst, int32_t pos, int32_t p0, int32_t idx, int32_t roff) {
+__device__ __forceinline__ void store_invalid_c(kvc_plan_c* dst) {
+  const u32x4 ones = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+  store16(dst, ones);
+}
+__device__ __forceinline__ void store_invalid_w(kvc_plan_w* dst) {
+  const uint2 ones = {0xFFFFFFFFu, 0xFFFFFFFFu};
+  *reinterpret_cast<uint2*>(dst) = ones;
+}
+
+// C record for the compressed row closing at position pos of batch entry b
+template <int CR, bool SWA>
+__device__ __forceinline__ void emit_c(const PlanPrefillArgs& a, kvc_plan_c* dst, int b, int32_t pos, int32_t p0,
+                                       int32_t idx, int32_t roff) {
   constexpr int32_t W = CR == 4 ? 8 : 128;
   const int32_t j = pos - p0;                                      // offset inside the chunk
   const uint32_t blen = (j + 1 < W) ? (uint32_t)(W - 1 - j) : 0u;  // window entries before the chunk
@@ -67,16 +114,44 @@ __device__ __forceinline__ void emit_c(kvc_plan_c* dst, int32_t pos, int32_t p0,
   u32x4 v;
   v.x = (uint32_t)(pos + 1);
   v.y = (uint32_t)(roff + j) | (blen << 24);
-  v.z = (uint32_t)page_of<CR>(idx, pos0);
-  v.w = (uint32_t)page_of<CR>(idx, pos);
+  if constexpr (SWA) {
+    int64_t rp0 = -1, rp1 = b;  // nothing is read from the state: left untranslated
+    if (blen > 0) {
+      const int64_t r0 = swa_row<CR>(a.swa, idx, pos0, a.num_state_rows);
+      const int64_t r1 = swa_row<CR>(a.swa, idx, pos, a.num_state_rows);
+      if (r0 < 0 || r1 < 0) {
+        if (a.status) atomicOr(a.status, KVC_DERR_INDEX);
+        store_invalid_c(dst);
+        return;
+      }
+      rp0 = r0 / CR;
+      rp1 = r1 / CR;
+    }
+    v.z = (uint32_t)(int32_t)rp0;
+    v.w = (uint32_t)(int32_t)rp1;
+  } else {
+    v.z = (uint32_t)page_of<CR>(idx, pos0);
+    v.w = (uint32_t)page_of<CR>(idx, pos);
+  }
   store16(dst, v);
 }
 
-template <int CR>
-__device__ __forceinline__ void emit_w(kvc_plan_w* dst, int32_t pos, int32_t p0, int32_t idx, int32_t roff) {
+template <int CR, bool SWA>
+__device__ __forceinline__ void emit_w(const PlanPrefillArgs& a, kvc_plan_w* dst, int32_t pos, int32_t p0,
+                                       int32_t idx, int32_t roff) {
   uint2 v;
   v.x = (uint32_t)(roff + (pos - p0));
-  v.y = (uint32_t)loc_of<CR>(idx, pos);
+  if constexpr (SWA) {
+    const int64_t row = swa_row<CR>(a.swa, idx, pos, a.num_state_rows);
+    if (row < 0) {
+      if (a.status) atomicOr(a.status, KVC_DERR_INDEX);
+      store_invalid_w(dst);
+      return;
+    }
+    v.y = (uint32_t)row;
+  } else {
+    v.y = (uint32_t)loc_of<CR>(idx, pos);
+  }
   *reinterpret_cast<uint2*>(dst) = v;
 }
 
@@ -103,10 +178,23 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v, int lane) {
   return v;
 }
 
-template <int CR>
+// First position written unconditionally: the block the next window overlaps
+// (ratio 4) or the current block (ratio 128); in SWA mode also capped at
+// s - mtp_pad, mtp_pad = min(ring_size - ratio, 4).
+template <int CR, bool SWA>
+__device__ __forceinline__ int32_t first_write(int32_t s, const SwaTables& t) {
+  int32_t fw = (s / CR) * CR - (CR == 4 ? 4 : 0);
+  if constexpr (SWA) {
+    const int32_t pad = min(t.ring_size - CR, 4);
+    fw = min(fw, s - pad);
+  }
+  return fw;
+}
+
+template <int CR, bool SWA>
 __global__ __launch_bounds__(kPlanThreads) void plan_prefill_kernel(PlanPrefillArgs a) {
   constexpr int32_t W = CR == 4 ? 8 : 128;
-  constexpr int32_t OV = CR == 4 ? 4 : 0;  // ratio 4 keeps the block the next window overlaps
+  constexpr bool kTails = SWA && CR == 4;  // ratio-4 SWA pages also keep their last 4 slots
   __shared__ RequestTable T;
   __shared__ uint32_t w_incl[kPlanWaves][3];
   __shared__ long long w_esum[kPlanWaves];
@@ -117,7 +205,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_prefill_kernel(PlanPrefillA
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1);
   const int wave = t / kWave;
-  const int64_t max_idx = a.num_state_rows / W;
+  const int64_t max_idx = SWA ? a.swa.num_reqs : a.num_state_rows / W;
+  const int sps = a.swa.swa_page_size;
 
   // ---- stage A: this thread's requests t*4 .. t*4+3 ----
   uint32_t ve[kPerThread], vc[kPerThread], vw[kPerThread];
@@ -133,13 +222,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_prefill_kernel(PlanPrefillA
       const bool ok = e >= 1 && e <= s;
       if (!ok) err |= KVC_DERR_EXTEND;
       if (idx < 0 || (int64_t)idx >= max_idx) err |= KVC_DERR_INDEX;
+      if (SWA && (int64_t)s > a.swa.stride) err |= KVC_DERR_INDEX;
       esum += e;
       const int32_t p0 = ok ? s - e : 0;
       if (ok) {
-        const int32_t fw = (s / CR) * CR - OV;
+        const int32_t fw = first_write<CR, SWA>(s, a.swa);
         ve[k] = (uint32_t)e;
         vc[k] = (uint32_t)(s / CR - p0 / CR);
-        vw[k] = (uint32_t)(s - (p0 > fw ? p0 : fw));
+        uint32_t nw = (uint32_t)(s - (p0 > fw ? p0 : fw));
+        if constexpr (kTails) nw += (uint32_t)tails_in(p0, min(fw, s), sps);
+        vw[k] = nw;
       }
       emin = min(emin, (uint32_t)e);
       emax = max(emax, (uint32_t)e);
@@ -237,57 +329,85 @@ __global__ __launch_bounds__(kPlanThreads) void plan_prefill_kernel(PlanPrefillA
       const int32_t j = k - b * E;
       const int32_t s = T.s[b], p0 = T.p0[b], idx = T.idx[b], roff = T.roff[b];
       const int32_t pos = p0 + j;
-      if (((pos + 1) & (CR - 1)) == 0) emit_c<CR>(a.plan_c + (T.coff[b] + pos / CR - p0 / CR), pos, p0, idx, roff);
-      const int32_t fw = (s / CR) * CR - OV;
-      if (pos >= fw) emit_w<CR>(a.plan_w + (T.woff[b] + pos - (p0 > fw ? p0 : fw)), pos, p0, idx, roff);
+      if (((pos + 1) & (CR - 1)) == 0)
+        emit_c<CR, SWA>(a, a.plan_c + (T.coff[b] + pos / CR - p0 / CR), b, pos, p0, idx, roff);
+      const int32_t fw = first_write<CR, SWA>(s, a.swa);
+      bool write = pos >= fw;
+      if constexpr (kTails) write = write || (pos % sps >= sps - 4);
+      if (write) {
+        // W records of this request before pos: page tails below fw, then the block from max(p0, fw)
+        int64_t before = pos >= fw ? (int64_t)pos - (p0 > fw ? p0 : fw) : 0;
+        if constexpr (kTails) before += tails_in(p0, min(pos, fw), sps);
+        emit_w<CR, SWA>(a, a.plan_w + (T.woff[b] + before), pos, p0, idx, roff);
+      }
     }
   } else {
     for (int k = gtid; k < n_c; k += gstride) {
       const int b = find_owner(T.coff, a.batch, k);
       const int32_t p0 = T.p0[b];
       const int32_t pos = (p0 / CR + 1 + (k - T.coff[b])) * CR - 1;  // (k - coff)-th boundary at or after p0
-      emit_c<CR>(a.plan_c + k, pos, p0, T.idx[b], T.roff[b]);
+      emit_c<CR, SWA>(a, a.plan_c + k, b, pos, p0, T.idx[b], T.roff[b]);
     }
     for (int k = gtid; k < n_w; k += gstride) {
       const int b = find_owner(T.woff, a.batch, k);
       const int32_t s = T.s[b], p0 = T.p0[b];
-      const int32_t fw = (s / CR) * CR - OV;
+      const int32_t fw = first_write<CR, SWA>(s, a.swa);
       const int32_t first = p0 > fw ? p0 : fw;
-      emit_w<CR>(a.plan_w + k, first + (k - T.woff[b]), p0, T.idx[b], T.roff[b]);
+      int64_t r = k - T.woff[b];
+      int32_t pos;
+      if constexpr (kTails) {
+        const int64_t nt = tails_in(p0, min(fw, s), sps);  // page tails precede the block
+        pos = r < nt ? tail_pos(p0, r, sps) : (int32_t)(first + (r - nt));
+      } else {
+        pos = (int32_t)(first + r);
+      }
+      emit_w<CR, SWA>(a, a.plan_w + k, pos, p0, T.idx[b], T.roff[b]);
     }
   }
 
   // ---- stage D: invalid padding ----
-  const u32x4 ones = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
-  for (int k = n_c + gtid; k < a.cap_c; k += gstride) store16(a.plan_c + k, ones);
-  const uint2 ones2 = {0xFFFFFFFFu, 0xFFFFFFFFu};
-  for (int k = n_w + gtid; k < a.cap_w; k += gstride) *reinterpret_cast<uint2*>(a.plan_w + k) = ones2;
+  for (int k = n_c + gtid; k < a.cap_c; k += gstride) store_invalid_c(a.plan_c + k);
+  for (int k = n_w + gtid; k < a.cap_w; k += gstride) store_invalid_w(a.plan_w + k);
 }
 
 constexpr int kDecodePlanThreads = 1024;
 
 // One workgroup; requests are independent, the error word needs the whole batch.
-template <int CR>
+template <int CR, bool SWA>
 __global__ __launch_bounds__(kDecodePlanThreads) void plan_decode_kernel(PlanDecodeArgs a) {
   constexpr int32_t W = CR == 4 ? 8 : 128;
   __shared__ int s_err;
   if (threadIdx.x == 0) s_err = 0;
   __syncthreads();
-  const int64_t max_idx = a.num_state_rows / W;
+  const int64_t max_idx = SWA ? a.swa.num_reqs : a.num_state_rows / W;
   int err = 0;
   for (int b = threadIdx.x; b < a.batch; b += kDecodePlanThreads) {
     const int32_t s = a.seq_lens[b], idx = a.state_index[b];
     int bad = 0;
     if (s <= 0) bad |= KVC_DERR_EXTEND;
     if (idx < 0 || (int64_t)idx >= max_idx) bad |= KVC_DERR_INDEX;
+    if (SWA && (int64_t)s > a.swa.stride) bad |= KVC_DERR_INDEX;
     u32x4 v = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
     if (!bad) {
       const int32_t pos1 = s - 1;  // the new token
       const int32_t pos0 = pos1 - CR > 0 ? pos1 - CR : 0;
-      v.x = (uint32_t)s;
-      v.y = (uint32_t)loc_of<CR>(idx, pos1);
-      v.z = (uint32_t)page_of<CR>(idx, pos0);
-      v.w = (uint32_t)page_of<CR>(idx, pos1);
+      if constexpr (SWA) {
+        const int64_t r0 = swa_row<CR>(a.swa, idx, pos0, a.num_state_rows);
+        const int64_t r1 = swa_row<CR>(a.swa, idx, pos1, a.num_state_rows);
+        if (r0 < 0 || r1 < 0) {
+          bad |= KVC_DERR_INDEX;
+        } else {
+          v.x = (uint32_t)s;
+          v.y = (uint32_t)r1;
+          v.z = (uint32_t)(r0 / CR);
+          v.w = (uint32_t)(r1 / CR);
+        }
+      } else {
+        v.x = (uint32_t)s;
+        v.y = (uint32_t)loc_of<CR>(idx, pos1);
+        v.z = (uint32_t)page_of<CR>(idx, pos0);
+        v.w = (uint32_t)page_of<CR>(idx, pos1);
+      }
     }
     store16(a.plan_d + b, v);
     err |= bad;
@@ -297,28 +417,32 @@ __global__ __launch_bounds__(kDecodePlanThreads) void plan_decode_kernel(PlanDec
   if (threadIdx.x == 0 && a.status) a.status[0] = s_err;
 }
 
-}  // namespace
-
-hipError_t launch_plan_prefill(int compress_ratio, const PlanPrefillArgs& a, hipStream_t stream) {
+template <int CR, bool SWA>
+hipError_t prefill_go(const PlanPrefillArgs& a, hipStream_t stream) {
   // enough workgroups that every record (or, on the uniform path, every
   // token) has a thread; the loops are grid-strided, so any count is correct
   const int64_t work = std::max<int64_t>((int64_t)a.cap_c + a.cap_w, std::min(a.num_q, a.batch * kUniformMaxExtend));
   const int grid = (int)std::min<int64_t>(1024, std::max<int64_t>(1, (work + kPlanThreads - 1) / kPlanThreads));
-  if (compress_ratio == 4) {
-    plan_prefill_kernel<4><<<grid, kPlanThreads, 0, stream>>>(a);
-  } else {
-    plan_prefill_kernel<128><<<grid, kPlanThreads, 0, stream>>>(a);
-  }
+  plan_prefill_kernel<CR, SWA><<<grid, kPlanThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
-hipError_t launch_plan_decode(int compress_ratio, const PlanDecodeArgs& a, hipStream_t stream) {
-  if (compress_ratio == 4) {
-    plan_decode_kernel<4><<<1, kDecodePlanThreads, 0, stream>>>(a);
-  } else {
-    plan_decode_kernel<128><<<1, kDecodePlanThreads, 0, stream>>>(a);
-  }
+template <int CR, bool SWA>
+hipError_t decode_go(const PlanDecodeArgs& a, hipStream_t stream) {
+  plan_decode_kernel<CR, SWA><<<1, kDecodePlanThreads, 0, stream>>>(a);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_plan_prefill(int compress_ratio, bool swa, const PlanPrefillArgs& a, hipStream_t stream) {
+  if (compress_ratio == 4) return swa ? prefill_go<4, true>(a, stream) : prefill_go<4, false>(a, stream);
+  return swa ? prefill_go<128, true>(a, stream) : prefill_go<128, false>(a, stream);
+}
+
+hipError_t launch_plan_decode(int compress_ratio, bool swa, const PlanDecodeArgs& a, hipStream_t stream) {
+  if (compress_ratio == 4) return swa ? decode_go<4, true>(a, stream) : decode_go<4, false>(a, stream);
+  return swa ? decode_go<128, true>(a, stream) : decode_go<128, false>(a, stream);
 }
 
 }  // namespace kvc

@@ -57,6 +57,8 @@ def load(build_if_missing: bool = False):
         "kvc_compress_c128": [I, I, P, L, P, I, P, P, I, P, P, P],
         "kvc_decode_c4": [I, I, P, L, P, P, P, I, P, P, P],
         "kvc_decode_c128": [I, I, P, L, P, P, P, I, P, P, P],
+        "kvc_plan_prefill_swa": [I, I, I, P, P, P, P, L, L, P, L, I, I, L, P, I, P, I, P, P, P],
+        "kvc_plan_decode_swa": [I, I, P, P, P, L, L, P, L, I, I, L, P, P, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -165,6 +167,43 @@ def plan_decode(cr, seq_lens, state_index, num_state_rows, plan_d, status=None, 
     rc = load().kvc_plan_decode(cr, seq_lens.numel(), _p(seq_lens), _p(state_index), num_state_rows, _p(plan_d),
                                 _p(status), _stream(stream))
     _check(rc, "kvc_plan_decode")
+
+
+def capacities_swa(cr: int, batch: int, num_q: int, swa_page_size: int):
+    """Record capacities that always suffice for an SWA-paged prefill chunk (ratio 4 adds up to
+    4 page-tail writes per SWA page)."""
+    cap_w = batch * (WINDOW[cr] - 1) + (4 * (num_q // swa_page_size + batch) if cr == 4 else 0)
+    return min(num_q, num_q // cr + batch), min(num_q, cap_w)
+
+
+def plan_prefill_swa(cr, seq_lens, extend_lens, req_pool_indices, req_to_token, full_to_swa, swa_page_size,
+                     ring_size, num_state_rows, num_q, plan_c, plan_w, counts, status=None, stream=None):
+    """req_to_token: int32 [num_reqs, stride]; full_to_swa: int32 [num_full]."""
+    _dev(seq_lens, extend_lens, req_pool_indices, req_to_token, full_to_swa, plan_c, plan_w, counts, status)
+    B = seq_lens.numel()
+    if extend_lens.numel() != B or req_pool_indices.numel() != B or counts.numel() < 4 or req_to_token.dim() != 2:
+        raise KvcError("one length and one request slot per request, counts 4, req_to_token 2-D")
+    _shape(plan_c, 0, C_BYTES, "plan_c")
+    _shape(plan_w, 0, W_BYTES, "plan_w")
+    rc = load().kvc_plan_prefill_swa(cr, B, num_q, _p(seq_lens), _p(extend_lens), _p(req_pool_indices),
+                                     _p(req_to_token), req_to_token.shape[1], req_to_token.shape[0],
+                                     _p(full_to_swa), full_to_swa.numel(), swa_page_size, ring_size, num_state_rows,
+                                     _p(plan_c), plan_c.shape[0], _p(plan_w), plan_w.shape[0], _p(counts),
+                                     _p(status), _stream(stream))
+    _check(rc, "kvc_plan_prefill_swa")
+
+
+def plan_decode_swa(cr, seq_lens, req_pool_indices, req_to_token, full_to_swa, swa_page_size, ring_size,
+                    num_state_rows, plan_d, status=None, stream=None):
+    _dev(seq_lens, req_pool_indices, req_to_token, full_to_swa, plan_d, status)
+    if req_pool_indices.numel() != seq_lens.numel() or req_to_token.dim() != 2:
+        raise KvcError("one request slot per request, req_to_token 2-D")
+    _shape(plan_d, seq_lens.numel(), D_BYTES, "plan_d")
+    rc = load().kvc_plan_decode_swa(cr, seq_lens.numel(), _p(seq_lens), _p(req_pool_indices), _p(req_to_token),
+                                    req_to_token.shape[1], req_to_token.shape[0], _p(full_to_swa),
+                                    full_to_swa.numel(), swa_page_size, ring_size, num_state_rows, _p(plan_d),
+                                    _p(status), _stream(stream))
+    _check(rc, "kvc_plan_decode_swa")
 
 
 def write(cr, head_dim, state, inp, plan_w, counts, stream=None):

@@ -63,6 +63,28 @@ class GpuBackend:
                         status)
         return pd.cpu().numpy(), int(status.item())
 
+    def plan_prefill_swa(self, cr, s, e, rid, r2t, f2s, sps, ring, rows, num_q, cap_c, cap_w):
+        d = self.device
+        pc, pw, counts = kvc.alloc_prefill_plan(cr, len(s), num_q, d, cap_c=cap_c, cap_w=cap_w)
+        pc.fill_(0x5A)
+        pw.fill_(0x5A)
+        counts.fill_(-7)
+        status = torch.zeros(1, dtype=torch.int32, device=d)
+        kvc.plan_prefill_swa(cr, to_dev(np.asarray(s, np.int32)), to_dev(np.asarray(e, np.int32)),
+                             to_dev(np.asarray(rid, np.int32)), to_dev(np.asarray(r2t, np.int32)),
+                             to_dev(np.asarray(f2s, np.int32)), sps, ring, int(rows), int(num_q), pc, pw, counts,
+                             status)
+        return pc.cpu().numpy(), pw.cpu().numpy(), counts.cpu().numpy(), int(status.item())
+
+    def plan_decode_swa(self, cr, s, rid, r2t, f2s, sps, ring, rows):
+        d = self.device
+        pd = torch.full((len(s), kvc.D_BYTES), 0x5A, dtype=torch.uint8, device=d)
+        status = torch.full((1,), -7, dtype=torch.int32, device=d)
+        kvc.plan_decode_swa(cr, to_dev(np.asarray(s, np.int32)), to_dev(np.asarray(rid, np.int32)),
+                            to_dev(np.asarray(r2t, np.int32)), to_dev(np.asarray(f2s, np.int32)), sps, ring,
+                            int(rows), pd, status)
+        return pd.cpu().numpy(), int(status.item())
+
     def decode(self, cr, hd, state, inp, ape, pd):
         d = self.device
         st = to_dev(state)

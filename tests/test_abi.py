@@ -19,7 +19,7 @@ def lib():
 def test_header_declares_the_boundary():
     assert kvc.header_functions() == sorted([
         "kvc_plan_prefill", "kvc_plan_decode", "kvc_write", "kvc_compress_c4", "kvc_compress_c128",
-        "kvc_decode_c4", "kvc_decode_c128", "kvc_strerror"])
+        "kvc_decode_c4", "kvc_decode_c128", "kvc_strerror", "kvc_plan_prefill_swa", "kvc_plan_decode_swa"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -65,6 +65,14 @@ def test_host_argument_checks_reject_without_enqueueing(lib):
     assert lib.kvc_compress_c4(1, 128, p, 8, p, 1, misaligned, p, 1, p, p, None) == E
     assert lib.kvc_decode_c4(1, 128, p, 8, p, p, p, 0, None, p, None) == E
     assert lib.kvc_decode_c128(1, 128, p, 8, p, p, None, 1, None, p, None) == E
+    # SWA planners: page size not a multiple of the ring, ratio-4 ring of 4, ratio-128 ring of 256
+    L = ctypes.c_int64
+    assert lib.kvc_plan_prefill_swa(4, 1, 8, p, p, p, p, L(64), L(1), p, L(64), 12, 8, L(8), p, 4, p, 8, p,
+                                    None, None) == E
+    assert lib.kvc_plan_prefill_swa(4, 1, 8, p, p, p, p, L(64), L(1), p, L(64), 16, 4, L(8), p, 4, p, 8, p,
+                                    None, None) == E
+    assert lib.kvc_plan_decode_swa(128, 1, p, p, p, L(64), L(1), p, L(64), 256, 256, L(256), p, None, None) == E
+    assert lib.kvc_plan_decode_swa(4, 1, p, p, p, L(0), L(1), p, L(64), 16, 8, L(8), p, None, None) == E
     # empty work is a no-op that needs no device
     assert lib.kvc_compress_c4(1, 128, p, 8, p, 1, p, p, 0, p, p, None) == kvc.KVC_OK
     assert lib.kvc_write(128, 1, 512, p, 8, p, 1, p, 0, p, None) == kvc.KVC_OK

@@ -1,0 +1,187 @@
+"""GPU parity of the SWA-paged planners (kvc_plan_prefill_swa, kvc_plan_decode_swa) against the
+oracle: plans, counts, padding and status bit-exact; end-to-end chunked prefill + decode through
+SWA pages (rows within tolerance, state bitwise), including a request that resumes at an SWA page
+boundary on another request's prefix pages."""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from sparse_attention_kv_plan_amd import workloads as wl  # noqa: E402
+from tests.chunked import OracleBackend, random_split, run_chunked  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+W = {4: 8, 128: 128}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tests.gpu_backend import GpuBackend
+    return GpuBackend()
+
+
+def _close(got, ref, dtype, what):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    tol = (1e-5 + 1e-5 * np.abs(ref)) if dtype == "f32" else 2e-2
+    assert np.all(np.isfinite(got)) and np.all(np.abs(got - ref) <= tol), what
+
+
+def _case(rng, cr, uniform):
+    B = int(rng.integers(1, 200))
+    prefix = rng.integers(0, 3000, size=B)
+    e = np.full(B, int(rng.integers(1, 33))) if uniform else rng.integers(1, 500, size=B)
+    s = prefix + e
+    sps = int(rng.choice([8, 16, 64, 128, 256])) if cr == 4 else int(rng.choice([128, 256, 1024]))
+    ring = int(rng.choice([r for r in (8, 16, 32) if sps % r == 0])) if cr == 4 else 128
+    num_reqs = B + int(rng.integers(0, 5))
+    stride = int(s.max()) + int(rng.integers(0, 9))
+    r2t, f2s, num_pages = wl.swa_tables(rng, stride, num_reqs, sps, stride=stride)
+    rows = num_pages * ring if cr == 4 else num_reqs * 128
+    rid = rng.permutation(num_reqs)[:B]
+    return s, e, rid, r2t, f2s, sps, ring, rows
+
+
+@pytest.mark.parametrize("cr", [4, 128])
+def test_plan_prefill_swa_fuzz(gpu, cr):
+    rng = np.random.default_rng(500 + cr)
+    for case in range(40):
+        s, e, rid, r2t, f2s, sps, ring, rows = _case(rng, cr, uniform=case % 3 == 1)
+        num_q = int(e.sum())
+        cap_c, cap_w = oracle.capacities_swa(cr, len(s), num_q, sps)
+        cap_c += int(rng.integers(0, 3))
+        cap_w += int(rng.integers(0, 3))
+        say("plan_prefill_swa cr=%d case=%d B=%d num_q=%d sps=%d ring=%d" % (cr, case, len(s), num_q, sps, ring))
+        g = gpu.plan_prefill_swa(cr, s, e, rid, r2t, f2s, sps, ring, rows, num_q, cap_c, cap_w)
+        o = oracle.plan_prefill_swa(cr, s, e, rid, r2t, f2s, sps, ring, rows, num_q, cap_c, cap_w)
+        assert g[2].tolist() == o[2].tolist() and g[3] == o[3]
+        assert np.array_equal(g[0], o[0]), "C records differ"
+        assert np.array_equal(g[1], o[1]), "W records differ"
+
+
+@pytest.mark.parametrize("cr", [4, 128])
+def test_plan_decode_swa(gpu, cr):
+    rng = np.random.default_rng(600 + cr)
+    for B in (1, 33, 1024, 5000):
+        stride = 3000
+        r2t, f2s, num_pages = wl.swa_tables(rng, stride, B + 3, 64 if cr == 4 else 128, stride=stride)
+        rows = num_pages * 8 if cr == 4 else (B + 3) * 128
+        s = rng.integers(1, stride + 1, size=B)
+        rid = rng.permutation(B + 3)[:B]
+        sps, ring = (64, 8) if cr == 4 else (128, 128)
+        say("plan_decode_swa cr=%d B=%d" % (cr, B))
+        g = gpu.plan_decode_swa(cr, s, rid, r2t, f2s, sps, ring, rows)
+        o = oracle.plan_decode_swa(cr, s, rid, r2t, f2s, sps, ring, rows)
+        assert g[1] == o[1] == 0 and np.array_equal(g[0], o[0])
+
+
+def test_swa_errors(gpu):
+    stride = 64
+    r2t = (np.arange(2)[:, None] * stride + np.arange(stride)[None, :]).astype(np.int32)
+    f2s = np.arange(2 * stride, dtype=np.int32)
+    bad = f2s.copy()
+    bad[9] = -1       # position 9 of request slot 0 has no SWA slot
+    bad[70] = 10 ** 6  # position 6 of slot 1 maps outside the state buffer
+    cases = [
+        (4, [8, 8], [4, 4], [0, 2], r2t, f2s, 64, 8, 16, 8, 6, 16),   # slot outside req_to_token
+        (4, [70], [4], [0], r2t, f2s, 64, 8, 16, 4, 6, 16),           # seq_len beyond the row
+        (4, [12], [12], [0], r2t, bad, 64, 8, 16, 12, 8, 16),         # one failed lookup
+        (4, [12, 9], [12, 9], [0, 1], r2t, bad, 64, 8, 16, 21, 8, 24),
+        (4, [12, 9], [12, 9], [0, 1], r2t, bad, 64, 8, 16, 21, 2, 24),  # capacity error: no lookups
+    ]
+    for c in cases:
+        say("swa errors", c[:4])
+        g = gpu.plan_prefill_swa(*c)
+        o = oracle.plan_prefill_swa(*c)
+        assert g[2].tolist() == o[2].tolist() and g[3] == o[3]
+        assert np.array_equal(g[0], o[0]) and np.array_equal(g[1], o[1])
+    for s in ([10, 12], [0, 7], [65, 3]):
+        g = gpu.plan_decode_swa(4, s, [0, 1], r2t, bad, 64, 8, 16)
+        o = oracle.plan_decode_swa(4, s, [0, 1], r2t, bad, 64, 8, 16)
+        assert g[1] == o[1] and np.array_equal(g[0], o[0])
+
+
+@pytest.mark.parametrize("cr,sps,ring,dtype", [(4, 16, 8, "bf16"), (4, 32, 16, "f32"), (128, 256, 128, "bf16")])
+def test_swa_chunked_prefill_then_decode(gpu, cr, sps, ring, dtype):
+    rng = np.random.default_rng(700 + sps)
+    hd = 128
+    B = 4
+    R = wl.ROW_MULT[cr] * hd
+    decode_steps = 10 if cr == 4 else 130
+    seqs, chunks = [], []
+    for b in range(B):
+        L = int(rng.integers(1, 6 * sps if cr == 4 else 700))
+        x = rng.standard_normal((L + decode_steps, R)).astype(np.float32)
+        seqs.append(wl.to_bf16_bits(x) if dtype == "bf16" else x)
+        chunks.append(random_split(rng, L, 5))
+    stride = max(len(x) for x in seqs) + 4
+    r2t, f2s, num_pages = wl.swa_tables(rng, stride, B + 2, sps, stride=stride)
+    rows = num_pages * ring if cr == 4 else (B + 2) * 128
+    swa = dict(req_to_token=r2t, full_to_swa=f2s, swa_page_size=sps, ring_size=ring, num_state_rows=rows)
+    ape_f = (0.1 * rng.standard_normal((W[cr], hd))).astype(np.float32)
+    ape = wl.to_bf16_bits(ape_f) if dtype == "bf16" else ape_f
+    idx = rng.permutation(B + 2)[:B]
+    say("swa chunked cr=%d sps=%d ring=%d chunks=%s" % (cr, sps, ring, chunks))
+    em_o, st_o = run_chunked(OracleBackend(oracle), cr, hd, dtype, seqs, chunks, decode_steps, idx, 0, ape, swa=swa)
+    em_g, st_g = run_chunked(gpu, cr, hd, dtype, seqs, chunks, decode_steps, idx, 0, ape, swa=swa)
+    assert sorted(em_o) == sorted(em_g)
+    for k in em_o:
+        _close(em_g[k], em_o[k], dtype, str(k))
+    assert np.array_equal(st_g.view(np.uint8), st_o.view(np.uint8))
+
+
+def test_swa_resume_at_page_boundary(gpu):
+    rng = np.random.default_rng(77)
+    hd, cr, sps, ring = 128, 4, 16, 8
+    R = 4 * hd
+    P = 3 * sps
+    L0, L1 = P + 2 * sps + 5, P + 2 * sps + 3
+    x0 = rng.standard_normal((L0, R)).astype(np.float32)
+    x1 = x0.copy()[:L1]
+    x1[P:] = rng.standard_normal((L1 - P, R)).astype(np.float32)
+    stride = max(L0, L1) + 8
+    r2t, f2s, num_pages = wl.swa_tables(rng, stride, 2, sps, stride=stride)
+    r2t[1, :P] = r2t[0, :P]
+    swa = dict(req_to_token=r2t, full_to_swa=f2s, swa_page_size=sps, ring_size=ring, num_state_rows=num_pages * ring)
+    ape = (0.1 * rng.standard_normal((8, hd))).astype(np.float32)
+    outs = []
+    for be in (OracleBackend(oracle), gpu):
+        em0, state = run_chunked(be, cr, hd, "f32", [x0], [[P + 2, L0 - P - 2]], 0, [0], 0, ape, swa=swa)
+        em1, state = run_chunked(be, cr, hd, "f32", [x1], [[L1 - P]], 0, [1], 0, ape, state=state, swa=swa,
+                                 start=[P])
+        outs.append((em0, em1, state))
+    (o0, o1, ost), (g0, g1, gst) = outs
+    assert sorted(o0) == sorted(g0) and sorted(o1) == sorted(g1) and (0, P + 4) in g1
+    for k in o0:
+        _close(g0[k], o0[k], "f32", str(k))
+    for k in o1:
+        _close(g1[k], o1[k], "f32", str(k))
+    assert np.array_equal(gst.view(np.uint8), ost.view(np.uint8))
+
+
+@pytest.mark.parametrize("cr", [4, 128])
+def test_swa_plan_mixed_prefill_full_size(gpu, cr):
+    """The 64-request mixed prefill (about 126k tokens) planned through SWA tables."""
+    s, e, _ = wl.config5_lens()
+    rng = np.random.default_rng(1005)
+    stride = int(s.max())
+    sps, ring = (128, 8) if cr == 4 else (128, 128)
+    r2t, f2s, num_pages = wl.swa_tables(rng, stride, 64, sps, stride=stride)
+    rows = num_pages * ring if cr == 4 else 64 * 128
+    rid = rng.permutation(64)
+    num_q = int(e.sum())
+    cap_c, cap_w = oracle.capacities_swa(cr, 64, num_q, sps)
+    say("swa full-size plan cr=%d num_q=%d" % (cr, num_q))
+    g = gpu.plan_prefill_swa(cr, s, e, rid, r2t, f2s, sps, ring, rows, num_q, cap_c, cap_w)
+    o = oracle.plan_prefill_swa(cr, s, e, rid, r2t, f2s, sps, ring, rows, num_q, cap_c, cap_w)
+    assert g[2].tolist() == o[2].tolist() and g[2][2] == 0 and g[3] == o[3] == 0
+    assert np.array_equal(g[0], o[0]) and np.array_equal(g[1], o[1])
