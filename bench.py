@@ -243,13 +243,17 @@ def main():
     torch.cuda.synchronize()
 
     # ---- timed region: exactly K steps ----
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # the dominant kernel is bracketed by events on every EVENT_EVERY-th step (each pair of events
+    # costs a few microseconds of stream time)
+    EVENT_EVERY = 4
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range((args.steps + EVENT_EVERY - 1) // EVENT_EVERY)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record(stream)
     for k in range(args.steps):
-        step(kev[k])
+        step(kev[k // EVENT_EVERY] if k % EVENT_EVERY == 0 else None)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -269,6 +273,34 @@ def main():
             bev[name].append((a, b))
     torch.cuda.synchronize()
     kernels_us = {n: round(float(np.median([a.elapsed_time(b) for a, b in v])) * 1e3, 2) for n, v in bev.items()}
+
+    # decode step alone (plan + fused decode for both ratios), eager and as a replayed HIP graph:
+    # small launch-bound kernels, where the graph removes the launch gaps
+    def decode_step():
+        for name, f in launches[6:]:
+            f()
+
+    def per_call_ms(f, n=200):
+        for _ in range(10):
+            f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            f()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    decode_us = {"eager": round(per_call_ms(decode_step) * 1e3, 2)}
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            decode_step()
+    stream.wait_stream(side)
+    decode_us["graph"] = round(per_call_ms(graph.replay) * 1e3, 2)
 
     # sanity: no device-side errors, plans as sized
     for P in (P4, P128):
@@ -322,6 +354,7 @@ def main():
             "avg_launch_us": round(dom_us, 2),
         },
         "kernels_us": kernels_us,
+        "decode_step_us": decode_us,
         "wall_s_timed": round(wall, 3),
     }
 

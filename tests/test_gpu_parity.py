@@ -352,3 +352,65 @@ def test_named_decode_workloads(gpu, name):
     assert err == 0
     assert_pool_close(out.cpu().numpy(), ref, w.dtype, w.name)
     assert np.array_equal(state.cpu().numpy().view(np.uint8), st_o.view(np.uint8))
+
+
+def test_plan_prefill_maximum_size(gpu):
+    """1024 requests and 2^24 - 1 tokens: ragged ids use all 24 bits of the C record."""
+    for cr in (4, 128):
+        rng = np.random.default_rng(99 + cr)
+        e = np.full(1024, 16384, np.int64)
+        e[-1] = (1 << 24) - 1 - int(e[:-1].sum())
+        prefix = rng.integers(0, 1 << 20, size=1024)
+        s = prefix + e
+        idx = rng.permutation(1024)
+        num_q = int(e.sum())
+        assert num_q == (1 << 24) - 1
+        cap_c, cap_w = oracle.capacities(cr, 1024, num_q)
+        say("plan_prefill maximum size cr=%d cap_c=%d" % (cr, cap_c))
+        g = gpu.plan_prefill(cr, s, e, idx, 1024 * W[cr], num_q, cap_c, cap_w)
+        o = oracle.plan_prefill(cr, s, e, idx, 1024 * W[cr], num_q, cap_c, cap_w)
+        _plans_equal(g, o)
+        last = oracle.unpack_c(g[0][g[2][0] - 1: g[2][0]])[0]
+        assert last[1] > (1 << 23)  # the high ragged-id bits are in use
+
+
+def test_prefill_chunk_under_graph_capture(gpu):
+    """A whole prefill chunk (plan, compress, write) captured in a HIP graph and replayed: every
+    replay matches the eager run.  Nothing in the path syncs, allocates or memsets."""
+    from tests.gpu_backend import to_dev
+    rng = np.random.default_rng(17)
+    w = wl.random_prefill(rng, 4, 512, "bf16", 8, prefix_hi=500, extend_lo=1, extend_hi=700, num_slots=12)
+    s_d, e_d, i_d = to_dev(w.seq_lens), to_dev(w.extend_lens), to_dev(w.state_index)
+    inp, ape = to_dev(w.input), to_dev(w.ape)
+    state0 = to_dev(w.state)
+    plan_c, plan_w, counts = kvc.alloc_prefill_plan(4, w.B, w.num_q)
+    state = state0.clone()
+    out = torch.zeros((plan_c.shape[0], w.hd), dtype=torch.float32, device="cuda")
+
+    def chunk():
+        kvc.plan_prefill(4, s_d, e_d, i_d, w.num_state_rows, w.num_q, plan_c, plan_w, counts)
+        kvc.compress_c4(w.hd, state, inp, ape, plan_c, counts, out)
+        kvc.write(4, w.hd, state, inp, plan_w, counts)
+
+    chunk()
+    torch.cuda.synchronize()
+    ref_out, ref_state, ref_counts = out.clone(), state.clone(), counts.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g = torch.cuda.CUDAGraph()
+        state.copy_(state0)
+        with torch.cuda.graph(g, stream=side):
+            chunk()
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(4):
+        say("graph replay", rep)
+        state.copy_(state0)
+        out.zero_()
+        counts.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(counts, ref_counts)
+        assert torch.equal(out, ref_out)
+        assert torch.equal(state, ref_state)
