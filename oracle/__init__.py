@@ -60,8 +60,12 @@ def _load():
         lib.oracle_decode.argtypes = [I, I, I, P, L, P, P, P, I, P]
         lib.oracle_plan_prefill_swa.argtypes = [I, I, I, P, P, P, P, L, L, P, L, I, I, L, P, I, P, I, P, P]
         lib.oracle_plan_decode_swa.argtypes = [I, I, P, P, P, L, L, P, L, I, I, L, P, P]
+        D = ctypes.c_double
+        lib.oracle_store_prefill.argtypes = [I, I, I, P, P, I, P, D, P, L, P, L, P, L]
+        lib.oracle_store_decode.argtypes = [I, I, I, P, P, I, P, D, P, L, P, L, P, L]
         for f in ("oracle_plan_prefill", "oracle_plan_decode", "oracle_compress", "oracle_write",
-                  "oracle_decode", "oracle_plan_prefill_swa", "oracle_plan_decode_swa"):
+                  "oracle_decode", "oracle_plan_prefill_swa", "oracle_plan_decode_swa", "oracle_store_prefill",
+                  "oracle_store_decode"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -190,6 +194,39 @@ def plan_decode_swa(cr, seq_lens, req_pool_indices, req_to_token, full_to_swa, s
     if rc != 0:
         raise OracleError("oracle_plan_decode_swa rejected its arguments")
     return pd, int(status[0])
+
+
+def _store(fn, cr, rows, plan, n, norm_weight, eps, freqs_cis, out_loc, cache):
+    rows = np.ascontiguousarray(rows, dtype=np.float32)
+    hd = rows.shape[1]
+    w = np.ascontiguousarray(norm_weight, dtype=np.float32)
+    freqs = np.ascontiguousarray(freqs_cis, dtype=np.float32)
+    rope_dim = 0 if freqs.size == 0 else freqs.shape[1] * 2
+    freqs = freqs.reshape(-1, max(rope_dim, 1)) if freqs.size else freqs
+    loc = _i32(out_loc)
+    cache = np.array(cache, dtype=np.float64, copy=True, order="C")
+    plan = np.ascontiguousarray(plan, dtype=np.uint8)
+    err = fn(cr, hd, rope_dim, _ptr(rows), _ptr(plan), int(n), _ptr(w), float(eps), _ptr(freqs),
+             freqs.shape[0] if freqs.size else 0, _ptr(loc), loc.size, _ptr(cache), cache.shape[0])
+    return cache, err
+
+
+def store_prefill(cr, rows, plan_c, num_c, norm_weight, eps, freqs_cis, out_loc, cache):
+    """Norm + rotary embedding + store of prefill compressed rows (float64).
+
+    rows: float32 [>= num_c, hd], row k belonging to C record k; freqs_cis:
+    float32 [max_position, rope_dim / 2, 2] (cos, sin), rope_dim = 0 when
+    empty; out_loc: int32 per ragged token; cache: float [rows, hd], copied.
+    Returns (cache with the stored rows replaced, error bits)."""
+    return _store(_load().oracle_store_prefill, cr, rows, plan_c, num_c, norm_weight, eps, freqs_cis, out_loc, cache)
+
+
+def store_decode(cr, rows, plan_d, norm_weight, eps, freqs_cis, out_loc, cache):
+    """Decode variant: rows [B, hd], out_loc int32 per request; only records
+    whose seq_len closes a block are stored."""
+    plan_d = np.ascontiguousarray(plan_d, dtype=np.uint8)
+    return _store(_load().oracle_store_decode, cr, rows, plan_d, plan_d.shape[0], norm_weight, eps, freqs_cis,
+                  out_loc, cache)
 
 
 def capacities_swa(cr, B, num_q, swa_page_size):

@@ -32,6 +32,10 @@
  *                   _c128_compress_decode_kernel: write the new token, then
  *                   pool the window if the new length is a multiple of the
  *                   ratio, else emit a zero row.
+ *   store         - compressor_v2.py, compress_norm_rope_store and the steps
+ *                   of _forward_unified_hip after the pool: RMSNorm, rotary
+ *                   embedding at seq_len - ratio, store at out_loc (the
+ *                   readings are listed beside oracle_store_prefill).
  *
  * All pooling arithmetic is float64: a two-pass softmax (max, then the sums
  * of exp(t - max) and exp(t - max) * kv).  bf16 and fp32 inputs are widened
@@ -601,4 +605,83 @@ int oracle_plan_decode_swa(int cr, int B, const int32_t* seq_lens, const int32_t
   }
   if (status) status[0] = err;
   return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* norm + rotary embedding + store of the compressed rows                    */
+/* ------------------------------------------------------------------------ */
+/*
+ * compressor_v2.py, _forward_unified_hip (steps 2 and 4) and
+ * compress_norm_rope_store: every compressed row goes through an RMSNorm over
+ * its head_dim channels, then a rotary embedding at the position of the
+ * compressed token, seq_len - ratio (_extract_positions_from_plan, clamped at
+ * 0), and is stored into the compressed cache row out_loc[...].  Readings
+ * taken here:
+ *   - RMSNorm: y_d = x_d / sqrt(mean_e x_e^2 + eps) * w_d.
+ *   - the rotated channels are the last rope_dim of the row (the stored pack
+ *     puts the un-rotated part first and the rotated part after it); channel
+ *     pairs (2k, 2k+1) of that slice are one complex number, multiplied by
+ *     freqs_cis[pos][k] = (cos, sin).
+ *   - the cache holds bf16 rows; this oracle returns the exact value (double),
+ *     the caller compares against the rounded bf16 store.
+ *   - prefill: one stored row per valid C record, at out_loc[ragged_id];
+ *     decode: one per valid D record whose seq_len closes a block, at
+ *     out_loc[b]; rows of other requests are not stored.
+ */
+static void norm_rope_row(int64_t hd, int64_t rope_dim, const float* x, const float* w, double eps,
+                          const float* cis, double* y) {
+  double ss = 0.0;
+  for (int64_t d = 0; d < hd; ++d) ss += (double)x[d] * (double)x[d];
+  const double inv = 1.0 / sqrt(ss / (double)hd + eps);
+  for (int64_t d = 0; d < hd; ++d) y[d] = (double)x[d] * inv * (double)w[d];
+  const int64_t base = hd - rope_dim;
+  for (int64_t k = 0; k < rope_dim / 2; ++k) {
+    const double re = y[base + 2 * k], im = y[base + 2 * k + 1];
+    const double c = cis[2 * k], s = cis[2 * k + 1];
+    y[base + 2 * k] = re * c - im * s;
+    y[base + 2 * k + 1] = re * s + im * c;
+  }
+}
+
+/* One record's store: row k of x at the position of seq_len into cache row
+ * out_loc[key].  Returns the error bits (nothing stored on error). */
+static int store_one(int cr, int64_t hd, int64_t rope_dim, const float* x, uint32_t seq_len, int64_t key,
+                     const float* w, double eps, const float* freqs, int64_t max_pos, const int32_t* out_loc,
+                     int64_t num_loc, double* cache, int64_t num_cache_rows) {
+  int64_t pos = (int64_t)seq_len - cr;
+  if (pos < 0) pos = 0;
+  if (key < 0 || key >= num_loc) return ERR_RECORD;
+  const int64_t loc = out_loc[key];
+  if (loc < 0 || loc >= num_cache_rows) return ERR_RECORD;
+  if (rope_dim > 0 && pos >= max_pos) return ERR_RECORD;
+  norm_rope_row(hd, rope_dim, x, w, eps, rope_dim > 0 ? freqs + pos * rope_dim : NULL, cache + loc * hd);
+  return 0;
+}
+
+int oracle_store_prefill(int cr, int hd, int rope_dim, const float* x, const uint8_t* plan_c, int num_c,
+                         const float* w, double eps, const float* freqs, int64_t max_pos, const int32_t* out_loc,
+                         int64_t num_loc, double* cache, int64_t num_cache_rows) {
+  int err = 0;
+  for (int k = 0; k < num_c; ++k) {
+    const uint8_t* r = plan_c + (size_t)k * 16;
+    const uint32_t seq_len = get_u32(r);
+    if (seq_len == 0xFFFFFFFFu) continue;
+    const int64_t ragged = get_u32(r + 4) & 0xFFFFFF;
+    err |= store_one(cr, hd, rope_dim, x + (size_t)k * hd, seq_len, ragged, w, eps, freqs, max_pos, out_loc, num_loc,
+                     cache, num_cache_rows);
+  }
+  return err;
+}
+
+int oracle_store_decode(int cr, int hd, int rope_dim, const float* x, const uint8_t* plan_d, int B, const float* w,
+                        double eps, const float* freqs, int64_t max_pos, const int32_t* out_loc, int64_t num_loc,
+                        double* cache, int64_t num_cache_rows) {
+  int err = 0;
+  for (int b = 0; b < B; ++b) {
+    const uint32_t seq_len = get_u32(plan_d + (size_t)b * 16);
+    if (seq_len == 0xFFFFFFFFu || seq_len % (uint32_t)cr != 0) continue;
+    err |= store_one(cr, hd, rope_dim, x + (size_t)b * hd, seq_len, b, w, eps, freqs, max_pos, out_loc, num_loc,
+                     cache, num_cache_rows);
+  }
+  return err;
 }

@@ -61,6 +61,22 @@ MUTANTS = [
     ("SWA ring of the wrong page", "row = (swa / sps) * ring + swa % ring;", "row = (swa / ring) * ring + swa % ring;"),
     ("SWA decode reads the overlap block from the new token's page",
      "put_u32(r + 8, as_u32((int32_t)(row0 / cr)));", "put_u32(r + 8, as_u32((int32_t)(row1 / cr)));"),
+    ("rotation sin sign flipped",
+     "y[base + 2 * k] = re * c - im * s;\n    y[base + 2 * k + 1] = re * s + im * c;",
+     "y[base + 2 * k] = re * c + im * s;\n    y[base + 2 * k + 1] = -re * s + im * c;"),
+    ("rotated channels at the head of the row", "const int64_t base = hd - rope_dim;", "const int64_t base = 0;"),
+    ("rotary pairs split in halves", "const double re = y[base + 2 * k], im = y[base + 2 * k + 1];",
+     "const double re = y[base + k], im = y[base + k + rope_dim / 2];"),
+    ("norm eps dropped", "sqrt(ss / (double)hd + eps)", "sqrt(ss / (double)hd)"),
+    ("norm over the sum, not the mean", "sqrt(ss / (double)hd + eps)", "sqrt(ss + eps)"),
+    ("norm weight dropped", "y[d] = (double)x[d] * inv * (double)w[d];", "y[d] = (double)x[d] * inv;"),
+    ("rotary position one late", "int64_t pos = (int64_t)seq_len - cr;", "int64_t pos = (int64_t)seq_len - cr + 1;"),
+    ("table row stride halved", "freqs + pos * rope_dim : NULL", "freqs + pos * (rope_dim / 2) : NULL"),
+    ("decode stores rows that close no block",
+     "if (seq_len == 0xFFFFFFFFu || seq_len % (uint32_t)cr != 0) continue;", "if (seq_len == 0xFFFFFFFFu) continue;"),
+    ("prefill location by record, not ragged id", "x + (size_t)k * hd, seq_len, ragged,", "x + (size_t)k * hd, seq_len, k,"),
+    ("store location range unchecked", "if (loc < 0 || loc >= num_cache_rows) return ERR_RECORD;",
+     "if (loc < 0) return ERR_RECORD;"),
 ]
 
 
@@ -87,6 +103,7 @@ def test_pins_catch_mutant(tmp_path, mutant):
     env = dict(os.environ, KVC_ORACLE_LIB=str(lib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_pins.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_swa_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_swa_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_store_pins.py")],
                        cwd=ROOT, env=env, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, timeout=600)
     assert r.returncode != 0, "pins did not catch mutant '%s':\n%s" % (name, r.stdout.decode()[-2000:])
