@@ -274,6 +274,74 @@ int kvc_decode_c128(kvc_dtype dtype, int head_dim, void* state, int64_t num_stat
                     const void* ape, const kvc_plan_d* plan_d, int batch, int32_t* status, float* out,
                     void* stream);
 
+/*
+ * Norm, rotary embedding and store of the compressed rows (compressor_v2.py
+ * page: compress_norm_rope_store, and the steps of _forward_unified_hip that
+ * follow the pool).  Each stored row x (head_dim fp32 channels) becomes
+ *
+ *     y_d = x_d / sqrt(mean_e x_e^2 + eps) * norm_weight[d]      (RMSNorm)
+ *
+ * then its last rope_dim channels, taken as rope_dim/2 complex numbers
+ * (y[2k] + i y[2k+1] of that slice), are multiplied by
+ * freqs_cis[pos][k] = cos + i sin, pos = seq_len - compress_ratio of the
+ * record (_extract_positions_from_plan; never negative for a stored row), and
+ * y is rounded to bf16 (nearest even) into cache row out_loc[key].  Prefill:
+ * one stored row per valid C record, key = its ragged_id.  Decode: one per
+ * valid D record whose seq_len is a multiple of the ratio, key = b; the rows
+ * of the other requests are not stored (the pages store a zero row at
+ * location 0 for them).  The fp8 / fp4 cache packs and the indexer's
+ * Hadamard rotation are not part of this step.  Arithmetic is fp32.
+ * A record whose key, location or position falls outside num_loc,
+ * num_cache_rows or max_position (position checked only when rope_dim > 0)
+ * is not stored and sets KVC_DERR_RECORD (prefill: counts[3]; decode:
+ * *status, may be NULL).  Two stored rows of one call must not share a
+ * location.
+ */
+typedef struct kvc_store_args {
+  const float* norm_weight; /* device fp32 [head_dim] */
+  const float* freqs_cis;   /* device fp32 [max_position, rope_dim / 2, 2] (cos, sin); unused if rope_dim == 0 */
+  const int32_t* out_loc;   /* device int32 [num_loc]: cache row per ragged token (prefill) or request (decode) */
+  uint16_t* cache;          /* device bf16 bit patterns [num_cache_rows, head_dim] */
+  int64_t num_loc;          /* 0 .. INT32_MAX */
+  int64_t max_position;     /* rows of freqs_cis, >= 0 */
+  int64_t num_cache_rows;   /* 0 .. INT32_MAX */
+  float eps;                /* >= 0, finite */
+  int32_t rope_dim;         /* 0 .. head_dim, a multiple of 8 */
+} kvc_store_args;
+
+/*
+ * kvc_norm_rope_store_prefill - store the compressed rows of a prefill
+ * chunk: row k of `rows` (float32 [cap_c, head_dim], as kvc_compress_c4 /
+ * kvc_compress_c128 leave it) for every valid C record k < counts[0].
+ * `args` is a HOST pointer, read during the call.
+ */
+int kvc_norm_rope_store_prefill(int compress_ratio, int head_dim, const float* rows, const kvc_plan_c* plan_c,
+                                int cap_c, int32_t* counts, const kvc_store_args* args, void* stream);
+
+/*
+ * kvc_norm_rope_store_decode - store the rows of a decode step that close a
+ * block: row b of `rows` (float32 [batch, head_dim], as kvc_decode_c4 /
+ * kvc_decode_c128 leave it) for every valid D record b with
+ * seq_len % compress_ratio == 0.  `args` is a HOST pointer.
+ */
+int kvc_norm_rope_store_decode(int compress_ratio, int head_dim, const float* rows, const kvc_plan_d* plan_d,
+                               int batch, int32_t* status, const kvc_store_args* args, void* stream);
+
+/*
+ * kvc_compress_c4_norm_rope_store / kvc_compress_c128_norm_rope_store -
+ * kvc_compress_c4 / kvc_compress_c128 followed by
+ * kvc_norm_rope_store_prefill in one kernel: the pooled row stays in
+ * registers and only its bf16 form reaches HBM (no float32 rows).  Same
+ * arguments as the pool, with `args` (HOST pointer) in place of `out`; the
+ * stored values are those of the two calls in sequence, up to fp32 rounding.
+ */
+int kvc_compress_c4_norm_rope_store(kvc_dtype dtype, int head_dim, const void* state, int64_t num_state_rows,
+                                    const void* input, int num_q, const void* ape, const kvc_plan_c* plan_c,
+                                    int cap_c, int32_t* counts, const kvc_store_args* args, void* stream);
+int kvc_compress_c128_norm_rope_store(kvc_dtype dtype, int head_dim, const void* state, int64_t num_state_rows,
+                                      const void* input, int num_q, const void* ape, const kvc_plan_c* plan_c,
+                                      int cap_c, int32_t* counts, const kvc_store_args* args, void* stream);
+
 /* kvc_strerror - static text for a host return code or a device error bit. */
 const char* kvc_strerror(int code);
 

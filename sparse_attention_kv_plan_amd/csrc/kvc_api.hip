@@ -3,6 +3,7 @@
 #include <stdint.h>
 
 #include <climits>
+#include <cmath>
 
 #include "kvc.h"
 #include "kvc_launch.hpp"
@@ -152,17 +153,42 @@ KVC_EXPORT int kvc_write(int compress_ratio, kvc_dtype dtype, int head_dim, void
 
 namespace {
 
+// Host checks of the norm / rotary / store parameters.
+bool store_args_ok(int hd, const kvc_store_args* st) {
+  if (st == nullptr) return false;
+  if (st->rope_dim < 0 || st->rope_dim > hd || st->rope_dim % 8 != 0) return false;
+  if (!(st->eps >= 0.f) || !std::isfinite(st->eps)) return false;
+  if (st->num_loc < 0 || st->num_loc > INT32_MAX || !rows_ok(st->num_cache_rows) || st->max_position < 0)
+    return false;
+  if (st->max_position > INT32_MAX) return false;
+  if (!aligned16(st->norm_weight)) return false;
+  if (st->num_cache_rows > 0 && !aligned16(st->cache)) return false;
+  if (st->num_loc > 0 && !aligned4(st->out_loc)) return false;
+  if (st->rope_dim > 0 && st->max_position > 0 && !aligned16(st->freqs_cis)) return false;
+  return true;
+}
+
+// out != nullptr: pool into float32 rows; st != nullptr: pool + norm + rotary + store
 int compress_common(bool c4, kvc_dtype dtype, int head_dim, const void* state, int64_t num_state_rows,
                     const void* input, int num_q, const void* ape, const kvc_plan_c* plan_c, int cap_c,
-                    int32_t* counts, float* out, void* stream) {
+                    int32_t* counts, float* out, const kvc_store_args* st, void* stream) {
   if (!dtype_ok(dtype) || !hd_ok(head_dim) || !rows_ok(num_state_rows)) return KVC_EINVAL;
   if (num_q < 0 || num_q >= KVC_MAX_TOKENS || cap_c < 0 || !aligned4(counts)) return KVC_EINVAL;
+  if (st != nullptr && !store_args_ok(head_dim, st)) return KVC_EINVAL;
   if (cap_c == 0) return KVC_OK;
-  if (!aligned16(input) || !aligned16(ape) || !aligned16(plan_c) || !aligned16(out)) return KVC_EINVAL;
+  if (!aligned16(input) || !aligned16(ape) || !aligned16(plan_c)) return KVC_EINVAL;
+  if (st == nullptr && !aligned16(out)) return KVC_EINVAL;
   if (num_state_rows > 0 && !aligned16(state)) return KVC_EINVAL;
-  kvc::CompressArgs a{state, input, ape, plan_c, counts, out, num_state_rows, num_q, cap_c};
-  const hipError_t e = c4 ? kvc::launch_compress_c4(dtype, head_dim, a, as_stream(stream))
-                          : kvc::launch_compress_c128(dtype, head_dim, a, as_stream(stream));
+  kvc::CompressArgs a{state, input, ape, plan_c, counts, out, num_state_rows, num_q, cap_c, {}};
+  hipError_t e;
+  if (st != nullptr) {
+    a.st = *st;
+    e = c4 ? kvc::launch_compress_c4_store(dtype, head_dim, a, as_stream(stream))
+           : kvc::launch_compress_c128_store(dtype, head_dim, a, as_stream(stream));
+  } else {
+    e = c4 ? kvc::launch_compress_c4(dtype, head_dim, a, as_stream(stream))
+           : kvc::launch_compress_c128(dtype, head_dim, a, as_stream(stream));
+  }
   return status_of(e);
 }
 
@@ -185,14 +211,55 @@ KVC_EXPORT int kvc_compress_c4(kvc_dtype dtype, int head_dim, const void* state,
                                const void* input, int num_q, const void* ape, const kvc_plan_c* plan_c, int cap_c,
                                int32_t* counts, float* out, void* stream) {
   return compress_common(true, dtype, head_dim, state, num_state_rows, input, num_q, ape, plan_c, cap_c, counts, out,
-                         stream);
+                         nullptr, stream);
 }
 
 KVC_EXPORT int kvc_compress_c128(kvc_dtype dtype, int head_dim, const void* state, int64_t num_state_rows,
                                  const void* input, int num_q, const void* ape, const kvc_plan_c* plan_c, int cap_c,
                                  int32_t* counts, float* out, void* stream) {
   return compress_common(false, dtype, head_dim, state, num_state_rows, input, num_q, ape, plan_c, cap_c, counts,
-                         out, stream);
+                         out, nullptr, stream);
+}
+
+KVC_EXPORT int kvc_compress_c4_norm_rope_store(kvc_dtype dtype, int head_dim, const void* state,
+                                               int64_t num_state_rows, const void* input, int num_q, const void* ape,
+                                               const kvc_plan_c* plan_c, int cap_c, int32_t* counts,
+                                               const kvc_store_args* args, void* stream) {
+  if (args == nullptr) return KVC_EINVAL;
+  return compress_common(true, dtype, head_dim, state, num_state_rows, input, num_q, ape, plan_c, cap_c, counts,
+                         nullptr, args, stream);
+}
+
+KVC_EXPORT int kvc_compress_c128_norm_rope_store(kvc_dtype dtype, int head_dim, const void* state,
+                                                 int64_t num_state_rows, const void* input, int num_q, const void* ape,
+                                                 const kvc_plan_c* plan_c, int cap_c, int32_t* counts,
+                                                 const kvc_store_args* args, void* stream) {
+  if (args == nullptr) return KVC_EINVAL;
+  return compress_common(false, dtype, head_dim, state, num_state_rows, input, num_q, ape, plan_c, cap_c, counts,
+                         nullptr, args, stream);
+}
+
+KVC_EXPORT int kvc_norm_rope_store_prefill(int compress_ratio, int head_dim, const float* rows,
+                                           const kvc_plan_c* plan_c, int cap_c, int32_t* counts,
+                                           const kvc_store_args* args, void* stream) {
+  if (!ratio_ok(compress_ratio) || !hd_ok(head_dim) || cap_c < 0 || cap_c >= KVC_MAX_TOKENS || !aligned4(counts))
+    return KVC_EINVAL;
+  if (!store_args_ok(head_dim, args)) return KVC_EINVAL;
+  if (cap_c == 0) return KVC_OK;
+  if (!aligned16(rows) || !aligned16(plan_c)) return KVC_EINVAL;
+  const kvc::NormRopeStoreArgs a{rows, plan_c, nullptr, counts, nullptr, cap_c, compress_ratio, *args};
+  return status_of(kvc::launch_norm_rope_store(head_dim, false, a, as_stream(stream)));
+}
+
+KVC_EXPORT int kvc_norm_rope_store_decode(int compress_ratio, int head_dim, const float* rows,
+                                          const kvc_plan_d* plan_d, int batch, int32_t* status,
+                                          const kvc_store_args* args, void* stream) {
+  if (!ratio_ok(compress_ratio) || !hd_ok(head_dim) || batch < 1 || batch > KVC_MAX_DECODE_BATCH) return KVC_EINVAL;
+  if (!store_args_ok(head_dim, args)) return KVC_EINVAL;
+  if (!aligned16(rows) || !aligned16(plan_d)) return KVC_EINVAL;
+  if (status != nullptr && !aligned4(status)) return KVC_EINVAL;
+  const kvc::NormRopeStoreArgs a{rows, nullptr, plan_d, nullptr, status, batch, compress_ratio, *args};
+  return status_of(kvc::launch_norm_rope_store(head_dim, true, a, as_stream(stream)));
 }
 
 KVC_EXPORT int kvc_decode_c4(kvc_dtype dtype, int head_dim, void* state, int64_t num_state_rows, const void* input,

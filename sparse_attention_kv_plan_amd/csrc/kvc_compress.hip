@@ -16,24 +16,29 @@
 #include "kvc_device.hpp"
 #include "kvc_launch.hpp"
 #include "kvc_pool.hpp"
+#include "kvc_store.hpp"
 
 namespace kvc {
 namespace {
 
 constexpr int kThreads = 256;
 
-template <typename T, int HD>
+// STORE = false: the pooled rows go to a.out as float32.  STORE = true: the
+// row is normalised, rotated and stored as bf16 into the compressed cache
+// (a.st) straight from registers.
+template <typename T, int HD, bool STORE>
 __global__ __launch_bounds__(kThreads) void compress_c4_kernel(CompressArgs a) {
-  typedef typename Elem<T>::storage E;
   constexpr int V = Elem<T>::kVec;
   constexpr int kLanes = HD / V;
   constexpr int kRows = kThreads / kLanes;
-  __shared__ float stage[kThreads * V];  // the workgroup's output rows
   const int64_t row = (int64_t)blockIdx.x * kRows + threadIdx.x / kLanes;
   const int lane = threadIdx.x % kLanes;
   const int c = lane * V;
   bool live = row < a.counts[0] && row < a.cap_c;
   float res[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) res[v] = 0.f;
+  int64_t pos = 0, loc = 0;
   if (live) {
     const kvc_plan_c rec = load_plan_c(a.plan_c + row);
     const int64_t ragged = rec.ragged_blen & 0xFFFFFFu;
@@ -45,10 +50,17 @@ __global__ __launch_bounds__(kThreads) void compress_c4_kernel(CompressArgs a) {
       if (c == 0) atomicOr(a.counts + 3, KVC_DERR_RECORD);
       live = false;
     }
+    if constexpr (STORE) {
+      pos = rec.seq_len >= 4u ? (int64_t)rec.seq_len - 4 : 0;
+      if (live && !store_target(a.st, ragged, pos, &loc)) {
+        if (c == 0) atomicOr(a.counts + 3, KVC_DERR_RECORD);
+        live = false;
+      }
+    }
     if (live) {
-      const E* state = static_cast<const E*>(a.state);
-      const E* input = static_cast<const E*>(a.input);
-      const E* ape = static_cast<const E*>(a.ape);
+      const typename Elem<T>::storage* state = static_cast<const typename Elem<T>::storage*>(a.state);
+      const typename Elem<T>::storage* input = static_cast<const typename Elem<T>::storage*>(a.input);
+      const typename Elem<T>::storage* ape = static_cast<const typename Elem<T>::storage*>(a.ape);
       if (first_block) {
         c4_pool<T, HD, 4>(state, input, ape, ragged, blen, rp0, rp1, c, res);
       } else {
@@ -56,22 +68,32 @@ __global__ __launch_bounds__(kThreads) void compress_c4_kernel(CompressArgs a) {
       }
     }
   }
-  // A lane holds V adjacent channels, so storing them directly would write
-  // 16-byte pieces at a 4*V-byte stride.  Staging the row in LDS lets every
-  // store instruction write 64 x 16 contiguous bytes instead.
-  float* w = stage + (threadIdx.x / kLanes) * HD;
-  store_floats<V>(w + c, res);
-  __syncthreads();
-  if (live) {
+  if constexpr (STORE) {
+    __shared__ float red[kThreads / kWave];
+    float ss = 0.f;
 #pragma unroll
-    for (int k = 0; k < V / 4; ++k) {
-      const int ch = k * (kLanes * 4) + lane * 4;
-      store16_stream(a.out + row * HD + ch, load16(w + ch));  // written once, read by a later kernel
+    for (int v = 0; v < V; ++v) ss = fmaf(res[v], res[v], ss);
+    ss = row_sum<kLanes>(ss, red);  // reached by every thread (rows wider than a wave sync)
+    if (live) norm_rope_store<V, HD>(res, ss, c, pos, loc, a.st);
+  } else {
+    // A lane holds V adjacent channels, so storing them directly would write
+    // 16-byte pieces at a 4*V-byte stride.  Staging the row in LDS lets every
+    // store instruction write 64 x 16 contiguous bytes instead.
+    __shared__ float stage[kThreads * V];  // the workgroup's output rows
+    float* w = stage + (threadIdx.x / kLanes) * HD;
+    store_floats<V>(w + c, res);
+    __syncthreads();
+    if (live) {
+#pragma unroll
+      for (int k = 0; k < V / 4; ++k) {
+        const int ch = k * (kLanes * 4) + lane * 4;
+        store16_stream(a.out + row * HD + ch, load16(w + ch));  // written once, read by a later kernel
+      }
     }
   }
 }
 
-template <typename T, int HD>
+template <typename T, int HD, bool STORE>
 __global__ __launch_bounds__(kThreads) void compress_c128_kernel(CompressArgs a) {
   typedef typename Elem<T>::storage E;
   typedef C128Pool<T, HD, kThreads> Pool;
@@ -83,12 +105,32 @@ __global__ __launch_bounds__(kThreads) void compress_c128_kernel(CompressArgs a)
   const int64_t ragged = rec.ragged_blen & 0xFFFFFFu;
   const int blen = (int)(rec.ragged_blen >> 24);
   const int64_t rp0 = rec.read_page_0;
-  if (!c128_record_ok(ragged, blen, rp0, a.num_q, a.num_state_rows)) {
+  bool ok = c128_record_ok(ragged, blen, rp0, a.num_q, a.num_state_rows);
+  const int64_t pos = rec.seq_len >= 128u ? (int64_t)rec.seq_len - 128 : 0;
+  int64_t loc = 0;
+  if constexpr (STORE) ok = ok && store_target(a.st, ragged, pos, &loc);
+  if (!ok) {  // the whole workgroup leaves: nothing below is reached by part of it
     if (threadIdx.x == 0) atomicOr(a.counts + 3, KVC_DERR_RECORD);
     return;
   }
-  Pool::run(static_cast<const E*>(a.state), static_cast<const E*>(a.input), static_cast<const E*>(a.ape), ragged,
-            blen, rp0, 0, a.out + row * HD, lds);
+  const E* state = static_cast<const E*>(a.state);
+  const E* input = static_cast<const E*>(a.input);
+  const E* ape = static_cast<const E*>(a.ape);
+  if constexpr (STORE) {
+    // thread t ends with channels 2t, 2t+1 (a rotary pair); threads past HD/2 hold zeros
+    __shared__ float red[kThreads / kWave];
+    Pool::accumulate(state, input, ape, ragged, blen, rp0, 0, lds);
+    const int c = 2 * threadIdx.x;
+    float x[2] = {0.f, 0.f};
+    if (c < HD) {
+      x[0] = Pool::merged(lds, c);
+      x[1] = Pool::merged(lds, c + 1);
+    }
+    const float ss = block_sum<kThreads>(fmaf(x[0], x[0], x[1] * x[1]), red);
+    if (c < HD) norm_rope_store<2, HD>(x, ss, c, pos, loc, a.st);
+  } else {
+    Pool::run(state, input, ape, ragged, blen, rp0, 0, a.out + row * HD, lds);
+  }
 }
 
 constexpr int kWriteRowsPerBlock = kThreads / kWave;
@@ -120,17 +162,17 @@ __global__ __launch_bounds__(kThreads) void write_kernel(WriteArgs a) {
   for (int u = 0; u < PER; ++u) store16_stream(dst + (int64_t)(lane + u * kWave) * 16, buf[u]);
 }
 
-template <typename T, int HD>
+template <typename T, int HD, bool STORE>
 hipError_t c4_launch(const CompressArgs& a, hipStream_t stream) {
   constexpr int kRows = kThreads / (HD / Elem<T>::kVec);
   const int grid = (a.cap_c + kRows - 1) / kRows;
-  compress_c4_kernel<T, HD><<<grid, kThreads, 0, stream>>>(a);
+  compress_c4_kernel<T, HD, STORE><<<grid, kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
-template <typename T, int HD>
+template <typename T, int HD, bool STORE>
 hipError_t c128_launch(const CompressArgs& a, hipStream_t stream) {
-  compress_c128_kernel<T, HD><<<a.cap_c, kThreads, 0, stream>>>(a);
+  compress_c128_kernel<T, HD, STORE><<<a.cap_c, kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -148,11 +190,19 @@ hipError_t dispatch(kvc_dtype dtype, int hd, const Args& a, hipStream_t stream) 
 
 template <typename T, int HD>
 struct C4Go {
-  static hipError_t go(const CompressArgs& a, hipStream_t s) { return c4_launch<T, HD>(a, s); }
+  static hipError_t go(const CompressArgs& a, hipStream_t s) { return c4_launch<T, HD, false>(a, s); }
 };
 template <typename T, int HD>
 struct C128Go {
-  static hipError_t go(const CompressArgs& a, hipStream_t s) { return c128_launch<T, HD>(a, s); }
+  static hipError_t go(const CompressArgs& a, hipStream_t s) { return c128_launch<T, HD, false>(a, s); }
+};
+template <typename T, int HD>
+struct C4StoreGo {
+  static hipError_t go(const CompressArgs& a, hipStream_t s) { return c4_launch<T, HD, true>(a, s); }
+};
+template <typename T, int HD>
+struct C128StoreGo {
+  static hipError_t go(const CompressArgs& a, hipStream_t s) { return c128_launch<T, HD, true>(a, s); }
 };
 
 }  // namespace
@@ -163,6 +213,14 @@ hipError_t launch_compress_c4(kvc_dtype dtype, int head_dim, const CompressArgs&
 
 hipError_t launch_compress_c128(kvc_dtype dtype, int head_dim, const CompressArgs& a, hipStream_t stream) {
   return dispatch<C128Go>(dtype, head_dim, a, stream);
+}
+
+hipError_t launch_compress_c4_store(kvc_dtype dtype, int head_dim, const CompressArgs& a, hipStream_t stream) {
+  return dispatch<C4StoreGo>(dtype, head_dim, a, stream);
+}
+
+hipError_t launch_compress_c128_store(kvc_dtype dtype, int head_dim, const CompressArgs& a, hipStream_t stream) {
+  return dispatch<C128StoreGo>(dtype, head_dim, a, stream);
 }
 
 hipError_t launch_write(const WriteArgs& a, hipStream_t stream) {

@@ -64,10 +64,11 @@ struct CompressArgs {
   const void* ape;
   const kvc_plan_c* plan_c;
   int32_t* counts;
-  float* out;
+  float* out;  // pool only
   int64_t num_state_rows;
   int num_q;
   int cap_c;
+  kvc_store_args st;  // pool + norm + rotary + store only
 };
 
 struct DecodeArgs {
@@ -81,11 +82,26 @@ struct DecodeArgs {
   int batch;
 };
 
+// norm + rotary + store of float32 rows (prefill: plan_c / counts; decode: plan_d / status)
+struct NormRopeStoreArgs {
+  const float* rows;
+  const kvc_plan_c* plan_c;
+  const kvc_plan_d* plan_d;
+  int32_t* counts;
+  int32_t* status;
+  int n;  // cap_c or batch
+  int compress_ratio;
+  kvc_store_args st;
+};
+
 hipError_t launch_plan_prefill(int compress_ratio, bool swa, const PlanPrefillArgs& a, hipStream_t stream);
 hipError_t launch_plan_decode(int compress_ratio, bool swa, const PlanDecodeArgs& a, hipStream_t stream);
 hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
 hipError_t launch_compress_c4(kvc_dtype dtype, int head_dim, const CompressArgs& a, hipStream_t stream);
 hipError_t launch_compress_c128(kvc_dtype dtype, int head_dim, const CompressArgs& a, hipStream_t stream);
+hipError_t launch_compress_c4_store(kvc_dtype dtype, int head_dim, const CompressArgs& a, hipStream_t stream);
+hipError_t launch_compress_c128_store(kvc_dtype dtype, int head_dim, const CompressArgs& a, hipStream_t stream);
+hipError_t launch_norm_rope_store(int head_dim, bool decode, const NormRopeStoreArgs& a, hipStream_t stream);
 hipError_t launch_decode_c4(kvc_dtype dtype, int head_dim, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_c128(kvc_dtype dtype, int head_dim, const DecodeArgs& a, hipStream_t stream);
 

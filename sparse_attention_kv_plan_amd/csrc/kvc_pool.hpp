@@ -103,10 +103,12 @@ struct C128Pool {
   static constexpr int kLdsFloats = 3 * S * HDW;
   static_assert(HD % CS == 0 && NT % kLanes == 0 && 128 % S == 0 && PER % U == 0, "bad c128 pool shape");
 
-  __device__ __forceinline__ static void run(const typename Elem<T>::storage* __restrict__ state,
-                                             const typename Elem<T>::storage* __restrict__ input,
-                                             const typename Elem<T>::storage* __restrict__ ape, int64_t ragged,
-                                             int blen, int64_t rp0, int cs, float* __restrict__ out_row, float* lds) {
+  // Every stream's partial (max, sum, weighted sum) per channel of the slice,
+  // left in lds (kLdsFloats) behind a workgroup barrier.
+  __device__ __forceinline__ static void accumulate(const typename Elem<T>::storage* __restrict__ state,
+                                                    const typename Elem<T>::storage* __restrict__ input,
+                                                    const typename Elem<T>::storage* __restrict__ ape,
+                                                    int64_t ragged, int blen, int64_t rp0, int cs, float* lds) {
     constexpr int64_t R = 2 * HD;
     const int sid = threadIdx.x / kLanes;
     const int cl = (threadIdx.x % kLanes) * V;  // channel inside the slice
@@ -165,19 +167,33 @@ struct C128Pool {
     store_floats<V>(ll + sid * HDW + cl, l);
     store_floats<V>(la + sid * HDW + cl, acc);
     __syncthreads();
-    for (int d = threadIdx.x; d < HDW; d += NT) {
-      float M = lm[d];
+  }
+
+  // The pooled value of channel d of the slice, merged from the partials.
+  __device__ __forceinline__ static float merged(const float* lds, int d) {
+    const float* lm = lds;
+    const float* ll = lds + S * HDW;
+    const float* la = lds + 2 * S * HDW;
+    float M = lm[d];
 #pragma unroll
-      for (int s = 1; s < S; ++s) M = fmaxf(M, lm[s * HDW + d]);
-      float Lsum = 0.f, Asum = 0.f;
+    for (int s = 1; s < S; ++s) M = fmaxf(M, lm[s * HDW + d]);
+    float Lsum = 0.f, Asum = 0.f;
 #pragma unroll
-      for (int s = 0; s < S; ++s) {
-        const float f = exp2_hw((lm[s * HDW + d] - M) * kLog2e);
-        Lsum = fmaf(ll[s * HDW + d], f, Lsum);
-        Asum = fmaf(la[s * HDW + d], f, Asum);
-      }
-      __builtin_nontemporal_store(Asum / Lsum, out_row + cs * HDW + d);
+    for (int s = 0; s < S; ++s) {
+      const float f = exp2_hw((lm[s * HDW + d] - M) * kLog2e);
+      Lsum = fmaf(ll[s * HDW + d], f, Lsum);
+      Asum = fmaf(la[s * HDW + d], f, Asum);
     }
+    return Asum / Lsum;
+  }
+
+  // accumulate, then the slice's channels into out_row (streaming stores)
+  __device__ __forceinline__ static void run(const typename Elem<T>::storage* __restrict__ state,
+                                             const typename Elem<T>::storage* __restrict__ input,
+                                             const typename Elem<T>::storage* __restrict__ ape, int64_t ragged,
+                                             int blen, int64_t rp0, int cs, float* __restrict__ out_row, float* lds) {
+    accumulate(state, input, ape, ragged, blen, rp0, cs, lds);
+    for (int d = threadIdx.x; d < HDW; d += NT) __builtin_nontemporal_store(merged(lds, d), out_row + cs * HDW + d);
   }
 };
 

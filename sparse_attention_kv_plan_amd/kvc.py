@@ -59,6 +59,10 @@ def load(build_if_missing: bool = False):
         "kvc_decode_c128": [I, I, P, L, P, P, P, I, P, P, P],
         "kvc_plan_prefill_swa": [I, I, I, P, P, P, P, L, L, P, L, I, I, L, P, I, P, I, P, P, P],
         "kvc_plan_decode_swa": [I, I, P, P, P, L, L, P, L, I, I, L, P, P, P],
+        "kvc_norm_rope_store_prefill": [I, I, P, P, I, P, P, P],
+        "kvc_norm_rope_store_decode": [I, I, P, P, I, P, P, P],
+        "kvc_compress_c4_norm_rope_store": [I, I, P, L, P, I, P, P, I, P, P, P],
+        "kvc_compress_c128_norm_rope_store": [I, I, P, L, P, I, P, P, I, P, P, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -243,6 +247,83 @@ def compress_c128(head_dim, state, inp, ape, plan_c, counts, out, stream=None):
 
 def compress(cr, head_dim, state, inp, ape, plan_c, counts, out, stream=None):
     (compress_c4 if cr == 4 else compress_c128)(head_dim, state, inp, ape, plan_c, counts, out, stream)
+
+
+# --------------------------------------------------------------------------
+# norm + rotary embedding + bf16 store of the compressed rows
+# --------------------------------------------------------------------------
+
+class StoreArgs(ctypes.Structure):
+    """kvc_store_args of include/kvc.h."""
+    _fields_ = [("norm_weight", ctypes.c_void_p), ("freqs_cis", ctypes.c_void_p), ("out_loc", ctypes.c_void_p),
+                ("cache", ctypes.c_void_p), ("num_loc", ctypes.c_int64), ("max_position", ctypes.c_int64),
+                ("num_cache_rows", ctypes.c_int64), ("eps", ctypes.c_float), ("rope_dim", ctypes.c_int32)]
+
+
+def store_args(head_dim, norm_weight, eps, freqs_cis, out_loc, cache):
+    """Pack the store parameters.  norm_weight: float32 [head_dim]; freqs_cis:
+    float32 [max_position, rope_dim / 2, 2] (cos, sin), or None for no rotated
+    channels; out_loc: int32 [num_loc]; cache: bf16 (or 16-bit bits) [rows, head_dim]."""
+    _dev(norm_weight, freqs_cis, out_loc, cache)
+    if norm_weight.dtype != torch.float32 or norm_weight.numel() != head_dim:
+        raise KvcError("norm_weight must be float32 [%d]" % head_dim)
+    if out_loc.dtype != torch.int32 or out_loc.dim() != 1:
+        raise KvcError("out_loc must be a 1-D int32 tensor")
+    _shape(cache, 0, head_dim, "cache")
+    if cache.element_size() != 2:
+        raise KvcError("cache must hold bf16 rows")
+    if freqs_cis is None or freqs_cis.numel() == 0:
+        rope_dim, max_pos, fptr = 0, 0, None
+    else:
+        if freqs_cis.dtype != torch.float32 or freqs_cis.dim() != 3 or freqs_cis.shape[2] != 2:
+            raise KvcError("freqs_cis must be float32 [max_position, rope_dim / 2, 2]")
+        rope_dim, max_pos, fptr = 2 * freqs_cis.shape[1], freqs_cis.shape[0], freqs_cis.data_ptr()
+    return StoreArgs(norm_weight.data_ptr(), fptr, out_loc.data_ptr(), cache.data_ptr(), out_loc.numel(), max_pos,
+                     cache.shape[0], float(eps), rope_dim)
+
+
+def norm_rope_store_prefill(cr, rows, plan_c, counts, norm_weight, eps, freqs_cis, out_loc, cache, stream=None):
+    """Store row k of rows (float32 [cap_c, hd]) for every valid C record k < counts[0]."""
+    _dev(rows, plan_c, counts)
+    hd = rows.shape[1]
+    _shape(plan_c, 0, C_BYTES, "plan_c")
+    _shape(rows, plan_c.shape[0], hd, "rows")
+    if rows.dtype != torch.float32:
+        raise KvcError("rows must be float32")
+    st = store_args(hd, norm_weight, eps, freqs_cis, out_loc, cache)
+    rc = load().kvc_norm_rope_store_prefill(cr, hd, _p(rows), _p(plan_c), plan_c.shape[0], _p(counts),
+                                            ctypes.byref(st), _stream(stream))
+    _check(rc, "kvc_norm_rope_store_prefill")
+
+
+def norm_rope_store_decode(cr, rows, plan_d, norm_weight, eps, freqs_cis, out_loc, cache, status=None, stream=None):
+    """Store row b of rows (float32 [batch, hd]) for every D record that closes a block."""
+    _dev(rows, plan_d, status)
+    hd = rows.shape[1]
+    _shape(plan_d, 1, D_BYTES, "plan_d")
+    _shape(rows, plan_d.shape[0], hd, "rows")
+    if rows.dtype != torch.float32:
+        raise KvcError("rows must be float32")
+    st = store_args(hd, norm_weight, eps, freqs_cis, out_loc, cache)
+    rc = load().kvc_norm_rope_store_decode(cr, hd, _p(rows), _p(plan_d), plan_d.shape[0], _p(status),
+                                           ctypes.byref(st), _stream(stream))
+    _check(rc, "kvc_norm_rope_store_decode")
+
+
+def compress_norm_rope_store(cr, head_dim, state, inp, ape, plan_c, counts, norm_weight, eps, freqs_cis, out_loc,
+                             cache, stream=None):
+    """Pool, norm, rotate and store in one kernel (kvc_compress_c{4,128}_norm_rope_store)."""
+    _dev(state, inp, ape, plan_c, counts)
+    _rows(cr, head_dim, state, inp)
+    _shape(ape, WINDOW[cr], head_dim, "ape")
+    _shape(plan_c, 0, C_BYTES, "plan_c")
+    if ape.element_size() != inp.element_size():
+        raise KvcError("ape must share the input dtype")
+    st = store_args(head_dim, norm_weight, eps, freqs_cis, out_loc, cache)
+    fn = load().kvc_compress_c4_norm_rope_store if cr == 4 else load().kvc_compress_c128_norm_rope_store
+    rc = fn(_dtype(inp), head_dim, _p(state), state.shape[0], _p(inp), inp.shape[0], _p(ape), _p(plan_c),
+            plan_c.shape[0], _p(counts), ctypes.byref(st), _stream(stream))
+    _check(rc, "kvc_compress_c%d_norm_rope_store" % cr)
 
 
 def decode_c4(head_dim, state, inp, ape, plan_d, out, status=None, stream=None):

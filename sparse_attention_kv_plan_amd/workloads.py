@@ -266,3 +266,33 @@ def swa_tables(rng, max_len, num_reqs, swa_page_size, stride=None):
     f2s = np.empty(num_reqs * stride, np.int64)
     f2s[full.ravel()] = swa.ravel()
     return full.astype(np.int32), f2s.astype(np.int32), int(num_pages)
+
+
+@dataclass
+class StoreInputs:
+    """Inputs of the norm / rotary / store step that follows the pool."""
+    norm_weight: np.ndarray  # float32 [hd]
+    eps: float
+    freqs_cis: np.ndarray    # float32 [max_position, rope_dim / 2, 2] (cos, sin)
+    out_loc: np.ndarray      # int32 [num_loc], distinct cache rows
+    num_cache_rows: int
+
+
+def rope_table(max_position: int, rope_dim: int, base: float = 10000.0) -> np.ndarray:
+    """A rotary table as a caller would pass it: angle p * base^(-2k / rope_dim)
+    for position p and pair k, stored as float32 (cos, sin)."""
+    if rope_dim == 0:
+        return np.zeros((0, 0, 2), np.float32)
+    inv = base ** (-np.arange(0, rope_dim, 2, dtype=np.float64) / rope_dim)
+    ang = np.arange(max_position, dtype=np.float64)[:, None] * inv[None, :]
+    return np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
+
+
+def store_inputs(rng, hd: int, rope_dim: int, max_position: int, num_loc: int, spare_rows: int = 7,
+                 eps: float = 1e-6) -> StoreInputs:
+    """Norm weight ~ N(1, 0.1); out_loc = the first num_loc entries of a
+    permutation of num_loc + spare_rows cache rows (all distinct)."""
+    w = (1.0 + 0.1 * rng.standard_normal(hd)).astype(np.float32)
+    rows = num_loc + spare_rows
+    loc = rng.permutation(rows)[:num_loc].astype(np.int32)
+    return StoreInputs(w, eps, rope_table(max_position, rope_dim), loc, rows)

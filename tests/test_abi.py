@@ -4,6 +4,7 @@ CPU only: no compute call is made.  The host argument checks run before any
 HIP call, so calls with bad host arguments return KVC_EINVAL here too.
 """
 import ctypes
+import os
 import subprocess
 
 import pytest
@@ -19,7 +20,24 @@ def lib():
 def test_header_declares_the_boundary():
     assert kvc.header_functions() == sorted([
         "kvc_plan_prefill", "kvc_plan_decode", "kvc_write", "kvc_compress_c4", "kvc_compress_c128",
-        "kvc_decode_c4", "kvc_decode_c128", "kvc_strerror", "kvc_plan_prefill_swa", "kvc_plan_decode_swa"])
+        "kvc_decode_c4", "kvc_decode_c128", "kvc_strerror", "kvc_plan_prefill_swa", "kvc_plan_decode_swa",
+        "kvc_norm_rope_store_prefill", "kvc_norm_rope_store_decode", "kvc_compress_c4_norm_rope_store",
+        "kvc_compress_c128_norm_rope_store"])
+
+
+def test_store_args_layout_matches_the_header(tmp_path):
+    """The ctypes mirror of kvc_store_args has the C compiler's size and offsets."""
+    src = tmp_path / "layout.c"
+    fields = [f[0] for f in kvc.StoreArgs._fields_]
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "kvc.h"\nint main(void) {\n'
+                   '  printf("%zu\\n", sizeof(kvc_store_args));\n'
+                   + "".join('  printf("%%zu\\n", offsetof(kvc_store_args, %s));\n' % f for f in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-std=c11", "-I", os.path.dirname(kvc.HEADER), "-o", str(exe), str(src)])
+    got = [int(v) for v in subprocess.check_output([str(exe)]).split()]
+    assert got[0] == ctypes.sizeof(kvc.StoreArgs)
+    assert got[1:] == [getattr(kvc.StoreArgs, f).offset for f in fields]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -73,6 +91,25 @@ def test_host_argument_checks_reject_without_enqueueing(lib):
                                     None, None) == E
     assert lib.kvc_plan_decode_swa(128, 1, p, p, p, L(64), L(1), p, L(64), 256, 256, L(256), p, None, None) == E
     assert lib.kvc_plan_decode_swa(4, 1, p, p, p, L(0), L(1), p, L(64), 16, 8, L(8), p, None, None) == E
+    # norm / rotary / store parameters
+    def st(**kw):
+        a = dict(norm_weight=p.value, freqs_cis=p.value, out_loc=p.value, cache=p.value, num_loc=4, max_position=8,
+                 num_cache_rows=4, eps=1e-6, rope_dim=64)
+        a.update(kw)
+        return ctypes.byref(kvc.StoreArgs(**a))
+    store_p = lib.kvc_norm_rope_store_prefill
+    for bad in (dict(rope_dim=12), dict(rope_dim=136), dict(rope_dim=-8), dict(eps=-1.0), dict(eps=float("nan")),
+                dict(eps=float("inf")), dict(norm_weight=None), dict(cache=misaligned.value), dict(num_loc=-1),
+                dict(max_position=-1), dict(freqs_cis=None)):
+        assert store_p(4, 128, p, p, 1, p, st(**bad), None) == E, bad
+    assert store_p(4, 128, p, p, 1, p, None, None) == E
+    assert store_p(4, 96, p, p, 1, p, st(), None) == E
+    assert store_p(4, 128, p, p, 0, p, st(rope_dim=0, freqs_cis=None), None) == kvc.KVC_OK
+    assert lib.kvc_norm_rope_store_decode(128, 128, p, p, 0, None, st(), None) == E
+    assert lib.kvc_norm_rope_store_decode(128, 128, p, misaligned, 1, None, st(), None) == E
+    assert lib.kvc_compress_c4_norm_rope_store(1, 128, p, 8, p, 1, p, p, 1, p, None, None) == E
+    assert lib.kvc_compress_c128_norm_rope_store(1, 128, p, 8, p, 1, p, p, 1, p, st(rope_dim=4), None) == E
+    assert lib.kvc_compress_c4_norm_rope_store(1, 128, p, 8, p, 1, p, p, 0, p, st(), None) == kvc.KVC_OK
     # empty work is a no-op that needs no device
     assert lib.kvc_compress_c4(1, 128, p, 8, p, 1, p, p, 0, p, p, None) == kvc.KVC_OK
     assert lib.kvc_write(128, 1, 512, p, 8, p, 1, p, 0, p, None) == kvc.KVC_OK
