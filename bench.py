@@ -58,7 +58,7 @@ def parse():
 # Sources of the dominant kernel: the traffic figure is only reported while they are
 # unchanged since the counters in TRAFFIC_FILE were taken.
 KERNEL_SOURCES = ["sparse_attention_kv_plan_amd/csrc/kvc_compress.hip", "sparse_attention_kv_plan_amd/csrc/kvc_pool.hpp",
-                  "sparse_attention_kv_plan_amd/csrc/kvc_device.hpp"]
+                  "sparse_attention_kv_plan_amd/csrc/kvc_device.hpp", "sparse_attention_kv_plan_amd/csrc/kvc_store.hpp"]
 TRAFFIC_FILE = "profiles/compress_c4_mixed_prefill_traffic.md"
 
 
@@ -117,6 +117,19 @@ def algorithmic_bytes_compress(cr, hd, esize, seq_lens_of_rows):
     kept = np.where((cr == 4) & (seq_lens_of_rows == 4), 4, W)
     per_row = kept * 2 * hd * esize + hd * 4 + 16
     return int(per_row.sum()) + W * hd * esize
+
+
+def algorithmic_bytes_store(hd, rope_dim, rows):
+    """Bytes the standalone store must move: the fp32 row in, the bf16 row out, the record, the
+    out_loc entry and the row of the rotary table; the norm weight once per launch."""
+    return rows * (hd * 4 + hd * 2 + 16 + 4 + rope_dim * 4) + hd * 4
+
+
+def algorithmic_bytes_fused_store(cr, hd, esize, seq_lens_of_rows, rope_dim):
+    """The pool's bytes with the bf16 row, the out_loc entry and the table row in place of the fp32 row."""
+    rows = len(seq_lens_of_rows)
+    return (algorithmic_bytes_compress(cr, hd, esize, seq_lens_of_rows) + rows * (hd * 2 + 4 + rope_dim * 4 - hd * 4)
+            + hd * 4)
 
 
 def main():
@@ -222,6 +235,38 @@ def main():
     swa_launches = [("plan_prefill_swa c4", SP4.plan), ("plan_prefill_swa c128", SP128.plan),
                     ("plan_decode_swa c4", SD4.plan)]
 
+    # norm + rotary + bf16 store of the compressed rows (breakdown pass only): rotary on the last 64
+    # channels, one cache row per ragged token (prefill) or request (decode)
+    class Store:
+        def __init__(self, X, n, seed):
+            self.X, w = X, X.w
+            si = wl.store_inputs(np.random.default_rng(seed), w.hd, 64, int(w.seq_lens.max()) + 1, n)
+            self.wt, self.f, self.loc = to_dev(si.norm_weight), to_dev(si.freqs_cis), to_dev(si.out_loc)
+            self.cache = torch.empty((si.num_cache_rows, w.hd), dtype=torch.int16, device=dev)
+            self.eps = si.eps
+
+        def fused(self):
+            X, w = self.X, self.X.w
+            kvc.compress_norm_rope_store(w.cr, w.hd, X.state, X.inp, X.ape, X.plan_c, X.counts, self.wt, self.eps,
+                                         self.f, self.loc, self.cache)
+
+        def prefill(self):
+            X = self.X
+            kvc.norm_rope_store_prefill(X.w.cr, X.out, X.plan_c, X.counts, self.wt, self.eps, self.f, self.loc,
+                                        self.cache)
+
+        def decode(self):
+            X = self.X
+            kvc.norm_rope_store_decode(X.w.cr, X.out, X.plan_d, self.wt, self.eps, self.f, self.loc, self.cache,
+                                       X.status)
+
+    ST4, ST128 = Store(P4, p4.num_q, 3004), Store(P128, p128.num_q, 3128)
+    SD4S, SD128S = Store(D4, d4.B, 3003), Store(D128, d128.B, 3129)
+    store_launches = [("compress_c4_norm_rope_store", ST4.fused), ("norm_rope_store_prefill c4", ST4.prefill),
+                      ("compress_c128_norm_rope_store", ST128.fused),
+                      ("norm_rope_store_prefill c128", ST128.prefill),
+                      ("norm_rope_store_decode c4", SD4S.decode), ("norm_rope_store_decode c128", SD128S.decode)]
+
     launches = [("plan_prefill c4", P4.plan), ("compress_c4", P4.compress), ("write c4", P4.write),
                 ("plan_prefill c128", P128.plan), ("compress_c128", P128.compress), ("write c128", P128.write),
                 ("plan_decode c4", D4.plan), ("decode_c4", D4.decode),
@@ -262,10 +307,11 @@ def main():
     dom_us = float(np.mean([a.elapsed_time(b) for a, b in kev])) * 1e3
 
     # per-kernel breakdown (separate, untimed pass; events around every launch), with the
-    # SWA-paged planners of the same requests
-    bev = {name: [] for name, _ in launches + swa_launches}
+    # SWA-paged planners of the same requests and the store step after the pool
+    extra = swa_launches + store_launches
+    bev = {name: [] for name, _ in launches + extra}
     for _ in range(5):
-        for name, f in launches + swa_launches:
+        for name, f in launches + extra:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             f()
@@ -308,6 +354,8 @@ def main():
         assert c[2] == 0 and c[3] == 0, ("device error", c)
     for D in (D4, D128):
         assert int(D.status.item()) == 0
+    for S in (ST4, ST128):
+        assert int(S.X.counts[3].item()) == 0
     for S in (SP4, SP128):
         c = S.counts.cpu().tolist()
         assert c[2] == 0 and int(S.status.item()) == 0, ("SWA plan error", c)
@@ -317,6 +365,21 @@ def main():
     rows_seq = P4.plan_c[:n_c4].cpu().numpy().view("<u4").reshape(-1, 4)[:, 0].astype(np.int64)
     dom_bytes = algorithmic_bytes_compress(4, p4.hd, p4.esize, rows_seq)
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+
+    # the store step after the pool: fused into the pool vs pool into fp32 rows + standalone store
+    store_step = {"rope_dim": 64}
+    for cr, P, w in ((4, P4, p4), (128, P128, p128)):
+        n = int(P.counts[0].item())
+        seqs = P.plan_c[:n].cpu().numpy().view("<u4").reshape(-1, 4)[:, 0].astype(np.int64)
+        fused_us = kernels_us["compress_c%d_norm_rope_store" % cr]
+        two_us = kernels_us["compress_c%d" % cr] + kernels_us["norm_rope_store_prefill c%d" % cr]
+        fb = algorithmic_bytes_fused_store(cr, w.hd, w.esize, seqs, 64)
+        sb = algorithmic_bytes_store(w.hd, 64, n)
+        store_step["c%d" % cr] = {
+            "rows": n, "fused_us": fused_us, "pool_then_store_us": round(two_us, 2),
+            "fused_GBps": round(fb / (fused_us * 1e-6) / 1e9, 1), "fused_bytes": fb,
+            "store_only_GBps": round(sb / (kernels_us["norm_rope_store_prefill c%d" % cr] * 1e-6) / 1e9, 1),
+            "store_only_bytes": sb}
 
     tokens = p4.num_q + p128.num_q + d4.B + d128.B
     value = tokens / (ms_per_step * 1e-3)
@@ -355,6 +418,7 @@ def main():
         },
         "kernels_us": kernels_us,
         "decode_step_us": decode_us,
+        "store_step": store_step,
         "wall_s_timed": round(wall, 3),
     }
 

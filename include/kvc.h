@@ -57,6 +57,10 @@
  *                 this chunk's writes: c4.cuh, flash_c4_prefill launches the
  *                 compress kernel before the write kernel);
  *  decode step:   kvc_plan_decode -> kvc_decode_c4 | kvc_decode_c128.
+ *  The compressed rows then go through norm + rotary embedding into a bf16
+ *  cache: kvc_norm_rope_store_prefill / kvc_norm_rope_store_decode after the
+ *  pool, or kvc_compress_c4_norm_rope_store / kvc_compress_c128_norm_rope_store
+ *  in place of the prefill pool (still before kvc_write).
  *  Plans depend only on lengths and indices, so one plan serves every layer.
  *  The state indices of one call must be distinct.
  */

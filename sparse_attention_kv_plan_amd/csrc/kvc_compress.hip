@@ -32,13 +32,14 @@ __global__ __launch_bounds__(kThreads) void compress_c4_kernel(CompressArgs a) {
   constexpr int kLanes = HD / V;
   constexpr int kRows = kThreads / kLanes;
   const int64_t row = (int64_t)blockIdx.x * kRows + threadIdx.x / kLanes;
-  const int lane = threadIdx.x % kLanes;
-  const int c = lane * V;
+  const int c = (threadIdx.x % kLanes) * V;
+  typedef typename Elem<T>::storage E;
   bool live = row < a.counts[0] && row < a.cap_c;
   float res[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) res[v] = 0.f;
-  int64_t pos = 0, loc = 0;
+  int32_t pos = 0, loc = -1;  // positions < 2^24, cache rows <= INT32_MAX
+  StoreOperands<V> ops;
   if (live) {
     const kvc_plan_c rec = load_plan_c(a.plan_c + row);
     const int64_t ragged = rec.ragged_blen & 0xFFFFFFu;
@@ -50,18 +51,28 @@ __global__ __launch_bounds__(kThreads) void compress_c4_kernel(CompressArgs a) {
       if (c == 0) atomicOr(a.counts + 3, KVC_DERR_RECORD);
       live = false;
     }
-    if constexpr (STORE) {
-      pos = rec.seq_len >= 4u ? (int64_t)rec.seq_len - 4 : 0;
-      if (live && !store_target(a.st, ragged, pos, &loc)) {
-        if (c == 0) atomicOr(a.counts + 3, KVC_DERR_RECORD);
-        live = false;
-      }
-    }
     if (live) {
-      const typename Elem<T>::storage* state = static_cast<const typename Elem<T>::storage*>(a.state);
-      const typename Elem<T>::storage* input = static_cast<const typename Elem<T>::storage*>(a.input);
-      const typename Elem<T>::storage* ape = static_cast<const typename Elem<T>::storage*>(a.ape);
-      if (first_block) {
+      const E* state = static_cast<const E*>(a.state);
+      const E* input = static_cast<const E*>(a.input);
+      const E* ape = static_cast<const E*>(a.ape);
+      if constexpr (STORE) {
+        // the store's own loads go out with the window's and are checked after the pool
+        pos = rec.seq_len >= 4u ? (int32_t)rec.seq_len - 4 : 0;
+        const auto pre = [&]() { loc = fetch_loc(a.st, ragged); };
+        if (first_block) {
+          c4_pool<T, HD, 4>(state, input, ape, ragged, blen, rp0, rp1, c, res, pre);
+        } else {
+          c4_pool<T, HD, 0>(state, input, ape, ragged, blen, rp0, rp1, c, res, pre);
+        }
+        if (store_ok(a.st, loc, pos)) {
+          fetch_operands<V, HD>(a.st, c, pos, ops);  // cached loads, in flight during the row reduction
+        } else {
+          if (c == 0) atomicOr(a.counts + 3, KVC_DERR_RECORD);
+          live = false;
+#pragma unroll
+          for (int v = 0; v < V; ++v) res[v] = 0.f;
+        }
+      } else if (first_block) {
         c4_pool<T, HD, 4>(state, input, ape, ragged, blen, rp0, rp1, c, res);
       } else {
         c4_pool<T, HD, 0>(state, input, ape, ragged, blen, rp0, rp1, c, res);
@@ -74,16 +85,18 @@ __global__ __launch_bounds__(kThreads) void compress_c4_kernel(CompressArgs a) {
 #pragma unroll
     for (int v = 0; v < V; ++v) ss = fmaf(res[v], res[v], ss);
     ss = row_sum<kLanes>(ss, red);  // reached by every thread (rows wider than a wave sync)
-    if (live) norm_rope_store<V, HD>(res, ss, c, pos, loc, a.st);
+    if (live) norm_rope_store<V, HD>(res, ss, c, loc, ops, a.st);
   } else {
     // A lane holds V adjacent channels, so storing them directly would write
     // 16-byte pieces at a 4*V-byte stride.  Staging the row in LDS lets every
-    // store instruction write 64 x 16 contiguous bytes instead.
+    // store instruction write 64 x 16 contiguous bytes instead (2% faster in
+    // the full step; with cold caches the two are even).
     __shared__ float stage[kThreads * V];  // the workgroup's output rows
     float* w = stage + (threadIdx.x / kLanes) * HD;
     store_floats<V>(w + c, res);
     __syncthreads();
     if (live) {
+      const int lane = threadIdx.x % kLanes;
 #pragma unroll
       for (int k = 0; k < V / 4; ++k) {
         const int ch = k * (kLanes * 4) + lane * 4;
@@ -105,29 +118,35 @@ __global__ __launch_bounds__(kThreads) void compress_c128_kernel(CompressArgs a)
   const int64_t ragged = rec.ragged_blen & 0xFFFFFFu;
   const int blen = (int)(rec.ragged_blen >> 24);
   const int64_t rp0 = rec.read_page_0;
-  bool ok = c128_record_ok(ragged, blen, rp0, a.num_q, a.num_state_rows);
-  const int64_t pos = rec.seq_len >= 128u ? (int64_t)rec.seq_len - 128 : 0;
-  int64_t loc = 0;
-  if constexpr (STORE) ok = ok && store_target(a.st, ragged, pos, &loc);
-  if (!ok) {  // the whole workgroup leaves: nothing below is reached by part of it
+  if (!c128_record_ok(ragged, blen, rp0, a.num_q, a.num_state_rows)) {
     if (threadIdx.x == 0) atomicOr(a.counts + 3, KVC_DERR_RECORD);
-    return;
+    return;  // the whole workgroup leaves: nothing below is reached by part of it
   }
   const E* state = static_cast<const E*>(a.state);
   const E* input = static_cast<const E*>(a.input);
   const E* ape = static_cast<const E*>(a.ape);
   if constexpr (STORE) {
-    // thread t ends with channels 2t, 2t+1 (a rotary pair); threads past HD/2 hold zeros
+    // thread t ends with channels 2t, 2t+1 (a rotary pair); threads past HD/2 hold zeros.
+    // The store's loads go out after the window's (holding them across the
+    // pool would cost a wave per SIMD of occupancy).
     __shared__ float red[kThreads / kWave];
-    Pool::accumulate(state, input, ape, ragged, blen, rp0, 0, lds);
     const int c = 2 * threadIdx.x;
+    const int32_t pos = rec.seq_len >= 128u ? (int32_t)rec.seq_len - 128 : 0;
+    Pool::accumulate(state, input, ape, ragged, blen, rp0, 0, lds);
+    const int32_t loc = fetch_loc(a.st, ragged);
+    if (!store_ok(a.st, loc, pos)) {  // uniform over the workgroup
+      if (threadIdx.x == 0) atomicOr(a.counts + 3, KVC_DERR_RECORD);
+      return;
+    }
+    StoreOperands<2> ops;
+    if (c < HD) fetch_operands<2, HD>(a.st, c, pos, ops);  // cached loads, in flight during the merge
     float x[2] = {0.f, 0.f};
     if (c < HD) {
       x[0] = Pool::merged(lds, c);
       x[1] = Pool::merged(lds, c + 1);
     }
     const float ss = block_sum<kThreads>(fmaf(x[0], x[0], x[1] * x[1]), red);
-    if (c < HD) norm_rope_store<2, HD>(x, ss, c, pos, loc, a.st);
+    if (c < HD) norm_rope_store<2, HD>(x, ss, c, loc, ops, a.st);
   } else {
     Pool::run(state, input, ape, ragged, blen, rp0, 0, a.out + row * HD, lds);
   }

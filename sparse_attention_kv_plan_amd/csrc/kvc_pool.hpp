@@ -23,12 +23,18 @@ namespace kvc {
 // input row ragged - 7 + i.  Entries 0..3 (the previous block) use the
 // |kv overlap| and |score overlap| quarters of their row, entries 4..7 the
 // |kv| and |score| quarters.  FIRST = 4 drops the entries before the start of
-// the sequence (the first block); they are not loaded at all.
-template <typename T, int HD, int FIRST>
+// the sequence (the first block); they are not loaded at all.  pre() runs
+// right after the window's loads are issued, so a caller's own loads overlap
+// them.
+struct NoPre {
+  __device__ void operator()() const {}
+};
+
+template <typename T, int HD, int FIRST, typename Pre = NoPre>
 __device__ __forceinline__ void c4_pool(const typename Elem<T>::storage* __restrict__ state,
                                         const typename Elem<T>::storage* __restrict__ input,
                                         const typename Elem<T>::storage* __restrict__ ape, int64_t ragged, int blen,
-                                        int64_t rp0, int64_t rp1, int c, float* res) {
+                                        int64_t rp0, int64_t rp1, int c, float* res, const Pre& pre = Pre()) {
   constexpr int V = Elem<T>::kVec;
   constexpr int64_t R = 4 * HD;
   // all kv / score loads of the window are issued before any use
@@ -40,6 +46,7 @@ __device__ __forceinline__ void c4_pool(const typename Elem<T>::storage* __restr
     kv_raw[i] = load16_stream(row + ((i < 4) ? 0 : HD) + c);
     sc_raw[i] = load16_stream(row + ((i < 4) ? 2 * HD : 3 * HD) + c);
   }
+  pre();
   float t[8][V];
 #pragma unroll
   for (int i = FIRST; i < 8; ++i) {

@@ -19,39 +19,45 @@ __global__ __launch_bounds__(kThreads) void norm_rope_store_kernel(NormRopeStore
   constexpr int kRows = kThreads / kLanes;
   const int64_t row = (int64_t)blockIdx.x * kRows + threadIdx.x / kLanes;
   const int c = (threadIdx.x % kLanes) * kK;
-  uint32_t seq_len;
-  int64_t key;
+  // the loads that depend on nothing go out first (the record, the row, the
+  // norm weight), then the lookups that need the record
+  bool live;
+  uint32_t seq_len = 0;
+  int64_t key = 0;
   int32_t* err;
   if constexpr (DECODE) {
     if (row >= a.n) return;
     const kvc_plan_d rec = load_plan_d(a.plan_d + row);
-    if (plan_d_invalid(rec) || rec.seq_len % (uint32_t)a.compress_ratio != 0) return;
+    live = !plan_d_invalid(rec) && rec.seq_len % (uint32_t)a.compress_ratio == 0;
     seq_len = rec.seq_len;
     key = row;
     err = a.status;
   } else {
     if (row >= a.counts[0] || row >= a.n) return;
     const kvc_plan_c rec = load_plan_c(a.plan_c + row);
-    if (plan_c_invalid(rec)) return;
+    live = !plan_c_invalid(rec);
     seq_len = rec.seq_len;
     key = rec.ragged_blen & 0xFFFFFFu;
     err = a.counts + 3;
   }
-  const int64_t pos = seq_len >= (uint32_t)a.compress_ratio ? (int64_t)seq_len - a.compress_ratio : 0;
-  int64_t loc;
-  if (!store_target(a.st, key, pos, &loc)) {
+  float x[kK];
+  const float* src = a.rows + row * HD + c;  // row < a.n: inside the rows buffer whatever the record holds
+#pragma unroll
+  for (int i = 0; i < kK; i += 4) widen16<float>(load16_stream(src + i), x + i);
+  const int32_t pos = seq_len >= (uint32_t)a.compress_ratio ? (int32_t)(seq_len - a.compress_ratio) : 0;
+  StoreOperands<kK> ops;
+  const int32_t loc = live ? fetch_loc(a.st, key) : -1;
+  if (live) fetch_operands<kK, HD>(a.st, c, pos, ops);
+  if (!live) return;
+  if (!store_ok(a.st, loc, pos)) {
     if (c == 0 && err != nullptr) atomicOr(err, KVC_DERR_RECORD);
     return;  // the whole row leaves together: the reduction below stays inside live rows
   }
-  float x[kK];
-  const float* src = a.rows + row * HD + c;
-#pragma unroll
-  for (int i = 0; i < kK; i += 4) widen16<float>(load16_stream(src + i), x + i);
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < kK; ++k) ss = fmaf(x[k], x[k], ss);
   ss = row_sum<kLanes>(ss, nullptr);
-  norm_rope_store<kK, HD>(x, ss, c, pos, loc, a.st);
+  norm_rope_store<kK, HD>(x, ss, c, loc, ops, a.st);
 }
 
 template <int HD, bool DECODE>

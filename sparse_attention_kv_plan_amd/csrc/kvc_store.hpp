@@ -14,11 +14,16 @@
 
 namespace kvc {
 
-// float -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN
-__device__ __forceinline__ uint32_t bf16_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> two bf16 (round to nearest even; a NaN stays a NaN) packed
+// low / high in one word.  gfx950 converts a pair in one instruction
+// (v_cvt_pk_bf16_f32); rounding by integer arithmetic instead costs ~7 VALU
+// operations per channel, and measurably slows the fused pool.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Sum over the kLanes consecutive lanes that hold one row (kLanes a power of
@@ -75,7 +80,7 @@ template <int K>
 __device__ __forceinline__ void store_bf16(uint16_t* dst, const float* y) {
   uint32_t w[K / 2];
 #pragma unroll
-  for (int i = 0; i < K / 2; ++i) w[i] = bf16_bits(y[2 * i]) | (bf16_bits(y[2 * i + 1]) << 16);
+  for (int i = 0; i < K / 2; ++i) w[i] = pack_bf16x2(y[2 * i], y[2 * i + 1]);
   if constexpr (K == 2) {
     __builtin_nontemporal_store(w[0], reinterpret_cast<uint32_t*>(dst));
   } else if constexpr (K == 4) {
@@ -90,39 +95,51 @@ __device__ __forceinline__ void store_bf16(uint16_t* dst, const float* y) {
   }
 }
 
-// Whether the row of a record can be stored: its key, cache location and
-// rotary position are inside their tables.  Sets *loc.
-__device__ __forceinline__ bool store_target(const kvc_store_args& st, int64_t key, int64_t pos, int64_t* loc) {
-  if (key < 0 || key >= st.num_loc) return false;
-  const int64_t l = st.out_loc[key];
-  if (l < 0 || l >= st.num_cache_rows) return false;
-  if (st.rope_dim > 0 && pos >= st.max_position) return false;
-  *loc = l;
-  return true;
+// The out_loc entry of a key, or -1 when the key has none.  Issued before the
+// pool's loads and checked after them, so the lookup adds no latency.
+__device__ __forceinline__ int32_t fetch_loc(const kvc_store_args& st, int64_t key) {
+  return (key >= 0 && key < st.num_loc) ? st.out_loc[key] : -1;
+}
+
+// Whether the row of a record can be stored: its location (from fetch_loc)
+// and rotary position are inside their tables.
+__device__ __forceinline__ bool store_ok(const kvc_store_args& st, int32_t loc, int32_t pos) {
+  return loc >= 0 && loc < st.num_cache_rows && (st.rope_dim == 0 || pos < st.max_position);
+}
+
+// Per-thread operands of the store: the norm weight of channels [c, c + K)
+// and, for rotated channels, their (cos, sin) pairs at the row's position.
+template <int K>
+struct StoreOperands {
+  float w[K];
+  float cs[K];
+};
+
+template <int K, int HD>
+__device__ __forceinline__ void fetch_operands(const kvc_store_args& st, int c, int32_t pos, StoreOperands<K>& o) {
+  load_floats<K>(st.norm_weight + c, o.w);
+  const int base = HD - st.rope_dim;
+  if (c >= base && pos < st.max_position)
+    load_floats<K>(st.freqs_cis + (int64_t)pos * st.rope_dim + (c - base), o.cs);
 }
 
 // Norm + rotation + store of channels [c, c + K) of one row whose sum of
 // squares over all HD channels is ss.  x is modified in place.
 template <int K, int HD>
-__device__ __forceinline__ void norm_rope_store(float* x, float ss, int c, int64_t pos, int64_t loc,
+__device__ __forceinline__ void norm_rope_store(float* x, float ss, int c, int32_t loc, const StoreOperands<K>& o,
                                                 const kvc_store_args& st) {
   const float inv = 1.0f / sqrtf(ss * (1.0f / HD) + st.eps);
-  float w[K];
-  load_floats<K>(st.norm_weight + c, w);
 #pragma unroll
-  for (int k = 0; k < K; ++k) x[k] = x[k] * inv * w[k];
-  const int base = HD - st.rope_dim;
-  if (c >= base) {
-    float cs[K];
-    load_floats<K>(st.freqs_cis + pos * st.rope_dim + (c - base), cs);
+  for (int k = 0; k < K; ++k) x[k] = x[k] * inv * o.w[k];
+  if (c >= HD - st.rope_dim) {
 #pragma unroll
     for (int k = 0; k < K; k += 2) {
       const float re = x[k], im = x[k + 1];
-      x[k] = re * cs[k] - im * cs[k + 1];
-      x[k + 1] = re * cs[k + 1] + im * cs[k];
+      x[k] = re * o.cs[k] - im * o.cs[k + 1];
+      x[k + 1] = re * o.cs[k + 1] + im * o.cs[k];
     }
   }
-  store_bf16<K>(st.cache + loc * HD + c, x);
+  store_bf16<K>(st.cache + (int64_t)loc * HD + c, x);
 }
 
 }  // namespace kvc
