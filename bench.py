@@ -18,7 +18,7 @@ divided by its average duration, timed with HIP events on the launch stream
 over the timed region.  cpu_baseline times the float64 C oracle on one host
 core over the same step.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--sweep]
 """
 from __future__ import annotations
 
@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=5)
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time the compress and decode kernels over growing workloads, and the two "
+                         "compress kernels with cold caches (reported under 'sweep')")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 1 GiB device to device 5 times (calibrates the HBM byte counters)")
     return ap.parse_args()
@@ -130,6 +133,83 @@ def algorithmic_bytes_fused_store(cr, hd, esize, seq_lens_of_rows, rope_dim):
     rows = len(seq_lens_of_rows)
     return (algorithmic_bytes_compress(cr, hd, esize, seq_lens_of_rows) + rows * (hd * 2 + 4 + rope_dim * 4 - hd * 4)
             + hd * 4)
+
+
+def algorithmic_bytes_decode(cr, hd, esize, seq_lens):
+    """Bytes a fused decode must move: the new row in and out of the state, the fp32 output row and
+    the record per request; on a boundary the window's other entries (3 of them at seq_len 4 for
+    ratio 4) from the state; ape once."""
+    R = (4 if cr == 4 else 2) * hd
+    W = 8 if cr == 4 else 128
+    s = np.asarray(seq_lens, np.int64)
+    boundary = s % cr == 0
+    others = np.where((cr == 4) & (s == 4), 3, W - 1)
+    per = 2 * R * esize + hd * 4 + 16 + np.where(boundary, others * 2 * hd * esize, 0)
+    return int(per.sum()) + W * hd * esize
+
+
+def sweep(torch, kvc, dev, P4, P128, to_dev):
+    """Extra, labelled results: kernel time and algorithmic GB/s as the work grows (prefill: the first
+    k requests of the mixed batch; decode: batches with device-generated inputs), and the two compress
+    kernels on the full mixed batch with cold caches (1 GiB written before every launch, untimed)."""
+    stream = torch.cuda.current_stream()
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def med_us(f, n=10, cold=False):
+        ts = []
+        for _ in range(n + 2):
+            if cold:
+                flush_buf.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            f()
+            b.record(stream)
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        return round(float(np.median([a.elapsed_time(b) for a, b in ts[2:]])) * 1e3, 2)
+
+    out = {"prefill": [], "decode": [], "cold": {}}
+    for P in (P4, P128):
+        w = P.w
+        for k in (1, 4, 16, 32, 64):
+            nq = int(w.extend_lens[:k].sum())
+            pc, pw, cnt = kvc.alloc_prefill_plan(w.cr, k, nq, dev)
+            kvc.plan_prefill(w.cr, to_dev(w.seq_lens[:k]), to_dev(w.extend_lens[:k]), to_dev(w.state_index[:k]),
+                             w.num_state_rows, nq, pc, pw, cnt)
+            o = torch.empty((pc.shape[0], w.hd), dtype=torch.float32, device=dev)
+            inp = P.inp[:nq]
+            us = med_us(lambda: kvc.compress(w.cr, w.hd, P.state, inp, P.ape, pc, cnt, o))
+            n = int(cnt[0].item())
+            seqs = pc[:n].cpu().numpy().view("<u4").reshape(-1, 4)[:, 0].astype(np.int64)
+            nbytes = algorithmic_bytes_compress(w.cr, w.hd, w.esize, seqs)
+            out["prefill"].append({"ratio": w.cr, "requests": k, "tokens": nq, "rows": n, "us": us,
+                                   "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)})
+        out["cold"]["compress_c%d" % w.cr] = med_us(P.compress, cold=True)
+    hd = 512
+    for cr, batches in ((4, (256, 1024, 4096, 16384, 65536)), (128, (1024, 4096, 16384, 32768))):
+        R, W = (4 if cr == 4 else 2) * hd, (8 if cr == 4 else 128)
+        for B in batches:
+            rng = np.random.default_rng(5000 + cr + B)
+            seq = (rng.integers(1, 65537, size=B) + 1).astype(np.int32)
+            idx = rng.permutation(B).astype(np.int32)
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(int(B) * 131 + cr)
+            state = torch.randn((B * W, R), generator=gen, device=dev, dtype=torch.bfloat16)
+            inp = torch.randn((B, R), generator=gen, device=dev, dtype=torch.bfloat16)
+            ape = torch.randn((W, hd), generator=gen, device=dev, dtype=torch.bfloat16) * 0.1
+            plan_d = torch.empty((B, kvc.D_BYTES), dtype=torch.uint8, device=dev)
+            status = torch.zeros(1, dtype=torch.int32, device=dev)
+            o = torch.empty((B, hd), dtype=torch.float32, device=dev)
+            kvc.plan_decode(cr, to_dev(seq), to_dev(idx), B * W, plan_d, status)
+            us = med_us(lambda: kvc.decode(cr, hd, state, inp, ape, plan_d, o, status))
+            assert int(status.item()) == 0
+            nbytes = algorithmic_bytes_decode(cr, hd, 2, seq)
+            out["decode"].append({"ratio": cr, "batch": B, "boundaries": int((seq % cr == 0).sum()), "us": us,
+                                  "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)})
+            del state, inp
+    del flush_buf
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -421,6 +501,10 @@ def main():
         "store_step": store_step,
         "wall_s_timed": round(wall, 3),
     }
+
+    if args.sweep:
+        log("sweep ...")
+        result["sweep"] = sweep(torch, kvc, dev, P4, P128, to_dev)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(p4, p128, d4, d128, tokens, args.cpu_reps)

@@ -68,17 +68,35 @@ __global__ __launch_bounds__(kThreads) void decode_c4_kernel(DecodeArgs a) {
   store_floats<V, true>(out, res);
 }
 
-// Ratio 128: CS workgroups of 128 threads per request, each owning HD / CS
-// channels (8 lanes x 16 bytes per stream, 16 streams, 8 entries each).  A
-// boundary request's 256 KiB window is thus read by CS workgroups on different
-// CUs at once; the light requests copy their slice of the row and write zeros.
+// Ratio 128: a workgroup of 128 threads owns a group of kDec128Group
+// requests and one slice of HD / CS channels; CS workgroups cover a group.
+// Every request's slice of the row is 16 vectors of 16 bytes, so each thread
+// copies one vector of one request into the state (and zeroes its part of the
+// output when the request closes no block).  The group's boundary requests
+// are then pooled one after another, each by its CS workgroups at once on
+// different CUs (8 lanes x 16 bytes per stream, 16 streams, 8 entries each).
+// The copy phase leaves each request's verdict in LDS, so the pool loop loads
+// no record again.
+// One request per workgroup would make the light requests (a 768-byte copy
+// each) a dispatch-bound stream of tiny workgroups at large batches.
 constexpr int kDec128Threads = 128;
+constexpr int kDec128SliceVecs = 16;  // 16-byte vectors of one request's row slice, for every T and HD
+constexpr int kDec128Group = kDec128Threads / kDec128SliceVecs;
 
 template <typename T, int HD>
 struct Dec128Shape {
   static constexpr int V = Elem<T>::kVec;
   static constexpr int CS = HD / (8 * V);  // channel slices per request
+  static_assert((2 * HD / V) / CS == kDec128SliceVecs, "slice of 16 vectors");
 };
+
+// Whether decode record rec (request b) can run, and whether it pools.
+__device__ __forceinline__ bool dec128_ok(const kvc_plan_d& rec, int64_t b, const DecodeArgs& a) {
+  const bool boundary = (rec.seq_len & 127u) == 0u;
+  bool ok = rec.write_loc >= 0 && rec.write_loc < a.num_state_rows;
+  if (boundary) ok = ok && c128_record_ok(b, 127, rec.read_page_0, a.batch, a.num_state_rows);
+  return ok;
+}
 
 template <typename T, int HD>
 __global__ __launch_bounds__(kDec128Threads) void decode_c128_kernel(DecodeArgs a) {
@@ -87,33 +105,42 @@ __global__ __launch_bounds__(kDec128Threads) void decode_c128_kernel(DecodeArgs 
   constexpr int CS = Dec128Shape<T, HD>::CS;
   typedef C128Pool<T, HD, kDec128Threads, CS> Pool;
   constexpr int64_t R = 2 * HD;
-  constexpr int kSliceVecs = (int)(R / V) / CS;  // 16-byte vectors of the row this workgroup copies
   constexpr int HDW = HD / CS;
   __shared__ float lds[Pool::kLdsFloats];
-  const int64_t b = blockIdx.x / CS;
+  const int64_t b0 = (int64_t)(blockIdx.x / CS) * kDec128Group;
   const int cs = blockIdx.x % CS;
-  float* out = a.out + b * HD;
-  const kvc_plan_d rec = load_plan_d(a.plan_d + b);
-  bool ok = !plan_d_invalid(rec);
-  const bool boundary = (rec.seq_len & 127u) == 0u;
-  const int64_t wl = rec.write_loc, rp0 = rec.read_page_0;
-  if (ok) {
-    ok = wl >= 0 && wl < a.num_state_rows;
-    if (boundary) ok = ok && c128_record_ok(b, 127, rp0, a.batch, a.num_state_rows);
-    if (!ok && cs == 0 && threadIdx.x == 0 && a.status) atomicOr(a.status, KVC_DERR_RECORD);
-  }
-  if (!ok || !boundary) {
-    for (int d = threadIdx.x * 4; d < HDW; d += kDec128Threads * 4) store_zeros<4>(out + cs * HDW + d);
-    if (!ok) return;
-  }
+  __shared__ int32_t pool_page[kDec128Group];  // read page of a request that pools, else -1
   E* state = static_cast<E*>(a.state);
   const E* input = static_cast<const E*>(a.input);
-  for (int v = threadIdx.x; v < kSliceVecs; v += kDec128Threads) {
-    const int64_t off = (int64_t)(cs * kSliceVecs + v) * V;
-    store16_stream(state + wl * R + off, load16(input + b * R + off));
+  {
+    // the copy: request b0 + t / 16, vector t % 16 of this slice
+    const int j = threadIdx.x / kDec128SliceVecs;
+    const int64_t b = b0 + j;
+    const int v = threadIdx.x % kDec128SliceVecs;
+    int32_t page = -1;
+    if (b < a.batch) {
+      const kvc_plan_d rec = load_plan_d(a.plan_d + b);
+      const bool valid = !plan_d_invalid(rec);
+      const bool ok = valid && dec128_ok(rec, b, a);
+      const bool boundary = (rec.seq_len & 127u) == 0u;
+      if (valid && !ok && cs == 0 && v == 0 && a.status) atomicOr(a.status, KVC_DERR_RECORD);
+      if (ok) {
+        const int64_t off = (int64_t)(cs * kDec128SliceVecs + v) * V;
+        store16_stream(state + (int64_t)rec.write_loc * R + off, load16(input + b * R + off));
+      }
+      if ((!ok || !boundary) && v < HDW / 4) store_zeros<4>(a.out + b * HD + cs * HDW + v * 4);
+      if (ok && boundary) page = rec.read_page_0;
+    }
+    if (v == 0) pool_page[j] = page;
   }
-  if (!boundary) return;
-  Pool::run(state, input, static_cast<const E*>(a.ape), b, 127, rp0, cs, out, lds);
+  __syncthreads();
+  // the pools, one boundary request at a time (the loop is uniform over the workgroup)
+  for (int j = 0; j < kDec128Group; ++j) {
+    const int32_t page = pool_page[j];
+    if (page < 0) continue;
+    Pool::run(state, input, static_cast<const E*>(a.ape), b0 + j, 127, page, cs, a.out + (b0 + j) * HD, lds);
+    __syncthreads();  // the next pool reuses lds
+  }
 }
 
 template <typename T, int HD>
@@ -128,7 +155,7 @@ struct C4Go {
 template <typename T, int HD>
 struct C128Go {
   static hipError_t go(const DecodeArgs& a, hipStream_t s) {
-    const int64_t grid = (int64_t)a.batch * Dec128Shape<T, HD>::CS;
+    const int64_t grid = (a.batch + kDec128Group - 1) / kDec128Group * Dec128Shape<T, HD>::CS;
     decode_c128_kernel<T, HD><<<(unsigned)grid, kDec128Threads, 0, s>>>(a);
     return hipGetLastError();
   }
