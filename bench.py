@@ -340,12 +340,18 @@ def main():
             kvc.norm_rope_store_decode(X.w.cr, X.out, X.plan_d, self.wt, self.eps, self.f, self.loc, self.cache,
                                        X.status)
 
+        def fused_decode(self):
+            X = self.X
+            kvc.decode_c4_norm_rope_store(X.w.hd, X.state, X.inp, X.ape, X.plan_d, self.wt, self.eps, self.f,
+                                          self.loc, self.cache, X.status)
+
     ST4, ST128 = Store(P4, p4.num_q, 3004), Store(P128, p128.num_q, 3128)
     SD4S, SD128S = Store(D4, d4.B, 3003), Store(D128, d128.B, 3129)
     store_launches = [("compress_c4_norm_rope_store", ST4.fused), ("norm_rope_store_prefill c4", ST4.prefill),
                       ("compress_c128_norm_rope_store", ST128.fused),
                       ("norm_rope_store_prefill c128", ST128.prefill),
-                      ("norm_rope_store_decode c4", SD4S.decode), ("norm_rope_store_decode c128", SD128S.decode)]
+                      ("norm_rope_store_decode c4", SD4S.decode), ("norm_rope_store_decode c128", SD128S.decode),
+                      ("decode_c4_norm_rope_store", SD4S.fused_decode)]
 
     launches = [("plan_prefill c4", P4.plan), ("compress_c4", P4.compress), ("write c4", P4.write),
                 ("plan_prefill c128", P128.plan), ("compress_c128", P128.compress), ("write c128", P128.write),

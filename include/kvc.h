@@ -60,7 +60,8 @@
  *  The compressed rows then go through norm + rotary embedding into a bf16
  *  cache: kvc_norm_rope_store_prefill / kvc_norm_rope_store_decode after the
  *  pool, or kvc_compress_c4_norm_rope_store / kvc_compress_c128_norm_rope_store
- *  in place of the prefill pool (still before kvc_write).
+ *  in place of the prefill pool (still before kvc_write), and
+ *  kvc_decode_c4_norm_rope_store in place of kvc_decode_c4.
  *  Plans depend only on lengths and indices, so one plan serves every layer.
  *  The state indices of one call must be distinct.
  */
@@ -345,6 +346,19 @@ int kvc_compress_c4_norm_rope_store(kvc_dtype dtype, int head_dim, const void* s
 int kvc_compress_c128_norm_rope_store(kvc_dtype dtype, int head_dim, const void* state, int64_t num_state_rows,
                                       const void* input, int num_q, const void* ape, const kvc_plan_c* plan_c,
                                       int cap_c, int32_t* counts, const kvc_store_args* args, void* stream);
+
+/*
+ * kvc_decode_c4_norm_rope_store - kvc_decode_c4 followed by
+ * kvc_norm_rope_store_decode in one kernel: the new token goes to the state
+ * as in kvc_decode_c4, and a request whose seq_len closes a block has its
+ * pooled row normalised, rotated and stored as bf16 at out_loc[b]; nothing
+ * is written for the other requests (no float32 rows).  Same arguments as
+ * kvc_decode_c4 with `args` (HOST pointer) in place of `out`.  A record or
+ * store target out of range sets KVC_DERR_RECORD in *status (may be NULL).
+ */
+int kvc_decode_c4_norm_rope_store(kvc_dtype dtype, int head_dim, void* state, int64_t num_state_rows,
+                                  const void* input, const void* ape, const kvc_plan_d* plan_d, int batch,
+                                  int32_t* status, const kvc_store_args* args, void* stream);
 
 /* kvc_strerror - static text for a host return code or a device error bit. */
 const char* kvc_strerror(int code);

@@ -192,16 +192,25 @@ int compress_common(bool c4, kvc_dtype dtype, int head_dim, const void* state, i
   return status_of(e);
 }
 
+// out != nullptr: pooled rows to float32; st != nullptr (ratio 4): pool + norm + rotary + store
 int decode_common(bool c4, kvc_dtype dtype, int head_dim, void* state, int64_t num_state_rows, const void* input,
-                  const void* ape, const kvc_plan_d* plan_d, int batch, int32_t* status, float* out, void* stream) {
+                  const void* ape, const kvc_plan_d* plan_d, int batch, int32_t* status, float* out,
+                  const kvc_store_args* st, void* stream) {
   if (!dtype_ok(dtype) || !hd_ok(head_dim) || !rows_ok(num_state_rows)) return KVC_EINVAL;
   if (batch < 1 || batch > KVC_MAX_DECODE_BATCH) return KVC_EINVAL;
-  if (!aligned16(input) || !aligned16(ape) || !aligned16(plan_d) || !aligned16(out)) return KVC_EINVAL;
+  if (!aligned16(input) || !aligned16(ape) || !aligned16(plan_d)) return KVC_EINVAL;
+  if (st == nullptr ? !aligned16(out) : !store_args_ok(head_dim, st)) return KVC_EINVAL;
   if (num_state_rows > 0 && !aligned16(state)) return KVC_EINVAL;
   if (status != nullptr && !aligned4(status)) return KVC_EINVAL;
-  kvc::DecodeArgs a{state, input, ape, plan_d, status, out, num_state_rows, batch};
-  const hipError_t e = c4 ? kvc::launch_decode_c4(dtype, head_dim, a, as_stream(stream))
-                          : kvc::launch_decode_c128(dtype, head_dim, a, as_stream(stream));
+  kvc::DecodeArgs a{state, input, ape, plan_d, status, out, num_state_rows, batch, {}};
+  hipError_t e;
+  if (st != nullptr) {
+    a.st = *st;
+    e = kvc::launch_decode_c4_store(dtype, head_dim, a, as_stream(stream));
+  } else {
+    e = c4 ? kvc::launch_decode_c4(dtype, head_dim, a, as_stream(stream))
+           : kvc::launch_decode_c128(dtype, head_dim, a, as_stream(stream));
+  }
   return status_of(e);
 }
 
@@ -265,14 +274,23 @@ KVC_EXPORT int kvc_norm_rope_store_decode(int compress_ratio, int head_dim, cons
 KVC_EXPORT int kvc_decode_c4(kvc_dtype dtype, int head_dim, void* state, int64_t num_state_rows, const void* input,
                              const void* ape, const kvc_plan_d* plan_d, int batch, int32_t* status, float* out,
                              void* stream) {
-  return decode_common(true, dtype, head_dim, state, num_state_rows, input, ape, plan_d, batch, status, out, stream);
+  return decode_common(true, dtype, head_dim, state, num_state_rows, input, ape, plan_d, batch, status, out, nullptr,
+                       stream);
 }
 
 KVC_EXPORT int kvc_decode_c128(kvc_dtype dtype, int head_dim, void* state, int64_t num_state_rows, const void* input,
                                const void* ape, const kvc_plan_d* plan_d, int batch, int32_t* status, float* out,
                                void* stream) {
   return decode_common(false, dtype, head_dim, state, num_state_rows, input, ape, plan_d, batch, status, out,
-                       stream);
+                       nullptr, stream);
+}
+
+KVC_EXPORT int kvc_decode_c4_norm_rope_store(kvc_dtype dtype, int head_dim, void* state, int64_t num_state_rows,
+                                             const void* input, const void* ape, const kvc_plan_d* plan_d, int batch,
+                                             int32_t* status, const kvc_store_args* args, void* stream) {
+  if (args == nullptr) return KVC_EINVAL;
+  return decode_common(true, dtype, head_dim, state, num_state_rows, input, ape, plan_d, batch, status, nullptr,
+                       args, stream);
 }
 
 KVC_EXPORT const char* kvc_strerror(int code) {

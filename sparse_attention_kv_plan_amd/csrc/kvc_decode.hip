@@ -11,9 +11,13 @@
 //  - ratio 128: a few workgroups per request, each owning a slice of the
 //    channels: it copies its slice of the row and, on a boundary, pools its
 //    channels over the 128-entry page.
+//  - ratio 4 with the store step (compressor_v2.py, compress_norm_rope_store):
+//    the pooled row is normalised, rotated and stored as bf16 into the
+//    compressed cache straight from registers; nothing else is written for it.
 #include "kvc_device.hpp"
 #include "kvc_launch.hpp"
 #include "kvc_pool.hpp"
+#include "kvc_store.hpp"
 
 namespace kvc {
 namespace {
@@ -66,6 +70,70 @@ __global__ __launch_bounds__(kThreads) void decode_c4_kernel(DecodeArgs a) {
     c4_pool<T, HD, 0>(state, input, ape, b, 7, rp0, rp1, c, res);
   }
   store_floats<V, true>(out, res);
+}
+
+// Ratio 4 with the store step.  No early return: a row of more than 64 lanes
+// (fp32, hd 512) reduces its sum of squares across two waves with a barrier.
+template <typename T, int HD>
+__global__ __launch_bounds__(kThreads) void decode_c4_store_kernel(DecodeArgs a) {
+  typedef typename Elem<T>::storage E;
+  constexpr int V = Elem<T>::kVec;
+  constexpr int kLanes = HD / V;
+  constexpr int kReq = kThreads / kLanes;
+  constexpr int64_t R = 4 * HD;
+  __shared__ float red[kThreads / kWave];
+  const int64_t b = (int64_t)blockIdx.x * kReq + threadIdx.x / kLanes;
+  const int c = (threadIdx.x % kLanes) * V;
+  float res[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) res[v] = 0.f;
+  bool pooled = false;
+  int32_t loc = -1, pos = 0;
+  StoreOperands<V> ops;
+  if (b < a.batch) {
+    const kvc_plan_d rec = load_plan_d(a.plan_d + b);
+    if (!plan_d_invalid(rec)) {
+      const bool boundary = (rec.seq_len & 3u) == 0u;
+      const bool first_block = rec.seq_len == 4u;
+      const int64_t wl = rec.write_loc, rp0 = rec.read_page_0, rp1 = rec.read_page_1;
+      bool ok = wl >= 0 && wl < a.num_state_rows;
+      if (boundary) ok = ok && c4_record_ok(b, 7, rp0, rp1, first_block ? 4 : 0, a.batch, a.num_state_rows);
+      if (!ok) {
+        if (c == 0 && a.status) atomicOr(a.status, KVC_DERR_RECORD);
+      } else {
+        E* state = static_cast<E*>(a.state);
+        const E* input = static_cast<const E*>(a.input);
+        u32x4 q[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = load16(input + b * R + i * HD + c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) store16_stream(state + wl * R + i * HD + c, q[i]);
+        if (boundary) {
+          pos = (int32_t)rec.seq_len - 4;
+          const auto pre = [&]() { loc = fetch_loc(a.st, b); };
+          const E* ape = static_cast<const E*>(a.ape);
+          if (first_block) {
+            c4_pool<T, HD, 4>(state, input, ape, b, 7, rp0, rp1, c, res, pre);
+          } else {
+            c4_pool<T, HD, 0>(state, input, ape, b, 7, rp0, rp1, c, res, pre);
+          }
+          pooled = store_ok(a.st, loc, pos);
+          if (pooled) {
+            fetch_operands<V, HD>(a.st, c, pos, ops);
+          } else {
+            if (c == 0 && a.status) atomicOr(a.status, KVC_DERR_RECORD);
+#pragma unroll
+            for (int v = 0; v < V; ++v) res[v] = 0.f;
+          }
+        }
+      }
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int v = 0; v < V; ++v) ss = fmaf(res[v], res[v], ss);
+  ss = row_sum<kLanes>(ss, red);  // reached by every thread
+  if (pooled) norm_rope_store<V, HD>(res, ss, c, loc, ops, a.st);
 }
 
 // Ratio 128: a workgroup of 128 threads owns a group of kDec128Group
@@ -174,6 +242,19 @@ hipError_t dispatch(kvc_dtype dtype, int hd, const DecodeArgs& a, hipStream_t st
 }
 
 }  // namespace
+
+template <typename T, int HD>
+struct C4StoreGo {
+  static hipError_t go(const DecodeArgs& a, hipStream_t s) {
+    constexpr int kReq = kThreads / (HD / Elem<T>::kVec);
+    decode_c4_store_kernel<T, HD><<<(a.batch + kReq - 1) / kReq, kThreads, 0, s>>>(a);
+    return hipGetLastError();
+  }
+};
+
+hipError_t launch_decode_c4_store(kvc_dtype dtype, int head_dim, const DecodeArgs& a, hipStream_t stream) {
+  return dispatch<C4StoreGo>(dtype, head_dim, a, stream);
+}
 
 hipError_t launch_decode_c4(kvc_dtype dtype, int head_dim, const DecodeArgs& a, hipStream_t stream) {
   return dispatch<C4Go>(dtype, head_dim, a, stream);

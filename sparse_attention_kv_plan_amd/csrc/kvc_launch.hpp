@@ -77,9 +77,10 @@ struct DecodeArgs {
   const void* ape;
   const kvc_plan_d* plan_d;
   int32_t* status;
-  float* out;
+  float* out;  // decode only
   int64_t num_state_rows;
   int batch;
+  kvc_store_args st;  // decode + norm + rotary + store only
 };
 
 // norm + rotary + store of float32 rows (prefill: plan_c / counts; decode: plan_d / status)
@@ -103,6 +104,7 @@ hipError_t launch_compress_c4_store(kvc_dtype dtype, int head_dim, const Compres
 hipError_t launch_compress_c128_store(kvc_dtype dtype, int head_dim, const CompressArgs& a, hipStream_t stream);
 hipError_t launch_norm_rope_store(int head_dim, bool decode, const NormRopeStoreArgs& a, hipStream_t stream);
 hipError_t launch_decode_c4(kvc_dtype dtype, int head_dim, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_c4_store(kvc_dtype dtype, int head_dim, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_c128(kvc_dtype dtype, int head_dim, const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace kvc

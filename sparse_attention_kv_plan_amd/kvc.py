@@ -63,6 +63,7 @@ def load(build_if_missing: bool = False):
         "kvc_norm_rope_store_decode": [I, I, P, P, I, P, P, P],
         "kvc_compress_c4_norm_rope_store": [I, I, P, L, P, I, P, P, I, P, P, P],
         "kvc_compress_c128_norm_rope_store": [I, I, P, L, P, I, P, P, I, P, P, P],
+        "kvc_decode_c4_norm_rope_store": [I, I, P, L, P, P, P, I, P, P, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -324,6 +325,23 @@ def compress_norm_rope_store(cr, head_dim, state, inp, ape, plan_c, counts, norm
     rc = fn(_dtype(inp), head_dim, _p(state), state.shape[0], _p(inp), inp.shape[0], _p(ape), _p(plan_c),
             plan_c.shape[0], _p(counts), ctypes.byref(st), _stream(stream))
     _check(rc, "kvc_compress_c%d_norm_rope_store" % cr)
+
+
+def decode_c4_norm_rope_store(head_dim, state, inp, ape, plan_d, norm_weight, eps, freqs_cis, out_loc, cache,
+                              status=None, stream=None):
+    """Ratio-4 decode with the store step in one kernel (kvc_decode_c4_norm_rope_store)."""
+    _dev(state, inp, ape, plan_d, status)
+    _rows(4, head_dim, state, inp)
+    _shape(ape, WINDOW[4], head_dim, "ape")
+    _shape(plan_d, 1, D_BYTES, "plan_d")
+    _shape(inp, plan_d.shape[0], 4 * head_dim, "input")
+    if ape.element_size() != inp.element_size():
+        raise KvcError("ape must share the input dtype")
+    st = store_args(head_dim, norm_weight, eps, freqs_cis, out_loc, cache)
+    rc = load().kvc_decode_c4_norm_rope_store(_dtype(inp), head_dim, _p(state), state.shape[0], _p(inp), _p(ape),
+                                              _p(plan_d), plan_d.shape[0], _p(status), ctypes.byref(st),
+                                              _stream(stream))
+    _check(rc, "kvc_decode_c4_norm_rope_store")
 
 
 def decode_c4(head_dim, state, inp, ape, plan_d, out, status=None, stream=None):

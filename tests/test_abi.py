@@ -22,7 +22,7 @@ def test_header_declares_the_boundary():
         "kvc_plan_prefill", "kvc_plan_decode", "kvc_write", "kvc_compress_c4", "kvc_compress_c128",
         "kvc_decode_c4", "kvc_decode_c128", "kvc_strerror", "kvc_plan_prefill_swa", "kvc_plan_decode_swa",
         "kvc_norm_rope_store_prefill", "kvc_norm_rope_store_decode", "kvc_compress_c4_norm_rope_store",
-        "kvc_compress_c128_norm_rope_store"])
+        "kvc_compress_c128_norm_rope_store", "kvc_decode_c4_norm_rope_store"])
 
 
 def test_store_args_layout_matches_the_header(tmp_path):
@@ -110,6 +110,9 @@ def test_host_argument_checks_reject_without_enqueueing(lib):
     assert lib.kvc_compress_c4_norm_rope_store(1, 128, p, 8, p, 1, p, p, 1, p, None, None) == E
     assert lib.kvc_compress_c128_norm_rope_store(1, 128, p, 8, p, 1, p, p, 1, p, st(rope_dim=4), None) == E
     assert lib.kvc_compress_c4_norm_rope_store(1, 128, p, 8, p, 1, p, p, 0, p, st(), None) == kvc.KVC_OK
+    assert lib.kvc_decode_c4_norm_rope_store(1, 128, p, 8, p, p, p, 1, None, None, None) == E
+    assert lib.kvc_decode_c4_norm_rope_store(1, 128, p, 8, p, p, p, 1, None, st(rope_dim=20), None) == E
+    assert lib.kvc_decode_c4_norm_rope_store(1, 128, p, 8, p, p, p, 0, None, st(), None) == E
     # empty work is a no-op that needs no device
     assert lib.kvc_compress_c4(1, 128, p, 8, p, 1, p, p, 0, p, p, None) == kvc.KVC_OK
     assert lib.kvc_write(128, 1, 512, p, 8, p, 1, p, 0, p, None) == kvc.KVC_OK

@@ -301,3 +301,86 @@ def test_decode_store_full_size(gpu, name):
                                    si.freqs_cis, si.out_loc, np.full((si.num_cache_rows, w.hd), np.nan))
     assert err == 0
     assert_store_close(_cache_host(cache), ref, name)
+
+
+DECODE_FUSED = [(512, "bf16", 64), (128, "f32", 64), (512, "f32", 64), (256, "bf16", 0), (128, "bf16", 128)]
+
+
+@pytest.mark.parametrize("hd,dtype,rope_dim", DECODE_FUSED)
+def test_decode_c4_norm_rope_store(gpu, hd, dtype, rope_dim):
+    """The fused ratio-4 decode + store against the oracle's decode followed by its store; the
+    state after the step is compared bit for bit."""
+    rng = np.random.default_rng(400 + hd + rope_dim + (dtype == "bf16"))
+    for trial in range(3):
+        B = int(rng.integers(1, 300))
+        w = wl.random_decode(rng, 4, hd, dtype, B, prefix_hi=24, num_slots=B + 2)
+        if trial == 2:  # every request closes a block, the first block included
+            w.seq_lens = (rng.integers(1, 4, size=B) * 4).astype(np.int32)
+        pd, status = oracle.plan_decode(4, w.seq_lens, w.state_index, w.num_state_rows)
+        assert status == 0
+        say("fused decode hd=%d %s rope=%d trial=%d B=%d boundaries=%d" % (hd, dtype, rope_dim, trial, B,
+                                                                           int((w.seq_lens % 4 == 0).sum())))
+        st_o = w.state.copy()
+        pooled, err = oracle.decode(4, hd, st_o, w.input, w.ape, pd)
+        assert err == 0
+        si = wl.store_inputs(rng, hd, rope_dim, int(w.seq_lens.max()) + 1, B)
+        ref, err = oracle.store_decode(4, pooled.astype(np.float32), pd, si.norm_weight, si.eps, si.freqs_cis,
+                                       si.out_loc, np.full((si.num_cache_rows, hd), np.nan))
+        assert err == 0
+        wt, f, loc, cache = _store_tensors(si, hd)
+        state = dev(w.state)
+        stt = torch.zeros(1, dtype=torch.int32, device="cuda")
+        kvc.decode_c4_norm_rope_store(hd, state, dev(w.input), dev(w.ape), dev(pd), wt, si.eps, f, loc, cache, stt)
+        assert int(stt.item()) == 0
+        assert_store_close(_cache_host(cache), ref, "fused decode")
+        got_state = state.cpu().numpy()
+        assert np.array_equal(got_state.view(np.uint8), st_o.view(np.uint8)), "state differs after the step"
+
+
+def test_decode_c4_norm_rope_store_bad_target(gpu):
+    """A boundary request whose location is out of range: its token still reaches the state,
+    its row is not stored, and the status word says so."""
+    hd = 512
+    rng = np.random.default_rng(77)
+    w = wl.random_decode(rng, 4, hd, "bf16", 16, prefix_hi=24, num_slots=18)
+    w.seq_lens = (rng.integers(1, 4, size=16) * 4).astype(np.int32)
+    pd, _ = oracle.plan_decode(4, w.seq_lens, w.state_index, w.num_state_rows)
+    st_o = w.state.copy()
+    pooled, _ = oracle.decode(4, hd, st_o, w.input, w.ape, pd)
+    si = wl.store_inputs(rng, hd, 64, int(w.seq_lens.max()) + 1, 16)
+    si.out_loc[5] = si.num_cache_rows  # one past the end
+    ref, err = oracle.store_decode(4, pooled.astype(np.float32), pd, si.norm_weight, si.eps, si.freqs_cis, si.out_loc,
+                                   np.full((si.num_cache_rows, hd), np.nan))
+    assert err == kvc.DERR_RECORD
+    wt, f, loc, cache = _store_tensors(si, hd)
+    state = dev(w.state)
+    stt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kvc.decode_c4_norm_rope_store(hd, state, dev(w.input), dev(w.ape), dev(pd), wt, si.eps, f, loc, cache, stt)
+    assert int(stt.item()) == kvc.DERR_RECORD
+    assert_store_close(_cache_host(cache), ref, "bad target")
+    assert np.array_equal(state.cpu().numpy().view(np.uint8), st_o.view(np.uint8))
+
+
+def test_decode_c4_norm_rope_store_full_size(gpu):
+    """256 requests, prefixes up to 32768: the fused step against decode + standalone store on the GPU
+    and against the oracle."""
+    w = wl.config3()
+    say("fused decode store workload %s: B=%d" % (w.name, w.B))
+    plan_d = torch.empty((w.B, kvc.D_BYTES), dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kvc.plan_decode(4, dev(w.seq_lens), dev(w.state_index), w.num_state_rows, plan_d, status)
+    si = wl.store_inputs(np.random.default_rng(1013), w.hd, 64, int(w.seq_lens.max()) + 1, w.B)
+    wt, f, loc, cache = _store_tensors(si, w.hd)
+    state = dev(w.state)
+    kvc.decode_c4_norm_rope_store(w.hd, state, dev(w.input), dev(w.ape), plan_d, wt, si.eps, f, loc, cache, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    pd = plan_d.cpu().numpy()
+    st_o = w.state.copy()
+    pooled, err = oracle.decode(4, w.hd, st_o, w.input, w.ape, pd)
+    assert err == 0
+    ref, err = oracle.store_decode(4, pooled.astype(np.float32), pd, si.norm_weight, si.eps, si.freqs_cis,
+                                   si.out_loc, np.full((si.num_cache_rows, w.hd), np.nan))
+    assert err == 0
+    assert_store_close(_cache_host(cache), ref, w.name)
+    assert np.array_equal(state.cpu().numpy().view(np.uint8), st_o.view(np.uint8))
