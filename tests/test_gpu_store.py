@@ -384,3 +384,50 @@ def test_decode_c4_norm_rope_store_full_size(gpu):
     assert err == 0
     assert_store_close(_cache_host(cache), ref, w.name)
     assert np.array_equal(state.cpu().numpy().view(np.uint8), st_o.view(np.uint8))
+
+
+def test_store_paths_under_graph_capture(gpu):
+    """A prefill chunk with the fused store (plan, pool + store, write) and a fused ratio-4 decode step,
+    captured in one HIP graph and replayed: every replay matches the eager run bit for bit."""
+    rng = np.random.default_rng(23)
+    w = wl.random_prefill(rng, 4, 512, "bf16", 8, prefix_hi=500, extend_lo=1, extend_hi=700, num_slots=12)
+    d = wl.random_decode(rng, 4, 512, "bf16", 64, prefix_hi=40, num_slots=64)
+    s_d, e_d, i_d = dev(w.seq_lens), dev(w.extend_lens), dev(w.state_index)
+    inp, ape, state0 = dev(w.input), dev(w.ape), dev(w.state)
+    d_inp, d_ape, d_state0 = dev(d.input), dev(d.ape), dev(d.state)
+    plan_c, plan_w, counts = kvc.alloc_prefill_plan(4, w.B, w.num_q)
+    plan_d = torch.empty((d.B, kvc.D_BYTES), dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    si = wl.store_inputs(rng, 512, 64, int(max(w.seq_lens.max(), d.seq_lens.max())) + 1, max(w.num_q, d.B))
+    wt, f, loc, cache = _store_tensors(si, 512)
+    state, d_state = state0.clone(), d_state0.clone()
+
+    def step():
+        kvc.plan_prefill(4, s_d, e_d, i_d, w.num_state_rows, w.num_q, plan_c, plan_w, counts)
+        kvc.compress_norm_rope_store(4, 512, state, inp, ape, plan_c, counts, wt, si.eps, f, loc, cache)
+        kvc.write(4, 512, state, inp, plan_w, counts)
+        kvc.plan_decode(4, dev_d_seq, dev_d_idx, d.num_state_rows, plan_d, status)
+        kvc.decode_c4_norm_rope_store(512, d_state, d_inp, d_ape, plan_d, wt, si.eps, f, loc[:d.B], cache, status)
+
+    dev_d_seq, dev_d_idx = dev(d.seq_lens), dev(d.state_index)
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (cache, state, d_state, counts, status)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(4):
+        say("store graph replay", rep)
+        state.copy_(state0)
+        d_state.copy_(d_state0)
+        cache.fill_(-1)
+        counts.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((cache, state, d_state, counts, status), ref):
+            assert torch.equal(got, want)
