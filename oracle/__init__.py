@@ -63,9 +63,12 @@ def _load():
         D = ctypes.c_double
         lib.oracle_store_prefill.argtypes = [I, I, I, P, P, I, P, D, P, L, P, L, P, L]
         lib.oracle_store_decode.argtypes = [I, I, I, P, P, I, P, D, P, L, P, L, P, L]
+        lib.oracle_compress_online.argtypes = [I, I, P, L, P, I, P, P, I, P]
+        lib.oracle_write_online.argtypes = [I, I, P, L, P, I, P, P, I]
+        lib.oracle_decode_online.argtypes = [I, I, P, L, P, P, P, I, P]
         for f in ("oracle_plan_prefill", "oracle_plan_decode", "oracle_compress", "oracle_write",
                   "oracle_decode", "oracle_plan_prefill_swa", "oracle_plan_decode_swa", "oracle_store_prefill",
-                  "oracle_store_decode"):
+                  "oracle_store_decode", "oracle_compress_online", "oracle_write_online", "oracle_decode_online"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -227,6 +230,50 @@ def store_decode(cr, rows, plan_d, norm_weight, eps, freqs_cis, out_loc, cache):
     plan_d = np.ascontiguousarray(plan_d, dtype=np.uint8)
     return _store(_load().oracle_store_decode, cr, rows, plan_d, plan_d.shape[0], norm_weight, eps, freqs_cis,
                   out_loc, cache)
+
+
+def _online_state(state, hd):
+    st = np.array(state, dtype=np.float64, copy=True, order="C")
+    if st.ndim != 3 or st.shape[1:] != (3, hd):
+        raise ValueError("online state must be [slots, 3, hd] (m, l, acc)")
+    return st
+
+
+def compress_online(hd, state, inp, ape, plan_c, num_c):
+    """Ratio-128 pool with the online state: state [slots, 3, hd] (m, l, acc) float64.
+    Returns (out float64 [cap_c, hd] (NaN where untouched), error bits)."""
+    inp, bf = _elem(inp)
+    ape, _ = _elem(ape)
+    st = _online_state(state, hd)
+    plan_c = np.ascontiguousarray(plan_c, dtype=np.uint8)
+    out = np.full((max(plan_c.shape[0], 1), hd), np.nan)
+    err = _load().oracle_compress_online(bf, hd, _ptr(st), st.shape[0], _ptr(inp), inp.shape[0], _ptr(ape),
+                                         _ptr(plan_c), int(num_c), _ptr(out))
+    return out[: plan_c.shape[0]], err
+
+
+def write_online(hd, state, inp, ape, plan_w, num_w):
+    """Fold each request's W records into its slot.  Returns (new state, error bits)."""
+    inp, bf = _elem(inp)
+    ape, _ = _elem(ape)
+    st = _online_state(state, hd)
+    plan_w = np.ascontiguousarray(plan_w, dtype=np.uint8)
+    err = _load().oracle_write_online(bf, hd, _ptr(st), st.shape[0], _ptr(inp), inp.shape[0], _ptr(ape),
+                                      _ptr(plan_w), int(num_w))
+    return st, err
+
+
+def decode_online(hd, state, inp, ape, plan_d):
+    """Decode step with the online state.  Returns (out float64 [B, hd], new state, error bits)."""
+    inp, bf = _elem(inp)
+    ape, _ = _elem(ape)
+    st = _online_state(state, hd)
+    plan_d = np.ascontiguousarray(plan_d, dtype=np.uint8)
+    B = plan_d.shape[0]
+    out = np.zeros((B, hd))
+    err = _load().oracle_decode_online(bf, hd, _ptr(st), st.shape[0], _ptr(inp), _ptr(ape), _ptr(plan_d), B,
+                                       _ptr(out))
+    return out, st, err
 
 
 def capacities_swa(cr, B, num_q, swa_page_size):

@@ -685,3 +685,150 @@ int oracle_store_decode(int cr, int hd, int rope_dim, const float* x, const uint
   }
   return err;
 }
+
+/* ------------------------------------------------------------------------ */
+/* online ratio-128 state                                                    */
+/* ------------------------------------------------------------------------ */
+/*
+ * compressor_v2.py, _use_online_compress and _forward_unified: with the
+ * online path the ratio-128 state of a request is one slot of 3 * head_dim
+ * values (the kv_score_buffer viewed as [slots, 1, 3 * head_dim]) instead of
+ * a 128-row page.  Reading taken here: the slot holds, per channel, the
+ * running maximum m, the running sum l = sum exp(t - m) and the running
+ * weighted sum acc = sum exp(t - m) kv over the positions of the current
+ * (unfinished) block, t = score + ape[pos % 128]; a block's compressed row is
+ * acc / l once its 128th position is folded in.  Slots here are float64
+ * [slots][3][hd] (m, l, acc).  The usual ratio-128 plans drive it: a C record
+ * with buffer_len > 0 starts from the slot's partial (the entries before the
+ * chunk); the W records of a request (its tail positions) are folded into the
+ * slot; a decode record folds one token.
+ */
+static void fold(double* m, double* l, double* acc, int fresh, double t, double kv) {
+  if (fresh) {
+    *m = t;
+    *l = 1.0;
+    *acc = kv;
+    return;
+  }
+  const double nm = t > *m ? t : *m;
+  const double a = exp(*m - nm), b = exp(t - nm);
+  *l = *l * a + b;
+  *acc = *acc * a + kv * b;
+  *m = nm;
+}
+
+/* Pool every valid C record of a ratio-128 plan with the online state.
+ * Entries [0, blen) are the slot's partial (slot = read_page_0); entries
+ * [blen, 128) are input rows ragged - 127 + i.  out[k] = acc / l. */
+int oracle_compress_online(int is_bf16, int hd, const double* state, int64_t num_slots, const void* input, int num_q,
+                           const void* ape, const uint8_t* plan_c, int num_c, double* out) {
+  const int64_t R = 2 * (int64_t)hd;
+  int err = 0;
+  for (int k = 0; k < num_c; ++k) {
+    const uint8_t* r = plan_c + (size_t)k * 16;
+    if (get_u32(r) == 0xFFFFFFFFu) continue;
+    const uint32_t rb = get_u32(r + 4);
+    const int64_t ragged = rb & 0xFFFFFF, blen = rb >> 24, slot = get_i32(r + 8);
+    if ((blen > 0 && (slot < 0 || slot >= num_slots)) || ragged - 127 + blen < 0 || ragged >= num_q) {
+      err |= ERR_RECORD;
+      continue;
+    }
+    for (int64_t d = 0; d < hd; ++d) {
+      double m = 0, l = 0, acc = 0;
+      int fresh = 1;
+      if (blen > 0) {
+        const double* s = state + slot * 3 * hd;
+        m = s[d];
+        l = s[hd + d];
+        acc = s[2 * hd + d];
+        fresh = 0;
+      }
+      for (int64_t i = blen; i < 128; ++i) {
+        const int64_t row = ragged - 127 + i;
+        const double t = widen(input, is_bf16, row, R, hd + d) + widen(ape, is_bf16, i, hd, d);
+        fold(&m, &l, &acc, fresh, t, widen(input, is_bf16, row, R, d));
+        fresh = 0;
+      }
+      out[(size_t)k * hd + d] = acc / l;
+    }
+  }
+  return err;
+}
+
+/* Fold each request's W records (its positions after the chunk's last
+ * completed block, consecutive records with the same slot = write_loc / 128)
+ * into its slot.  The run starts a fresh block when its first position is a
+ * multiple of 128 (write_loc % 128 == 0), else it continues the slot. */
+int oracle_write_online(int is_bf16, int hd, double* state, int64_t num_slots, const void* input, int num_q,
+                        const void* ape, const uint8_t* plan_w, int num_w) {
+  const int64_t R = 2 * (int64_t)hd;
+  int err = 0;
+  int k = 0;
+  while (k < num_w) {
+    const uint8_t* r = plan_w + (size_t)k * 8;
+    const uint32_t ragged = get_u32(r);
+    const int64_t loc = get_i32(r + 4);
+    if (ragged == 0xFFFFFFFFu) {
+      ++k;
+      continue;
+    }
+    const int64_t slot = loc / 128, p0 = loc % 128;
+    int n = 1;
+    while (k + n < num_w && get_u32(plan_w + (size_t)(k + n) * 8) != 0xFFFFFFFFu &&
+           get_i32(plan_w + (size_t)(k + n) * 8 + 4) / 128 == slot)
+      ++n;
+    if (loc < 0 || slot >= num_slots || (int64_t)ragged + n > num_q || p0 + n > 128) {
+      err |= ERR_RECORD;
+      k += n;
+      continue;
+    }
+    double* s = state + slot * 3 * hd;
+    for (int64_t d = 0; d < hd; ++d) {
+      double m = s[d], l = s[hd + d], acc = s[2 * hd + d];
+      int fresh = p0 == 0;
+      for (int i = 0; i < n; ++i) {
+        const int64_t row = (int64_t)ragged + i;
+        const double t = widen(input, is_bf16, row, R, hd + d) + widen(ape, is_bf16, p0 + i, hd, d);
+        fold(&m, &l, &acc, fresh, t, widen(input, is_bf16, row, R, d));
+        fresh = 0;
+      }
+      s[d] = m;
+      s[hd + d] = l;
+      s[2 * hd + d] = acc;
+    }
+    k += n;
+  }
+  return err;
+}
+
+/* Decode with the online state: fold input row b at position seq_len - 1
+ * into slot read_page_0 (fresh when that position is a multiple of 128); if
+ * seq_len closes a block, out[b] = acc / l, else a zero row. */
+int oracle_decode_online(int is_bf16, int hd, double* state, int64_t num_slots, const void* input, const void* ape,
+                         const uint8_t* plan_d, int B, double* out) {
+  const int64_t R = 2 * (int64_t)hd;
+  int err = 0;
+  for (int b = 0; b < B; ++b) {
+    const uint8_t* r = plan_d + (size_t)b * 16;
+    double* o = out + (size_t)b * hd;
+    for (int64_t d = 0; d < hd; ++d) o[d] = 0.0;
+    const uint32_t seq_len = get_u32(r);
+    if (seq_len == 0xFFFFFFFFu) continue;
+    const int64_t slot = get_i32(r + 8), pos = (int64_t)seq_len - 1;
+    if (slot < 0 || slot >= num_slots) {
+      err |= ERR_RECORD;
+      continue;
+    }
+    double* s = state + slot * 3 * hd;
+    for (int64_t d = 0; d < hd; ++d) {
+      double m = s[d], l = s[hd + d], acc = s[2 * hd + d];
+      const double t = widen(input, is_bf16, b, R, hd + d) + widen(ape, is_bf16, pos % 128, hd, d);
+      fold(&m, &l, &acc, pos % 128 == 0, t, widen(input, is_bf16, b, R, d));
+      s[d] = m;
+      s[hd + d] = l;
+      s[2 * hd + d] = acc;
+      if (seq_len % 128 == 0) o[d] = acc / l;
+    }
+  }
+  return err;
+}

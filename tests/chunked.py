@@ -128,6 +128,56 @@ class OracleBackend:
         return out, state, err
 
 
+class OnlineBackend:
+    """The online ratio-128 state behind the same calls: plans are the ordinary ratio-128 plans
+    over 128 virtual rows per slot; ``state`` is [slots, 3, hd] (m, l, acc).  ``inner`` provides
+    plan_prefill / plan_decode and compress_online / write_online / decode_online; the fold of the
+    tail tokens needs ``ape``, which the state-buffer write does not take."""
+
+    def __init__(self, inner, ape):
+        self.inner = inner
+        self.ape = ape
+
+    def plan_prefill(self, cr, s, e, idx, rows, num_q, cap_c, cap_w):
+        return self.inner.plan_prefill(cr, s, e, idx, rows * 128, num_q, cap_c, cap_w)
+
+    def plan_decode(self, cr, s, idx, rows):
+        return self.inner.plan_decode(cr, s, idx, rows * 128)
+
+    def compress(self, cr, hd, state, inp, ape, pc, num_c):
+        return self.inner.compress_online(hd, state, inp, ape, pc, num_c)
+
+    def write(self, cr, hd, state, inp, pw, num_w):
+        st, err = self.inner.write_online(hd, state, inp, self.ape, pw, num_w)
+        assert err == 0
+        return st
+
+    def decode(self, cr, hd, state, inp, ape, pd):
+        return self.inner.decode_online(hd, state, inp, ape, pd)
+
+
+class OracleOnline:
+    """The oracle's online functions in OnlineBackend's ``inner`` convention."""
+
+    def __init__(self, oracle):
+        self.o = oracle
+
+    def plan_prefill(self, *a):
+        return self.o.plan_prefill(*a)
+
+    def plan_decode(self, *a):
+        return self.o.plan_decode(*a)
+
+    def compress_online(self, hd, state, inp, ape, pc, num_c):
+        return self.o.compress_online(hd, state, inp, ape, pc, num_c)
+
+    def write_online(self, hd, state, inp, ape, pw, num_w):
+        return self.o.write_online(hd, state, inp, ape, pw, num_w)
+
+    def decode_online(self, hd, state, inp, ape, pd):
+        return self.o.decode_online(hd, state, inp, ape, pd)
+
+
 def as_float(a, dtype):
     if dtype == "bf16":
         return (np.asarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)

@@ -77,6 +77,24 @@ MUTANTS = [
     ("prefill location by record, not ragged id", "x + (size_t)k * hd, seq_len, ragged,", "x + (size_t)k * hd, seq_len, k,"),
     ("store location range unchecked", "if (loc < 0 || loc >= num_cache_rows) return ERR_RECORD;",
      "if (loc < 0) return ERR_RECORD;"),
+    ("online fold drops the sum rescale", "*l = *l * a + b;",
+     "*l = *l + b;"),
+    ("online fold drops the weighted-sum rescale", "*acc = *acc * a + kv * b;",
+     "*acc = *acc + kv * b;"),
+    ("online compress ignores the partial in the slot", "      if (blen > 0) {\n        const double* s = state + slot * 3 * hd;",
+     "      if (0) {\n        const double* s = state + slot * 3 * hd;"),
+    ("online write always starts a fresh block", "int fresh = p0 == 0;",
+     "int fresh = 1;"),
+    ("online write takes ape by run index", "widen(ape, is_bf16, p0 + i, hd, d)",
+     "widen(ape, is_bf16, i, hd, d)"),
+    ("online decode never starts a fresh block", "fold(&m, &l, &acc, pos % 128 == 0, t,",
+     "fold(&m, &l, &acc, 0, t,"),
+    ("online decode emits one token early", "if (seq_len % 128 == 0) o[d] = acc / l;",
+     "if (pos % 128 == 0) o[d] = acc / l;"),
+    ("online write merges runs of different slots", "get_i32(plan_w + (size_t)(k + n) * 8 + 4) / 128 == slot",
+     "1"),
+    ("online compress window off by one", "        const int64_t row = ragged - 127 + i;\n        const double t",
+     "        const int64_t row = ragged - 126 + i;\n        const double t"),
 ]
 
 
@@ -104,6 +122,7 @@ def test_pins_catch_mutant(tmp_path, mutant):
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_pins.py"),
                         os.path.join(ROOT, "tests", "test_oracle_swa_pins.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_store_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_store_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_online_pins.py")],
                        cwd=ROOT, env=env, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, timeout=600)
     assert r.returncode != 0, "pins did not catch mutant '%s':\n%s" % (name, r.stdout.decode()[-2000:])

@@ -1,0 +1,134 @@
+"""Pins of the oracle's online ratio-128 state (one slot of m, l, acc per request).
+
+* chunking invariance: any split of requests into prefill chunks and decode
+  steps, run through the ordinary ratio-128 plans with the online state,
+  emits exactly the rows of the brute-force window definition
+  (oracle/brute.py), starting from NaN-filled slots (a read of a slot that
+  holds nothing yet shows up as NaN);
+* the slot after a partial block is the closed form over the positions folded
+  so far: max t, sum exp(t - max), sum exp(t - max) kv;
+* an online decode at s equals a one-token online prefill at s;
+* error bits for slots and rows out of range.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import brute
+from sparse_attention_kv_plan_amd import workloads as wl
+from tests.chunked import OnlineBackend, OracleOnline, as_float, random_split, run_chunked
+
+ERR_RECORD = 16
+
+
+def _nan_slots(n, hd):
+    return np.full((n, 3, hd), np.nan)
+
+
+def _seqs(rng, B, hd, dtype, lo, hi, extra):
+    seqs, chunks = [], []
+    for _ in range(B):
+        L = int(rng.integers(lo, hi))
+        x = rng.standard_normal((L + extra, 2 * hd)).astype(np.float32)
+        seqs.append(wl.to_bf16_bits(x) if dtype == "bf16" else x)
+        chunks.append(random_split(rng, L, 6))
+    return seqs, chunks
+
+
+@pytest.mark.parametrize("dtype,trial", [("f32", 0), ("bf16", 1), ("f32", 2), ("bf16", 3)])
+def test_online_chunking_matches_the_window_definition(dtype, trial):
+    rng = np.random.default_rng(500 + trial)
+    hd, B, decode_steps = 2, 4, 150
+    seqs, chunks = _seqs(rng, B, hd, dtype, 1, 600, decode_steps)
+    ape_f = (0.1 * rng.standard_normal((128, hd))).astype(np.float32)
+    ape = wl.to_bf16_bits(ape_f) if dtype == "bf16" else ape_f
+    idx = rng.permutation(6)[:B]
+    emitted, _ = run_chunked(OnlineBackend(OracleOnline(oracle), ape), 128, hd, dtype, seqs, chunks, decode_steps,
+                             idx, 6, ape, state=_nan_slots(6, hd))
+    apef = as_float(ape, dtype).tolist()
+    seen = set()
+    for b, seq in enumerate(seqs):
+        seqf = as_float(seq, dtype).tolist()
+        for s in range(128, len(seq) + 1, 128):
+            assert (b, s) in emitted, ("missing row", b, s)
+            seen.add((b, s))
+            ref = brute.pooled_row(128, hd, seqf, apef, s)
+            np.testing.assert_allclose(emitted[(b, s)], ref, rtol=1e-12, atol=1e-12, err_msg=str((b, s)))
+    assert set(emitted) == seen
+
+
+def test_slot_is_the_closed_form_of_the_positions_folded():
+    """After chunks that end inside a block, each slot holds max t, sum exp(t - max) and
+    sum exp(t - max) kv over that block's positions so far."""
+    rng = np.random.default_rng(11)
+    hd, B = 3, 5
+    L = np.array([5, 128, 300, 129, 255])
+    ape = rng.standard_normal((128, hd)).astype(np.float32)
+    seqs = [rng.standard_normal((int(n), 2 * hd)).astype(np.float32) for n in L]
+    chunks = [random_split(rng, int(n), 4) for n in L]
+    idx = np.array([4, 0, 2, 1, 3])
+    _, slots = run_chunked(OnlineBackend(OracleOnline(oracle), ape), 128, hd, "f32", seqs, chunks, 0, idx, 5, ape,
+                           state=_nan_slots(5, hd))
+    for b in range(B):
+        start = (int(L[b]) // 128) * 128
+        pos = np.arange(start, int(L[b]))
+        slot = slots[idx[b]]
+        if len(pos) == 0:
+            continue  # the block closed exactly: nothing is pending (the slot is not read again)
+        x = seqs[b][pos].astype(np.float64)
+        t = x[:, hd:] + ape[pos % 128].astype(np.float64)
+        m = t.max(axis=0)
+        e = np.exp(t - m)
+        np.testing.assert_array_equal(slot[0], m)
+        np.testing.assert_allclose(slot[1], e.sum(axis=0), rtol=1e-13)
+        np.testing.assert_allclose(slot[2], (e * x[:, :hd]).sum(axis=0), rtol=1e-12, atol=1e-14)
+
+
+def test_online_decode_equals_one_token_prefill():
+    rng = np.random.default_rng(12)
+    hd, B = 4, 6
+    s = np.array([128, 256, 200, 1, 129, 640], np.int32)
+    idx = rng.permutation(B)
+    slots0 = rng.standard_normal((B, 3, hd))
+    slots0[:, 1] = np.abs(slots0[:, 1]) + 0.5  # a running sum is positive
+    ape = rng.standard_normal((128, hd)).astype(np.float32)
+    inp = rng.standard_normal((B, 2 * hd)).astype(np.float32)
+    pd, status = oracle.plan_decode(128, s, idx, B * 128)
+    out_d, st_d, err = oracle.decode_online(hd, slots0, inp, ape, pd)
+    assert status == 0 and err == 0
+    pc, pw, counts = oracle.plan_prefill(128, s, np.ones(B, np.int32), idx, B * 128, B, B, B)
+    out_p, err = oracle.compress_online(hd, slots0, inp, ape, pc, counts[0])
+    assert err == 0
+    st_p, err = oracle.write_online(hd, slots0, inp, ape, pw, counts[1])
+    assert err == 0
+    C = oracle.unpack_c(pc[: counts[0]])
+    for k in range(int(counts[0])):
+        b = int(C[k, 1])  # one token per request: ragged id = batch index
+        np.testing.assert_allclose(out_p[k], out_d[b], rtol=1e-13)
+    for b in range(B):
+        if s[b] % 128 != 0:
+            np.testing.assert_allclose(st_p[idx[b]], st_d[idx[b]], rtol=1e-13)
+            assert np.all(out_d[b] == 0)
+
+
+def test_online_errors():
+    hd = 2
+    ape = np.zeros((128, hd), np.float32)
+    inp = np.ones((4, 2 * hd), np.float32)
+    slots = np.zeros((2, 3, hd))
+    # a C record continuing a slot outside the array
+    pc = np.zeros((1, 16), np.uint8)
+    pc[0] = np.array([130, 3 | (125 << 24), 7, 7], np.uint32).view(np.uint8)
+    _, err = oracle.compress_online(hd, slots, inp, ape, pc, 1)
+    assert err == ERR_RECORD
+    # W records of a slot outside the array
+    pw = np.zeros((2, 8), np.uint8)
+    pw[0] = np.array([0, 5 * 128], np.uint32).view(np.uint8)
+    pw[1] = np.array([1, 5 * 128 + 1], np.uint32).view(np.uint8)
+    _, err = oracle.write_online(hd, slots, inp, ape, pw, 2)
+    assert err == ERR_RECORD
+    # decode record of a slot outside the array
+    pd = np.zeros((1, 16), np.uint8)
+    pd[0] = np.array([5, 9 * 128 + 4, 9, 9], np.uint32).view(np.uint8)
+    _, _, err = oracle.decode_online(hd, slots, inp, ape, pd)
+    assert err == ERR_RECORD
