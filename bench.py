@@ -345,6 +345,32 @@ def main():
             kvc.decode_c4_norm_rope_store(X.w.hd, X.state, X.inp, X.ape, X.plan_d, self.wt, self.eps, self.f,
                                           self.loc, self.cache, X.status)
 
+    # the online ratio-128 state (breakdown pass only): one fp32 slot of (m, l, acc) per request
+    # instead of a 128-row page, driven by the same plans
+    class Online:
+        def __init__(self, X, n, seed):
+            self.X, w = X, X.w
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(seed)
+            self.slots = torch.randn((n, 3, w.hd), generator=gen, device=dev, dtype=torch.float32)
+            self.slots[:, 1].abs_().add_(1.0)  # running sums are positive
+
+        def compress(self):
+            X, w = self.X, self.X.w
+            kvc.compress_c128_online(w.hd, self.slots, X.inp, X.ape, X.plan_c, X.counts, X.out)
+
+        def write(self):
+            X, w = self.X, self.X.w
+            kvc.write_c128_online(w.hd, self.slots, X.inp, X.ape, X.plan_w, X.counts)
+
+        def decode(self):
+            X, w = self.X, self.X.w
+            kvc.decode_c128_online(w.hd, self.slots, X.inp, X.ape, X.plan_d, X.out, X.status)
+
+    OP128, OD128 = Online(P128, p128.B, 4128), Online(D128, d128.B, 4129)
+    online_launches = [("compress_c128_online", OP128.compress), ("write_c128_online", OP128.write),
+                       ("decode_c128_online", OD128.decode)]
+
     ST4, ST128 = Store(P4, p4.num_q, 3004), Store(P128, p128.num_q, 3128)
     SD4S, SD128S = Store(D4, d4.B, 3003), Store(D128, d128.B, 3129)
     store_launches = [("compress_c4_norm_rope_store", ST4.fused), ("norm_rope_store_prefill c4", ST4.prefill),
@@ -394,7 +420,7 @@ def main():
 
     # per-kernel breakdown (separate, untimed pass; events around every launch), with the
     # SWA-paged planners of the same requests and the store step after the pool
-    extra = swa_launches + store_launches
+    extra = swa_launches + store_launches + online_launches
     bev = {name: [] for name, _ in launches + extra}
     for _ in range(5):
         for name, f in launches + extra:

@@ -360,6 +360,55 @@ int kvc_decode_c4_norm_rope_store(kvc_dtype dtype, int head_dim, void* state, in
                                   const void* input, const void* ape, const kvc_plan_d* plan_d, int batch,
                                   int32_t* status, const kvc_store_args* args, void* stream);
 
+/*
+ * Online ratio-128 state (compressor_v2.py page, _use_online_compress and
+ * _forward_unified: the state of a request is one slot of 3 * head_dim
+ * values instead of a 128-row page).  A slot is fp32 [3, hd]: per channel
+ * the running maximum m, the running sum l = sum exp(t - m) and the running
+ * weighted sum acc = sum exp(t - m) kv over the positions of the request's
+ * unfinished block, t = score + ape[pos % 128].  `state` is a device fp32
+ * array of num_slots such slots (6 KiB each at hd 512).  The ordinary
+ * ratio-128 plans drive it, built with num_state_rows = 128 * num_slots
+ * (request slot idx owns virtual rows idx*128 .. idx*128+127); record fields
+ * keep their meaning, and a slot holds nothing until its first token.
+ * Call order per prefill chunk: kvc_plan_prefill (or _swa) ->
+ * kvc_compress_c128_online -> kvc_write_c128_online; per decode step:
+ * kvc_plan_decode (or _swa) -> kvc_decode_c128_online.
+ *
+ * kvc_compress_c128_online - for each valid C record k < counts[0]: pool
+ * window entries [buffer_len, 128) (input rows ragged_id - 127 + i, ape row
+ * i) and, when buffer_len > 0, the partial in slot read_page_0; out[k] =
+ * acc / l (float32 [cap_c, hd]).  A record whose rows or slot are out of
+ * range is skipped and sets KVC_DERR_RECORD in counts[3].
+ */
+int kvc_compress_c128_online(kvc_dtype dtype, int head_dim, const float* state, int64_t num_slots,
+                             const void* input, int num_q, const void* ape, const kvc_plan_c* plan_c, int cap_c,
+                             int32_t* counts, float* out, void* stream);
+
+/*
+ * kvc_write_c128_online - fold each request's run of W records (consecutive
+ * records of one slot, write_loc / 128, with consecutive rows and positions)
+ * into its slot: positions write_loc % 128 .. on of the block, input rows
+ * from ragged_id, ape rows by position.  The run starts a fresh block when
+ * its first position is a multiple of 128, else it continues the slot.  Must
+ * run after the chunk's kvc_compress_c128_online.  A run whose rows or slot
+ * are out of range is skipped and sets KVC_DERR_RECORD in counts[3].
+ */
+int kvc_write_c128_online(kvc_dtype dtype, int head_dim, float* state, int64_t num_slots, const void* input,
+                          int num_q, const void* ape, const kvc_plan_w* plan_w, int cap_w, int32_t* counts,
+                          void* stream);
+
+/*
+ * kvc_decode_c128_online - for each request b: fold input row b at position
+ * seq_len - 1 into slot read_page_0 (a fresh block when that position is a
+ * multiple of 128); out[b] = acc / l when seq_len % 128 == 0, else zeros
+ * (float32 [batch, hd]).  An invalid record gives a zero row; a slot out of
+ * range gives a zero row and KVC_DERR_RECORD in *status (may be NULL).
+ */
+int kvc_decode_c128_online(kvc_dtype dtype, int head_dim, float* state, int64_t num_slots, const void* input,
+                           const void* ape, const kvc_plan_d* plan_d, int batch, int32_t* status, float* out,
+                           void* stream);
+
 /* kvc_strerror - static text for a host return code or a device error bit. */
 const char* kvc_strerror(int code);
 

@@ -293,6 +293,50 @@ KVC_EXPORT int kvc_decode_c4_norm_rope_store(kvc_dtype dtype, int head_dim, void
                        args, stream);
 }
 
+namespace {
+
+bool online_common_ok(kvc_dtype dtype, int head_dim, const float* state, int64_t num_slots, const void* input,
+                      const void* ape) {
+  if (!dtype_ok(dtype) || !hd_ok(head_dim) || num_slots < 0 || num_slots > INT32_MAX / 128) return false;
+  if (!aligned16(input) || !aligned16(ape)) return false;
+  return num_slots == 0 || aligned16(state);
+}
+
+}  // namespace
+
+KVC_EXPORT int kvc_compress_c128_online(kvc_dtype dtype, int head_dim, const float* state, int64_t num_slots,
+                                        const void* input, int num_q, const void* ape, const kvc_plan_c* plan_c,
+                                        int cap_c, int32_t* counts, float* out, void* stream) {
+  if (!online_common_ok(dtype, head_dim, state, num_slots, input, ape)) return KVC_EINVAL;
+  if (num_q < 0 || num_q >= KVC_MAX_TOKENS || cap_c < 0 || !aligned4(counts)) return KVC_EINVAL;
+  if (cap_c == 0) return KVC_OK;
+  if (!aligned16(plan_c) || !aligned16(out)) return KVC_EINVAL;
+  kvc::OnlineArgs a{const_cast<float*>(state), input, ape, plan_c, nullptr, nullptr, counts, nullptr, out,
+                    num_slots, num_q, cap_c};
+  return status_of(kvc::launch_compress_online(dtype, head_dim, a, as_stream(stream)));
+}
+
+KVC_EXPORT int kvc_write_c128_online(kvc_dtype dtype, int head_dim, float* state, int64_t num_slots,
+                                     const void* input, int num_q, const void* ape, const kvc_plan_w* plan_w,
+                                     int cap_w, int32_t* counts, void* stream) {
+  if (!online_common_ok(dtype, head_dim, state, num_slots, input, ape)) return KVC_EINVAL;
+  if (num_q < 0 || num_q >= KVC_MAX_TOKENS || cap_w < 0 || !aligned4(counts)) return KVC_EINVAL;
+  if (cap_w == 0) return KVC_OK;
+  if (plan_w == nullptr || (reinterpret_cast<uintptr_t>(plan_w) & 7u)) return KVC_EINVAL;
+  kvc::OnlineArgs a{state, input, ape, nullptr, plan_w, nullptr, counts, nullptr, nullptr, num_slots, num_q, cap_w};
+  return status_of(kvc::launch_write_online(dtype, head_dim, a, as_stream(stream)));
+}
+
+KVC_EXPORT int kvc_decode_c128_online(kvc_dtype dtype, int head_dim, float* state, int64_t num_slots,
+                                      const void* input, const void* ape, const kvc_plan_d* plan_d, int batch,
+                                      int32_t* status, float* out, void* stream) {
+  if (!online_common_ok(dtype, head_dim, state, num_slots, input, ape)) return KVC_EINVAL;
+  if (batch < 1 || batch > KVC_MAX_DECODE_BATCH || !aligned16(plan_d) || !aligned16(out)) return KVC_EINVAL;
+  if (status != nullptr && !aligned4(status)) return KVC_EINVAL;
+  kvc::OnlineArgs a{state, input, ape, nullptr, nullptr, plan_d, nullptr, status, out, num_slots, 0, batch};
+  return status_of(kvc::launch_decode_online(dtype, head_dim, a, as_stream(stream)));
+}
+
 KVC_EXPORT const char* kvc_strerror(int code) {
   switch (code) {
     case KVC_OK:

@@ -95,6 +95,22 @@ struct NormRopeStoreArgs {
   kvc_store_args st;
 };
 
+// the ratio-128 online state: slots [num_slots, 3, hd] fp32 (m, l, acc)
+struct OnlineArgs {
+  float* state;
+  const void* input;
+  const void* ape;
+  const kvc_plan_c* plan_c;  // compress
+  const kvc_plan_w* plan_w;  // write
+  const kvc_plan_d* plan_d;  // decode
+  int32_t* counts;           // compress (counts[0], [3]) and write (counts[1], [3])
+  int32_t* status;           // decode (may be null)
+  float* out;                // compress and decode
+  int64_t num_slots;
+  int num_q;
+  int cap;  // cap_c, cap_w or batch
+};
+
 hipError_t launch_plan_prefill(int compress_ratio, bool swa, const PlanPrefillArgs& a, hipStream_t stream);
 hipError_t launch_plan_decode(int compress_ratio, bool swa, const PlanDecodeArgs& a, hipStream_t stream);
 hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
@@ -105,6 +121,9 @@ hipError_t launch_compress_c128_store(kvc_dtype dtype, int head_dim, const Compr
 hipError_t launch_norm_rope_store(int head_dim, bool decode, const NormRopeStoreArgs& a, hipStream_t stream);
 hipError_t launch_decode_c4(kvc_dtype dtype, int head_dim, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_c4_store(kvc_dtype dtype, int head_dim, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_compress_online(kvc_dtype dtype, int head_dim, const OnlineArgs& a, hipStream_t stream);
+hipError_t launch_write_online(kvc_dtype dtype, int head_dim, const OnlineArgs& a, hipStream_t stream);
+hipError_t launch_decode_online(kvc_dtype dtype, int head_dim, const OnlineArgs& a, hipStream_t stream);
 hipError_t launch_decode_c128(kvc_dtype dtype, int head_dim, const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace kvc

@@ -176,6 +176,104 @@ struct C128Pool {
     __syncthreads();
   }
 
+  // The online-state form: entry e (0..127) is input row row0 + e with ape row
+  // ape0 + e, and only entries lo <= e < hi take part (0 <= lo < hi <= 128).
+  // The others are loaded from row row0 + lo (always in range, so the load
+  // count stays fixed) and weighted 0.  A chunk whose entries are all out of
+  // range leaves its stream's partial untouched.
+  __device__ __forceinline__ static void accumulate_range(const typename Elem<T>::storage* __restrict__ input,
+                                                          const typename Elem<T>::storage* __restrict__ ape,
+                                                          int64_t row0, int ape0, int lo, int hi, int cs, float* lds) {
+    constexpr int64_t R = 2 * HD;
+    const int sid = threadIdx.x / kLanes;
+    const int cl = (threadIdx.x % kLanes) * V;
+    const int c = cs * HDW + cl;
+    float m[V], l[V], acc[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      m[v] = -INFINITY;
+      l[v] = 0.f;
+      acc[v] = 0.f;
+    }
+    for (int k0 = 0; k0 < PER; k0 += U) {
+      u32x4 kv_raw[U], sc_raw[U], ap_raw[U];
+      bool in[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = sid + S * (k0 + u);
+        in[u] = e >= lo && e < hi;
+        const int es = in[u] ? e : lo;
+        const typename Elem<T>::storage* row = input + (row0 + es) * R;
+        kv_raw[u] = load16_stream(row + c);
+        sc_raw[u] = load16_stream(row + HD + c);
+        ap_raw[u] = load16(ape + (int64_t)(ape0 + es) * HD + c);
+      }
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        float t[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float sc[V], ap[V];
+          widen16<T>(sc_raw[u], sc);
+          widen16<T>(ap_raw[u], ap);
+          t[u] = in[u] ? sc[v] + ap[v] : -INFINITY;
+        }
+        float cm = t[0];
+#pragma unroll
+        for (int u = 1; u < U; ++u) cm = fmaxf(cm, t[u]);
+        const float nm = fmaxf(m[v], cm);
+        const float sh = nm == -INFINITY ? 0.f : nm;  // nothing in range yet: keep the zeros
+        const float scale = exp2_hw((m[v] - sh) * kLog2e);
+        float lv = l[v] * scale, av = acc[v] * scale;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float kv[V];
+          widen16<T>(kv_raw[u], kv);
+          const float w = exp2_hw((t[u] - sh) * kLog2e);
+          lv += w;
+          av = fmaf(w, in[u] ? kv[v] : 0.f, av);
+        }
+        m[v] = nm;
+        l[v] = lv;
+        acc[v] = av;
+      }
+    }
+    float* lm = lds;
+    float* ll = lds + S * HDW;
+    float* la = lds + 2 * S * HDW;
+    store_floats<V>(lm + sid * HDW + cl, m);
+    store_floats<V>(ll + sid * HDW + cl, l);
+    store_floats<V>(la + sid * HDW + cl, acc);
+    __syncthreads();
+  }
+
+  // The merged (max, sum, weighted sum) of channel d of the slice, with an
+  // extra partial (m0, l0, a0) folded in when `extra` (an online slot).
+  __device__ __forceinline__ static void merged_partial(const float* lds, int d, bool extra, float m0, float l0,
+                                                        float a0, float* M_out, float* L_out, float* A_out) {
+    const float* lm = lds;
+    const float* ll = lds + S * HDW;
+    const float* la = lds + 2 * S * HDW;
+    float M = extra ? m0 : -INFINITY;
+#pragma unroll
+    for (int s = 0; s < S; ++s) M = fmaxf(M, lm[s * HDW + d]);
+    float Lsum = 0.f, Asum = 0.f;
+    if (extra) {
+      const float f = exp2_hw((m0 - M) * kLog2e);
+      Lsum = l0 * f;
+      Asum = a0 * f;
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const float f = exp2_hw((lm[s * HDW + d] - M) * kLog2e);  // 0 for a stream with nothing in range
+      Lsum = fmaf(ll[s * HDW + d], f, Lsum);
+      Asum = fmaf(la[s * HDW + d], f, Asum);
+    }
+    *M_out = M;
+    *L_out = Lsum;
+    *A_out = Asum;
+  }
+
   // The pooled value of channel d of the slice, merged from the partials.
   __device__ __forceinline__ static float merged(const float* lds, int d) {
     const float* lm = lds;

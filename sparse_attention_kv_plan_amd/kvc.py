@@ -64,6 +64,9 @@ def load(build_if_missing: bool = False):
         "kvc_compress_c4_norm_rope_store": [I, I, P, L, P, I, P, P, I, P, P, P],
         "kvc_compress_c128_norm_rope_store": [I, I, P, L, P, I, P, P, I, P, P, P],
         "kvc_decode_c4_norm_rope_store": [I, I, P, L, P, P, P, I, P, P, P],
+        "kvc_compress_c128_online": [I, I, P, L, P, I, P, P, I, P, P, P],
+        "kvc_write_c128_online": [I, I, P, L, P, I, P, P, I, P, P],
+        "kvc_decode_c128_online": [I, I, P, L, P, P, P, I, P, P, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -342,6 +345,56 @@ def decode_c4_norm_rope_store(head_dim, state, inp, ape, plan_d, norm_weight, ep
                                               _p(plan_d), plan_d.shape[0], _p(status), ctypes.byref(st),
                                               _stream(stream))
     _check(rc, "kvc_decode_c4_norm_rope_store")
+
+
+# --------------------------------------------------------------------------
+# online ratio-128 state: slots float32 [num_slots, 3, hd] (m, l, acc)
+# --------------------------------------------------------------------------
+
+def _online_state(state, head_dim):
+    if state.dtype != torch.float32 or state.dim() != 3 or tuple(state.shape[1:]) != (3, head_dim):
+        raise KvcError("online state must be float32 [slots, 3, %d]" % head_dim)
+
+
+def compress_c128_online(head_dim, state, inp, ape, plan_c, counts, out, stream=None):
+    _dev(state, inp, ape, plan_c, counts, out)
+    _online_state(state, head_dim)
+    _shape(inp, 0, 2 * head_dim, "input")
+    _shape(ape, WINDOW[128], head_dim, "ape")
+    _shape(plan_c, 0, C_BYTES, "plan_c")
+    _shape(out, plan_c.shape[0], head_dim, "out")
+    if out.dtype != torch.float32 or ape.element_size() != inp.element_size():
+        raise KvcError("out must be float32 and ape share the input dtype")
+    rc = load().kvc_compress_c128_online(_dtype(inp), head_dim, _p(state), state.shape[0], _p(inp), inp.shape[0],
+                                         _p(ape), _p(plan_c), plan_c.shape[0], _p(counts), _p(out), _stream(stream))
+    _check(rc, "kvc_compress_c128_online")
+
+
+def write_c128_online(head_dim, state, inp, ape, plan_w, counts, stream=None):
+    _dev(state, inp, ape, plan_w, counts)
+    _online_state(state, head_dim)
+    _shape(inp, 0, 2 * head_dim, "input")
+    _shape(ape, WINDOW[128], head_dim, "ape")
+    _shape(plan_w, 0, W_BYTES, "plan_w")
+    if ape.element_size() != inp.element_size():
+        raise KvcError("ape must share the input dtype")
+    rc = load().kvc_write_c128_online(_dtype(inp), head_dim, _p(state), state.shape[0], _p(inp), inp.shape[0],
+                                      _p(ape), _p(plan_w), plan_w.shape[0], _p(counts), _stream(stream))
+    _check(rc, "kvc_write_c128_online")
+
+
+def decode_c128_online(head_dim, state, inp, ape, plan_d, out, status=None, stream=None):
+    _dev(state, inp, ape, plan_d, out, status)
+    _online_state(state, head_dim)
+    _shape(plan_d, 1, D_BYTES, "plan_d")
+    _shape(inp, plan_d.shape[0], 2 * head_dim, "input")
+    _shape(ape, WINDOW[128], head_dim, "ape")
+    _shape(out, plan_d.shape[0], head_dim, "out")
+    if out.dtype != torch.float32 or ape.element_size() != inp.element_size():
+        raise KvcError("out must be float32 and ape share the input dtype")
+    rc = load().kvc_decode_c128_online(_dtype(inp), head_dim, _p(state), state.shape[0], _p(inp), _p(ape),
+                                       _p(plan_d), plan_d.shape[0], _p(status), _p(out), _stream(stream))
+    _check(rc, "kvc_decode_c128_online")
 
 
 def decode_c4(head_dim, state, inp, ape, plan_d, out, status=None, stream=None):

@@ -92,3 +92,27 @@ class GpuBackend:
         status = torch.zeros(1, dtype=torch.int32, device=d)
         kvc.decode(cr, hd, st, to_dev(inp), to_dev(ape), to_dev(pd), out, status)
         return out.cpu().numpy().astype(np.float64), to_host(st, state), int(status.item())
+
+    # online ratio-128 state: slots float32 [slots, 3, hd] on the device, numpy on the host
+    def compress_online(self, hd, state, inp, ape, pc, num_c):
+        d = self.device
+        out = torch.full((max(pc.shape[0], 1), hd), float("nan"), dtype=torch.float32, device=d)
+        counts = torch.tensor([num_c, 0, 0, 0], dtype=torch.int32, device=d)
+        st = to_dev(np.asarray(state, np.float32))
+        kvc.compress_c128_online(hd, st, to_dev(inp), to_dev(ape), to_dev(pc), counts, out[: pc.shape[0]])
+        return out[: pc.shape[0]].cpu().numpy().astype(np.float64), int(counts[3].item())
+
+    def write_online(self, hd, state, inp, ape, pw, num_w):
+        d = self.device
+        counts = torch.tensor([0, num_w, 0, 0], dtype=torch.int32, device=d)
+        st = to_dev(np.asarray(state, np.float32))
+        kvc.write_c128_online(hd, st, to_dev(inp), to_dev(ape), to_dev(pw), counts)
+        return st.cpu().numpy(), int(counts[3].item())
+
+    def decode_online(self, hd, state, inp, ape, pd):
+        d = self.device
+        out = torch.full((pd.shape[0], hd), float("nan"), dtype=torch.float32, device=d)
+        status = torch.zeros(1, dtype=torch.int32, device=d)
+        st = to_dev(np.asarray(state, np.float32))
+        kvc.decode_c128_online(hd, st, to_dev(inp), to_dev(ape), to_dev(pd), out, status)
+        return out.cpu().numpy().astype(np.float64), st.cpu().numpy(), int(status.item())

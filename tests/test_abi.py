@@ -22,7 +22,8 @@ def test_header_declares_the_boundary():
         "kvc_plan_prefill", "kvc_plan_decode", "kvc_write", "kvc_compress_c4", "kvc_compress_c128",
         "kvc_decode_c4", "kvc_decode_c128", "kvc_strerror", "kvc_plan_prefill_swa", "kvc_plan_decode_swa",
         "kvc_norm_rope_store_prefill", "kvc_norm_rope_store_decode", "kvc_compress_c4_norm_rope_store",
-        "kvc_compress_c128_norm_rope_store", "kvc_decode_c4_norm_rope_store"])
+        "kvc_compress_c128_norm_rope_store", "kvc_decode_c4_norm_rope_store", "kvc_compress_c128_online",
+        "kvc_write_c128_online", "kvc_decode_c128_online"])
 
 
 def test_store_args_layout_matches_the_header(tmp_path):
@@ -113,6 +114,14 @@ def test_host_argument_checks_reject_without_enqueueing(lib):
     assert lib.kvc_decode_c4_norm_rope_store(1, 128, p, 8, p, p, p, 1, None, None, None) == E
     assert lib.kvc_decode_c4_norm_rope_store(1, 128, p, 8, p, p, p, 1, None, st(rope_dim=20), None) == E
     assert lib.kvc_decode_c4_norm_rope_store(1, 128, p, 8, p, p, p, 0, None, st(), None) == E
+    # online ratio-128 state: head_dim, slot count, alignment, batch
+    assert lib.kvc_compress_c128_online(1, 96, p, 2, p, 1, p, p, 1, p, p, None) == E
+    assert lib.kvc_compress_c128_online(1, 128, p, -1, p, 1, p, p, 1, p, p, None) == E
+    assert lib.kvc_compress_c128_online(1, 128, misaligned, 2, p, 1, p, p, 1, p, p, None) == E
+    assert lib.kvc_write_c128_online(1, 128, p, 2, p, 1, p, misaligned, 1, p, None) == E
+    assert lib.kvc_decode_c128_online(1, 128, p, 2, p, p, p, 0, None, p, None) == E
+    assert lib.kvc_compress_c128_online(1, 128, p, 2, p, 1, p, p, 0, p, p, None) == kvc.KVC_OK
+    assert lib.kvc_write_c128_online(1, 128, p, 2, p, 1, p, p, 0, p, None) == kvc.KVC_OK
     # empty work is a no-op that needs no device
     assert lib.kvc_compress_c4(1, 128, p, 8, p, 1, p, p, 0, p, p, None) == kvc.KVC_OK
     assert lib.kvc_write(128, 1, 512, p, 8, p, 1, p, 0, p, None) == kvc.KVC_OK
