@@ -64,11 +64,14 @@ def _load():
         lib.oracle_store_prefill.argtypes = [I, I, I, P, P, I, P, D, P, L, P, L, P, L]
         lib.oracle_store_decode.argtypes = [I, I, I, P, P, I, P, D, P, L, P, L, P, L]
         lib.oracle_compress_online.argtypes = [I, I, P, L, P, I, P, P, I, P]
+        lib.oracle_plan_prefill_page4.argtypes = [I, I, P, P, P, P, L, P, I, P, I, P, P]
+        lib.oracle_plan_decode_page4.argtypes = [I, P, P, P, L, P, P]
         lib.oracle_write_online.argtypes = [I, I, P, L, P, I, P, P, I]
         lib.oracle_decode_online.argtypes = [I, I, P, L, P, P, P, I, P]
         for f in ("oracle_plan_prefill", "oracle_plan_decode", "oracle_compress", "oracle_write",
                   "oracle_decode", "oracle_plan_prefill_swa", "oracle_plan_decode_swa", "oracle_store_prefill",
-                  "oracle_store_decode", "oracle_compress_online", "oracle_write_online", "oracle_decode_online"):
+                  "oracle_store_decode", "oracle_compress_online", "oracle_write_online", "oracle_decode_online",
+                  "oracle_plan_prefill_page4", "oracle_plan_decode_page4"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -274,6 +277,38 @@ def decode_online(hd, state, inp, ape, plan_d):
     err = _load().oracle_decode_online(bf, hd, _ptr(st), st.shape[0], _ptr(inp), _ptr(ape), _ptr(plan_d), B,
                                        _ptr(out))
     return out, st, err
+
+
+def plan_prefill_page4(seq_lens, extend_lens, page_index, bundle, num_state_rows, num_q, cap_c, cap_w):
+    """Ratio-4 prefill plan over caller-allocated 4-row pages.  bundle: int32 [B, 4] =
+    (load_first_page, load_second_page, write_first_page, last_position).
+    Returns (plan_c, plan_w, counts, status)."""
+    s, e, idx = _i32(seq_lens), _i32(extend_lens), _i32(page_index)
+    bnd = np.ascontiguousarray(np.asarray(bundle, np.int32).reshape(-1, 4))
+    B = s.size
+    pc = np.zeros((cap_c, C_BYTES), np.uint8)
+    pw = np.zeros((cap_w, W_BYTES), np.uint8)
+    counts = np.zeros(4, np.int32)
+    status = np.zeros(1, np.int32)
+    rc = _load().oracle_plan_prefill_page4(B, int(num_q), _ptr(s), _ptr(e), _ptr(idx), _ptr(bnd),
+                                           int(num_state_rows), _ptr(pc), int(cap_c), _ptr(pw), int(cap_w),
+                                           _ptr(counts), _ptr(status))
+    if rc < 0:
+        raise ValueError("bad host arguments")
+    return pc, pw, counts, int(status[0])
+
+
+def plan_decode_page4(seq_lens, page_index, prev_page, num_state_rows):
+    """Ratio-4 decode plan over caller-allocated pages: page_index[b] takes the new token,
+    prev_page[b] holds the window's overlap block.  Returns (plan_d, status)."""
+    s, idx, prev = _i32(seq_lens), _i32(page_index), _i32(prev_page)
+    pd = np.zeros((s.size, D_BYTES), np.uint8)
+    status = np.zeros(1, np.int32)
+    rc = _load().oracle_plan_decode_page4(s.size, _ptr(s), _ptr(idx), _ptr(prev), int(num_state_rows), _ptr(pd),
+                                          _ptr(status))
+    if rc < 0:
+        raise ValueError("bad host arguments")
+    return pd, int(status[0])
 
 
 def capacities_swa(cr, B, num_q, swa_page_size):

@@ -832,3 +832,138 @@ int oracle_decode_online(int is_bf16, int hd, double* state, int64_t num_slots, 
   }
   return err;
 }
+
+/* ------------------------------------------------------------------------ */
+/* ratio 4 with caller-allocated 4-row pages (Page4Align)                    */
+/* ------------------------------------------------------------------------ */
+/*
+ * c4.cuh, PageMode::Page4Align with C4IndexBundle (flash_c4_prefill) and the
+ * previous page of flash_c4_decode: instead of a ring of two 4-row pages per
+ * request, the caller hands over the pages.  Prefill, per request b: its
+ * page index[b] (the page of positions >= last_position) and a bundle
+ * {load_first_page, load_second_page, write_first_page, last_position}.
+ *   - the window entries before the chunk (buffer_len of them) come from
+ *     load_second_page alone when buffer_len <= 4 (they all lie in the block
+ *     before the closing one), else entries 0..3 from load_first_page and
+ *     4.. from load_second_page: read_page_0 / read_page_1 of the record;
+ *     a record that reads nothing from the state keeps pages -1, and only
+ *     pages that are read are checked (the first block's entries 0..3 are
+ *     masked, so a request starting at position 0 needs no earlier page);
+ *   - the written positions are those of the ratio-4 rule (the next window's
+ *     overlap block and the current block); position p goes to row
+ *     (p < last_position ? write_first_page : index[b]) * 4 + p % 4.
+ * Decode, per request: page index[b] takes the new token at slot
+ * (seq_len - 1) % 4; the window's overlap block is page prev[b].
+ * A page outside [0, num_state_rows / 4) that a record needs makes that
+ * record invalid and sets ERR_INDEX in *status.
+ */
+static int page4_ok(int64_t page, int64_t num_state_rows) { return page >= 0 && page < num_state_rows / 4; }
+
+int oracle_plan_prefill_page4(int B, int num_q, const int32_t* seq_lens, const int32_t* extend_lens,
+                              const int32_t* page_index, const int32_t* bundle, int64_t num_state_rows,
+                              uint8_t* plan_c, int cap_c, uint8_t* plan_w, int cap_w, int32_t* counts,
+                              int32_t* status) {
+  if (bad_host_args(4, B)) return -1;
+  int err = 0, st = 0;
+  int64_t total = 0;
+  for (int b = 0; b < B; ++b) {
+    if (extend_lens[b] < 1 || extend_lens[b] > seq_lens[b]) err |= ERR_EXTEND;
+    if (!page4_ok(page_index[b], num_state_rows)) err |= ERR_INDEX;
+    total += extend_lens[b];
+  }
+  if (!(err & ERR_EXTEND) && total != num_q) err |= ERR_NUMQ;
+  int nc = 0, nw = 0;
+  if (!err) {
+    int64_t ragged_base = 0;
+    for (int b = 0; b < B && !err; ++b) {
+      const int64_t s = seq_lens[b], e = extend_lens[b], p0 = s - e;
+      const int64_t lfp = bundle[4 * b], lsp = bundle[4 * b + 1], wfp = bundle[4 * b + 2], last = bundle[4 * b + 3];
+      const int64_t first_w = (s / 4) * 4 - 4;
+      for (int64_t j = 0; j < e; ++j) {
+        const int64_t pos = p0 + j, ragged = ragged_base + j;
+        if ((pos + 1) % 4 == 0) {
+          if (nc >= cap_c) {
+            err |= ERR_CAPACITY;
+            break;
+          }
+          uint8_t* r = plan_c + (size_t)nc * 16;
+          const int64_t in_chunk = (j + 1 < 8) ? j + 1 : 8;
+          const int64_t blen = 8 - in_chunk;
+          int64_t rp0 = -1, rp1 = -1;
+          if (blen > 0) {
+            rp0 = blen <= 4 ? lsp : lfp;
+            rp1 = lsp;
+          }
+          /* pages the consumer reads: entries 0..3 unless masked (seq_len 4), entries 4.. when blen > 4 */
+          const int needs0 = blen > 0 && pos + 1 != 4, needs1 = blen > 4;
+          if ((needs0 && !page4_ok(rp0, num_state_rows)) || (needs1 && !page4_ok(rp1, num_state_rows))) {
+            memset(r, 0xFF, 16);
+            st |= ERR_INDEX;
+          } else {
+            put_u32(r, (uint32_t)(pos + 1));
+            put_u32(r + 4, (uint32_t)ragged | ((uint32_t)blen << 24));
+            put_u32(r + 8, as_u32((int32_t)rp0));
+            put_u32(r + 12, as_u32((int32_t)rp1));
+          }
+          ++nc;
+        }
+        if (pos >= first_w) {
+          if (nw >= cap_w) {
+            err |= ERR_CAPACITY;
+            break;
+          }
+          uint8_t* r = plan_w + (size_t)nw * 8;
+          const int64_t page = pos < last ? wfp : page_index[b];
+          if (!page4_ok(page, num_state_rows)) {
+            memset(r, 0xFF, 8);
+            st |= ERR_INDEX;
+          } else {
+            put_u32(r, (uint32_t)ragged);
+            put_u32(r + 4, as_u32((int32_t)(page * 4 + pos % 4)));
+          }
+          ++nw;
+        }
+      }
+      ragged_base += e;
+    }
+  }
+  if (err) {
+    nc = nw = 0;
+    st = 0;
+  }
+  memset(plan_c + (size_t)nc * 16, 0xFF, (size_t)(cap_c - nc) * 16);
+  memset(plan_w + (size_t)nw * 8, 0xFF, (size_t)(cap_w - nw) * 8);
+  counts[0] = nc;
+  counts[1] = nw;
+  counts[2] = err;
+  counts[3] = 0;
+  if (status) *status |= st;
+  return err;
+}
+
+int oracle_plan_decode_page4(int B, const int32_t* seq_lens, const int32_t* page_index, const int32_t* prev_page,
+                             int64_t num_state_rows, uint8_t* plan_d, int32_t* status) {
+  if (B < 1 || B > 65536) return -1;
+  int err = 0;
+  for (int b = 0; b < B; ++b) {
+    uint8_t* r = plan_d + (size_t)b * 16;
+    const int64_t s = seq_lens[b];
+    memset(r, 0xFF, 16);
+    if (s <= 0) {
+      err |= ERR_EXTEND;
+      continue;
+    }
+    const int64_t page = page_index[b], prev = prev_page[b];
+    const int needs_prev = (s % 4 == 0) && s > 4; /* the overlap block exists and is read */
+    if (!page4_ok(page, num_state_rows) || (needs_prev && !page4_ok(prev, num_state_rows))) {
+      err |= ERR_INDEX;
+      continue;
+    }
+    put_u32(r, (uint32_t)s);
+    put_u32(r + 4, as_u32((int32_t)(page * 4 + (s - 1) % 4)));
+    put_u32(r + 8, as_u32((int32_t)prev));
+    put_u32(r + 12, as_u32((int32_t)page));
+  }
+  if (status) *status = err;
+  return err;
+}

@@ -95,6 +95,18 @@ MUTANTS = [
      "1"),
     ("online compress window off by one", "        const int64_t row = ragged - 127 + i;\n        const double t",
      "        const int64_t row = ragged - 126 + i;\n        const double t"),
+    ("page4 overlap entries always from the first load page", "rp0 = blen <= 4 ? lsp : lfp;",
+     "rp0 = lfp;"),
+    ("page4 overlap threshold off by one", "rp0 = blen <= 4 ? lsp : lfp;",
+     "rp0 = blen < 4 ? lsp : lfp;"),
+    ("page4 write split at the wrong position", "const int64_t page = pos < last ? wfp : page_index[b];",
+     "const int64_t page = pos <= last ? wfp : page_index[b];"),
+    ("page4 writes only the current block", "const int64_t first_w = (s / 4) * 4 - 4;",
+     "const int64_t first_w = (s / 4) * 4;"),
+    ("page4 decode slot one late", "put_u32(r + 4, as_u32((int32_t)(page * 4 + (s - 1) % 4)));",
+     "put_u32(r + 4, as_u32((int32_t)(page * 4 + s % 4)));"),
+    ("page4 decode overlap from the page of the new token", "put_u32(r + 8, as_u32((int32_t)prev));",
+     "put_u32(r + 8, as_u32((int32_t)page));"),
 ]
 
 
@@ -123,6 +135,7 @@ def test_pins_catch_mutant(tmp_path, mutant):
                         os.path.join(ROOT, "tests", "test_oracle_pins.py"),
                         os.path.join(ROOT, "tests", "test_oracle_swa_pins.py"),
                         os.path.join(ROOT, "tests", "test_oracle_store_pins.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_online_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_online_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_page4_pins.py")],
                        cwd=ROOT, env=env, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, timeout=600)
     assert r.returncode != 0, "pins did not catch mutant '%s':\n%s" % (name, r.stdout.decode()[-2000:])

@@ -14,7 +14,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "kvc_oracle.c")
-PINS = ["test_oracle_pins.py", "test_oracle_swa_pins.py", "test_oracle_store_pins.py", "test_oracle_online_pins.py"]
+PINS = ["test_oracle_pins.py", "test_oracle_swa_pins.py", "test_oracle_store_pins.py", "test_oracle_online_pins.py",
+        "test_oracle_page4_pins.py"]
 
 
 def _runtime(name):
