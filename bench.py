@@ -311,9 +311,48 @@ def main():
             kvc.plan_decode_swa(self.w.cr, self.s, self.rid, self.r2t, self.f2s, 128, 8 if self.w.cr == 4 else 128,
                                 self.rows, self.pd, self.status)
 
+    # ratio 4 over caller-allocated 4-row pages (Page4Align): a page for every block of every request
+    class Page4:
+        def __init__(self, P, D, seed):
+            rng = np.random.default_rng(seed)
+            w, d = P.w, D.w
+            p0 = (w.seq_lens - w.extend_lens).astype(np.int64)
+            last = (w.seq_lens // 4) * 4
+            n_pages = int((w.seq_lens // 4 + 4).sum() + (d.seq_lens // 4 + 4).sum())
+            perm = rng.permutation(n_pages).astype(np.int32)
+            base = np.concatenate([[0], np.cumsum(w.seq_lens // 4 + 4)])[:-1]  # request b's pages: base[b] + block
+
+            def page(b, blk):
+                return np.where(blk >= 0, perm[base[b] + np.maximum(blk, 0)], -1)
+
+            b_ = np.arange(w.B)
+            bundle = np.stack([page(b_, (p0 - 1) // 4 - 1) * (p0 > 4) - (p0 <= 4),
+                               page(b_, (p0 - 1) // 4) * (p0 > 0) - (p0 <= 0),
+                               page(b_, last // 4 - 1), last], axis=1).astype(np.int32)
+            self.w, self.rows = w, n_pages * 4
+            self.s, self.e = to_dev(w.seq_lens), to_dev(w.extend_lens)
+            self.idx, self.bundle = to_dev(page(b_, last // 4).astype(np.int32)), to_dev(bundle)
+            self.pc, self.pw, self.counts = kvc.alloc_prefill_plan(4, w.B, w.num_q, dev)
+            self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+            # decode: the new token's page and the page before it, from the pages the prefill requests left
+            dpages = perm[n_pages - 2 * d.B:]
+            self.ds = to_dev(d.seq_lens)
+            self.didx, self.dprev = to_dev(dpages[: d.B].copy()), to_dev(dpages[d.B:].copy())
+            self.pd = torch.empty((d.B, kvc.D_BYTES), dtype=torch.uint8, device=dev)
+
+        def plan(self):
+            kvc.plan_prefill_page4(self.s, self.e, self.idx, self.bundle, self.rows, self.w.num_q, self.pc, self.pw,
+                                   self.counts, self.status)
+
+        def plan_decode(self):
+            kvc.plan_decode_page4(self.ds, self.didx, self.dprev, self.rows, self.pd, self.status)
+
+    PG4 = Page4(P4, D4, 2404)
+
     SP4, SP128, SD4 = SwaPrefill(p4, 2004), SwaPrefill(p128, 2128), SwaDecode(d4, 2003)
     swa_launches = [("plan_prefill_swa c4", SP4.plan), ("plan_prefill_swa c128", SP128.plan),
-                    ("plan_decode_swa c4", SD4.plan)]
+                    ("plan_decode_swa c4", SD4.plan), ("plan_prefill_page4", PG4.plan),
+                    ("plan_decode_page4", PG4.plan_decode)]
 
     # norm + rotary + bf16 store of the compressed rows (breakdown pass only): rotary on the last 64
     # channels, one cache row per ragged token (prefill) or request (decode)
@@ -472,6 +511,7 @@ def main():
         c = S.counts.cpu().tolist()
         assert c[2] == 0 and int(S.status.item()) == 0, ("SWA plan error", c)
     assert int(SD4.status.item()) == 0
+    assert int(PG4.counts[2].item()) == 0 and int(PG4.status.item()) == 0, "page-4 plan error"
 
     n_c4 = int(P4.counts[0].item())
     rows_seq = P4.plan_c[:n_c4].cpu().numpy().view("<u4").reshape(-1, 4)[:, 0].astype(np.int64)

@@ -222,6 +222,47 @@ int kvc_plan_decode_swa(int compress_ratio, int batch, const int32_t* seq_lens, 
                         kvc_plan_d* plan_d, int32_t* status, void* stream);
 
 /*
+ * Ratio 4 over caller-allocated 4-row pages (c4.cuh page, PageMode::Page4Align
+ * with C4IndexBundle in flash_c4_prefill, and the previous page of
+ * flash_c4_decode).  Instead of the per-request ring of two pages, the caller
+ * hands over the pages (4 state rows each; page P is rows 4P .. 4P+3); the
+ * records are ordinary C / W / D records for kvc_compress_c4, kvc_write and
+ * kvc_decode_c4.
+ *
+ * kvc_plan_prefill_page4 - as kvc_plan_prefill (ratio 4) with, per request
+ * b, page_index[b] (the page of the positions from last_position on) and
+ * bundle[b] (device int32 [batch, 4], 16-byte aligned) = {load_first_page,
+ * load_second_page, write_first_page, last_position}:
+ *  - a C record whose window reaches before the chunk (buffer_len > 0)
+ *    reads those entries from load_second_page when buffer_len <= 4, else
+ *    entries 0..3 from load_first_page and 4.. from load_second_page
+ *    (read_page_0 / read_page_1); other C records carry pages -1;
+ *  - the written positions are those of kvc_plan_prefill; position p goes to
+ *    row (p < last_position ? write_first_page : page_index[b]) * 4 + p % 4.
+ * A page_index outside [0, num_state_rows / 4) is a plan error
+ * (KVC_DERR_INDEX in counts[2], no records).  A bundle page outside that
+ * range which a record reads or writes makes that record invalid and ORs
+ * KVC_DERR_INDEX into *status (may be NULL; the caller clears it); pages that
+ * are not read (the first block's masked entries) are not checked.
+ */
+int kvc_plan_prefill_page4(int batch, int num_q, const int32_t* seq_lens, const int32_t* extend_lens,
+                           const int32_t* page_index, const int32_t* bundle, int64_t num_state_rows,
+                           kvc_plan_c* plan_c, int cap_c, kvc_plan_w* plan_w, int cap_w, int32_t* counts,
+                           int32_t* status, void* stream);
+
+/*
+ * kvc_plan_decode_page4 - one decode record per request: the new token
+ * (position seq_len - 1) goes to page_index[b] at slot (seq_len - 1) % 4
+ * (write_loc), read_page_1 = page_index[b], read_page_0 = prev_page[b] (the
+ * page of the block before; read only when seq_len % 4 == 0 and
+ * seq_len > 4).  A request with seq_len <= 0 or a needed page out of range
+ * gets an invalid record; *status (may be NULL) receives the error bits.
+ *  batch 1 .. KVC_MAX_DECODE_BATCH.
+ */
+int kvc_plan_decode_page4(int batch, const int32_t* seq_lens, const int32_t* page_index, const int32_t* prev_page,
+                          int64_t num_state_rows, kvc_plan_d* plan_d, int32_t* status, void* stream);
+
+/*
  * kvc_write - for each valid W record k < counts[1], copy input row
  * ragged_id (all 4*hd or 2*hd elements, bit for bit) into state row
  * write_loc (c4.cuh, c4_write; compressor_v2.py,

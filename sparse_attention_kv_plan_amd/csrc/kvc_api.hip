@@ -46,7 +46,7 @@ KVC_EXPORT int kvc_plan_prefill(int compress_ratio, int batch, int num_q, const 
   a.num_q = num_q;
   a.cap_c = cap_c;
   a.cap_w = cap_w;
-  return status_of(kvc::launch_plan_prefill(compress_ratio, false, a, as_stream(stream)));
+  return status_of(kvc::launch_plan_prefill(compress_ratio, kvc::kPlanRing, a, as_stream(stream)));
 }
 
 KVC_EXPORT int kvc_plan_decode(int compress_ratio, int batch, const int32_t* seq_lens, const int32_t* state_index,
@@ -62,7 +62,7 @@ KVC_EXPORT int kvc_plan_decode(int compress_ratio, int batch, const int32_t* seq
   a.plan_d = plan_d;
   a.status = status;
   a.batch = batch;
-  return status_of(kvc::launch_plan_decode(compress_ratio, false, a, as_stream(stream)));
+  return status_of(kvc::launch_plan_decode(compress_ratio, kvc::kPlanRing, a, as_stream(stream)));
 }
 
 namespace {
@@ -112,7 +112,7 @@ KVC_EXPORT int kvc_plan_prefill_swa(int compress_ratio, int batch, int num_q, co
   a.num_q = num_q;
   a.cap_c = cap_c;
   a.cap_w = cap_w;
-  return status_of(kvc::launch_plan_prefill(compress_ratio, true, a, as_stream(stream)));
+  return status_of(kvc::launch_plan_prefill(compress_ratio, kvc::kPlanSwa, a, as_stream(stream)));
 }
 
 KVC_EXPORT int kvc_plan_decode_swa(int compress_ratio, int batch, const int32_t* seq_lens,
@@ -134,7 +134,54 @@ KVC_EXPORT int kvc_plan_decode_swa(int compress_ratio, int batch, const int32_t*
   a.plan_d = plan_d;
   a.status = status;
   a.batch = batch;
-  return status_of(kvc::launch_plan_decode(compress_ratio, true, a, as_stream(stream)));
+  return status_of(kvc::launch_plan_decode(compress_ratio, kvc::kPlanSwa, a, as_stream(stream)));
+}
+
+KVC_EXPORT int kvc_plan_prefill_page4(int batch, int num_q, const int32_t* seq_lens, const int32_t* extend_lens,
+                                      const int32_t* page_index, const int32_t* bundle, int64_t num_state_rows,
+                                      kvc_plan_c* plan_c, int cap_c, kvc_plan_w* plan_w, int cap_w, int32_t* counts,
+                                      int32_t* status, void* stream) {
+  if (batch < 1 || batch > KVC_MAX_PREFILL_BATCH) return KVC_EINVAL;
+  if (num_q < batch || num_q >= KVC_MAX_TOKENS || cap_c < 0 || cap_w < 0 || !rows_ok(num_state_rows))
+    return KVC_EINVAL;
+  if (!aligned4(seq_lens) || !aligned4(extend_lens) || !aligned4(page_index) || !aligned16(bundle) ||
+      !aligned4(counts))
+    return KVC_EINVAL;
+  if ((cap_c > 0 && !aligned16(plan_c)) || (cap_w > 0 && (plan_w == nullptr || (reinterpret_cast<uintptr_t>(plan_w) & 7u))))
+    return KVC_EINVAL;
+  if (status != nullptr && !aligned4(status)) return KVC_EINVAL;
+  kvc::PlanPrefillArgs a{};
+  a.seq_lens = seq_lens;
+  a.extend_lens = extend_lens;
+  a.state_index = page_index;
+  a.num_state_rows = num_state_rows;
+  a.plan_c = plan_c;
+  a.plan_w = plan_w;
+  a.counts = counts;
+  a.status = status;
+  a.batch = batch;
+  a.num_q = num_q;
+  a.cap_c = cap_c;
+  a.cap_w = cap_w;
+  a.bundle = bundle;
+  return status_of(kvc::launch_plan_prefill(4, kvc::kPlanPage4, a, as_stream(stream)));
+}
+
+KVC_EXPORT int kvc_plan_decode_page4(int batch, const int32_t* seq_lens, const int32_t* page_index,
+                                     const int32_t* prev_page, int64_t num_state_rows, kvc_plan_d* plan_d,
+                                     int32_t* status, void* stream) {
+  if (batch < 1 || batch > KVC_MAX_DECODE_BATCH || !rows_ok(num_state_rows)) return KVC_EINVAL;
+  if (!aligned4(seq_lens) || !aligned4(page_index) || !aligned4(prev_page) || !aligned16(plan_d)) return KVC_EINVAL;
+  if (status != nullptr && !aligned4(status)) return KVC_EINVAL;
+  kvc::PlanDecodeArgs a{};
+  a.seq_lens = seq_lens;
+  a.state_index = page_index;
+  a.num_state_rows = num_state_rows;
+  a.plan_d = plan_d;
+  a.status = status;
+  a.batch = batch;
+  a.prev_page = prev_page;
+  return status_of(kvc::launch_plan_decode(4, kvc::kPlanPage4, a, as_stream(stream)));
 }
 
 KVC_EXPORT int kvc_write(int compress_ratio, kvc_dtype dtype, int head_dim, void* state, int64_t num_state_rows,

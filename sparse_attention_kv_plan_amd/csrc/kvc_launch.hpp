@@ -21,6 +21,10 @@ struct SwaTables {
   int ring_size;
 };
 
+// how plan records name state rows: the per-request ring or page, the SWA
+// pool's rings, or 4-row pages that the caller hands over (ratio 4)
+enum PlanMap { kPlanRing = 0, kPlanSwa = 1, kPlanPage4 = 2 };
+
 struct PlanPrefillArgs {
   const int32_t* seq_lens;
   const int32_t* extend_lens;
@@ -35,6 +39,7 @@ struct PlanPrefillArgs {
   int cap_c;
   int cap_w;
   SwaTables swa;
+  const int32_t* bundle;  // page-4 mode: [batch, 4] load_first, load_second, write_first page, last position
 };
 
 struct PlanDecodeArgs {
@@ -45,6 +50,7 @@ struct PlanDecodeArgs {
   int32_t* status;
   int batch;
   SwaTables swa;
+  const int32_t* prev_page;  // page-4 mode: [batch] page of the block before the new token's
 };
 
 struct WriteArgs {
@@ -111,8 +117,8 @@ struct OnlineArgs {
   int cap;  // cap_c, cap_w or batch
 };
 
-hipError_t launch_plan_prefill(int compress_ratio, bool swa, const PlanPrefillArgs& a, hipStream_t stream);
-hipError_t launch_plan_decode(int compress_ratio, bool swa, const PlanDecodeArgs& a, hipStream_t stream);
+hipError_t launch_plan_prefill(int compress_ratio, int map, const PlanPrefillArgs& a, hipStream_t stream);
+hipError_t launch_plan_decode(int compress_ratio, int map, const PlanDecodeArgs& a, hipStream_t stream);
 hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
 hipError_t launch_compress_c4(kvc_dtype dtype, int head_dim, const CompressArgs& a, hipStream_t stream);
 hipError_t launch_compress_c128(kvc_dtype dtype, int head_dim, const CompressArgs& a, hipStream_t stream);

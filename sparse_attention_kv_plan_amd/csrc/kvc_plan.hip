@@ -85,6 +85,11 @@ __device__ __forceinline__ int32_t tail_pos(int64_t lo, int64_t t, int sps) {
   return (int32_t)((n / 4) * sps + sps - 4 + n % 4);
 }
 
+// a 4-row page of the state buffer (page-4 mode)
+__device__ __forceinline__ bool page4_ok(int32_t page, int64_t num_state_rows) {
+  return page >= 0 && (int64_t)page < num_state_rows / 4;
+}
+
 struct RequestTable {
   int32_t s[KVC_MAX_PREFILL_BATCH];
   int32_t p0[KVC_MAX_PREFILL_BATCH];
@@ -104,7 +109,7 @@ __device__ __forceinline__ void store_invalid_w(kvc_plan_w* dst) {
 }
 
 // C record for the compressed row closing at position pos of batch entry b
-template <int CR, bool SWA>
+template <int CR, int MAP>
 __device__ __forceinline__ void emit_c(const PlanPrefillArgs& a, kvc_plan_c* dst, int b, int32_t pos, int32_t p0,
                                        int32_t idx, int32_t roff) {
   constexpr int32_t W = CR == 4 ? 8 : 128;
@@ -114,7 +119,7 @@ __device__ __forceinline__ void emit_c(const PlanPrefillArgs& a, kvc_plan_c* dst
   u32x4 v;
   v.x = (uint32_t)(pos + 1);
   v.y = (uint32_t)(roff + j) | (blen << 24);
-  if constexpr (SWA) {
+  if constexpr (MAP == kPlanSwa) {
     int64_t rp0 = -1, rp1 = b;  // nothing is read from the state: left untranslated
     if (blen > 0) {
       const int64_t r0 = swa_row<CR>(a.swa, idx, pos0, a.num_state_rows);
@@ -129,6 +134,24 @@ __device__ __forceinline__ void emit_c(const PlanPrefillArgs& a, kvc_plan_c* dst
     }
     v.z = (uint32_t)(int32_t)rp0;
     v.w = (uint32_t)(int32_t)rp1;
+  } else if constexpr (MAP == kPlanPage4) {
+    // the entries before the chunk lie on load_second_page alone when there are at most 4 of
+    // them, else entries 0..3 on load_first_page; only pages that are read are checked (the
+    // first block's entries 0..3 are masked)
+    int32_t rp0 = -1, rp1 = -1;
+    if (blen > 0) {
+      rp0 = blen <= 4 ? a.bundle[4 * b + 1] : a.bundle[4 * b];
+      rp1 = a.bundle[4 * b + 1];
+      const bool bad0 = pos + 1 != 4 && !page4_ok(rp0, a.num_state_rows);
+      const bool bad1 = blen > 4 && !page4_ok(rp1, a.num_state_rows);
+      if (bad0 || bad1) {
+        if (a.status) atomicOr(a.status, KVC_DERR_INDEX);
+        store_invalid_c(dst);
+        return;
+      }
+    }
+    v.z = (uint32_t)rp0;
+    v.w = (uint32_t)rp1;
   } else {
     v.z = (uint32_t)page_of<CR>(idx, pos0);
     v.w = (uint32_t)page_of<CR>(idx, pos);
@@ -136,12 +159,12 @@ __device__ __forceinline__ void emit_c(const PlanPrefillArgs& a, kvc_plan_c* dst
   store16(dst, v);
 }
 
-template <int CR, bool SWA>
-__device__ __forceinline__ void emit_w(const PlanPrefillArgs& a, kvc_plan_w* dst, int32_t pos, int32_t p0,
+template <int CR, int MAP>
+__device__ __forceinline__ void emit_w(const PlanPrefillArgs& a, kvc_plan_w* dst, int b, int32_t pos, int32_t p0,
                                        int32_t idx, int32_t roff) {
   uint2 v;
   v.x = (uint32_t)(roff + (pos - p0));
-  if constexpr (SWA) {
+  if constexpr (MAP == kPlanSwa) {
     const int64_t row = swa_row<CR>(a.swa, idx, pos, a.num_state_rows);
     if (row < 0) {
       if (a.status) atomicOr(a.status, KVC_DERR_INDEX);
@@ -149,6 +172,15 @@ __device__ __forceinline__ void emit_w(const PlanPrefillArgs& a, kvc_plan_w* dst
       return;
     }
     v.y = (uint32_t)row;
+  } else if constexpr (MAP == kPlanPage4) {
+    // positions before last_position go to write_first_page, the rest to the request's page
+    const int32_t page = pos < a.bundle[4 * b + 3] ? a.bundle[4 * b + 2] : idx;
+    if (!page4_ok(page, a.num_state_rows)) {
+      if (a.status) atomicOr(a.status, KVC_DERR_INDEX);
+      store_invalid_w(dst);
+      return;
+    }
+    v.y = (uint32_t)(page * 4 + (pos & 3));
   } else {
     v.y = (uint32_t)loc_of<CR>(idx, pos);
   }
@@ -181,20 +213,20 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v, int lane) {
 // First position written unconditionally: the block the next window overlaps
 // (ratio 4) or the current block (ratio 128); in SWA mode also capped at
 // s - mtp_pad, mtp_pad = min(ring_size - ratio, 4).
-template <int CR, bool SWA>
+template <int CR, int MAP>
 __device__ __forceinline__ int32_t first_write(int32_t s, const SwaTables& t) {
   int32_t fw = (s / CR) * CR - (CR == 4 ? 4 : 0);
-  if constexpr (SWA) {
+  if constexpr (MAP == kPlanSwa) {
     const int32_t pad = min(t.ring_size - CR, 4);
     fw = min(fw, s - pad);
   }
   return fw;
 }
 
-template <int CR, bool SWA>
+template <int CR, int MAP>
 __global__ __launch_bounds__(kPlanThreads) void plan_prefill_kernel(PlanPrefillArgs a) {
   constexpr int32_t W = CR == 4 ? 8 : 128;
-  constexpr bool kTails = SWA && CR == 4;  // ratio-4 SWA pages also keep their last 4 slots
+  constexpr bool kTails = MAP == kPlanSwa && CR == 4;  // ratio-4 SWA pages also keep their last 4 slots
   __shared__ RequestTable T;
   __shared__ uint32_t w_incl[kPlanWaves][3];
   __shared__ long long w_esum[kPlanWaves];
@@ -205,7 +237,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_prefill_kernel(PlanPrefillA
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1);
   const int wave = t / kWave;
-  const int64_t max_idx = SWA ? a.swa.num_reqs : a.num_state_rows / W;
+  const int64_t max_idx = MAP == kPlanSwa ? a.swa.num_reqs : a.num_state_rows / (MAP == kPlanPage4 ? 4 : W);
   const int sps = a.swa.swa_page_size;
 
   // ---- stage A: this thread's requests t*4 .. t*4+3 ----
@@ -222,11 +254,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_prefill_kernel(PlanPrefillA
       const bool ok = e >= 1 && e <= s;
       if (!ok) err |= KVC_DERR_EXTEND;
       if (idx < 0 || (int64_t)idx >= max_idx) err |= KVC_DERR_INDEX;
-      if (SWA && (int64_t)s > a.swa.stride) err |= KVC_DERR_INDEX;
+      if (MAP == kPlanSwa && (int64_t)s > a.swa.stride) err |= KVC_DERR_INDEX;
       esum += e;
       const int32_t p0 = ok ? s - e : 0;
       if (ok) {
-        const int32_t fw = first_write<CR, SWA>(s, a.swa);
+        const int32_t fw = first_write<CR, MAP>(s, a.swa);
         ve[k] = (uint32_t)e;
         vc[k] = (uint32_t)(s / CR - p0 / CR);
         uint32_t nw = (uint32_t)(s - (p0 > fw ? p0 : fw));
@@ -330,15 +362,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_prefill_kernel(PlanPrefillA
       const int32_t s = T.s[b], p0 = T.p0[b], idx = T.idx[b], roff = T.roff[b];
       const int32_t pos = p0 + j;
       if (((pos + 1) & (CR - 1)) == 0)
-        emit_c<CR, SWA>(a, a.plan_c + (T.coff[b] + pos / CR - p0 / CR), b, pos, p0, idx, roff);
-      const int32_t fw = first_write<CR, SWA>(s, a.swa);
+        emit_c<CR, MAP>(a, a.plan_c + (T.coff[b] + pos / CR - p0 / CR), b, pos, p0, idx, roff);
+      const int32_t fw = first_write<CR, MAP>(s, a.swa);
       bool write = pos >= fw;
       if constexpr (kTails) write = write || (pos % sps >= sps - 4);
       if (write) {
         // W records of this request before pos: page tails below fw, then the block from max(p0, fw)
         int64_t before = pos >= fw ? (int64_t)pos - (p0 > fw ? p0 : fw) : 0;
         if constexpr (kTails) before += tails_in(p0, min(pos, fw), sps);
-        emit_w<CR, SWA>(a, a.plan_w + (T.woff[b] + before), pos, p0, idx, roff);
+        emit_w<CR, MAP>(a, a.plan_w + (T.woff[b] + before), b, pos, p0, idx, roff);
       }
     }
   } else {
@@ -346,12 +378,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_prefill_kernel(PlanPrefillA
       const int b = find_owner(T.coff, a.batch, k);
       const int32_t p0 = T.p0[b];
       const int32_t pos = (p0 / CR + 1 + (k - T.coff[b])) * CR - 1;  // (k - coff)-th boundary at or after p0
-      emit_c<CR, SWA>(a, a.plan_c + k, b, pos, p0, T.idx[b], T.roff[b]);
+      emit_c<CR, MAP>(a, a.plan_c + k, b, pos, p0, T.idx[b], T.roff[b]);
     }
     for (int k = gtid; k < n_w; k += gstride) {
       const int b = find_owner(T.woff, a.batch, k);
       const int32_t s = T.s[b], p0 = T.p0[b];
-      const int32_t fw = first_write<CR, SWA>(s, a.swa);
+      const int32_t fw = first_write<CR, MAP>(s, a.swa);
       const int32_t first = p0 > fw ? p0 : fw;
       int64_t r = k - T.woff[b];
       int32_t pos;
@@ -361,7 +393,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_prefill_kernel(PlanPrefillA
       } else {
         pos = (int32_t)(first + r);
       }
-      emit_w<CR, SWA>(a, a.plan_w + k, pos, p0, T.idx[b], T.roff[b]);
+      emit_w<CR, MAP>(a, a.plan_w + k, b, pos, p0, T.idx[b], T.roff[b]);
     }
   }
 
@@ -373,25 +405,25 @@ __global__ __launch_bounds__(kPlanThreads) void plan_prefill_kernel(PlanPrefillA
 constexpr int kDecodePlanThreads = 1024;
 
 // One workgroup; requests are independent, the error word needs the whole batch.
-template <int CR, bool SWA>
+template <int CR, int MAP>
 __global__ __launch_bounds__(kDecodePlanThreads) void plan_decode_kernel(PlanDecodeArgs a) {
   constexpr int32_t W = CR == 4 ? 8 : 128;
   __shared__ int s_err;
   if (threadIdx.x == 0) s_err = 0;
   __syncthreads();
-  const int64_t max_idx = SWA ? a.swa.num_reqs : a.num_state_rows / W;
+  const int64_t max_idx = MAP == kPlanSwa ? a.swa.num_reqs : a.num_state_rows / (MAP == kPlanPage4 ? 4 : W);
   int err = 0;
   for (int b = threadIdx.x; b < a.batch; b += kDecodePlanThreads) {
     const int32_t s = a.seq_lens[b], idx = a.state_index[b];
     int bad = 0;
     if (s <= 0) bad |= KVC_DERR_EXTEND;
     if (idx < 0 || (int64_t)idx >= max_idx) bad |= KVC_DERR_INDEX;
-    if (SWA && (int64_t)s > a.swa.stride) bad |= KVC_DERR_INDEX;
+    if (MAP == kPlanSwa && (int64_t)s > a.swa.stride) bad |= KVC_DERR_INDEX;
     u32x4 v = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
     if (!bad) {
       const int32_t pos1 = s - 1;  // the new token
       const int32_t pos0 = pos1 - CR > 0 ? pos1 - CR : 0;
-      if constexpr (SWA) {
+      if constexpr (MAP == kPlanSwa) {
         const int64_t r0 = swa_row<CR>(a.swa, idx, pos0, a.num_state_rows);
         const int64_t r1 = swa_row<CR>(a.swa, idx, pos1, a.num_state_rows);
         if (r0 < 0 || r1 < 0) {
@@ -401,6 +433,18 @@ __global__ __launch_bounds__(kDecodePlanThreads) void plan_decode_kernel(PlanDec
           v.y = (uint32_t)r1;
           v.z = (uint32_t)(r0 / CR);
           v.w = (uint32_t)(r1 / CR);
+        }
+      } else if constexpr (MAP == kPlanPage4) {
+        // the new token goes to its block's page; the window's overlap block is the previous page,
+        // needed only when the token closes a block past the first
+        const int32_t prev = a.prev_page[b];
+        if ((s & 3) == 0 && s > 4 && !page4_ok(prev, a.num_state_rows)) {
+          bad |= KVC_DERR_INDEX;
+        } else {
+          v.x = (uint32_t)s;
+          v.y = (uint32_t)(idx * 4 + (pos1 & 3));
+          v.z = (uint32_t)prev;
+          v.w = (uint32_t)idx;
         }
       } else {
         v.x = (uint32_t)s;
@@ -417,32 +461,38 @@ __global__ __launch_bounds__(kDecodePlanThreads) void plan_decode_kernel(PlanDec
   if (threadIdx.x == 0 && a.status) a.status[0] = s_err;
 }
 
-template <int CR, bool SWA>
+template <int CR, int MAP>
 hipError_t prefill_go(const PlanPrefillArgs& a, hipStream_t stream) {
   // enough workgroups that every record (or, on the uniform path, every
   // token) has a thread; the loops are grid-strided, so any count is correct
   const int64_t work = std::max<int64_t>((int64_t)a.cap_c + a.cap_w, std::min(a.num_q, a.batch * kUniformMaxExtend));
   const int grid = (int)std::min<int64_t>(1024, std::max<int64_t>(1, (work + kPlanThreads - 1) / kPlanThreads));
-  plan_prefill_kernel<CR, SWA><<<grid, kPlanThreads, 0, stream>>>(a);
+  plan_prefill_kernel<CR, MAP><<<grid, kPlanThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
-template <int CR, bool SWA>
+template <int CR, int MAP>
 hipError_t decode_go(const PlanDecodeArgs& a, hipStream_t stream) {
-  plan_decode_kernel<CR, SWA><<<1, kDecodePlanThreads, 0, stream>>>(a);
+  plan_decode_kernel<CR, MAP><<<1, kDecodePlanThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_plan_prefill(int compress_ratio, bool swa, const PlanPrefillArgs& a, hipStream_t stream) {
-  if (compress_ratio == 4) return swa ? prefill_go<4, true>(a, stream) : prefill_go<4, false>(a, stream);
-  return swa ? prefill_go<128, true>(a, stream) : prefill_go<128, false>(a, stream);
+hipError_t launch_plan_prefill(int compress_ratio, int map, const PlanPrefillArgs& a, hipStream_t stream) {
+  if (compress_ratio == 4) {
+    if (map == kPlanPage4) return prefill_go<4, kPlanPage4>(a, stream);
+    return map == kPlanSwa ? prefill_go<4, kPlanSwa>(a, stream) : prefill_go<4, kPlanRing>(a, stream);
+  }
+  return map == kPlanSwa ? prefill_go<128, kPlanSwa>(a, stream) : prefill_go<128, kPlanRing>(a, stream);
 }
 
-hipError_t launch_plan_decode(int compress_ratio, bool swa, const PlanDecodeArgs& a, hipStream_t stream) {
-  if (compress_ratio == 4) return swa ? decode_go<4, true>(a, stream) : decode_go<4, false>(a, stream);
-  return swa ? decode_go<128, true>(a, stream) : decode_go<128, false>(a, stream);
+hipError_t launch_plan_decode(int compress_ratio, int map, const PlanDecodeArgs& a, hipStream_t stream) {
+  if (compress_ratio == 4) {
+    if (map == kPlanPage4) return decode_go<4, kPlanPage4>(a, stream);
+    return map == kPlanSwa ? decode_go<4, kPlanSwa>(a, stream) : decode_go<4, kPlanRing>(a, stream);
+  }
+  return map == kPlanSwa ? decode_go<128, kPlanSwa>(a, stream) : decode_go<128, kPlanRing>(a, stream);
 }
 
 }  // namespace kvc

@@ -65,6 +65,8 @@ def load(build_if_missing: bool = False):
         "kvc_compress_c128_norm_rope_store": [I, I, P, L, P, I, P, P, I, P, P, P],
         "kvc_decode_c4_norm_rope_store": [I, I, P, L, P, P, P, I, P, P, P],
         "kvc_compress_c128_online": [I, I, P, L, P, I, P, P, I, P, P, P],
+        "kvc_plan_prefill_page4": [I, I, P, P, P, P, L, P, I, P, I, P, P, P],
+        "kvc_plan_decode_page4": [I, P, P, P, L, P, P, P],
         "kvc_write_c128_online": [I, I, P, L, P, I, P, P, I, P, P],
         "kvc_decode_c128_online": [I, I, P, L, P, P, P, I, P, P, P],
     }
@@ -212,6 +214,26 @@ def plan_decode_swa(cr, seq_lens, req_pool_indices, req_to_token, full_to_swa, s
                                     full_to_swa.numel(), swa_page_size, ring_size, num_state_rows, _p(plan_d),
                                     _p(status), _stream(stream))
     _check(rc, "kvc_plan_decode_swa")
+
+
+def plan_prefill_page4(seq_lens, extend_lens, page_index, bundle, num_state_rows, num_q, plan_c, plan_w, counts,
+                       status=None, stream=None):
+    """Ratio-4 prefill plan over caller-allocated 4-row pages; bundle: int32 [batch, 4]."""
+    _dev(seq_lens, extend_lens, page_index, bundle, plan_c, plan_w, counts, status)
+    B = seq_lens.numel()
+    if bundle.dtype != torch.int32 or tuple(bundle.shape) != (B, 4):
+        raise KvcError("bundle must be int32 [batch, 4]")
+    rc = load().kvc_plan_prefill_page4(B, num_q, _p(seq_lens), _p(extend_lens), _p(page_index), _p(bundle),
+                                       num_state_rows, _p(plan_c), plan_c.shape[0], _p(plan_w), plan_w.shape[0],
+                                       _p(counts), _p(status), _stream(stream))
+    _check(rc, "kvc_plan_prefill_page4")
+
+
+def plan_decode_page4(seq_lens, page_index, prev_page, num_state_rows, plan_d, status=None, stream=None):
+    _dev(seq_lens, page_index, prev_page, plan_d, status)
+    rc = load().kvc_plan_decode_page4(seq_lens.numel(), _p(seq_lens), _p(page_index), _p(prev_page), num_state_rows,
+                                      _p(plan_d), _p(status), _stream(stream))
+    _check(rc, "kvc_plan_decode_page4")
 
 
 def write(cr, head_dim, state, inp, plan_w, counts, stream=None):

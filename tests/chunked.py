@@ -96,6 +96,81 @@ def run_chunked(backend, cr, hd, dtype, seqs, chunks, decode_steps, state_index,
     return emitted, state
 
 
+class Pages:
+    """A caller's page table: one 4-row page per (request, block), allocated on first use."""
+
+    def __init__(self, rng, n):
+        self.free = list(rng.permutation(n))
+        self.table = {}
+
+    def __call__(self, b, block, allocate=True):
+        if block < 0:
+            return -1
+        key = (b, block)
+        if key not in self.table:
+            if not allocate:
+                return -1
+            self.table[key] = int(self.free.pop())
+        return self.table[key]
+
+
+def _chunk_pages(pages, b, s, e):
+    p0 = s - e
+    last = (s // 4) * 4
+    lsp = pages(b, (p0 - 1) // 4) if p0 > 0 else -1
+    lfp = pages(b, (p0 - 1) // 4 - 1) if p0 > 4 else -1
+    wfp = pages(b, last // 4 - 1)
+    idx = pages(b, last // 4)
+    return idx, (lfp, lsp, wfp, last)
+
+
+def run_chunked_page4(backend, rng, hd, dtype, seqs, chunks, decode_steps, ape, n_pages):
+    """Ratio 4 over caller-allocated pages: every block of every request gets a page of its own
+    (from a shuffled pool of n_pages); chunks and decode steps as in run_chunked.
+    Returns (emitted, state)."""
+    B = len(seqs)
+    R = 4 * hd
+    state = nan_state(n_pages * 4, R, dtype)
+    pages = Pages(rng, n_pages)
+    length = [0] * B
+    emitted = {}
+    for r in range(max(len(c) for c in chunks)):
+        active = [b for b in range(B) if r < len(chunks[b])]
+        e = np.array([chunks[b][r] for b in active], np.int32)
+        s = np.array([length[b] + chunks[b][r] for b in active], np.int32)
+        idx, bundle = zip(*[_chunk_pages(pages, b, int(sb), int(eb)) for b, sb, eb in zip(active, s, e)])
+        inp = np.concatenate([seqs[b][length[b]:length[b] + chunks[b][r]] for b in active])
+        num_q = int(e.sum())
+        cap_c = min(num_q, num_q // 4 + len(active))
+        cap_w = min(num_q, len(active) * 7)
+        pc, pw, counts, status = backend.plan_prefill_page4(s, e, idx, bundle, state.shape[0], num_q, cap_c, cap_w)
+        assert counts[2] == 0 and status == 0, (counts, status)
+        out, err = backend.compress(4, hd, state, inp, ape, pc, int(counts[0]))
+        assert err == 0
+        state = backend.write(4, hd, state, inp, pw, int(counts[1]))
+        base = np.concatenate([[0], np.cumsum(e)])
+        recs = np.ascontiguousarray(pc[: counts[0]]).view("<u4").reshape(-1, 4)
+        for k in range(int(counts[0])):
+            a_ = int(np.searchsorted(base, int(recs[k, 1]) & 0xFFFFFF, side="right") - 1)
+            emitted[(active[a_], int(recs[k, 0]))] = out[k].copy()
+        for b in active:
+            length[b] += chunks[b][r]
+    for _ in range(decode_steps):
+        s = np.array([length[b] + 1 for b in range(B)], np.int32)
+        idx = [pages(b, (int(s[b]) - 1) // 4) for b in range(B)]
+        prev = [pages(b, (int(s[b]) - 1) // 4 - 1) for b in range(B)]
+        pd, status = backend.plan_decode_page4(s, idx, prev, state.shape[0])
+        assert status == 0
+        inp = np.stack([seqs[b][length[b]] for b in range(B)])
+        out, state, err = backend.decode(4, hd, state, inp, ape, pd)
+        assert err == 0
+        for b in range(B):
+            if s[b] % 4 == 0:
+                emitted[(b, int(s[b]))] = out[b].copy()
+            length[b] += 1
+    return emitted, state
+
+
 class OracleBackend:
     """The CPU oracle in the driver's calling convention."""
 
@@ -121,6 +196,12 @@ class OracleBackend:
 
     def plan_decode_swa(self, *a):
         return self.o.plan_decode_swa(*a)
+
+    def plan_prefill_page4(self, *a):
+        return self.o.plan_prefill_page4(*a)
+
+    def plan_decode_page4(self, *a):
+        return self.o.plan_decode_page4(*a)
 
     def decode(self, cr, hd, state, inp, ape, pd):
         state = state.copy()

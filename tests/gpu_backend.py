@@ -116,3 +116,25 @@ class GpuBackend:
         st = to_dev(np.asarray(state, np.float32))
         kvc.decode_c128_online(hd, st, to_dev(inp), to_dev(ape), to_dev(pd), out, status)
         return out.cpu().numpy().astype(np.float64), st.cpu().numpy(), int(status.item())
+
+    # ratio 4 over caller-allocated 4-row pages
+    def plan_prefill_page4(self, s, e, idx, bundle, rows, num_q, cap_c, cap_w):
+        d = self.device
+        pc, pw, counts = kvc.alloc_prefill_plan(4, len(s), num_q, d, cap_c=cap_c, cap_w=cap_w)
+        pc.fill_(0x5A)
+        pw.fill_(0x5A)
+        counts.fill_(-7)
+        status = torch.zeros(1, dtype=torch.int32, device=d)
+        kvc.plan_prefill_page4(to_dev(np.asarray(s, np.int32)), to_dev(np.asarray(e, np.int32)),
+                               to_dev(np.asarray(idx, np.int32)),
+                               to_dev(np.asarray(bundle, np.int32).reshape(-1, 4)), int(rows), int(num_q), pc, pw,
+                               counts, status)
+        return pc.cpu().numpy(), pw.cpu().numpy(), counts.cpu().numpy(), int(status.item())
+
+    def plan_decode_page4(self, s, idx, prev, rows):
+        d = self.device
+        pd = torch.full((len(s), kvc.D_BYTES), 0x5A, dtype=torch.uint8, device=d)
+        status = torch.full((1,), -7, dtype=torch.int32, device=d)
+        kvc.plan_decode_page4(to_dev(np.asarray(s, np.int32)), to_dev(np.asarray(idx, np.int32)),
+                              to_dev(np.asarray(prev, np.int32)), int(rows), pd, status)
+        return pd.cpu().numpy(), int(status.item())

@@ -23,7 +23,7 @@ def test_header_declares_the_boundary():
         "kvc_decode_c4", "kvc_decode_c128", "kvc_strerror", "kvc_plan_prefill_swa", "kvc_plan_decode_swa",
         "kvc_norm_rope_store_prefill", "kvc_norm_rope_store_decode", "kvc_compress_c4_norm_rope_store",
         "kvc_compress_c128_norm_rope_store", "kvc_decode_c4_norm_rope_store", "kvc_compress_c128_online",
-        "kvc_write_c128_online", "kvc_decode_c128_online"])
+        "kvc_write_c128_online", "kvc_decode_c128_online", "kvc_plan_prefill_page4", "kvc_plan_decode_page4"])
 
 
 def test_store_args_layout_matches_the_header(tmp_path):
@@ -114,6 +114,12 @@ def test_host_argument_checks_reject_without_enqueueing(lib):
     assert lib.kvc_decode_c4_norm_rope_store(1, 128, p, 8, p, p, p, 1, None, None, None) == E
     assert lib.kvc_decode_c4_norm_rope_store(1, 128, p, 8, p, p, p, 1, None, st(rope_dim=20), None) == E
     assert lib.kvc_decode_c4_norm_rope_store(1, 128, p, 8, p, p, p, 0, None, st(), None) == E
+    # page-4 planners: batch, token count, bundle alignment
+    assert lib.kvc_plan_prefill_page4(0, 1, p, p, p, p, L(64), p, 1, p, 1, p, None, None) == E
+    assert lib.kvc_plan_prefill_page4(2, 1, p, p, p, p, L(64), p, 1, p, 1, p, None, None) == E
+    assert lib.kvc_plan_prefill_page4(1, 1, p, p, p, misaligned, L(64), p, 1, p, 1, p, None, None) == E
+    assert lib.kvc_plan_decode_page4(0, p, p, p, L(64), p, None, None) == E
+    assert lib.kvc_plan_decode_page4(1, p, p, p, L(64), misaligned, None, None) == E
     # online ratio-128 state: head_dim, slot count, alignment, batch
     assert lib.kvc_compress_c128_online(1, 96, p, 2, p, 1, p, p, 1, p, p, None) == E
     assert lib.kvc_compress_c128_online(1, 128, p, -1, p, 1, p, p, 1, p, p, None) == E

@@ -15,82 +15,9 @@ import pytest
 import oracle
 from oracle import brute
 from sparse_attention_kv_plan_amd import workloads as wl
-from tests.chunked import as_float, nan_state, random_split
+from tests.chunked import OracleBackend, as_float, random_split, run_chunked_page4
 
 ERR_INDEX = 4
-
-
-class Pages:
-    """A caller's page table: one 4-row page per (request, block), allocated on first use."""
-
-    def __init__(self, rng, n):
-        self.free = list(rng.permutation(n))
-        self.table = {}
-
-    def __call__(self, b, block, allocate=True):
-        if block < 0:
-            return -1
-        key = (b, block)
-        if key not in self.table:
-            if not allocate:
-                return -1
-            self.table[key] = int(self.free.pop())
-        return self.table[key]
-
-
-def _chunk_pages(pages, b, s, e):
-    p0 = s - e
-    last = (s // 4) * 4
-    lsp = pages(b, (p0 - 1) // 4) if p0 > 0 else -1
-    lfp = pages(b, (p0 - 1) // 4 - 1) if p0 > 4 else -1
-    wfp = pages(b, last // 4 - 1)
-    idx = pages(b, last // 4)
-    return idx, (lfp, lsp, wfp, last)
-
-
-def _run(rng, dtype, seqs, chunks, decode_steps, hd, n_pages):
-    B = len(seqs)
-    R = 4 * hd
-    a = (0.1 * rng.standard_normal((8, hd))).astype(np.float32)
-    ape = wl.to_bf16_bits(a) if dtype == "bf16" else a
-    state = nan_state(n_pages * 4, R, dtype)
-    pages = Pages(rng, n_pages)
-    length = [0] * B
-    emitted = {}
-    for r in range(max(len(c) for c in chunks)):
-        active = [b for b in range(B) if r < len(chunks[b])]
-        e = np.array([chunks[b][r] for b in active], np.int32)
-        s = np.array([length[b] + chunks[b][r] for b in active], np.int32)
-        idx, bundle = zip(*[_chunk_pages(pages, b, int(sb), int(eb)) for b, sb, eb in zip(active, s, e)])
-        inp = np.concatenate([seqs[b][length[b]:length[b] + chunks[b][r]] for b in active])
-        num_q = int(e.sum())
-        cap_c, cap_w = oracle.capacities(4, len(active), num_q)
-        pc, pw, counts, status = oracle.plan_prefill_page4(s, e, idx, bundle, state.shape[0], num_q, cap_c, cap_w)
-        assert counts[2] == 0 and status == 0, (counts, status)
-        out, err = oracle.compress(4, hd, state, inp, ape, pc, int(counts[0]))
-        assert err == 0
-        assert oracle.write(4, hd, state, inp, pw, int(counts[1])) == 0
-        base = np.concatenate([[0], np.cumsum(e)])
-        C = oracle.unpack_c(pc[: counts[0]])
-        for k in range(int(counts[0])):
-            a_ = int(np.searchsorted(base, int(C[k, 1]), side="right") - 1)
-            emitted[(active[a_], int(C[k, 0]))] = out[k].copy()
-        for b in active:
-            length[b] += chunks[b][r]
-    for _ in range(decode_steps):
-        s = np.array([length[b] + 1 for b in range(B)], np.int32)
-        idx = [pages(b, (int(s[b]) - 1) // 4) for b in range(B)]
-        prev = [pages(b, (int(s[b]) - 1) // 4 - 1) for b in range(B)]
-        pd, status = oracle.plan_decode_page4(s, idx, prev, state.shape[0])
-        assert status == 0
-        inp = np.stack([seqs[b][length[b]] for b in range(B)])
-        out, err = oracle.decode(4, hd, state, inp, ape, pd)
-        assert err == 0
-        for b in range(B):
-            if s[b] % 4 == 0:
-                emitted[(b, int(s[b]))] = out[b].copy()
-            length[b] += 1
-    return emitted, ape
 
 
 @pytest.mark.parametrize("dtype,trial", [("f32", 0), ("bf16", 1), ("f32", 2)])
@@ -103,7 +30,9 @@ def test_page4_chunking_matches_the_window_definition(dtype, trial):
         x = rng.standard_normal((L + steps, 4 * hd)).astype(np.float32)
         seqs.append(wl.to_bf16_bits(x) if dtype == "bf16" else x)
         chunks.append(random_split(rng, L, 6))
-    emitted, ape = _run(rng, dtype, seqs, chunks, steps, hd, n_pages=200)
+    a = (0.1 * rng.standard_normal((8, hd))).astype(np.float32)
+    ape = wl.to_bf16_bits(a) if dtype == "bf16" else a
+    emitted, _ = run_chunked_page4(OracleBackend(oracle), rng, hd, dtype, seqs, chunks, steps, ape, n_pages=200)
     apef = as_float(ape, dtype).tolist()
     seen = set()
     for b, seq in enumerate(seqs):
