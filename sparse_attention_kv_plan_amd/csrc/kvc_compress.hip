@@ -22,6 +22,10 @@ namespace kvc {
 namespace {
 
 constexpr int kThreads = 256;
+// The ratio-128 pool runs 512 threads per row: 8 streams of 16 entries, so a row
+// takes half as many rounds of loads as with 256 (with the pool's priority by
+// progress, 6% faster on the mixed prefill).
+constexpr int kC128Threads = 512;
 
 // STORE = false: the pooled rows go to a.out as float32.  STORE = true: the
 // row is normalised, rotated and stored as bf16 into the compressed cache
@@ -107,9 +111,9 @@ __global__ __launch_bounds__(kThreads) void compress_c4_kernel(CompressArgs a) {
 }
 
 template <typename T, int HD, bool STORE>
-__global__ __launch_bounds__(kThreads) void compress_c128_kernel(CompressArgs a) {
+__global__ __launch_bounds__(kC128Threads) void compress_c128_kernel(CompressArgs a) {
   typedef typename Elem<T>::storage E;
-  typedef C128Pool<T, HD, kThreads> Pool;
+  typedef C128Pool<T, HD, kC128Threads> Pool;
   __shared__ float lds[Pool::kLdsFloats];
   const int64_t row = blockIdx.x;
   if (row >= a.counts[0] || row >= a.cap_c) return;
@@ -129,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void compress_c128_kernel(CompressArgs a)
     // thread t ends with channels 2t, 2t+1 (a rotary pair); threads past HD/2 hold zeros.
     // The store's loads go out after the window's (holding them across the
     // pool would cost a wave per SIMD of occupancy).
-    __shared__ float red[kThreads / kWave];
+    __shared__ float red[kC128Threads / kWave];
     const int c = 2 * threadIdx.x;
     const int32_t pos = rec.seq_len >= 128u ? (int32_t)rec.seq_len - 128 : 0;
     Pool::accumulate(state, input, ape, ragged, blen, rp0, 0, lds);
@@ -145,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void compress_c128_kernel(CompressArgs a)
       x[0] = Pool::merged(lds, c);
       x[1] = Pool::merged(lds, c + 1);
     }
-    const float ss = block_sum<kThreads>(fmaf(x[0], x[0], x[1] * x[1]), red);
+    const float ss = block_sum<kC128Threads>(fmaf(x[0], x[0], x[1] * x[1]), red);
     if (c < HD) norm_rope_store<2, HD>(x, ss, c, loc, ops, a.st);
   } else {
     Pool::run(state, input, ape, ragged, blen, rp0, 0, a.out + row * HD, lds);
@@ -191,7 +195,7 @@ hipError_t c4_launch(const CompressArgs& a, hipStream_t stream) {
 
 template <typename T, int HD, bool STORE>
 hipError_t c128_launch(const CompressArgs& a, hipStream_t stream) {
-  compress_c128_kernel<T, HD, STORE><<<a.cap_c, kThreads, 0, stream>>>(a);
+  compress_c128_kernel<T, HD, STORE><<<a.cap_c, kC128Threads, 0, stream>>>(a);
   return hipGetLastError();
 }
 

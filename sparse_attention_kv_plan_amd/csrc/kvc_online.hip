@@ -23,12 +23,13 @@ namespace kvc {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kCompressThreads = 512;  // as the paged ratio-128 pool: 8 streams of 16 entries
 
 // one workgroup per C record
 template <typename T, int HD>
-__global__ __launch_bounds__(kThreads) void compress_online_kernel(OnlineArgs a) {
+__global__ __launch_bounds__(kCompressThreads) void compress_online_kernel(OnlineArgs a) {
   typedef typename Elem<T>::storage E;
-  typedef C128Pool<T, HD, kThreads> Pool;
+  typedef C128Pool<T, HD, kCompressThreads> Pool;
   __shared__ float lds[Pool::kLdsFloats];
   const int64_t row = blockIdx.x;
   if (row >= a.counts[0] || row >= a.cap) return;
@@ -45,7 +46,7 @@ __global__ __launch_bounds__(kThreads) void compress_online_kernel(OnlineArgs a)
   Pool::accumulate_range(static_cast<const E*>(a.input), static_cast<const E*>(a.ape), ragged - 127, 0, blen, 128, 0,
                          lds);
   const float* st = blen > 0 ? a.state + slot * 3 * HD : nullptr;  // slot is read only when blen > 0
-  for (int d = threadIdx.x; d < HD; d += kThreads) {
+  for (int d = threadIdx.x; d < HD; d += kCompressThreads) {
     float M, L, A;
     Pool::merged_partial(lds, d, st != nullptr, st ? st[d] : 0.f, st ? st[HD + d] : 0.f, st ? st[2 * HD + d] : 0.f,
                          &M, &L, &A);
@@ -224,21 +225,21 @@ struct Launch {
   }
 };
 
-#define KVC_ONLINE_KERNEL(NAME, KERNEL)                                                  \
+#define KVC_ONLINE_KERNEL(NAME, KERNEL, NT)                                              \
   template <typename T, int HD>                                                          \
   struct NAME {                                                                          \
     static void launch(const OnlineArgs& a, int64_t grid, hipStream_t s) {               \
-      KERNEL<T, HD><<<(unsigned)grid, kThreads, 0, s>>>(a);                              \
+      KERNEL<T, HD><<<(unsigned)grid, NT, 0, s>>>(a);                                    \
     }                                                                                    \
   };
-KVC_ONLINE_KERNEL(CompressK, compress_online_kernel)
+KVC_ONLINE_KERNEL(CompressK, compress_online_kernel, kCompressThreads)
 template <typename T, int HD>
 struct WriteK {
   static void launch(const OnlineArgs& a, int64_t grid, hipStream_t s) {
     write_online_kernel<T, HD><<<(unsigned)(grid * WriteShape<T, HD>::CS), kWriteThreads, 0, s>>>(a);
   }
 };
-KVC_ONLINE_KERNEL(DecodeK, decode_online_kernel)
+KVC_ONLINE_KERNEL(DecodeK, decode_online_kernel, kThreads)
 #undef KVC_ONLINE_KERNEL
 
 template <template <typename, int> class K>

@@ -96,10 +96,30 @@ __device__ __forceinline__ bool c4_record_ok(int64_t ragged, int blen, int64_t r
 // per channel, so the slices need no merge).  Stream s owns entries s, s + S,
 // s + 2S, ... (at any moment the streams read adjacent rows) and runs an online
 // softmax over them in chunks of U entries, all loads of a chunk issued before
-// any use.  U = 4 keeps a 256-thread workgroup under 128 VGPRs (4 waves per
-// SIMD).  The S partial (max, sum, weighted sum) triples are merged in LDS.
+// any use.  U = 4 keeps the streams under 128 VGPRs (4 waves per SIMD).  The S
+// partial (max, sum, weighted sum) triples are merged in LDS.
 // Entry i is state row rp0*128 + i when i < blen, else input row
 // ragged - 127 + i.
+//
+// Wave priority by progress: when a stream runs 4 or more chunks, its wave
+// sets its issue priority from 3 (first quarter of its chunks) down to 0 (last
+// quarter).  The waves sharing a SIMD belong to different rows; with equal
+// priority the oldest wave wins the issue slots, so rows dispatched first
+// finish far ahead of the rest and the last rows run with too few loads in
+// flight to keep HBM busy.  Serving the waves that are behind first evens the
+// rows out (on MI355X, 6% less time for the ratio-128 prefill pool).
+__device__ __forceinline__ void progress_priority(int quarter) {
+  if (quarter == 0) {
+    __builtin_amdgcn_s_setprio(3);
+  } else if (quarter == 1) {
+    __builtin_amdgcn_s_setprio(2);
+  } else if (quarter == 2) {
+    __builtin_amdgcn_s_setprio(1);
+  } else {
+    __builtin_amdgcn_s_setprio(0);
+  }
+}
+
 template <typename T, int HD, int NT, int CS = 1, int U = 4>
 struct C128Pool {
   static constexpr int V = Elem<T>::kVec;
@@ -108,6 +128,7 @@ struct C128Pool {
   static constexpr int S = NT / kLanes;   // streams per workgroup
   static constexpr int PER = 128 / S;     // entries per stream
   static constexpr int kLdsFloats = 3 * S * HDW;
+  static constexpr bool kPrio = PER / U >= 4;  // priority by progress (see above)
   static_assert(HD % CS == 0 && NT % kLanes == 0 && 128 % S == 0 && PER % U == 0, "bad c128 pool shape");
 
   // Every stream's partial (max, sum, weighted sum) per channel of the slice,
@@ -128,6 +149,7 @@ struct C128Pool {
       acc[v] = 0.f;
     }
     for (int k0 = 0; k0 < PER; k0 += U) {
+      if constexpr (kPrio) progress_priority(k0 * 4 / PER);
       u32x4 kv_raw[U], sc_raw[U], ap_raw[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -167,6 +189,7 @@ struct C128Pool {
         acc[v] = av;
       }
     }
+    if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
     float* lm = lds;
     float* ll = lds + S * HDW;
     float* la = lds + 2 * S * HDW;
@@ -196,6 +219,7 @@ struct C128Pool {
       acc[v] = 0.f;
     }
     for (int k0 = 0; k0 < PER; k0 += U) {
+      if constexpr (kPrio) progress_priority(k0 * 4 / PER);
       u32x4 kv_raw[U], sc_raw[U], ap_raw[U];
       bool in[U];
 #pragma unroll
@@ -238,6 +262,7 @@ struct C128Pool {
         acc[v] = av;
       }
     }
+    if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
     float* lm = lds;
     float* ll = lds + S * HDW;
     float* la = lds + 2 * S * HDW;
