@@ -4,10 +4,10 @@
 // c4_write; compressor_v2.py, _c128_compress_prefill_write_kernel).
 //
 // All three are HBM-streaming kernels (no dense contraction, so no MFMA):
-//  - compress c4: 64 lanes x 16 B cover one half-row of hd 512 bf16, so a
+//  - compress c4: 64 lanes x 16 B cover the 512 channels of one bf16 row, so a
 //    lane group reads each of its 8 window entries' kv and score quarters
 //    with one 16-byte load each, all 16 (+8 ape) loads in flight before the
-//    first use; 256-thread workgroups hold 256 / lanes-per-row rows.
+//    first use; 512-thread workgroups hold 512 / lanes-per-row rows.
 //  - compress c128: one workgroup per compressed row; its streams split the
 //    128 window entries and merge their online-softmax partials in LDS.
 //  - write: one wave per record, the whole row copied with 16-byte vectors.
@@ -22,6 +22,10 @@ namespace kvc {
 namespace {
 
 constexpr int kThreads = 256;
+// The ratio-4 pool runs 512-thread workgroups (8 rows of hd 512 bf16): against
+// 256 threads, 4-5% less time on the mixed prefill (12 or 16 rows per
+// workgroup are slower again).
+constexpr int kC4Threads = 512;
 // The ratio-128 pool runs 512 threads per row: 8 streams of 16 entries, so a row
 // takes half as many rounds of loads as with 256 (with the pool's priority by
 // progress, 6% faster on the mixed prefill).
@@ -31,10 +35,10 @@ constexpr int kC128Threads = 512;
 // row is normalised, rotated and stored as bf16 into the compressed cache
 // (a.st) straight from registers.
 template <typename T, int HD, bool STORE>
-__global__ __launch_bounds__(kThreads) void compress_c4_kernel(CompressArgs a) {
+__global__ __launch_bounds__(kC4Threads) void compress_c4_kernel(CompressArgs a) {
   constexpr int V = Elem<T>::kVec;
   constexpr int kLanes = HD / V;
-  constexpr int kRows = kThreads / kLanes;
+  constexpr int kRows = kC4Threads / kLanes;
   const int64_t row = (int64_t)blockIdx.x * kRows + threadIdx.x / kLanes;
   const int c = (threadIdx.x % kLanes) * V;
   typedef typename Elem<T>::storage E;
@@ -84,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void compress_c4_kernel(CompressArgs a) {
     }
   }
   if constexpr (STORE) {
-    __shared__ float red[kThreads / kWave];
+    __shared__ float red[kC4Threads / kWave];
     float ss = 0.f;
 #pragma unroll
     for (int v = 0; v < V; ++v) ss = fmaf(res[v], res[v], ss);
@@ -95,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void compress_c4_kernel(CompressArgs a) {
     // 16-byte pieces at a 4*V-byte stride.  Staging the row in LDS lets every
     // store instruction write 64 x 16 contiguous bytes instead (2% faster in
     // the full step; with cold caches the two are even).
-    __shared__ float stage[kThreads * V];  // the workgroup's output rows
+    __shared__ float stage[kC4Threads * V];  // the workgroup's output rows
     float* w = stage + (threadIdx.x / kLanes) * HD;
     store_floats<V>(w + c, res);
     __syncthreads();
@@ -187,9 +191,9 @@ __global__ __launch_bounds__(kThreads) void write_kernel(WriteArgs a) {
 
 template <typename T, int HD, bool STORE>
 hipError_t c4_launch(const CompressArgs& a, hipStream_t stream) {
-  constexpr int kRows = kThreads / (HD / Elem<T>::kVec);
+  constexpr int kRows = kC4Threads / (HD / Elem<T>::kVec);
   const int grid = (a.cap_c + kRows - 1) / kRows;
-  compress_c4_kernel<T, HD, STORE><<<grid, kThreads, 0, stream>>>(a);
+  compress_c4_kernel<T, HD, STORE><<<grid, kC4Threads, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -75,8 +75,12 @@ __device__ __forceinline__ void c4_pool(const typename Elem<T>::storage* __restr
 }
 
 // Rows the ratio-4 window of a record reads, checked against the buffers.
+// Nearly every record reads the input only (blen = 0); its check is two
+// compares, taken before the general form (whose 64-bit page arithmetic sits
+// between the record load and the window loads, and cost ~4% of the pool).
 __device__ __forceinline__ bool c4_record_ok(int64_t ragged, int blen, int64_t rp0, int64_t rp1, int first,
                                              int64_t num_q, int64_t num_state_rows) {
+  if (blen == 0) return ragged - 7 + first >= 0 && ragged < num_q;
   const int s_hi = blen < 8 ? blen : 8;
   const int lo0 = first, hi0 = s_hi < 4 ? s_hi : 4;
   const int lo1 = first > 4 ? first : 4, hi1 = s_hi;
