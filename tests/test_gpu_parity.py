@@ -15,7 +15,7 @@ torch = pytest.importorskip("torch")
 import oracle  # noqa: E402
 from sparse_attention_kv_plan_amd import kvc  # noqa: E402
 from sparse_attention_kv_plan_amd import workloads as wl  # noqa: E402
-from tests.chunked import OracleBackend, nan_state, random_split, run_chunked  # noqa: E402
+from tests.chunked import OracleBackend, as_float, nan_state, random_split, run_chunked  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -201,6 +201,49 @@ def test_decode(gpu, cr, hd, dtype):
         nb = w.seq_lens % cr != 0
         assert np.all(got[nb] == 0.0)
         assert np.array_equal(st_g.view(np.uint8), st_o.view(np.uint8)), "state differs after decode"
+
+
+def _scale_scores(a, cr, hd, dtype, factor):
+    """Multiply the score columns of input or state rows (|kv ov|kv|sc ov|sc| for ratio 4, |kv|sc| for
+    ratio 128) by factor, staying in the storage dtype."""
+    x = as_float(a, dtype).astype(np.float32)
+    lo = 2 * hd if cr == 4 else hd
+    x[:, lo:] *= np.float32(factor)
+    return wl.to_bf16_bits(x) if dtype == "bf16" else x
+
+
+@pytest.mark.parametrize("cr", [4, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_large_magnitude_scores(gpu, cr, dtype):
+    """Scores of size ~1e30: exp of an unshifted score overflows, so the pool is finite only
+    because the window maximum is subtracted first; the weights are then one-hot up to
+    rounding, and the rows must still match the float64 oracle."""
+    hd = 128
+    rng = np.random.default_rng(40 + cr + (dtype == "bf16"))
+    B = 6
+    w = wl.random_prefill(rng, cr, hd, dtype, B, prefix_hi=3 * W[cr], extend_lo=1, extend_hi=3 * W[cr],
+                          num_slots=B + 1)
+    w.input = _scale_scores(w.input, cr, hd, dtype, 1e30)
+    w.state = _scale_scores(w.state, cr, hd, dtype, 1e30)
+    cap_c, cap_w = oracle.capacities(cr, B, w.num_q)
+    pc, pw, counts = oracle.plan_prefill(cr, w.seq_lens, w.extend_lens, w.state_index, w.num_state_rows,
+                                         w.num_q, cap_c, cap_w)
+    say("large scores cr=%d %s num_c=%d" % (cr, dtype, counts[0]))
+    ref, err = oracle.compress(cr, hd, w.state, w.input, w.ape, pc, counts[0])
+    got, gerr = gpu.compress(cr, hd, w.state, w.input, w.ape, pc, counts[0])
+    assert err == gerr == 0
+    n = int(counts[0])
+    assert n > 0
+    assert_pool_close(got[:n], ref[:n], dtype, "compress, large scores")
+    d = wl.random_decode(rng, cr, hd, dtype, 64, prefix_hi=3 * W[cr], num_slots=65)
+    d.seq_lens = (rng.integers(1, 4, size=64) * cr).astype(np.int32)  # every request pools
+    d.input = _scale_scores(d.input, cr, hd, dtype, 1e30)
+    d.state = _scale_scores(d.state, cr, hd, dtype, 1e30)
+    pd, status = oracle.plan_decode(cr, d.seq_lens, d.state_index, d.num_state_rows)
+    ref, err = oracle.decode(cr, hd, d.state.copy(), d.input, d.ape, pd)
+    got, _, gerr = gpu.decode(cr, hd, d.state, d.input, d.ape, pd)
+    assert status == err == gerr == 0
+    assert_pool_close(got, ref, dtype, "decode, large scores")
 
 
 def test_first_block_never_reads_masked_rows(gpu):
