@@ -148,6 +148,24 @@ def algorithmic_bytes_decode(cr, hd, esize, seq_lens):
     return int(per.sum()) + W * hd * esize
 
 
+def algorithmic_bytes_plan_prefill(B, cap_c, cap_w):
+    """Bytes a prefill planner must move: three int32 per request in, every record slot out (records
+    and their invalid padding), the four counters."""
+    return 12 * B + 16 * cap_c + 8 * cap_w + 16
+
+
+def algorithmic_bytes_plan_decode(B):
+    """Bytes a decode planner must move: two int32 per request in, one 16-byte record out."""
+    return 8 * B + 16 * B
+
+
+def algorithmic_bytes_write(cr, hd, esize, num_w):
+    """Bytes the state write must move: each written input row read once and stored once, plus its
+    8-byte record."""
+    R = (4 if cr == 4 else 2) * hd
+    return num_w * (2 * R * esize + 8)
+
+
 def sweep(torch, kvc, dev, P4, P128, to_dev):
     """Extra, labelled results: kernel time and algorithmic GB/s as the work grows (prefill: the first
     k requests of the mixed batch; decode: batches with device-generated inputs), and the two compress
@@ -533,6 +551,31 @@ def main():
             "store_only_GBps": round(sb / (kernels_us["norm_rope_store_prefill c%d" % cr] * 1e-6) / 1e9, 1),
             "store_only_bytes": sb}
 
+    # every launch of the step against its bound: the pools stream HBM; the planners, the writes (a
+    # few MB of rows behind a record load) and the fused decodes are chains of dependent loads
+    def row_entry(name, nbytes, bound):
+        us = kernels_us[name]
+        gbps = nbytes / (us * 1e-6) / 1e9
+        return {"us": us, "bytes": int(nbytes), "GBps": round(gbps, 1), "frac": round(gbps / 8000.0, 4),
+                "bound": bound}
+
+    step_rows = {}
+    for cr, P, w in ((4, P4, p4), (128, P128, p128)):
+        c = P.counts.cpu().tolist()
+        seqs = P.plan_c[: c[0]].cpu().numpy().view("<u4").reshape(-1, 4)[:, 0].astype(np.int64)
+        step_rows["plan_prefill c%d" % cr] = row_entry(
+            "plan_prefill c%d" % cr, algorithmic_bytes_plan_prefill(w.B, P.plan_c.shape[0], P.plan_w.shape[0]),
+            "latency")
+        step_rows["compress_c%d" % cr] = row_entry(
+            "compress_c%d" % cr, algorithmic_bytes_compress(cr, w.hd, w.esize, seqs), "hbm")
+        step_rows["write c%d" % cr] = row_entry(
+            "write c%d" % cr, algorithmic_bytes_write(cr, w.hd, w.esize, c[1]), "latency")
+    for cr, D, w in ((4, D4, d4), (128, D128, d128)):
+        step_rows["plan_decode c%d" % cr] = row_entry("plan_decode c%d" % cr, algorithmic_bytes_plan_decode(w.B),
+                                                      "latency")
+        step_rows["decode_c%d" % cr] = row_entry(
+            "decode_c%d" % cr, algorithmic_bytes_decode(cr, w.hd, w.esize, w.seq_lens), "latency")
+
     tokens = p4.num_q + p128.num_q + d4.B + d128.B
     value = tokens / (ms_per_step * 1e-3)
 
@@ -569,6 +612,7 @@ def main():
             "avg_launch_us": round(dom_us, 2),
         },
         "kernels_us": kernels_us,
+        "step_rows": step_rows,
         "decode_step_us": decode_us,
         "store_step": store_step,
         "wall_s_timed": round(wall, 3),
