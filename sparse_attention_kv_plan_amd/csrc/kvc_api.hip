@@ -13,6 +13,7 @@
 namespace {
 
 bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned8(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 bool aligned4(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool ratio_ok(int cr) { return cr == 4 || cr == 128; }
 bool dtype_ok(int dt) { return dt == KVC_F32 || dt == KVC_BF16; }
@@ -32,7 +33,7 @@ KVC_EXPORT int kvc_plan_prefill(int compress_ratio, int batch, int num_q, const 
     return KVC_EINVAL;
   if (!aligned4(seq_lens) || !aligned4(extend_lens) || !aligned4(state_index) || !aligned4(counts))
     return KVC_EINVAL;
-  if ((cap_c > 0 && !aligned16(plan_c)) || (cap_w > 0 && (plan_w == nullptr || (reinterpret_cast<uintptr_t>(plan_w) & 7u))))
+  if ((cap_c > 0 && !aligned16(plan_c)) || (cap_w > 0 && !aligned8(plan_w)))
     return KVC_EINVAL;
   kvc::PlanPrefillArgs a{};
   a.seq_lens = seq_lens;
@@ -93,7 +94,7 @@ KVC_EXPORT int kvc_plan_prefill_swa(int compress_ratio, int batch, int num_q, co
     return KVC_EINVAL;
   if (!aligned4(seq_lens) || !aligned4(extend_lens) || !aligned4(req_pool_indices) || !aligned4(counts))
     return KVC_EINVAL;
-  if ((cap_c > 0 && !aligned16(plan_c)) || (cap_w > 0 && (plan_w == nullptr || (reinterpret_cast<uintptr_t>(plan_w) & 7u))))
+  if ((cap_c > 0 && !aligned16(plan_c)) || (cap_w > 0 && !aligned8(plan_w)))
     return KVC_EINVAL;
   if (status != nullptr && !aligned4(status)) return KVC_EINVAL;
   kvc::PlanPrefillArgs a{};
@@ -147,7 +148,7 @@ KVC_EXPORT int kvc_plan_prefill_page4(int batch, int num_q, const int32_t* seq_l
   if (!aligned4(seq_lens) || !aligned4(extend_lens) || !aligned4(page_index) || !aligned16(bundle) ||
       !aligned4(counts))
     return KVC_EINVAL;
-  if ((cap_c > 0 && !aligned16(plan_c)) || (cap_w > 0 && (plan_w == nullptr || (reinterpret_cast<uintptr_t>(plan_w) & 7u))))
+  if ((cap_c > 0 && !aligned16(plan_c)) || (cap_w > 0 && !aligned8(plan_w)))
     return KVC_EINVAL;
   if (status != nullptr && !aligned4(status)) return KVC_EINVAL;
   kvc::PlanPrefillArgs a{};
@@ -190,7 +191,7 @@ KVC_EXPORT int kvc_write(int compress_ratio, kvc_dtype dtype, int head_dim, void
   if (!ratio_ok(compress_ratio) || !dtype_ok(dtype) || !hd_ok(head_dim) || !rows_ok(num_state_rows)) return KVC_EINVAL;
   if (num_q < 0 || num_q >= KVC_MAX_TOKENS || cap_w < 0 || !aligned4(counts)) return KVC_EINVAL;
   if (cap_w == 0) return KVC_OK;
-  if (!aligned16(state) || !aligned16(input) || plan_w == nullptr || (reinterpret_cast<uintptr_t>(plan_w) & 7u))
+  if (!aligned16(state) || !aligned16(input) || !aligned8(plan_w))
     return KVC_EINVAL;
   const int esize = dtype == KVC_BF16 ? 2 : 4;
   const int row_vecs = (compress_ratio == 4 ? 4 : 2) * head_dim * esize / 16;
@@ -369,7 +370,7 @@ KVC_EXPORT int kvc_write_c128_online(kvc_dtype dtype, int head_dim, float* state
   if (!online_common_ok(dtype, head_dim, state, num_slots, input, ape)) return KVC_EINVAL;
   if (num_q < 0 || num_q >= KVC_MAX_TOKENS || cap_w < 0 || !aligned4(counts)) return KVC_EINVAL;
   if (cap_w == 0) return KVC_OK;
-  if (plan_w == nullptr || (reinterpret_cast<uintptr_t>(plan_w) & 7u)) return KVC_EINVAL;
+  if (!aligned8(plan_w)) return KVC_EINVAL;
   kvc::OnlineArgs a{state, input, ape, nullptr, plan_w, nullptr, counts, nullptr, nullptr, num_slots, num_q, cap_w};
   return status_of(kvc::launch_write_online(dtype, head_dim, a, as_stream(stream)));
 }
