@@ -131,3 +131,39 @@ def test_host_argument_checks_reject_without_enqueueing(lib):
     # empty work is a no-op that needs no device
     assert lib.kvc_compress_c4(1, 128, p, 8, p, 1, p, p, 0, p, p, None) == kvc.KVC_OK
     assert lib.kvc_write(128, 1, 512, p, 8, p, 1, p, 0, p, None) == kvc.KVC_OK
+
+
+def test_binding_rejects_host_tensors():
+    """A host tensor's pointer must never reach a kernel: every wrapper checks that its tensors are
+    contiguous device tensors before calling the library (the check runs before any HIP call)."""
+    torch = pytest.importorskip("torch")
+    kvc.load(build_if_missing=True)
+    i32 = lambda n: torch.zeros(n, dtype=torch.int32)  # noqa: E731
+    hd = 128
+    st4, in4 = torch.zeros((8, 4 * hd)), torch.zeros((8, 4 * hd))
+    st128, in128 = torch.zeros((128, 2 * hd)), torch.zeros((128, 2 * hd))
+    pc, pw, pd = (torch.zeros((4, kvc.C_BYTES), dtype=torch.uint8), torch.zeros((4, kvc.W_BYTES), dtype=torch.uint8),
+                  torch.zeros((1, kvc.D_BYTES), dtype=torch.uint8))
+    ape4, ape128, out = torch.zeros((8, hd)), torch.zeros((128, hd)), torch.zeros((4, hd))
+    wgt, cache = torch.ones(hd), torch.zeros((4, hd), dtype=torch.bfloat16)
+    slots = torch.zeros((1, 3, hd))
+    calls = [
+        lambda: kvc.plan_prefill(4, i32(1), i32(1), i32(1), 8, 1, pc, pw, i32(4)),
+        lambda: kvc.plan_decode(4, i32(1), i32(1), 8, pd),
+        lambda: kvc.plan_prefill_page4(i32(1), i32(1), i32(1), torch.zeros((1, 4), dtype=torch.int32), 8, 1, pc, pw,
+                                       i32(4)),
+        lambda: kvc.plan_decode_page4(i32(1), i32(1), i32(1), 8, pd),
+        lambda: kvc.write(4, hd, st4, in4, pw, i32(4)),
+        lambda: kvc.compress_c4(hd, st4, in4, ape4, pc, i32(4), out),
+        lambda: kvc.compress_c128(hd, st128, in128, ape128, pc, i32(4), out),
+        lambda: kvc.decode_c4(hd, st4, in4, ape4, pd, out),
+        lambda: kvc.decode_c128(hd, st128, in128, ape128, pd, out),
+        lambda: kvc.norm_rope_store_prefill(4, out, pc, i32(4), wgt, 1e-6, None, i32(4), cache),
+        lambda: kvc.compress_norm_rope_store(4, hd, st4, in4, ape4, pc, i32(4), wgt, 1e-6, None, i32(4), cache),
+        lambda: kvc.compress_c128_online(hd, slots, in128, ape128, pc, i32(4), out),
+        lambda: kvc.write_c128_online(hd, slots, in128, ape128, pw, i32(4)),
+        lambda: kvc.decode_c128_online(hd, slots, in128, ape128, pd, out),
+    ]
+    for call in calls:
+        with pytest.raises(kvc.KvcError, match="CUDA"):
+            call()
