@@ -202,6 +202,10 @@ def plan_decode_swa(cr, seq_lens, req_pool_indices, req_to_token, full_to_swa, s
     return pd, int(status[0])
 
 
+_GUARD_ROWS = 16
+_GUARD = -3.0e300  # a value no stored row holds
+
+
 def _store(fn, cr, rows, plan, n, norm_weight, eps, freqs_cis, out_loc, cache):
     rows = np.ascontiguousarray(rows, dtype=np.float32)
     hd = rows.shape[1]
@@ -210,11 +214,17 @@ def _store(fn, cr, rows, plan, n, norm_weight, eps, freqs_cis, out_loc, cache):
     rope_dim = 0 if freqs.size == 0 else freqs.shape[1] * 2
     freqs = freqs.reshape(-1, max(rope_dim, 1)) if freqs.size else freqs
     loc = _i32(out_loc)
-    cache = np.array(cache, dtype=np.float64, copy=True, order="C")
+    cache = np.asarray(cache, dtype=np.float64)
+    rows_c = cache.shape[0]
+    # guard rows after the cache: a store past its last row shows up here instead of in other memory
+    buf = np.full((rows_c + _GUARD_ROWS, hd), _GUARD)
+    buf[:rows_c] = cache
     plan = np.ascontiguousarray(plan, dtype=np.uint8)
     err = fn(cr, hd, rope_dim, _ptr(rows), _ptr(plan), int(n), _ptr(w), float(eps), _ptr(freqs),
-             freqs.shape[0] if freqs.size else 0, _ptr(loc), loc.size, _ptr(cache), cache.shape[0])
-    return cache, err
+             freqs.shape[0] if freqs.size else 0, _ptr(loc), loc.size, _ptr(buf), rows_c)
+    if not np.all(buf[rows_c:] == _GUARD):
+        raise AssertionError("the store wrote past the last cache row")
+    return buf[:rows_c], err
 
 
 def store_prefill(cr, rows, plan_c, num_c, norm_weight, eps, freqs_cis, out_loc, cache):

@@ -202,6 +202,15 @@ def test_errors_skip_only_the_bad_record():
                                       np.full((4, hd), np.nan))
     assert err == ERR_RECORD
     assert np.isfinite(cache[0]).all() and np.isnan(cache[1:]).all()
+    # each kind of bad record alone, so that no other record sets the error bit: a location one
+    # past the last cache row, a ragged id one past out_loc, a position one past the table
+    for recs, out_loc in (([(8, 0, 0, 0, 0), (12, 1, 0, 0, 0)], [0, 4]),
+                          ([(8, 0, 0, 0, 0), (12, 2, 0, 0, 0)], [0, 1]),
+                          ([(8, 0, 0, 0, 0), (14, 1, 0, 0, 0)], [0, 1])):
+        cache, err = oracle.store_prefill(4, rows, _pack_c(recs), 2, w, 0.0, freqs, np.array(out_loc, np.int32),
+                                          np.full((4, hd), np.nan))
+        assert err == ERR_RECORD, (recs, out_loc)
+        assert np.isfinite(cache[0]).all() and np.isnan(cache[1:]).all(), (recs, out_loc)
     # without rotated channels the position is not looked up
     cache, err = oracle.store_prefill(4, rows[:, :6], _pack_c([(64, 0, 0, 0, 0)]), 1, w[:6], 0.0,
                                       np.zeros((0, 0, 2), np.float32), np.array([1], np.int32),
