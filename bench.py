@@ -428,6 +428,13 @@ def main():
     online_launches = [("compress_c128_online", OP128.compress), ("write_c128_online", OP128.write),
                        ("decode_c128_online", OD128.decode)]
 
+    # the uniform-extend variant of the mixed batch (every extend 2, the multi-token-prediction shape):
+    # the planner's equal-extend path, timed in the breakdown pass only
+    M4, M128 = Prefill(wl.config5(4, uniform_extend=2)), Prefill(wl.config5(128, uniform_extend=2))
+    mtp_launches = [("plan_prefill c4 e=2", M4.plan), ("compress_c4 e=2", M4.compress), ("write c4 e=2", M4.write),
+                    ("plan_prefill c128 e=2", M128.plan), ("compress_c128 e=2", M128.compress),
+                    ("write c128 e=2", M128.write)]
+
     ST4, ST128 = Store(P4, p4.num_q, 3004), Store(P128, p128.num_q, 3128)
     SD4S, SD128S = Store(D4, d4.B, 3003), Store(D128, d128.B, 3129)
     store_launches = [("compress_c4_norm_rope_store", ST4.fused), ("norm_rope_store_prefill c4", ST4.prefill),
@@ -477,7 +484,7 @@ def main():
 
     # per-kernel breakdown (separate, untimed pass; events around every launch), with the
     # SWA-paged planners of the same requests and the store step after the pool
-    extra = swa_launches + store_launches + online_launches
+    extra = swa_launches + store_launches + online_launches + mtp_launches
     bev = {name: [] for name, _ in launches + extra}
     for _ in range(5):
         for name, f in launches + extra:
@@ -518,7 +525,7 @@ def main():
     decode_us["graph"] = round(per_call_ms(graph.replay) * 1e3, 2)
 
     # sanity: no device-side errors, plans as sized
-    for P in (P4, P128):
+    for P in (P4, P128, M4, M128):
         c = P.counts.cpu().tolist()
         assert c[2] == 0 and c[3] == 0, ("device error", c)
     for D in (D4, D128):
