@@ -246,6 +246,38 @@ def test_large_magnitude_scores(gpu, cr, dtype):
     assert_pool_close(got, ref, dtype, "decode, large scores")
 
 
+@pytest.mark.parametrize("cr,s,e,expect", [
+    (4, [2, 7], [2, 2], (0, 4)),   # no row closes: no C records, the tokens are written
+    (128, [128], [128], (1, 0)),   # the chunk closes exactly one block: one row, nothing written
+    (4, [1], [1], (0, 1)),         # a single token
+])
+def test_empty_record_sets(gpu, cr, s, e, expect):
+    """Chunks whose C or W set is empty, planned with capacities equal to the counts (so zero-size
+    plan buffers): the planner, the pool and the write match the oracle and touch nothing else."""
+    hd, B, num_q = 128, len(s), int(sum(e))
+    w = wl.prefill_workload("empty", cr, hd, "f32", s, e, list(range(B)), B, [77, cr])
+    cap_c, cap_w = expect
+    say("empty record sets cr=%d s=%s e=%s" % (cr, s, e))
+    g = gpu.plan_prefill(cr, w.seq_lens, w.extend_lens, w.state_index, w.num_state_rows, num_q, cap_c, cap_w)
+    o = oracle.plan_prefill(cr, w.seq_lens, w.extend_lens, w.state_index, w.num_state_rows, num_q, cap_c, cap_w)
+    _plans_equal(g, o)
+    pc, pw, counts = o
+    assert tuple(counts[:2]) == expect and counts[2] == 0
+    got, gerr = gpu.compress(cr, hd, w.state, w.input, w.ape, pc, counts[0])
+    ref, err = oracle.compress(cr, hd, w.state, w.input, w.ape, pc, counts[0])
+    assert gerr == err == 0
+    if counts[0] == 0:
+        assert got.shape[0] == 0
+    else:
+        assert_pool_close(got, ref, "f32", "compress")
+    st_o = w.state.copy()
+    assert oracle.write(cr, hd, st_o, w.input, pw, counts[1]) == 0
+    st_g = gpu.write(cr, hd, w.state, w.input, pw, counts[1])
+    assert np.array_equal(st_g.view(np.uint8), st_o.view(np.uint8))
+    if counts[1] == 0:
+        assert np.array_equal(st_g.view(np.uint8), w.state.view(np.uint8)), "a write with no records changed the state"
+
+
 def test_first_block_never_reads_masked_rows(gpu):
     """Block 0 of ratio 4: the overlap entries precede the sequence and must not be loaded.
     The state is NaN and the ragged rows before the request hold +-inf; a read of either
