@@ -278,6 +278,34 @@ def test_empty_record_sets(gpu, cr, s, e, expect):
         assert np.array_equal(st_g.view(np.uint8), w.state.view(np.uint8)), "a write with no records changed the state"
 
 
+def test_decode_maximum_batch(gpu):
+    """Ratio-4 decode at the largest batch the ABI takes (65 536 requests, hd 128 bf16, a 512 MiB
+    state): every pooled row against the oracle, the whole state bit for bit."""
+    rng = np.random.default_rng(65536)
+    B, hd, cr = 65536, 128, 4
+    R = 4 * hd
+
+    def bf16_bits(n):  # finite bf16 values in [0.5, 1) with random signs, drawn quickly
+        return (rng.integers(0, 1 << 7, size=n, dtype=np.uint16) | np.uint16(0x3F00)
+                | (rng.integers(0, 2, size=n, dtype=np.uint16) << np.uint16(15))).astype(np.uint16)
+
+    s = rng.integers(1, 4097, size=B).astype(np.int32)
+    idx = rng.permutation(B).astype(np.int32)
+    state = bf16_bits(B * 8 * R).reshape(B * 8, R)
+    inp = bf16_bits(B * R).reshape(B, R)
+    ape = wl.to_bf16_bits((0.1 * rng.standard_normal((8, hd))).astype(np.float32))
+    pd, status = oracle.plan_decode(cr, s, idx, B * 8)
+    assert status == 0
+    say("decode maximum batch B=%d boundaries=%d" % (B, int((s % cr == 0).sum())))
+    st_o = state.copy()
+    ref, err = oracle.decode(cr, hd, st_o, inp, ape, pd)
+    got, st_g, gerr = gpu.decode(cr, hd, state, inp, ape, pd)
+    assert err == gerr == 0
+    assert_pool_close(got, ref, "bf16", "decode at the maximum batch")
+    assert np.all(got[s % cr != 0] == 0.0)
+    assert np.array_equal(st_g, st_o), "state differs after decode"
+
+
 def test_first_block_never_reads_masked_rows(gpu):
     """Block 0 of ratio 4: the overlap entries precede the sequence and must not be loaded.
     The state is NaN and the ragged rows before the request hold +-inf; a read of either
