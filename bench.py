@@ -166,6 +166,40 @@ def algorithmic_bytes_write(cr, hd, esize, num_w):
     return num_w * (2 * R * esize + 8)
 
 
+def algorithmic_bytes_store_decode(hd, rope_dim, seq_lens, cr):
+    """Bytes the standalone decode store must move: every record; for a request that closes a block
+    the fp32 row in, the bf16 row out, its out_loc entry and rotary row; the norm weight once."""
+    boundary = int((np.asarray(seq_lens, np.int64) % cr == 0).sum())
+    return len(seq_lens) * 16 + boundary * (hd * 4 + hd * 2 + 4 + rope_dim * 4) + hd * 4
+
+
+def algorithmic_bytes_fused_decode_store(hd, esize, seq_lens, rope_dim):
+    """Ratio-4 decode with the store fused: the decode's bytes with the boundary rows stored as bf16
+    (plus out_loc and the rotary row) instead of every fp32 output row."""
+    s = np.asarray(seq_lens, np.int64)
+    boundary = s % 4 == 0
+    others = np.where(s == 4, 3, 7)
+    per = 2 * 4 * hd * esize + 16 + np.where(boundary, others * 2 * hd * esize + hd * 2 + 4 + rope_dim * 4, 0)
+    return int(per.sum()) + 8 * hd * esize + hd * 4
+
+
+def algorithmic_bytes_online(hd, esize, blen_of_rows, write_runs, decode_seq_lens):
+    """The online ratio-128 calls.  Pool: per row the (128 - buffer_len) input entries, the slot's
+    partial when buffer_len > 0, the fp32 row and the record; ape once.  State update: per run of n
+    tokens the n rows and records, the old slot when the run continues a block, the new slot; ape
+    once.  Decode: per request its row and record, the old slot unless it starts a block, the new
+    slot and the fp32 output row; ape once."""
+    slot = 3 * hd * 4
+    blen = np.asarray(blen_of_rows, np.int64)
+    pool = int(((128 - blen) * 2 * hd * esize + np.where(blen > 0, slot, 0) + hd * 4 + 16).sum())
+    write = sum(n * (2 * hd * esize + 8) + (slot if cont else 0) + slot for n, cont in write_runs)
+    s = np.asarray(decode_seq_lens, np.int64)
+    fresh = (s - 1) % 128 == 0
+    dec = int((2 * hd * esize + 16 + np.where(fresh, 0, slot) + slot + hd * 4).sum())
+    ape = 128 * hd * esize
+    return pool + ape, write + ape, dec + ape
+
+
 def sweep(torch, kvc, dev, P4, P128, to_dev):
     """Extra, labelled results: kernel time and algorithmic GB/s as the work grows (prefill: the first
     k requests of the mixed batch; decode: batches with device-generated inputs), and the two compress
@@ -583,6 +617,45 @@ def main():
         step_rows["decode_c%d" % cr] = row_entry(
             "decode_c%d" % cr, algorithmic_bytes_decode(cr, w.hd, w.esize, w.seq_lens), "latency")
 
+    # the launches of the "next" rows against their bounds (breakdown-pass times): the store after the
+    # pool, the online ratio-128 state, and the planners of the SWA-paged and Page4Align mappings
+    f_rows = {}
+    for cr, P, w in ((4, P4, p4), (128, P128, p128)):
+        c = P.counts.cpu().tolist()
+        seqs = P.plan_c[: c[0]].cpu().numpy().view("<u4").reshape(-1, 4)[:, 0].astype(np.int64)
+        f_rows["compress_c%d_norm_rope_store" % cr] = row_entry(
+            "compress_c%d_norm_rope_store" % cr, algorithmic_bytes_fused_store(cr, w.hd, w.esize, seqs, 64), "hbm")
+        sb = algorithmic_bytes_store(w.hd, 64, c[0])  # 105 MB for ratio 4, 3 MB (latency-bound) for 128
+        f_rows["norm_rope_store_prefill c%d" % cr] = row_entry("norm_rope_store_prefill c%d" % cr, sb,
+                                                               "hbm" if sb > 50e6 else "latency")
+    for cr, w in ((4, d4), (128, d128)):
+        f_rows["norm_rope_store_decode c%d" % cr] = row_entry(
+            "norm_rope_store_decode c%d" % cr, algorithmic_bytes_store_decode(w.hd, 64, w.seq_lens, cr), "latency")
+    f_rows["decode_c4_norm_rope_store"] = row_entry(
+        "decode_c4_norm_rope_store", algorithmic_bytes_fused_decode_store(d4.hd, d4.esize, d4.seq_lens, 64), "latency")
+    c = P128.counts.cpu().tolist()
+    rec_c = P128.plan_c[: c[0]].cpu().numpy().view("<u4").reshape(-1, 4)
+    blen = (rec_c[:, 1] >> 24).astype(np.int64)
+    rec_w = P128.plan_w[: c[1]].cpu().numpy().view("<u4").reshape(-1, 2).astype(np.int64)
+    runs, k = [], 0
+    while k < len(rec_w):  # a run: consecutive records of one slot and consecutive positions
+        j = k + 1
+        while (j < len(rec_w) and rec_w[j, 1] // 128 == rec_w[k, 1] // 128
+               and rec_w[j, 1] - rec_w[k, 1] == j - k and rec_w[j, 0] - rec_w[k, 0] == j - k):
+            j += 1
+        runs.append((j - k, rec_w[k, 1] % 128 > 0))
+        k = j
+    ob = algorithmic_bytes_online(p128.hd, p128.esize, blen, runs, d128.seq_lens)
+    f_rows["compress_c128_online"] = row_entry("compress_c128_online", ob[0], "hbm")
+    f_rows["write_c128_online"] = row_entry("write_c128_online", ob[1], "latency")
+    f_rows["decode_c128_online"] = row_entry("decode_c128_online", ob[2], "latency")
+    for name, P, w in (("plan_prefill_swa c4", SP4, p4), ("plan_prefill_swa c128", SP128, p128),
+                       ("plan_prefill_page4", PG4, p4)):
+        f_rows[name] = row_entry(name, algorithmic_bytes_plan_prefill(w.B, P.pc.shape[0], P.pw.shape[0]), "latency")
+    f_rows["plan_decode_swa c4"] = row_entry("plan_decode_swa c4", algorithmic_bytes_plan_decode(d4.B), "latency")
+    f_rows["plan_decode_page4"] = row_entry("plan_decode_page4", algorithmic_bytes_plan_decode(d4.B) + 4 * d4.B,
+                                            "latency")
+
     tokens = p4.num_q + p128.num_q + d4.B + d128.B
     value = tokens / (ms_per_step * 1e-3)
 
@@ -620,6 +693,7 @@ def main():
         },
         "kernels_us": kernels_us,
         "step_rows": step_rows,
+        "f_rows": f_rows,
         "decode_step_us": decode_us,
         "store_step": store_step,
         "wall_s_timed": round(wall, 3),
