@@ -2,7 +2,10 @@
 // plan_compress_prefill_kernel0 / plan_compress_prefill_legacy with the
 // per-request translation of plan_compress_prefill_legacy_kernel, the
 // SWA-paged translation of plan_compress_prefill_kernel_1, and
-// plan_compress_decode_legacy_kernel / plan_compress_decode_kernel).
+// plan_compress_decode_legacy_kernel / plan_compress_decode_kernel; and the
+// ratio-4 mapping onto caller-allocated 4-row pages of the c4.cuh page,
+// PageMode::Page4Align with C4IndexBundle).  The mapping is a template
+// parameter: per-request ring or page, SWA pages, or 4-row pages.
 //
 // Prefill plan, one launch, no host sync, no scratch memory:
 //   stage A  every workgroup loads the <= 1024 requests (4 per thread), checks
@@ -22,7 +25,8 @@
 //                              multi-token-prediction shape), one thread per
 //                              token: request k / E, offset k % E, no search;
 //            in SWA mode each record's rows are looked up through
-//            req_to_token and full_to_swa as it is written;
+//            req_to_token and full_to_swa as it is written; in page-4 mode
+//            they come from the request's page index and bundle;
 //   stage D  [num_c, cap_c) and [num_w, cap_w) are filled with 0xFF records.
 // Every workgroup repeats stages A/B (12 KiB of L2-resident loads), which is
 // cheaper than a second launch and needs no workspace; workgroup 0 writes
