@@ -42,20 +42,23 @@ __global__ __launch_bounds__(kC4Threads) void compress_c4_kernel(CompressArgs a)
   const int64_t row = (int64_t)blockIdx.x * kRows + threadIdx.x / kLanes;
   const int c = (threadIdx.x % kLanes) * V;
   typedef typename Elem<T>::storage E;
-  bool live = row < a.counts[0] && row < a.cap_c;
+  // The record and the count share one round trip: the record load is
+  // unconditional, clamped into the buffer (every index below cap_c holds a
+  // record: valid, padding or, after a planner error, stale), and only rows
+  // below counts[0] use theirs.
+  const kvc_plan_c rec = load_plan_c(a.plan_c + (row < a.cap_c ? row : a.cap_c - 1));
+  bool live = (row < a.cap_c) & (row < a.counts[0]) & !plan_c_invalid(rec);
   float res[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) res[v] = 0.f;
   int32_t pos = 0, loc = -1;  // positions < 2^24, cache rows <= INT32_MAX
   StoreOperands<V> ops;
   if (live) {
-    const kvc_plan_c rec = load_plan_c(a.plan_c + row);
     const int64_t ragged = rec.ragged_blen & 0xFFFFFFu;
     const int blen = (int)(rec.ragged_blen >> 24);
     const int64_t rp0 = rec.read_page_0, rp1 = rec.read_page_1;
     const bool first_block = rec.seq_len == 4u;
-    live = !plan_c_invalid(rec);
-    if (live && !c4_record_ok(ragged, blen, rp0, rp1, first_block ? 4 : 0, a.num_q, a.num_state_rows)) {
+    if (!c4_record_ok(ragged, blen, rp0, rp1, first_block ? 4 : 0, a.num_q, a.num_state_rows)) {
       if (c == 0) atomicOr(a.counts + 3, KVC_DERR_RECORD);
       live = false;
     }
@@ -119,10 +122,9 @@ __global__ __launch_bounds__(kC128Threads) void compress_c128_kernel(CompressArg
   typedef typename Elem<T>::storage E;
   typedef C128Pool<T, HD, kC128Threads> Pool;
   __shared__ float lds[Pool::kLdsFloats];
-  const int64_t row = blockIdx.x;
-  if (row >= a.counts[0] || row >= a.cap_c) return;
-  const kvc_plan_c rec = load_plan_c(a.plan_c + row);
-  if (plan_c_invalid(rec)) return;
+  const int64_t row = blockIdx.x;  // < cap_c (the grid)
+  const kvc_plan_c rec = load_plan_c(a.plan_c + row);  // in flight with the count (as in compress_c4)
+  if ((row >= a.counts[0]) | plan_c_invalid(rec)) return;
   const int64_t ragged = rec.ragged_blen & 0xFFFFFFu;
   const int blen = (int)(rec.ragged_blen >> 24);
   const int64_t rp0 = rec.read_page_0;
@@ -163,18 +165,21 @@ __global__ __launch_bounds__(kC128Threads) void compress_c128_kernel(CompressArg
 constexpr int kWriteRowsPerBlock = kThreads / kWave;
 
 // One wave per record.  PER = 16-byte vectors per lane (a row holds up to
-// 64 * PER vectors); the input row is read once (streaming load) and stored
-// to the state with ordinary stores, since the next chunk reads it back.
+// 64 * PER vectors); the input row is read once and stored to the state, both
+// streaming: the row is read back only by a later chunk's kernels, and a
+// cached store would leave dirty lines that slow the next streaming kernel.
 template <int PER>
 __global__ __launch_bounds__(kThreads) void write_kernel(WriteArgs a) {
   const int64_t k = (int64_t)blockIdx.x * kWriteRowsPerBlock + threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
-  if (k >= a.counts[1] || k >= a.cap_w) return;
-  const uint2 rec = *reinterpret_cast<const uint2*>(a.plan_w + k);
-  if (rec.x == 0xFFFFFFFFu) return;
+  // the record (clamped into the buffer, as in compress_c4) is in flight with the count
+  const u32x2 rec = load8(a.plan_w + (k < a.cap_w ? k : a.cap_w - 1));
+  __builtin_amdgcn_sched_barrier(0);  // keep the count's load (and its wait) after this one
   const int64_t ragged = rec.x;
   const int64_t loc = (int32_t)rec.y;
-  if (ragged >= a.num_q || loc < 0 || loc >= a.num_state_rows) {
+  const bool bad = (ragged >= a.num_q) | (loc < 0) | (loc >= a.num_state_rows);
+  if ((k >= a.cap_w) | (k >= a.counts[1]) | (rec.x == 0xFFFFFFFFu)) return;
+  if (bad) {
     if (lane == 0) atomicOr(a.counts + 3, KVC_DERR_RECORD);
     return;
   }

@@ -17,6 +17,7 @@ constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct Bf16 {};  // tag type: bf16 stored as uint16_t bit patterns
 
@@ -35,6 +36,7 @@ struct Elem<Bf16> {
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ u32x2 load8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
 
 // Streaming (non-temporal) 16-byte access for data touched once per launch: the
 // line is not kept in L2 / the last-level cache, so a stream of kv/score rows
