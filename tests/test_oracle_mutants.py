@@ -5,6 +5,7 @@ term, an off-by-one, a wrong sign, a swapped operand or page), builds it with
 gcc on the CPU, and runs the pin suite against it in a subprocess.  The suite
 must fail for every mutant; the unmodified oracle passes it (test_oracle_pins).
 """
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -121,21 +122,39 @@ def _plant(src, old, new, nth):
     return src[:at] + new + src[at + len(old):]
 
 
-@pytest.mark.parametrize("mutant", MUTANTS, ids=[m[0].replace(" ", "_") for m in MUTANTS])
-def test_pins_catch_mutant(tmp_path, mutant):
+PIN_FILES = ["test_oracle_pins.py", "test_oracle_swa_pins.py", "test_oracle_store_pins.py",
+             "test_oracle_online_pins.py", "test_oracle_page4_pins.py"]
+
+
+def _run_pins_against(mutant, workdir):
+    """Build the mutant oracle and run the pin suite on it; returns (exit code, output tail)."""
     name, old, new = mutant[:3]
     nth = mutant[3] if len(mutant) > 3 else None
-    src = open(SRC).read()
-    mutated = tmp_path / "kvc_oracle_mutant.c"
-    mutated.write_text(_plant(src, old, new, nth))
-    lib = tmp_path / "libkvc_oracle_mutant.so"
-    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", str(lib), str(mutated), "-lm"])
-    env = dict(os.environ, KVC_ORACLE_LIB=str(lib))
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_swa_pins.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_store_pins.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_online_pins.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_page4_pins.py")],
+    d = os.path.join(workdir, name.replace(" ", "_").replace("'", ""))
+    os.makedirs(d)
+    mutated = os.path.join(d, "kvc_oracle_mutant.c")
+    with open(mutated, "w") as f:
+        f.write(_plant(open(SRC).read(), old, new, nth))
+    lib = os.path.join(d, "libkvc_oracle_mutant.so")
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", lib, mutated, "-lm"])
+    env = dict(os.environ, KVC_ORACLE_LIB=lib, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider"] +
+                       [os.path.join(ROOT, "tests", f) for f in PIN_FILES],
                        cwd=ROOT, env=env, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, timeout=600)
-    assert r.returncode != 0, "pins did not catch mutant '%s':\n%s" % (name, r.stdout.decode()[-2000:])
+    return r.returncode, r.stdout.decode(errors="replace")[-2000:]
+
+
+@pytest.fixture(scope="module")
+def pin_runs(tmp_path_factory):
+    """Every mutant's pin run, done once and in parallel (each run is a separate process)."""
+    workdir = str(tmp_path_factory.mktemp("mutants"))
+    workers = max(1, min(8, len(os.sched_getaffinity(0))))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        runs = list(ex.map(lambda m: _run_pins_against(m, workdir), MUTANTS))
+    return {m[0]: run for m, run in zip(MUTANTS, runs)}
+
+
+@pytest.mark.parametrize("mutant", MUTANTS, ids=[m[0].replace(" ", "_") for m in MUTANTS])
+def test_pins_catch_mutant(pin_runs, mutant):
+    code, tail = pin_runs[mutant[0]]
+    assert code != 0, "pins did not catch mutant '%s':\n%s" % (mutant[0], tail)
