@@ -154,8 +154,9 @@ def test_plan_decode(gpu):
 # write / compress / decode on oracle-built plans
 # --------------------------------------------------------------------------
 
-SHAPES = [(4, 128, "f32"), (4, 512, "bf16"), (4, 256, "bf16"), (4, 128, "bf16"), (4, 512, "f32"),
-          (128, 512, "bf16"), (128, 128, "f32"), (128, 256, "f32"), (128, 128, "bf16"), (128, 512, "f32")]
+SHAPES = [(4, 128, "f32"), (4, 512, "bf16"), (4, 256, "bf16"), (4, 128, "bf16"), (4, 512, "f32"), (4, 256, "f32"),
+          (128, 512, "bf16"), (128, 128, "f32"), (128, 256, "f32"), (128, 128, "bf16"), (128, 512, "f32"),
+          (128, 256, "bf16")]
 
 
 @pytest.mark.parametrize("cr,hd,dtype", SHAPES)
