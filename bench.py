@@ -289,8 +289,8 @@ def main():
 
     t0 = time.time()
     log("generating workloads ...")
-    p4, p128 = wl.config5(4), wl.config5(128)
-    d4, d128 = wl.config3(), wl.config4()
+    p4, p128 = wl.mixed_prefill(4), wl.mixed_prefill(128)
+    d4, d128 = wl.c4_decode_b256(), wl.c128_decode_b1024()
     log("workloads ready in %.1f s: prefill num_q=%d, decode B=%d/%d" % (time.time() - t0, p4.num_q, d4.B, d128.B))
 
     class Prefill:
@@ -464,7 +464,7 @@ def main():
 
     # the uniform-extend variant of the mixed batch (every extend 2, the multi-token-prediction shape):
     # the planner's equal-extend path, timed in the breakdown pass only
-    M4, M128 = Prefill(wl.config5(4, uniform_extend=2)), Prefill(wl.config5(128, uniform_extend=2))
+    M4, M128 = Prefill(wl.mixed_prefill(4, uniform_extend=2)), Prefill(wl.mixed_prefill(128, uniform_extend=2))
     mtp_launches = [("plan_prefill c4 e=2", M4.plan), ("compress_c4 e=2", M4.compress), ("write c4 e=2", M4.write),
                     ("plan_prefill c128 e=2", M128.plan), ("compress_c128 e=2", M128.compress),
                     ("write c128 e=2", M128.write)]

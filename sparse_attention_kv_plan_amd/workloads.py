@@ -162,17 +162,18 @@ def decode_workload(name, cr, hd, dtype, seq_lens, state_index, num_slots, tenso
 
 
 # --------------------------------------------------------------------------
-# the five named workloads
+# the named workloads: small ratio-4 prefill, ratio-128 prefill, the two decode
+# batches and the mixed chunked prefill
 # --------------------------------------------------------------------------
 
-def config1(with_tensors=True):
+def c4_prefill_1x64(with_tensors=True):
     """c4 prefill, 1 request, prefix 0, extend 64, fp32, head_dim 128."""
     seed = 1001
     return prefill_workload("c4 prefill 1x64 fp32 hd128", 4, 128, "f32", [64], [64], [0], 1, [seed, 4],
                             with_tensors=with_tensors)
 
 
-def config2(with_tensors=True):
+def c128_prefill_4req(with_tensors=True):
     """c128 prefill, 4 requests, prefix 0, extends uniform in [1, 2048], bf16, head_dim 512."""
     seed = 1002
     rng = np.random.default_rng(seed)
@@ -182,7 +183,7 @@ def config2(with_tensors=True):
                             [seed, 128], score_sigma=2.0, with_tensors=with_tensors)
 
 
-def config3(with_tensors=True):
+def c4_decode_b256(with_tensors=True):
     """c4 decode, batch 256, prefixes uniform in [1, 32768], bf16, head_dim 512."""
     seed = 1003
     rng = np.random.default_rng(seed)
@@ -192,7 +193,7 @@ def config3(with_tensors=True):
                            with_tensors=with_tensors)
 
 
-def config4(with_tensors=True):
+def c128_decode_b1024(with_tensors=True):
     """c128 decode, batch 1024, prefixes uniform in [1, 65536], bf16, head_dim 512."""
     seed = 1004
     rng = np.random.default_rng(seed)
@@ -202,7 +203,7 @@ def config4(with_tensors=True):
                            with_tensors=with_tensors)
 
 
-def config5_lens(uniform_extend: Optional[int] = None):
+def mixed_prefill_lens(uniform_extend: Optional[int] = None):
     seed = 1005
     rng = np.random.default_rng(seed)
     prefix = rng.integers(0, 65536, size=64, endpoint=True)
@@ -214,11 +215,11 @@ def config5_lens(uniform_extend: Optional[int] = None):
     return prefix + e, e, idx
 
 
-def config5(cr, uniform_extend: Optional[int] = None, with_tensors=True):
+def mixed_prefill(cr, uniform_extend: Optional[int] = None, with_tensors=True):
     """Mixed chunked prefill, 64 requests, prefixes in [0, 65536], extends in [1, 4096] (or all equal).
 
     The same lengths and indices serve ratio 4 and ratio 128."""
-    s, e, idx = config5_lens(uniform_extend)
+    s, e, idx = mixed_prefill_lens(uniform_extend)
     tag = "mixed" if uniform_extend is None else "uniform e=%d" % uniform_extend
     seed = [1005, cr] if uniform_extend is None else [1005, cr, uniform_extend]
     return prefill_workload("c%d %s prefill 64 req bf16 hd512" % (cr, tag), cr, 512, "bf16", s, e, idx, 64,

@@ -177,7 +177,7 @@ def test_online_matches_paged_pool_full_size(gpu):
     rows before each request's chunk; the online pool equals the paged pool on the same windows,
     and the written slots equal the oracle's."""
     from tests.gpu_backend import to_dev
-    w = wl.config5(128)
+    w = wl.mixed_prefill(128)
     hd = w.hd
     say("online full size: B=%d num_q=%d" % (w.B, w.num_q))
     state_f = (w.state.astype(np.uint32) << 16).view(np.float32).astype(np.float64)

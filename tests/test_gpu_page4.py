@@ -127,7 +127,7 @@ def test_page4_chunked_prefill_then_decode(gpu, dtype, hd):
 
 def test_plan_prefill_page4_full_size(gpu):
     """The mixed prefill's 64 requests (125 792 tokens) with a page for every block."""
-    w = wl.config5(4, with_tensors=False)
+    w = wl.mixed_prefill(4, with_tensors=False)
     rng = np.random.default_rng(1400)
     n_pages = int((w.seq_lens // 4 + 3).sum())
     idx, bundle = _bundles(rng, w.seq_lens, w.extend_lens, n_pages)

@@ -91,7 +91,7 @@ def test_plan_prefill_fuzz(gpu, cr):
 @pytest.mark.parametrize("E", [1, 2, 3, 4, 5, 31, 32, 33])
 @pytest.mark.parametrize("cr", [4, 128])
 def test_plan_prefill_uniform_extend(gpu, cr, E):
-    s, e, idx = wl.config5_lens(uniform_extend=E)
+    s, e, idx = wl.mixed_prefill_lens(uniform_extend=E)
     num_q = int(e.sum())
     cap_c, cap_w = oracle.capacities(cr, 64, num_q)
     say("plan_prefill uniform cr=%d E=%d" % (cr, E))
@@ -411,13 +411,13 @@ def _run_prefill_pipeline(w):
             state.cpu().numpy())
 
 
-@pytest.mark.parametrize("name", ["config1", "config2", "config5_c4", "config5_c128", "config5_c4_mtp",
-                                  "config5_c128_mtp"])
+@pytest.mark.parametrize("name", ["c4_prefill_1x64", "c128_prefill_4req", "mixed_c4", "mixed_c128", "mixed_c4_e2",
+                                  "mixed_c128_e2"])
 def test_named_prefill_workloads(gpu, name):
-    w = {"config1": lambda: wl.config1(), "config2": lambda: wl.config2(),
-         "config5_c4": lambda: wl.config5(4), "config5_c128": lambda: wl.config5(128),
-         "config5_c4_mtp": lambda: wl.config5(4, uniform_extend=2),
-         "config5_c128_mtp": lambda: wl.config5(128, uniform_extend=2)}[name]()
+    w = {"c4_prefill_1x64": lambda: wl.c4_prefill_1x64(), "c128_prefill_4req": lambda: wl.c128_prefill_4req(),
+         "mixed_c4": lambda: wl.mixed_prefill(4), "mixed_c128": lambda: wl.mixed_prefill(128),
+         "mixed_c4_e2": lambda: wl.mixed_prefill(4, uniform_extend=2),
+         "mixed_c128_e2": lambda: wl.mixed_prefill(128, uniform_extend=2)}[name]()
     say("workload %s: B=%d num_q=%d" % (w.name, w.B, w.num_q))
     pc, pw, counts, out, state = _run_prefill_pipeline(w)
     cap_c, cap_w = oracle.capacities(w.cr, w.B, w.num_q)
@@ -432,14 +432,14 @@ def test_named_prefill_workloads(gpu, name):
     st_o = w.state.copy()
     oracle.write(w.cr, w.hd, st_o, w.input, opw, int(ocounts[1]))
     assert np.array_equal(state.view(np.uint8), st_o.view(np.uint8))
-    if name == "config1":
+    if name == "c4_prefill_1x64":
         assert n == 16 and counts[1] == 4
 
 
-@pytest.mark.parametrize("name", ["config3", "config4"])
+@pytest.mark.parametrize("name", ["c4_decode_b256", "c128_decode_b1024"])
 def test_named_decode_workloads(gpu, name):
     from tests.gpu_backend import to_dev
-    w = wl.config3() if name == "config3" else wl.config4()
+    w = wl.c4_decode_b256() if name == "c4_decode_b256" else wl.c128_decode_b1024()
     say("workload %s: B=%d boundaries=%d" % (w.name, w.B, int((w.seq_lens % w.cr == 0).sum())))
     plan_d = torch.empty((w.B, kvc.D_BYTES), dtype=torch.uint8, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")

@@ -258,7 +258,7 @@ def test_fused_store_record_errors(gpu, cr):
 @pytest.mark.parametrize("cr", [4, 128])
 def test_mixed_prefill_fused_store_full_size(gpu, cr):
     """64 requests, 125,792 tokens: GPU plan -> fused pool + store, against the oracle's pool + store."""
-    w = wl.config5(cr)
+    w = wl.mixed_prefill(cr)
     say("fused store workload %s: B=%d num_q=%d" % (w.name, w.B, w.num_q))
     plan_c, plan_w, counts = kvc.alloc_prefill_plan(cr, w.B, w.num_q)
     kvc.plan_prefill(cr, dev(w.seq_lens), dev(w.extend_lens), dev(w.state_index), w.num_state_rows, w.num_q,
@@ -281,9 +281,9 @@ def test_mixed_prefill_fused_store_full_size(gpu, cr):
     assert_store_close(_cache_host(cache), ref, w.name)
 
 
-@pytest.mark.parametrize("name", ["config3", "config4"])
+@pytest.mark.parametrize("name", ["c4_decode_b256", "c128_decode_b1024"])
 def test_decode_store_full_size(gpu, name):
-    w = wl.config3() if name == "config3" else wl.config4()
+    w = wl.c4_decode_b256() if name == "c4_decode_b256" else wl.c128_decode_b1024()
     say("decode store workload %s: B=%d" % (w.name, w.B))
     plan_d = torch.empty((w.B, kvc.D_BYTES), dtype=torch.uint8, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -364,7 +364,7 @@ def test_decode_c4_norm_rope_store_bad_target(gpu):
 def test_decode_c4_norm_rope_store_full_size(gpu):
     """256 requests, prefixes up to 32768: the fused step against decode + standalone store on the GPU
     and against the oracle."""
-    w = wl.config3()
+    w = wl.c4_decode_b256()
     say("fused decode store workload %s: B=%d" % (w.name, w.B))
     plan_d = torch.empty((w.B, kvc.D_BYTES), dtype=torch.uint8, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")

@@ -171,7 +171,7 @@ def test_swa_resume_at_page_boundary(gpu):
 @pytest.mark.parametrize("cr", [4, 128])
 def test_swa_plan_mixed_prefill_full_size(gpu, cr):
     """The 64-request mixed prefill (about 126k tokens) planned through SWA tables."""
-    s, e, _ = wl.config5_lens()
+    s, e, _ = wl.mixed_prefill_lens()
     rng = np.random.default_rng(1005)
     stride = int(s.max())
     sps, ring = (128, 8) if cr == 4 else (128, 128)

@@ -144,17 +144,37 @@ def _run_pins_against(mutant, workdir):
     return r.returncode, r.stdout.decode(errors="replace")[-2000:]
 
 
+class _PinRuns:
+    """Pin runs of the mutants, one process each.  In a plain pytest run every mutant is started
+    at once on a pool of workers; under pytest-xdist (which already spreads the cases over its
+    workers) a case runs its own mutant when it asks for it."""
+
+    def __init__(self, workdir, prefetch):
+        self.workdir = workdir
+        workers = max(1, min(8, len(os.sched_getaffinity(0)))) if prefetch else 1
+        self.ex = concurrent.futures.ThreadPoolExecutor(max_workers=workers)
+        self.futures = {}
+        if prefetch:
+            for m in MUTANTS:
+                self._submit(m)
+
+    def _submit(self, mutant):
+        if mutant[0] not in self.futures:
+            self.futures[mutant[0]] = self.ex.submit(_run_pins_against, mutant, self.workdir)
+        return self.futures[mutant[0]]
+
+    def result(self, mutant):
+        return self._submit(mutant).result()
+
+
 @pytest.fixture(scope="module")
 def pin_runs(tmp_path_factory):
-    """Every mutant's pin run, done once and in parallel (each run is a separate process)."""
-    workdir = str(tmp_path_factory.mktemp("mutants"))
-    workers = max(1, min(8, len(os.sched_getaffinity(0))))
-    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
-        runs = list(ex.map(lambda m: _run_pins_against(m, workdir), MUTANTS))
-    return {m[0]: run for m, run in zip(MUTANTS, runs)}
+    runs = _PinRuns(str(tmp_path_factory.mktemp("mutants")), prefetch="PYTEST_XDIST_WORKER" not in os.environ)
+    yield runs
+    runs.ex.shutdown(wait=True, cancel_futures=True)
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=[m[0].replace(" ", "_") for m in MUTANTS])
 def test_pins_catch_mutant(pin_runs, mutant):
-    code, tail = pin_runs[mutant[0]]
+    code, tail = pin_runs.result(mutant)
     assert code != 0, "pins did not catch mutant '%s':\n%s" % (mutant[0], tail)
