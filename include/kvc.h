@@ -20,7 +20,10 @@
  * Conventions for every call
  * --------------------------
  *  - Pointers to tensors, plans, counts and status words are DEVICE pointers
- *    (HBM of the current HIP device), 16-byte aligned.  Sizes are host ints.
+ *    (HBM of the current HIP device).  Tensors and C / D record buffers are
+ *    16-byte aligned, W record buffers 8-byte, int32 arrays (lengths,
+ *    indices, counts, status words) 4-byte; a misaligned or null pointer is
+ *    KVC_EINVAL.  Sizes are host ints.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Every call only enqueues work on `stream`: it never synchronises, never
  *    allocates and keeps no pointer after it returns.  The caller owns every
