@@ -431,3 +431,80 @@ def test_store_paths_under_graph_capture(gpu):
         torch.cuda.synchronize()
         for got, want in zip((cache, state, d_state, counts, status), ref):
             assert torch.equal(got, want)
+
+
+STORE_FUZZ_CASES = 120
+
+
+def store_fuzz_case(rng):
+    """One random store case (the four calls in turn: standalone prefill and decode stores, the
+    fused prefill pools, the fused ratio-4 decode); checks the GPU against the oracle."""
+    kind = str(rng.choice(["prefill", "decode", "fused", "fused_decode"]))
+    cr = 4 if kind == "fused_decode" else int(rng.choice([4, 128]))
+    hd = int(rng.choice([128, 256, 512]))
+    dtype = str(rng.choice(["f32", "bf16"]))
+    rope_dim = int(rng.choice([0, 8, 64, hd // 2, hd]))
+    eps = float(rng.choice([1e-6, 1e-3, 0.0]))
+    label = "store fuzz %s cr=%d hd=%d %s rope=%d eps=%g" % (kind, cr, hd, dtype, rope_dim, eps)
+    if kind in ("prefill", "fused"):
+        B = int(rng.integers(1, 10))
+        w = wl.random_prefill(rng, cr, hd, dtype, B, prefix_hi=3 * W[cr], extend_lo=1,
+                              extend_hi=int(rng.choice([3 * W[cr], 700])), num_slots=B + 2)
+        cap_c, cap_w = oracle.capacities(cr, B, w.num_q)
+        pc, _, counts = oracle.plan_prefill(cr, w.seq_lens, w.extend_lens, w.state_index, w.num_state_rows,
+                                            w.num_q, cap_c + int(rng.integers(0, 3)), cap_w)
+        n = int(counts[0])
+        si = wl.store_inputs(rng, hd, rope_dim, int(w.seq_lens.max()) + 1, w.num_q, eps=eps)
+        if kind == "prefill":
+            rows = (rng.standard_normal((pc.shape[0], hd)) * rng.uniform(0.05, 4, size=(pc.shape[0], 1))).astype(
+                np.float32)
+        else:
+            pooled, err = oracle.compress(cr, hd, w.state, w.input, w.ape, pc, n)
+            assert err == 0
+            rows = np.zeros((pc.shape[0], hd), np.float32)
+            rows[:n] = pooled[:n]
+        say("%s B=%d num_c=%d" % (label, B, n))
+        ref, err = oracle.store_prefill(cr, rows, pc, n, si.norm_weight, si.eps, si.freqs_cis, si.out_loc,
+                                        np.full((si.num_cache_rows, hd), np.nan))
+        assert err == 0
+        wt, f, loc, cache = _store_tensors(si, hd)
+        cnt = dev(np.array([n, 0, 0, 0], np.int32))
+        if kind == "prefill":
+            kvc.norm_rope_store_prefill(cr, dev(rows), dev(pc), cnt, wt, si.eps, f, loc, cache)
+        else:
+            kvc.compress_norm_rope_store(cr, hd, dev(w.state), dev(w.input), dev(w.ape), dev(pc), cnt, wt, si.eps,
+                                         f, loc, cache)
+        assert int(cnt[3].item()) == 0, label
+        assert_store_close(_cache_host(cache), ref, label)
+        return
+    B = int(rng.integers(1, 400))
+    w = wl.random_decode(rng, cr, hd, dtype, B, prefix_hi=3 * cr, num_slots=B + 2)
+    pd, status = oracle.plan_decode(cr, w.seq_lens, w.state_index, w.num_state_rows)
+    assert status == 0
+    si = wl.store_inputs(rng, hd, rope_dim, int(w.seq_lens.max()) + 1, B, eps=eps)
+    say("%s B=%d boundaries=%d" % (label, B, int((w.seq_lens % cr == 0).sum())))
+    wt, f, loc, cache = _store_tensors(si, hd)
+    stt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    if kind == "decode":
+        rows = rng.standard_normal((B, hd)).astype(np.float32)
+        ref, err = oracle.store_decode(cr, rows, pd, si.norm_weight, si.eps, si.freqs_cis, si.out_loc,
+                                       np.full((si.num_cache_rows, hd), np.nan))
+        assert err == 0
+        kvc.norm_rope_store_decode(cr, dev(rows), dev(pd), wt, si.eps, f, loc, cache, stt)
+    else:
+        st_o = w.state.copy()
+        pooled, err = oracle.decode(4, hd, st_o, w.input, w.ape, pd)
+        assert err == 0
+        ref, err = oracle.store_decode(4, pooled.astype(np.float32), pd, si.norm_weight, si.eps, si.freqs_cis,
+                                       si.out_loc, np.full((si.num_cache_rows, hd), np.nan))
+        assert err == 0
+        state = dev(w.state)
+        kvc.decode_c4_norm_rope_store(hd, state, dev(w.input), dev(w.ape), dev(pd), wt, si.eps, f, loc, cache, stt)
+        assert np.array_equal(state.cpu().numpy().view(np.uint8), st_o.view(np.uint8)), label
+    assert int(stt.item()) == 0, label
+    assert_store_close(_cache_host(cache), ref, label)
+
+
+def test_random_store_cases(gpu):
+    for case in range(STORE_FUZZ_CASES):
+        store_fuzz_case(np.random.default_rng([2026, case]))
