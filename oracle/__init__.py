@@ -160,7 +160,7 @@ def decode(cr, hd, state, inp, ape, plan_d):
     assert sb == ib == ab
     pd = np.ascontiguousarray(plan_d, dtype=np.uint8)
     B = pd.shape[0]
-    out = np.zeros((B, hd), np.float64)
+    out = np.full((B, hd), np.nan, np.float64)  # every row is the oracle's own: pooled or zero
     err = _load().oracle_decode(cr, ib, hd, _ptr(state), state.shape[0], _ptr(inp), _ptr(ape), _ptr(pd), B,
                                 _ptr(out))
     return out, err

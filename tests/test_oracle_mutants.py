@@ -108,6 +108,35 @@ MUTANTS = [
      "put_u32(r + 4, as_u32((int32_t)(page * 4 + s % 4)));"),
     ("page4 decode overlap from the page of the new token", "put_u32(r + 8, as_u32((int32_t)prev));",
      "put_u32(r + 8, as_u32((int32_t)page));"),
+    ("C padding written as zeros",
+     "if (cap_c > num_c) memset(plan_c + (size_t)num_c * 16, 0xFF, (size_t)(cap_c - num_c) * 16);",
+     "if (cap_c > num_c) memset(plan_c + (size_t)num_c * 16, 0x00, (size_t)(cap_c - num_c) * 16);", 0),
+    ("W padding written as zeros",
+     "if (cap_w > num_w) memset(plan_w + (size_t)num_w * 8, 0xFF, (size_t)(cap_w - num_w) * 8);",
+     "if (cap_w > num_w) memset(plan_w + (size_t)num_w * 8, 0x00, (size_t)(cap_w - num_w) * 8);", 0),
+    ("counts kept after a planner error", "  if (err) {\n    num_c = 0;\n    num_w = 0;\n  } else {",
+     "  if (err) {\n  } else {", 0),
+    ("capacity check off by one", "if (num_c > cap_c || num_w > cap_w) err |= ERR_CAPACITY;",
+     "if (num_c >= cap_c || num_w > cap_w) err |= ERR_CAPACITY;", 0),
+    ("extend beyond seq_len accepted", "if (e <= 0 || e > s) err |= ERR_EXTEND;", "if (e <= 0) err |= ERR_EXTEND;", 0),
+    ("decode leaves rows that close no block unwritten",
+     "    for (int d = 0; d < hd; ++d) o[d] = 0.0;\n    if (seq_len == 0xFFFFFFFFu) continue;",
+     "    if (seq_len == 0xFFFFFFFFu) continue;"),
+    ("softmax max not subtracted", "const double w = exp(t[i] - m);", "const double w = exp(t[i]);"),
+    ("write copies half a row",
+     "    memcpy((uint8_t*)state + (size_t)(loc * R * esz), (const uint8_t*)input + (size_t)((int64_t)ragged * R * esz),\n"
+     "           (size_t)(R * esz));",
+     "    memcpy((uint8_t*)state + (size_t)(loc * R * esz), (const uint8_t*)input + (size_t)((int64_t)ragged * R * esz),\n"
+     "           (size_t)(R * esz / 2));"),
+    ("ratio 128 keeps an overlap block too", "const int64_t first_w = last_c - (cr == 4 ? 4 : 0);",
+     "const int64_t first_w = last_c - 4;"),
+    ("ape row by kept-entry count", "t[n] = sc + widen(ape, is_bf16, i, hd, d);",
+     "t[n] = sc + widen(ape, is_bf16, n, hd, d);"),
+    ("first-block mask also on the second block", "const int first = (cr == 4 && seq_len == 4) ? 4 : 0;\n  for (int64_t d",
+     "const int first = (cr == 4 && seq_len <= 8) ? 4 : 0;\n  for (int64_t d"),
+    ("ratio-4 entries before the chunk read from the input",
+     "static entry_src c4_entry(int i, int64_t blen, int64_t ragged, int64_t rp0, int64_t rp1, int64_t hd) {\n  entry_src e;\n  if (i < blen) {",
+     "static entry_src c4_entry(int i, int64_t blen, int64_t ragged, int64_t rp0, int64_t rp1, int64_t hd) {\n  entry_src e;\n  if (i < blen && 0) {"),
 ]
 
 
