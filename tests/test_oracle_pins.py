@@ -273,6 +273,33 @@ def test_c128_matches_library_softmax():
         np.testing.assert_allclose(out[k], ref, rtol=1e-12, atol=1e-12)
 
 
+def test_c4_matches_library_softmax():
+    """The c4 pool equals torch.softmax (float64, CPU) over the 8-position window, with the previous
+    block's entries taken from the overlap quarters |kv overlap| and |score overlap| of their rows
+    and the closing block's from |kv| and |score|; at seq_len 4 only the closing block's 4 entries
+    (c4.cuh page, c4_forward)."""
+    torch = pytest.importorskip("torch")
+    hd = 16
+    rng = np.random.default_rng(5)
+    L = 4 * 11 + 3
+    inp_f = rng.standard_normal((L, 4 * hd)).astype(np.float32)
+    inp = wl.to_bf16_bits(inp_f)
+    ape = wl.to_bf16_bits(0.1 * rng.standard_normal((8, hd)).astype(np.float32))
+    out, C = _one_row_prefill(4, hd, inp, ape, state=nan_state(8, 4 * hd, "bf16"))
+    x = torch.from_numpy(as_float(inp, "bf16"))
+    a = torch.from_numpy(as_float(ape, "bf16"))
+    assert len(C) == L // 4
+    for k, row in enumerate(C):
+        s = int(row[0])
+        prev, cur = x[max(s - 8, 0):s - 4], x[s - 4:s]
+        kv = torch.cat([prev[:, 0:hd], cur[:, hd:2 * hd]])
+        sc = torch.cat([prev[:, 2 * hd:3 * hd], cur[:, 3 * hd:4 * hd]])
+        ap = a[8 - kv.shape[0]:]  # ape rows 4..7 only, for the first block
+        wts = torch.softmax(sc + ap, dim=0)
+        ref = (wts * kv).sum(dim=0).numpy()
+        np.testing.assert_allclose(out[k], ref, rtol=1e-12, atol=1e-12)
+
+
 # --------------------------------------------------------------------------
 # chunking invariance against the brute-force definition
 # --------------------------------------------------------------------------
