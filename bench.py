@@ -688,6 +688,10 @@ def main():
 
     tokens = p4.num_q + p128.num_q + d4.B + d128.B
     value = tokens / (ms_per_step * 1e-3)
+    # the compressed rows one step emits: every C record of both prefills and every decode request
+    # that closes a block
+    rows = (int(P4.counts[0].item()) + int(P128.counts[0].item()) + int((d4.seq_lens % 4 == 0).sum())
+            + int((d128.seq_lens % 128 == 0).sum()))
 
     result = {
         "metric": METRIC,
@@ -724,6 +728,7 @@ def main():
         "kernels_us": kernels_us,
         "step_rows": step_rows,
         "f_rows": f_rows,
+        "compressed_rows": {"per_step": rows, "per_s": round(rows / (ms_per_step * 1e-3), 1)},
         "decode_step_us": decode_us,
         "overlapped_step": {"streams": 4, "ms_per_step": round(overlap_ms, 4),
                             "tokens_per_s": round((p4.num_q + p128.num_q + d4.B + d128.B) / (overlap_ms * 1e-3), 1)},
