@@ -53,6 +53,21 @@
  *  - `ape` is [8, hd] (ratio 4) or [128, hd] (ratio 128).
  *  - Compressed output is float32 [rows, hd].
  *
+ * Arithmetic and accuracy of the pool
+ * -----------------------------------
+ *  - bf16 inputs are pooled in fp32 (bf16 widens exactly).  score + ape and
+ *    the differences to the window maximum are then exact for scores of any
+ *    usual size, and a weight carries the exponential's few-ulp error: a
+ *    pooled value is within 2e-2 of the exact one for |kv| up to about 10^4.
+ *  - fp32 inputs are pooled in fp64 (score + ape, the window maximum, the
+ *    exponential, both sums and the quotient), then rounded once to fp32.
+ *    For any finite input with |kv| <= 2^30 a pooled value is within
+ *    1e-5 + 1e-5 * |exact| of the exact one, whatever the scores' size.
+ *  - The online ratio-128 slot (kvc_*_c128_online) keeps its running sums
+ *    in fp32 between calls: each call that stores a slot moves the value it
+ *    stands for by at most 2^-23 * max |kv| of the block, so rows built
+ *    over many calls carry that much more.
+ *
  * Call order
  * ----------
  *  prefill chunk: kvc_plan_prefill -> kvc_compress_c4 | kvc_compress_c128 ->

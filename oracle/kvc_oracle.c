@@ -719,7 +719,10 @@ static void fold(double* m, double* l, double* acc, int fresh, double t, double 
 
 /* Pool every valid C record of a ratio-128 plan with the online state.
  * Entries [0, blen) are the slot's partial (slot = read_page_0); entries
- * [blen, 128) are input rows ragged - 127 + i.  out[k] = acc / l. */
+ * [blen, 128) are input rows ragged - 127 + i.  out[k] = acc / l.
+ * A planner never emits buffer_len above 127 (the row's own token is always
+ * in the chunk), so a larger one marks a malformed record: skipped, with
+ * ERR_RECORD. */
 int oracle_compress_online(int is_bf16, int hd, const double* state, int64_t num_slots, const void* input, int num_q,
                            const void* ape, const uint8_t* plan_c, int num_c, double* out) {
   const int64_t R = 2 * (int64_t)hd;
@@ -729,7 +732,8 @@ int oracle_compress_online(int is_bf16, int hd, const double* state, int64_t num
     if (get_u32(r) == 0xFFFFFFFFu) continue;
     const uint32_t rb = get_u32(r + 4);
     const int64_t ragged = rb & 0xFFFFFF, blen = rb >> 24, slot = get_i32(r + 8);
-    if ((blen > 0 && (slot < 0 || slot >= num_slots)) || ragged - 127 + blen < 0 || ragged >= num_q) {
+    if (blen > 127 || (blen > 0 && (slot < 0 || slot >= num_slots)) || ragged - 127 + blen < 0 ||
+        ragged >= num_q) {
       err |= ERR_RECORD;
       continue;
     }

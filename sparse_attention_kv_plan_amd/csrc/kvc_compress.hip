@@ -121,7 +121,7 @@ template <typename T, int HD, bool STORE>
 __global__ __launch_bounds__(kC128Threads) void compress_c128_kernel(CompressArgs a) {
   typedef typename Elem<T>::storage E;
   typedef C128Pool<T, HD, kC128Threads> Pool;
-  __shared__ float lds[Pool::kLdsFloats];
+  __shared__ typename Pool::A lds[Pool::kLdsElems];
   const int64_t row = blockIdx.x;  // < cap_c (the grid)
   const kvc_plan_c rec = load_plan_c(a.plan_c + row);  // in flight with the count (as in compress_c4)
   if ((row >= a.counts[0]) | plan_c_invalid(rec)) return;

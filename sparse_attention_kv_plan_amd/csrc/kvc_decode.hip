@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kDec128Threads) void decode_c128_kernel(DecodeArgs 
   typedef C128Pool<T, HD, kDec128Threads, CS> Pool;
   constexpr int64_t R = 2 * HD;
   constexpr int HDW = HD / CS;
-  __shared__ float lds[Pool::kLdsFloats];
+  __shared__ typename Pool::A lds[Pool::kLdsElems];
   const int64_t b0 = (int64_t)(blockIdx.x / CS) * kDec128Group;
   const int cs = blockIdx.x % CS;
   __shared__ int32_t pool_page[kDec128Group];  // read page of a request that pools, else -1

@@ -79,6 +79,40 @@ __device__ __forceinline__ void widen16<Bf16>(u32x4 raw, float* out) {
 // 2^x on the hardware exp unit; the softmax weights are exp(d) = 2^(d*log2 e)
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The arithmetic type of the pool for an input element type.
+//  - bf16 inputs: fp32.  bf16 widens exactly, and the weights' relative error
+//    of a few fp32 ulp is far inside the bf16 bar (2e-2 absolute).
+//  - fp32 inputs: fp64.  score + ape, the shift by the window maximum, the
+//    exponential and both sums are then exact to about 1e-15 relative for
+//    any finite input, so the result is the pooled value rounded once to
+//    fp32.  In fp32 arithmetic a weight carries a relative error of about
+//    |score| * 2^-24 (the rounding of score + ape and of the scaled
+//    exponent), which grows with the scores' magnitude.
+template <typename T>
+struct Acc;
+template <>
+struct Acc<Bf16> {
+  typedef float type;
+};
+template <>
+struct Acc<float> {
+  typedef double type;
+};
+
+// exp(d) of a shifted score (d <= 0 apart from rounding of the shift)
+__device__ __forceinline__ float softmax_exp(float d) { return exp2_hw(d * kLog2e); }
+__device__ __forceinline__ double softmax_exp(double d) { return exp(d); }
+
+__device__ __forceinline__ float amax(float a, float b) { return fmaxf(a, b); }
+__device__ __forceinline__ double amax(double a, double b) { return fmax(a, b); }
+__device__ __forceinline__ float afma(float a, float b, float c) { return fmaf(a, b, c); }
+__device__ __forceinline__ double afma(double a, double b, double c) { return fma(a, b, c); }
+
+// A running maximum as it is kept in an fp32 slot: the sums that go with it
+// must be taken relative to exactly that value.  Identity in fp32.
+__device__ __forceinline__ float slot_shift(float m) { return m; }
+__device__ __forceinline__ double slot_shift(double m) { return (double)(float)m; }
+
 // store n (a multiple of 4) floats as 16-byte vectors
 template <int N, bool STREAM = false>
 __device__ __forceinline__ void store_floats(float* dst, const float* v) {
@@ -95,6 +129,17 @@ __device__ __forceinline__ void store_floats(float* dst, const float* v) {
       store16(dst + i, w);
     }
   }
+}
+
+// store n partials of the pool's arithmetic type (LDS)
+template <int N>
+__device__ __forceinline__ void store_acc(float* dst, const float* v) {
+  store_floats<N>(dst, v);
+}
+template <int N>
+__device__ __forceinline__ void store_acc(double* dst, const double* v) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) dst[i] = v[i];
 }
 
 template <int N>

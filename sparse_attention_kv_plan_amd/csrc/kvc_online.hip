@@ -30,7 +30,7 @@ template <typename T, int HD>
 __global__ __launch_bounds__(kCompressThreads) void compress_online_kernel(OnlineArgs a) {
   typedef typename Elem<T>::storage E;
   typedef C128Pool<T, HD, kCompressThreads> Pool;
-  __shared__ float lds[Pool::kLdsFloats];
+  __shared__ typename Pool::A lds[Pool::kLdsElems];
   const int64_t row = blockIdx.x;
   if (row >= a.counts[0] || row >= a.cap) return;
   const kvc_plan_c rec = load_plan_c(a.plan_c + row);
@@ -38,7 +38,9 @@ __global__ __launch_bounds__(kCompressThreads) void compress_online_kernel(Onlin
   const int64_t ragged = rec.ragged_blen & 0xFFFFFFu;
   const int blen = (int)(rec.ragged_blen >> 24);
   const int64_t slot = rec.read_page_0;
-  const bool ok = (blen == 0 || (slot >= 0 && slot < a.num_slots)) && ragged - 127 + blen >= 0 && ragged < a.num_q;
+  // buffer_len is an 8-bit field; a window holds at most 127 entries before its own token
+  const bool ok = blen <= 127 && (blen == 0 || (slot >= 0 && slot < a.num_slots)) && ragged - 127 + blen >= 0 &&
+                  ragged < a.num_q;
   if (!ok) {  // uniform over the workgroup
     if (threadIdx.x == 0) atomicOr(a.counts + 3, KVC_DERR_RECORD);
     return;
@@ -47,10 +49,10 @@ __global__ __launch_bounds__(kCompressThreads) void compress_online_kernel(Onlin
                          lds);
   const float* st = blen > 0 ? a.state + slot * 3 * HD : nullptr;  // slot is read only when blen > 0
   for (int d = threadIdx.x; d < HD; d += kCompressThreads) {
-    float M, L, A;
+    typename Pool::A M, L, Acc;
     Pool::merged_partial(lds, d, st != nullptr, st ? st[d] : 0.f, st ? st[HD + d] : 0.f, st ? st[2 * HD + d] : 0.f,
-                         &M, &L, &A);
-    __builtin_nontemporal_store(A / L, a.out + row * HD + d);
+                         &M, &L, &Acc);
+    __builtin_nontemporal_store((float)(Acc / L), a.out + row * HD + d);
   }
 }
 
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(kWriteThreads) void write_online_kernel(OnlineArgs 
   constexpr int HDW = HD / CS;
   static_assert(HDW <= kWriteThreads, "one channel of the slice per thread");
   typedef C128Pool<T, HD, kWriteThreads, CS, 8> Pool;  // a stream's 8 entries in one round of loads
-  __shared__ float lds[Pool::kLdsFloats];
+  __shared__ typename Pool::A lds[Pool::kLdsElems];
   __shared__ uint2 recs[kWriteRecs];
   __shared__ int heads[kWriteGroup];
   __shared__ int n_heads, run_end;
@@ -139,11 +141,11 @@ __global__ __launch_bounds__(kWriteThreads) void write_online_kernel(OnlineArgs 
     Pool::accumulate_range(static_cast<const E*>(a.input), static_cast<const E*>(a.ape), ragged - p0, 0, p0, p0 + n,
                            cs, lds);
     if (d < HDW) {
-      float M, L, A;
-      Pool::merged_partial(lds, d, cont, m0, l0, a0, &M, &L, &A);
-      st[d] = M;
-      st[HD + d] = L;
-      st[2 * HD + d] = A;
+      typename Pool::A M, L, Acc;  // M is already a value an fp32 slot holds exactly
+      Pool::merged_partial(lds, d, cont, m0, l0, a0, &M, &L, &Acc);
+      st[d] = (float)M;
+      st[HD + d] = (float)L;
+      st[2 * HD + d] = (float)Acc;
     }
     __syncthreads();  // lds is reused by the next run
   }
@@ -188,28 +190,35 @@ __global__ __launch_bounds__(kThreads) void decode_online_kernel(OnlineArgs a) {
       widen16<float>(load16(st + 2 * HD + v), acc + v);
     }
   }
+  // the fold in the pool's arithmetic type (fp64 for fp32 inputs); the new
+  // maximum is taken as the fp32 value the slot keeps, so the stored sums
+  // are relative to exactly the stored maximum
+  typedef typename Acc<T>::type A;
+  const bool closes = rec.seq_len % 128u == 0u;
+  float o[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    const float tv = t[v] + ap[v];
+    const A tv = (A)t[v] + (A)ap[v];
+    A nm, lv, av;
     if (fresh) {
-      m[v] = tv;
-      l[v] = 1.f;
-      acc[v] = kv[v];
+      nm = slot_shift(tv);
+      lv = softmax_exp(tv - nm);  // 1 unless the shift rounded tv
+      av = lv * (A)kv[v];
     } else {
-      const float nm = fmaxf(m[v], tv);
-      const float f = exp2_hw((m[v] - nm) * kLog2e), w = exp2_hw((tv - nm) * kLog2e);
-      l[v] = l[v] * f + w;
-      acc[v] = fmaf(acc[v], f, w * kv[v]);
-      m[v] = nm;
+      nm = slot_shift(amax((A)m[v], tv));
+      const A f = softmax_exp((A)m[v] - nm), w = softmax_exp(tv - nm);
+      lv = (A)l[v] * f + w;
+      av = afma((A)acc[v], f, w * (A)kv[v]);
     }
+    m[v] = (float)nm;
+    l[v] = (float)lv;
+    acc[v] = (float)av;
+    o[v] = closes ? (float)(av / lv) : 0.f;
   }
   store_floats<V>(st, m);
   store_floats<V>(st + HD, l);
   store_floats<V>(st + 2 * HD, acc);
-  if (rec.seq_len % 128u == 0u) {
-    float o[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v) o[v] = acc[v] / l[v];
+  if (closes) {
     store_floats<V, true>(out, o);
   } else {
     store_zeros<V>(out);

@@ -3,11 +3,12 @@
 // the prefill compress and the fused decode kernels.
 //
 // For every channel d of a compressed row:
-//   t_i = score_i[d] + ape[i][d]          (fp32)
-//   out = sum_i 2^((t_i - m) log2 e) kv_i[d] / sum_i 2^((t_i - m) log2 e),
-//   m = max_i t_i
+//   t_i = score_i[d] + ape[i][d]
+//   out = sum_i exp(t_i - m) kv_i[d] / sum_i exp(t_i - m),   m = max_i t_i
 // A lane owns one 16-byte group of channels (8 bf16 or 4 fp32) and keeps the
-// maximum, the sum of weights and the weighted sum in fp32 registers.
+// maximum, the sum of weights and the weighted sum in registers of the
+// pool's arithmetic type (Acc<T>: fp32 for bf16 inputs, where the weight is
+// 2^((t - m) log2 e) on the hardware exp unit; fp64 for fp32 inputs).
 #pragma once
 
 #include "kvc_device.hpp"
@@ -35,6 +36,7 @@ __device__ __forceinline__ void c4_pool(const typename Elem<T>::storage* __restr
                                         const typename Elem<T>::storage* __restrict__ input,
                                         const typename Elem<T>::storage* __restrict__ ape, int64_t ragged, int blen,
                                         int64_t rp0, int64_t rp1, int c, float* res, const Pre& pre = Pre()) {
+  typedef typename Acc<T>::type A;
   constexpr int V = Elem<T>::kVec;
   constexpr int64_t R = 4 * HD;
   // all kv / score loads of the window are issued before any use
@@ -47,30 +49,30 @@ __device__ __forceinline__ void c4_pool(const typename Elem<T>::storage* __restr
     sc_raw[i] = load16_stream(row + ((i < 4) ? 2 * HD : 3 * HD) + c);
   }
   pre();
-  float t[8][V];
+  A t[8][V];
 #pragma unroll
   for (int i = FIRST; i < 8; ++i) {
-    float a[V];
-    widen16<T>(sc_raw[i], t[i]);
+    float sc[V], a[V];
+    widen16<T>(sc_raw[i], sc);
     widen16<T>(load16(ape + i * HD + c), a);  // ape is reused by every row: cached load
 #pragma unroll
-    for (int v = 0; v < V; ++v) t[i][v] += a[v];
+    for (int v = 0; v < V; ++v) t[i][v] = (A)sc[v] + (A)a[v];
   }
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    float m = t[FIRST][v];
+    A m = t[FIRST][v];
 #pragma unroll
-    for (int i = FIRST + 1; i < 8; ++i) m = fmaxf(m, t[i][v]);
-    float den = 0.f, num = 0.f;
+    for (int i = FIRST + 1; i < 8; ++i) m = amax(m, t[i][v]);
+    A den = 0, num = 0;
 #pragma unroll
     for (int i = FIRST; i < 8; ++i) {
       float kv[V];
       widen16<T>(kv_raw[i], kv);  // widened per channel: keeps the raw 16-byte vectors as the only live copy
-      const float w = exp2_hw((t[i][v] - m) * kLog2e);
+      const A w = softmax_exp(t[i][v] - m);
       den += w;
-      num = fmaf(w, kv[v], num);
+      num = afma(w, (A)kv[v], num);
     }
-    res[v] = num / den;
+    res[v] = (float)(num / den);
   }
 }
 
@@ -126,31 +128,32 @@ __device__ __forceinline__ void progress_priority(int quarter) {
 
 template <typename T, int HD, int NT, int CS = 1, int U = 4>
 struct C128Pool {
+  typedef typename Acc<T>::type A;        // the arithmetic type; LDS partials are kept in it too
   static constexpr int V = Elem<T>::kVec;
   static constexpr int HDW = HD / CS;     // channels of this workgroup
   static constexpr int kLanes = HDW / V;  // lanes per stream
   static constexpr int S = NT / kLanes;   // streams per workgroup
   static constexpr int PER = 128 / S;     // entries per stream
-  static constexpr int kLdsFloats = 3 * S * HDW;
+  static constexpr int kLdsElems = 3 * S * HDW;
   static constexpr bool kPrio = PER / U >= 4;  // priority by progress (see above)
   static_assert(HD % CS == 0 && NT % kLanes == 0 && 128 % S == 0 && PER % U == 0, "bad c128 pool shape");
 
   // Every stream's partial (max, sum, weighted sum) per channel of the slice,
-  // left in lds (kLdsFloats) behind a workgroup barrier.
+  // left in lds (kLdsElems) behind a workgroup barrier.
   __device__ __forceinline__ static void accumulate(const typename Elem<T>::storage* __restrict__ state,
                                                     const typename Elem<T>::storage* __restrict__ input,
                                                     const typename Elem<T>::storage* __restrict__ ape,
-                                                    int64_t ragged, int blen, int64_t rp0, int cs, float* lds) {
+                                                    int64_t ragged, int blen, int64_t rp0, int cs, A* lds) {
     constexpr int64_t R = 2 * HD;
     const int sid = threadIdx.x / kLanes;
     const int cl = (threadIdx.x % kLanes) * V;  // channel inside the slice
     const int c = cs * HDW + cl;
-    float m[V], l[V], acc[V];
+    A m[V], l[V], acc[V];
 #pragma unroll
     for (int v = 0; v < V; ++v) {
       m[v] = -INFINITY;
-      l[v] = 0.f;
-      acc[v] = 0.f;
+      l[v] = 0;
+      acc[v] = 0;
     }
     for (int k0 = 0; k0 < PER; k0 += U) {
       if constexpr (kPrio) progress_priority(k0 * 4 / PER);
@@ -166,27 +169,27 @@ struct C128Pool {
       }
 #pragma unroll
       for (int v = 0; v < V; ++v) {
-        float t[U];
+        A t[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           float sc[V], ap[V];
           widen16<T>(sc_raw[u], sc);
           widen16<T>(ap_raw[u], ap);
-          t[u] = sc[v] + ap[v];
+          t[u] = (A)sc[v] + (A)ap[v];
         }
-        float cm = t[0];
+        A cm = t[0];
 #pragma unroll
-        for (int u = 1; u < U; ++u) cm = fmaxf(cm, t[u]);
-        const float nm = fmaxf(m[v], cm);
-        const float scale = exp2_hw((m[v] - nm) * kLog2e);  // 0 on the first chunk (m = -inf)
-        float lv = l[v] * scale, av = acc[v] * scale;
+        for (int u = 1; u < U; ++u) cm = amax(cm, t[u]);
+        const A nm = amax(m[v], cm);
+        const A scale = softmax_exp(m[v] - nm);  // 0 on the first chunk (m = -inf)
+        A lv = l[v] * scale, av = acc[v] * scale;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           float kv[V];
           widen16<T>(kv_raw[u], kv);
-          const float w = exp2_hw((t[u] - nm) * kLog2e);
+          const A w = softmax_exp(t[u] - nm);
           lv += w;
-          av = fmaf(w, kv[v], av);
+          av = afma(w, (A)kv[v], av);
         }
         m[v] = nm;
         l[v] = lv;
@@ -194,12 +197,12 @@ struct C128Pool {
       }
     }
     if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
-    float* lm = lds;
-    float* ll = lds + S * HDW;
-    float* la = lds + 2 * S * HDW;
-    store_floats<V>(lm + sid * HDW + cl, m);
-    store_floats<V>(ll + sid * HDW + cl, l);
-    store_floats<V>(la + sid * HDW + cl, acc);
+    A* lm = lds;
+    A* ll = lds + S * HDW;
+    A* la = lds + 2 * S * HDW;
+    store_acc<V>(lm + sid * HDW + cl, m);
+    store_acc<V>(ll + sid * HDW + cl, l);
+    store_acc<V>(la + sid * HDW + cl, acc);
     __syncthreads();
   }
 
@@ -210,17 +213,17 @@ struct C128Pool {
   // range leaves its stream's partial untouched.
   __device__ __forceinline__ static void accumulate_range(const typename Elem<T>::storage* __restrict__ input,
                                                           const typename Elem<T>::storage* __restrict__ ape,
-                                                          int64_t row0, int ape0, int lo, int hi, int cs, float* lds) {
+                                                          int64_t row0, int ape0, int lo, int hi, int cs, A* lds) {
     constexpr int64_t R = 2 * HD;
     const int sid = threadIdx.x / kLanes;
     const int cl = (threadIdx.x % kLanes) * V;
     const int c = cs * HDW + cl;
-    float m[V], l[V], acc[V];
+    A m[V], l[V], acc[V];
 #pragma unroll
     for (int v = 0; v < V; ++v) {
       m[v] = -INFINITY;
-      l[v] = 0.f;
-      acc[v] = 0.f;
+      l[v] = 0;
+      acc[v] = 0;
     }
     for (int k0 = 0; k0 < PER; k0 += U) {
       if constexpr (kPrio) progress_priority(k0 * 4 / PER);
@@ -238,28 +241,28 @@ struct C128Pool {
       }
 #pragma unroll
       for (int v = 0; v < V; ++v) {
-        float t[U];
+        A t[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           float sc[V], ap[V];
           widen16<T>(sc_raw[u], sc);
           widen16<T>(ap_raw[u], ap);
-          t[u] = in[u] ? sc[v] + ap[v] : -INFINITY;
+          t[u] = in[u] ? (A)sc[v] + (A)ap[v] : (A)-INFINITY;
         }
-        float cm = t[0];
+        A cm = t[0];
 #pragma unroll
-        for (int u = 1; u < U; ++u) cm = fmaxf(cm, t[u]);
-        const float nm = fmaxf(m[v], cm);
-        const float sh = nm == -INFINITY ? 0.f : nm;  // nothing in range yet: keep the zeros
-        const float scale = exp2_hw((m[v] - sh) * kLog2e);
-        float lv = l[v] * scale, av = acc[v] * scale;
+        for (int u = 1; u < U; ++u) cm = amax(cm, t[u]);
+        const A nm = amax(m[v], cm);
+        const A sh = nm == (A)-INFINITY ? (A)0 : nm;  // nothing in range yet: keep the zeros
+        const A scale = softmax_exp(m[v] - sh);
+        A lv = l[v] * scale, av = acc[v] * scale;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           float kv[V];
           widen16<T>(kv_raw[u], kv);
-          const float w = exp2_hw((t[u] - sh) * kLog2e);
+          const A w = softmax_exp(t[u] - sh);
           lv += w;
-          av = fmaf(w, in[u] ? kv[v] : 0.f, av);
+          av = afma(w, in[u] ? (A)kv[v] : (A)0, av);
         }
         m[v] = nm;
         l[v] = lv;
@@ -267,36 +270,39 @@ struct C128Pool {
       }
     }
     if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
-    float* lm = lds;
-    float* ll = lds + S * HDW;
-    float* la = lds + 2 * S * HDW;
-    store_floats<V>(lm + sid * HDW + cl, m);
-    store_floats<V>(ll + sid * HDW + cl, l);
-    store_floats<V>(la + sid * HDW + cl, acc);
+    A* lm = lds;
+    A* ll = lds + S * HDW;
+    A* la = lds + 2 * S * HDW;
+    store_acc<V>(lm + sid * HDW + cl, m);
+    store_acc<V>(ll + sid * HDW + cl, l);
+    store_acc<V>(la + sid * HDW + cl, acc);
     __syncthreads();
   }
 
   // The merged (max, sum, weighted sum) of channel d of the slice, with an
-  // extra partial (m0, l0, a0) folded in when `extra` (an online slot).
-  __device__ __forceinline__ static void merged_partial(const float* lds, int d, bool extra, float m0, float l0,
-                                                        float a0, float* M_out, float* L_out, float* A_out) {
-    const float* lm = lds;
-    const float* ll = lds + S * HDW;
-    const float* la = lds + 2 * S * HDW;
-    float M = extra ? m0 : -INFINITY;
+  // extra partial (m0, l0, a0) folded in when `extra` (an online slot).  The
+  // sums are taken relative to slot_shift(max), the value an fp32 slot can
+  // hold, which is returned as the maximum.
+  __device__ __forceinline__ static void merged_partial(const A* lds, int d, bool extra, float m0, float l0,
+                                                        float a0, A* M_out, A* L_out, A* A_out) {
+    const A* lm = lds;
+    const A* ll = lds + S * HDW;
+    const A* la = lds + 2 * S * HDW;
+    A M = extra ? (A)m0 : (A)-INFINITY;
 #pragma unroll
-    for (int s = 0; s < S; ++s) M = fmaxf(M, lm[s * HDW + d]);
-    float Lsum = 0.f, Asum = 0.f;
+    for (int s = 0; s < S; ++s) M = amax(M, lm[s * HDW + d]);
+    M = slot_shift(M);
+    A Lsum = 0, Asum = 0;
     if (extra) {
-      const float f = exp2_hw((m0 - M) * kLog2e);
-      Lsum = l0 * f;
-      Asum = a0 * f;
+      const A f = softmax_exp((A)m0 - M);
+      Lsum = (A)l0 * f;
+      Asum = (A)a0 * f;
     }
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      const float f = exp2_hw((lm[s * HDW + d] - M) * kLog2e);  // 0 for a stream with nothing in range
-      Lsum = fmaf(ll[s * HDW + d], f, Lsum);
-      Asum = fmaf(la[s * HDW + d], f, Asum);
+      const A f = softmax_exp(lm[s * HDW + d] - M);  // 0 for a stream with nothing in range
+      Lsum = afma(ll[s * HDW + d], f, Lsum);
+      Asum = afma(la[s * HDW + d], f, Asum);
     }
     *M_out = M;
     *L_out = Lsum;
@@ -304,28 +310,28 @@ struct C128Pool {
   }
 
   // The pooled value of channel d of the slice, merged from the partials.
-  __device__ __forceinline__ static float merged(const float* lds, int d) {
-    const float* lm = lds;
-    const float* ll = lds + S * HDW;
-    const float* la = lds + 2 * S * HDW;
-    float M = lm[d];
+  __device__ __forceinline__ static float merged(const A* lds, int d) {
+    const A* lm = lds;
+    const A* ll = lds + S * HDW;
+    const A* la = lds + 2 * S * HDW;
+    A M = lm[d];
 #pragma unroll
-    for (int s = 1; s < S; ++s) M = fmaxf(M, lm[s * HDW + d]);
-    float Lsum = 0.f, Asum = 0.f;
+    for (int s = 1; s < S; ++s) M = amax(M, lm[s * HDW + d]);
+    A Lsum = 0, Asum = 0;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      const float f = exp2_hw((lm[s * HDW + d] - M) * kLog2e);
-      Lsum = fmaf(ll[s * HDW + d], f, Lsum);
-      Asum = fmaf(la[s * HDW + d], f, Asum);
+      const A f = softmax_exp(lm[s * HDW + d] - M);
+      Lsum = afma(ll[s * HDW + d], f, Lsum);
+      Asum = afma(la[s * HDW + d], f, Asum);
     }
-    return Asum / Lsum;
+    return (float)(Asum / Lsum);
   }
 
   // accumulate, then the slice's channels into out_row (streaming stores)
   __device__ __forceinline__ static void run(const typename Elem<T>::storage* __restrict__ state,
                                              const typename Elem<T>::storage* __restrict__ input,
                                              const typename Elem<T>::storage* __restrict__ ape, int64_t ragged,
-                                             int blen, int64_t rp0, int cs, float* __restrict__ out_row, float* lds) {
+                                             int blen, int64_t rp0, int cs, float* __restrict__ out_row, A* lds) {
     accumulate(state, input, ape, ragged, blen, rp0, cs, lds);
     for (int d = threadIdx.x; d < HDW; d += NT) __builtin_nontemporal_store(merged(lds, d), out_row + cs * HDW + d);
   }

@@ -118,6 +118,14 @@ def _dev(*ts):
             raise KvcError("tensors must be contiguous CUDA tensors")
 
 
+def _i32(*ts):
+    """Lengths, indices, tables, counts and status words are int32 in the ABI: an int64 tensor
+    would be read as pairs of int32 words, giving wrong (often in-range) values silently."""
+    for t in ts:
+        if t is not None and t.dtype != torch.int32:
+            raise KvcError("index, length, count and status tensors must be int32, got %s" % t.dtype)
+
+
 def _shape(t, rows_at_least, cols, what):
     """The library cannot see device buffer sizes: check them before handing pointers over."""
     if t.dim() != 2 or t.shape[0] < rows_at_least or t.shape[1] != cols:
@@ -157,6 +165,7 @@ def alloc_prefill_plan(cr: int, batch: int, num_q: int, device="cuda", cap_c=Non
 
 def plan_prefill(cr, seq_lens, extend_lens, state_index, num_state_rows, num_q, plan_c, plan_w, counts,
                  stream=None):
+    _i32(seq_lens, extend_lens, state_index, counts)
     _dev(seq_lens, extend_lens, state_index, plan_c, plan_w, counts)
     B = seq_lens.numel()
     if extend_lens.numel() != B or state_index.numel() != B or counts.numel() < 4:
@@ -170,6 +179,7 @@ def plan_prefill(cr, seq_lens, extend_lens, state_index, num_state_rows, num_q, 
 
 
 def plan_decode(cr, seq_lens, state_index, num_state_rows, plan_d, status=None, stream=None):
+    _i32(seq_lens, state_index, status)
     _dev(seq_lens, state_index, plan_d, status)
     if state_index.numel() != seq_lens.numel():
         raise KvcError("seq_lens and state_index must have one entry per request")
@@ -189,6 +199,7 @@ def capacities_swa(cr: int, batch: int, num_q: int, swa_page_size: int):
 def plan_prefill_swa(cr, seq_lens, extend_lens, req_pool_indices, req_to_token, full_to_swa, swa_page_size,
                      ring_size, num_state_rows, num_q, plan_c, plan_w, counts, status=None, stream=None):
     """req_to_token: int32 [num_reqs, stride]; full_to_swa: int32 [num_full]."""
+    _i32(seq_lens, extend_lens, req_pool_indices, req_to_token, full_to_swa, counts, status)
     _dev(seq_lens, extend_lens, req_pool_indices, req_to_token, full_to_swa, plan_c, plan_w, counts, status)
     B = seq_lens.numel()
     if extend_lens.numel() != B or req_pool_indices.numel() != B or counts.numel() < 4 or req_to_token.dim() != 2:
@@ -205,6 +216,7 @@ def plan_prefill_swa(cr, seq_lens, extend_lens, req_pool_indices, req_to_token, 
 
 def plan_decode_swa(cr, seq_lens, req_pool_indices, req_to_token, full_to_swa, swa_page_size, ring_size,
                     num_state_rows, plan_d, status=None, stream=None):
+    _i32(seq_lens, req_pool_indices, req_to_token, full_to_swa, status)
     _dev(seq_lens, req_pool_indices, req_to_token, full_to_swa, plan_d, status)
     if req_pool_indices.numel() != seq_lens.numel() or req_to_token.dim() != 2:
         raise KvcError("one request slot per request, req_to_token 2-D")
@@ -219,10 +231,15 @@ def plan_decode_swa(cr, seq_lens, req_pool_indices, req_to_token, full_to_swa, s
 def plan_prefill_page4(seq_lens, extend_lens, page_index, bundle, num_state_rows, num_q, plan_c, plan_w, counts,
                        status=None, stream=None):
     """Ratio-4 prefill plan over caller-allocated 4-row pages; bundle: int32 [batch, 4]."""
+    _i32(seq_lens, extend_lens, page_index, bundle, counts, status)
     _dev(seq_lens, extend_lens, page_index, bundle, plan_c, plan_w, counts, status)
     B = seq_lens.numel()
-    if bundle.dtype != torch.int32 or tuple(bundle.shape) != (B, 4):
+    if tuple(bundle.shape) != (B, 4):
         raise KvcError("bundle must be int32 [batch, 4]")
+    if extend_lens.numel() != B or page_index.numel() != B or counts.numel() < 4:
+        raise KvcError("seq_lens, extend_lens, page_index must have one entry per request; counts 4")
+    _shape(plan_c, 0, C_BYTES, "plan_c")
+    _shape(plan_w, 0, W_BYTES, "plan_w")
     rc = load().kvc_plan_prefill_page4(B, num_q, _p(seq_lens), _p(extend_lens), _p(page_index), _p(bundle),
                                        num_state_rows, _p(plan_c), plan_c.shape[0], _p(plan_w), plan_w.shape[0],
                                        _p(counts), _p(status), _stream(stream))
@@ -230,13 +247,18 @@ def plan_prefill_page4(seq_lens, extend_lens, page_index, bundle, num_state_rows
 
 
 def plan_decode_page4(seq_lens, page_index, prev_page, num_state_rows, plan_d, status=None, stream=None):
+    _i32(seq_lens, page_index, prev_page, status)
     _dev(seq_lens, page_index, prev_page, plan_d, status)
+    if page_index.numel() != seq_lens.numel() or prev_page.numel() != seq_lens.numel():
+        raise KvcError("seq_lens, page_index and prev_page must have one entry per request")
+    _shape(plan_d, seq_lens.numel(), D_BYTES, "plan_d")
     rc = load().kvc_plan_decode_page4(seq_lens.numel(), _p(seq_lens), _p(page_index), _p(prev_page), num_state_rows,
                                       _p(plan_d), _p(status), _stream(stream))
     _check(rc, "kvc_plan_decode_page4")
 
 
 def write(cr, head_dim, state, inp, plan_w, counts, stream=None):
+    _i32(counts)
     _dev(state, inp, plan_w, counts)
     _rows(cr, head_dim, state, inp)
     _shape(plan_w, 0, W_BYTES, "plan_w")
@@ -246,6 +268,7 @@ def write(cr, head_dim, state, inp, plan_w, counts, stream=None):
 
 
 def compress_c4(head_dim, state, inp, ape, plan_c, counts, out, stream=None):
+    _i32(counts)
     _dev(state, inp, ape, plan_c, counts, out)
     _rows(4, head_dim, state, inp)
     _shape(ape, WINDOW[4], head_dim, "ape")
@@ -259,6 +282,7 @@ def compress_c4(head_dim, state, inp, ape, plan_c, counts, out, stream=None):
 
 
 def compress_c128(head_dim, state, inp, ape, plan_c, counts, out, stream=None):
+    _i32(counts)
     _dev(state, inp, ape, plan_c, counts, out)
     _rows(128, head_dim, state, inp)
     _shape(ape, WINDOW[128], head_dim, "ape")
@@ -310,6 +334,7 @@ def store_args(head_dim, norm_weight, eps, freqs_cis, out_loc, cache):
 
 def norm_rope_store_prefill(cr, rows, plan_c, counts, norm_weight, eps, freqs_cis, out_loc, cache, stream=None):
     """Store row k of rows (float32 [cap_c, hd]) for every valid C record k < counts[0]."""
+    _i32(counts)
     _dev(rows, plan_c, counts)
     hd = rows.shape[1]
     _shape(plan_c, 0, C_BYTES, "plan_c")
@@ -324,6 +349,7 @@ def norm_rope_store_prefill(cr, rows, plan_c, counts, norm_weight, eps, freqs_ci
 
 def norm_rope_store_decode(cr, rows, plan_d, norm_weight, eps, freqs_cis, out_loc, cache, status=None, stream=None):
     """Store row b of rows (float32 [batch, hd]) for every D record that closes a block."""
+    _i32(status)
     _dev(rows, plan_d, status)
     hd = rows.shape[1]
     _shape(plan_d, 1, D_BYTES, "plan_d")
@@ -339,6 +365,7 @@ def norm_rope_store_decode(cr, rows, plan_d, norm_weight, eps, freqs_cis, out_lo
 def compress_norm_rope_store(cr, head_dim, state, inp, ape, plan_c, counts, norm_weight, eps, freqs_cis, out_loc,
                              cache, stream=None):
     """Pool, norm, rotate and store in one kernel (kvc_compress_c{4,128}_norm_rope_store)."""
+    _i32(counts)
     _dev(state, inp, ape, plan_c, counts)
     _rows(cr, head_dim, state, inp)
     _shape(ape, WINDOW[cr], head_dim, "ape")
@@ -355,6 +382,7 @@ def compress_norm_rope_store(cr, head_dim, state, inp, ape, plan_c, counts, norm
 def decode_c4_norm_rope_store(head_dim, state, inp, ape, plan_d, norm_weight, eps, freqs_cis, out_loc, cache,
                               status=None, stream=None):
     """Ratio-4 decode with the store step in one kernel (kvc_decode_c4_norm_rope_store)."""
+    _i32(status)
     _dev(state, inp, ape, plan_d, status)
     _rows(4, head_dim, state, inp)
     _shape(ape, WINDOW[4], head_dim, "ape")
@@ -379,6 +407,7 @@ def _online_state(state, head_dim):
 
 
 def compress_c128_online(head_dim, state, inp, ape, plan_c, counts, out, stream=None):
+    _i32(counts)
     _dev(state, inp, ape, plan_c, counts, out)
     _online_state(state, head_dim)
     _shape(inp, 0, 2 * head_dim, "input")
@@ -393,6 +422,7 @@ def compress_c128_online(head_dim, state, inp, ape, plan_c, counts, out, stream=
 
 
 def write_c128_online(head_dim, state, inp, ape, plan_w, counts, stream=None):
+    _i32(counts)
     _dev(state, inp, ape, plan_w, counts)
     _online_state(state, head_dim)
     _shape(inp, 0, 2 * head_dim, "input")
@@ -406,6 +436,7 @@ def write_c128_online(head_dim, state, inp, ape, plan_w, counts, stream=None):
 
 
 def decode_c128_online(head_dim, state, inp, ape, plan_d, out, status=None, stream=None):
+    _i32(status)
     _dev(state, inp, ape, plan_d, out, status)
     _online_state(state, head_dim)
     _shape(plan_d, 1, D_BYTES, "plan_d")
@@ -420,6 +451,7 @@ def decode_c128_online(head_dim, state, inp, ape, plan_d, out, status=None, stre
 
 
 def decode_c4(head_dim, state, inp, ape, plan_d, out, status=None, stream=None):
+    _i32(status)
     _dev(state, inp, ape, plan_d, out, status)
     _rows(4, head_dim, state, inp)
     _shape(plan_d, 0, D_BYTES, "plan_d")
@@ -435,6 +467,7 @@ def decode_c4(head_dim, state, inp, ape, plan_d, out, status=None, stream=None):
 
 
 def decode_c128(head_dim, state, inp, ape, plan_d, out, status=None, stream=None):
+    _i32(status)
     _dev(state, inp, ape, plan_d, out, status)
     _rows(128, head_dim, state, inp)
     _shape(plan_d, 0, D_BYTES, "plan_d")

@@ -167,3 +167,48 @@ def test_binding_rejects_host_tensors():
     for call in calls:
         with pytest.raises(kvc.KvcError, match="CUDA"):
             call()
+
+
+def test_binding_rejects_non_int32_index_tensors():
+    """Lengths, indices, tables, counts and status words are int32 in the ABI: an int64 tensor would
+    be read as pairs of int32 words.  Every wrapper refuses one before a pointer reaches the library
+    (the check runs before the device check, so it is seen here on host tensors)."""
+    torch = pytest.importorskip("torch")
+    kvc.load(build_if_missing=True)
+    i32 = lambda n: torch.zeros(n, dtype=torch.int32)  # noqa: E731
+    i64 = lambda n: torch.zeros(n, dtype=torch.int64)  # noqa: E731
+    hd = 128
+    st4, in4 = torch.zeros((8, 4 * hd)), torch.zeros((8, 4 * hd))
+    st128, in128 = torch.zeros((128, 2 * hd)), torch.zeros((128, 2 * hd))
+    pc, pw, pd = (torch.zeros((4, kvc.C_BYTES), dtype=torch.uint8), torch.zeros((4, kvc.W_BYTES), dtype=torch.uint8),
+                  torch.zeros((1, kvc.D_BYTES), dtype=torch.uint8))
+    ape4, ape128, out = torch.zeros((8, hd)), torch.zeros((128, hd)), torch.zeros((4, hd))
+    slots = torch.zeros((1, 3, hd))
+    b4 = torch.zeros((1, 4), dtype=torch.int32)
+    r2t, f2s = torch.zeros((1, 16), dtype=torch.int32), i32(16)
+    calls = [
+        lambda: kvc.plan_prefill(4, i64(1), i32(1), i32(1), 8, 1, pc, pw, i32(4)),
+        lambda: kvc.plan_prefill(4, i32(1), i64(1), i32(1), 8, 1, pc, pw, i32(4)),
+        lambda: kvc.plan_prefill(4, i32(1), i32(1), i64(1), 8, 1, pc, pw, i32(4)),
+        lambda: kvc.plan_prefill(4, i32(1), i32(1), i32(1), 8, 1, pc, pw, i64(4)),
+        lambda: kvc.plan_decode(4, i32(1), i64(1), 8, pd),
+        lambda: kvc.plan_decode(4, i32(1), i32(1), 8, pd, i64(1)),
+        lambda: kvc.plan_prefill_swa(4, i32(1), i32(1), i64(1), r2t, f2s, 16, 8, 8, 1, pc, pw, i32(4)),
+        lambda: kvc.plan_prefill_swa(4, i32(1), i32(1), i32(1), r2t.long(), f2s, 16, 8, 8, 1, pc, pw, i32(4)),
+        lambda: kvc.plan_prefill_swa(4, i32(1), i32(1), i32(1), r2t, f2s.long(), 16, 8, 8, 1, pc, pw, i32(4)),
+        lambda: kvc.plan_decode_swa(4, i32(1), i32(1), r2t, f2s.long(), 16, 8, 8, pd),
+        lambda: kvc.plan_prefill_page4(i32(1), i32(1), i64(1), b4, 8, 1, pc, pw, i32(4)),
+        lambda: kvc.plan_prefill_page4(i32(1), i32(1), i32(1), b4.long(), 8, 1, pc, pw, i32(4)),
+        lambda: kvc.plan_decode_page4(i32(1), i32(1), i64(1), 8, pd),
+        lambda: kvc.write(4, hd, st4, in4, pw, i64(4)),
+        lambda: kvc.compress_c4(hd, st4, in4, ape4, pc, i64(4), out),
+        lambda: kvc.compress_c128(hd, st128, in128, ape128, pc, i64(4), out),
+        lambda: kvc.decode_c4(hd, st4, in4, ape4, pd, out, i64(1)),
+        lambda: kvc.decode_c128(hd, st128, in128, ape128, pd, out, i64(1)),
+        lambda: kvc.compress_c128_online(hd, slots, in128, ape128, pc, i64(4), out),
+        lambda: kvc.write_c128_online(hd, slots, in128, ape128, pw, i64(4)),
+        lambda: kvc.decode_c128_online(hd, slots, in128, ape128, pd, out, i64(1)),
+    ]
+    for k, call in enumerate(calls):
+        with pytest.raises(kvc.KvcError, match="int32"):
+            call()

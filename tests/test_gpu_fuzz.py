@@ -5,10 +5,8 @@ pages.  Every emitted row is
 compared with the oracle's (fp32 bar 1e-5 + 1e-5 |ref|, bf16 bar 2e-2) and the state buffer after
 the last step bit for bit.
 
-fp32 inputs keep scores of the configs' size (standard deviation 1 or 2): the score + ape sum and
-its exponent are formed in fp32, so a weight carries a relative error of about |score| * 2^-24 and
-a row whose terms nearly cancel can miss the absolute 1e-5 once scores reach tens.  bf16 inputs
-also take scores and values 3 and 30 times larger (bar 2e-2)."""
+Inputs of either dtype take scores and values of the configs' size and 2, 3 and 30 times larger
+(fp32: the pool runs in float64, so the bar holds at every scale; bf16: bar 2e-2)."""
 import numpy as np
 import pytest
 
@@ -43,7 +41,7 @@ def _case(rng):
     seqs, chunks = [], []
     for _ in range(B):
         L = int(rng.integers(1, 6 * W[cr] if cr == 4 else 3 * W[cr]))
-        scale = float(rng.choice([1.0, 2.0])) if dtype == "f32" else float(rng.choice([1.0, 3.0, 30.0]))
+        scale = float(rng.choice([1.0, 2.0, 3.0, 30.0]))
         x = (scale * rng.standard_normal((L + decode_steps, R))).astype(np.float32)
         seqs.append(wl.to_bf16_bits(x) if dtype == "bf16" else x)
         chunks.append(random_split(rng, L, int(rng.integers(1, 7))))

@@ -161,6 +161,9 @@ def test_online_record_errors(gpu):
     pc[0] = np.array([130, 3 | (125 << 24), 7, 7], np.uint32).view(np.uint8)  # continues slot 7 of 2
     out, err = gpu.compress_online(hd, slots, inp, ape, pc, 1)
     assert err == kvc.DERR_RECORD and np.isnan(out).all()
+    pc[0] = np.array([200, 3 | (200 << 24), 0, 0], np.uint32).view(np.uint8)  # buffer_len above 127
+    out, err = gpu.compress_online(hd, slots, inp, ape, pc, 1)
+    assert err == kvc.DERR_RECORD and np.isnan(out).all()
     pw = np.zeros((2, 8), np.uint8)
     pw[0] = np.array([0, 5 * 128], np.uint32).view(np.uint8)
     pw[1] = np.array([1, 5 * 128 + 1], np.uint32).view(np.uint8)

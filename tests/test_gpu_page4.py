@@ -101,6 +101,34 @@ def test_plan_page4_errors(gpu):
         assert g[1] == o[1] and np.array_equal(g[0], o[0])
 
 
+def test_page4_wrappers_check_buffer_sizes(gpu):
+    """A record buffer shorter than the batch, a table of the wrong length or an int64 table is
+    refused by the binding before anything is launched (a short plan_d would take device writes
+    past its end)."""
+    from sparse_attention_kv_plan_amd import kvc
+    from tests.gpu_backend import to_dev
+    i32 = lambda a: to_dev(np.asarray(a, np.int32))  # noqa: E731
+    s, idx, prev = i32([5, 8, 12]), i32([0, 1, 2]), i32([-1, 3, 4])
+    short_d = torch.zeros((2, kvc.D_BYTES), dtype=torch.uint8, device="cuda")
+    with pytest.raises(kvc.KvcError, match="plan_d"):
+        kvc.plan_decode_page4(s, idx, prev, 40, short_d)
+    pd = torch.zeros((3, kvc.D_BYTES), dtype=torch.uint8, device="cuda")
+    with pytest.raises(kvc.KvcError, match="one entry per request"):
+        kvc.plan_decode_page4(s, idx[:2], prev, 40, pd)
+    with pytest.raises(kvc.KvcError, match="int32"):
+        kvc.plan_decode_page4(s, idx.long(), prev, 40, pd)
+    e = i32([5, 8, 12])
+    bundle = i32(np.zeros((3, 4)))
+    pc, pw, counts = kvc.alloc_prefill_plan(4, 3, 25, "cuda")
+    with pytest.raises(kvc.KvcError, match="one entry per request"):
+        kvc.plan_prefill_page4(s, e[:2], idx, bundle, 40, 25, pc, pw, counts)
+    with pytest.raises(kvc.KvcError, match="plan_c"):
+        kvc.plan_prefill_page4(s, e, idx, bundle, 40, 25, pc.view(-1), pw, counts)
+    with pytest.raises(kvc.KvcError, match="int32"):
+        kvc.plan_prefill_page4(s, e, idx, bundle, 40, 25, pc, pw, counts.long())
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("dtype,hd", [("bf16", 512), ("f32", 128)])
 def test_page4_chunked_prefill_then_decode(gpu, dtype, hd):
     rng = np.random.default_rng(1300 + hd)

@@ -96,6 +96,8 @@ MUTANTS = [
      "1"),
     ("online compress window off by one", "        const int64_t row = ragged - 127 + i;\n        const double t",
      "        const int64_t row = ragged - 126 + i;\n        const double t"),
+    ("online compress accepts buffer_len above 127", "    if (blen > 127 || (blen > 0 && (slot < 0",
+     "    if ((blen > 0 && (slot < 0"),
     ("page4 overlap entries always from the first load page", "rp0 = blen <= 4 ? lsp : lfp;",
      "rp0 = lfp;"),
     ("page4 overlap threshold off by one", "rp0 = blen <= 4 ? lsp : lfp;",

@@ -121,6 +121,11 @@ def test_online_errors():
     pc[0] = np.array([130, 3 | (125 << 24), 7, 7], np.uint32).view(np.uint8)
     _, err = oracle.compress_online(hd, slots, inp, ape, pc, 1)
     assert err == ERR_RECORD
+    # a C record whose buffer_len (an 8-bit field) exceeds the 127 entries a window can hold before
+    # its own token: malformed, skipped and flagged, the row left untouched
+    pc[0] = np.array([200, 3 | (200 << 24), 0, 0], np.uint32).view(np.uint8)
+    out, err = oracle.compress_online(hd, slots, inp, ape, pc, 1)
+    assert err == ERR_RECORD and np.isnan(out).all()
     # W records of a slot outside the array
     pw = np.zeros((2, 8), np.uint8)
     pw[0] = np.array([0, 5 * 128], np.uint32).view(np.uint8)
