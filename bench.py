@@ -12,11 +12,22 @@ the C ABI on one HIP stream:
 Inputs are synthetic (seeded normals), resident in HBM before timing starts.
 
 value = tokens consumed per second (each compressor pass counts its tokens,
-decode one token per request).  The roofline object reports the dominant
-kernel (kvc_compress_c4 on the prefill batch): algorithmic bytes per launch
-divided by its average duration, timed with HIP events on the launch stream
-over the timed region.  cpu_baseline times the float64 C oracle on one host
-core over the same step.
+decode one token per request), over K steps run back to back.  The roofline
+object reports the dominant kernel (kvc_compress_c4 on the prefill batch):
+algorithmic bytes per launch divided by its average duration, timed with HIP
+events on the launch stream over the timed region ("cache": "warm"), and its
+cold-cache time beside it.  After the timed region, untimed passes give:
+  * every launch's time and algorithmic GB/s (step_rows, f_rows);
+  * the four kernels of the step with cold caches: before each launch the
+    state is restored from a pristine copy and 1 GiB is written to a scratch
+    buffer (cold_us, cold_frac);
+  * each named workload as its own chain (configs): the ratio-4 prefill of one
+    64-token request (fp32, head_dim 128) and the ratio-128 prefill of four
+    requests, plan -> compress -> write; the two decode batches, plan ->
+    decode;
+  * the decode step as a replayed HIP graph, and the step on four streams.
+cpu_baseline times the float64 C oracle over the same step on the host cores
+(all this process may use, up to 16, then one).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--sweep]
 """
@@ -49,10 +60,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=11)
+    ap.add_argument("--cpu-reps", type=int, default=7)
     ap.add_argument("--sweep", action="store_true",
-                    help="also time the compress and decode kernels over growing workloads, and the two "
-                         "compress kernels with cold caches (reported under 'sweep')")
+                    help="also time the compress and decode kernels over growing workloads (reported under "
+                         "'sweep')")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 1 GiB device to device 5 times (calibrates the HBM byte counters)")
     return ap.parse_args()
@@ -202,8 +213,8 @@ def algorithmic_bytes_online(hd, esize, blen_of_rows, write_runs, decode_seq_len
 
 def sweep(torch, kvc, dev, P4, P128, to_dev):
     """Extra, labelled results: kernel time and algorithmic GB/s as the work grows (prefill: the first
-    k requests of the mixed batch; decode: batches with device-generated inputs), and the two compress
-    kernels on the full mixed batch with cold caches (1 GiB written before every launch, untimed)."""
+    k requests of the mixed batch; decode: batches with device-generated inputs), warm and with cold
+    caches (1 GiB written before every launch, untimed)."""
     stream = torch.cuda.current_stream()
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
 
@@ -220,7 +231,7 @@ def sweep(torch, kvc, dev, P4, P128, to_dev):
         torch.cuda.synchronize()
         return round(float(np.median([a.elapsed_time(b) for a, b in ts[2:]])) * 1e3, 2)
 
-    out = {"prefill": [], "decode": [], "cold": {}}
+    out = {"prefill": [], "decode": []}
     for P in (P4, P128):
         w = P.w
         for k in (1, 4, 16, 32, 64):
@@ -234,9 +245,10 @@ def sweep(torch, kvc, dev, P4, P128, to_dev):
             n = int(cnt[0].item())
             seqs = pc[:n].cpu().numpy().view("<u4").reshape(-1, 4)[:, 0].astype(np.int64)
             nbytes = algorithmic_bytes_compress(w.cr, w.hd, w.esize, seqs)
+            cold_us = med_us(lambda: kvc.compress(w.cr, w.hd, P.state, inp, P.ape, pc, cnt, o), cold=True)
             out["prefill"].append({"ratio": w.cr, "requests": k, "tokens": nq, "rows": n, "us": us,
-                                   "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)})
-        out["cold"]["compress_c%d" % w.cr] = med_us(P.compress, cold=True)
+                                   "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "cold_us": cold_us,
+                                   "cold_GBps": round(nbytes / (cold_us * 1e-6) / 1e9, 1)})
     hd = 512
     for cr, batches in ((4, (256, 1024, 4096, 16384, 65536)), (128, (1024, 4096, 16384, 32768))):
         R, W = (4 if cr == 4 else 2) * hd, (8 if cr == 4 else 128)
@@ -254,12 +266,65 @@ def sweep(torch, kvc, dev, P4, P128, to_dev):
             o = torch.empty((B, hd), dtype=torch.float32, device=dev)
             kvc.plan_decode(cr, to_dev(seq), to_dev(idx), B * W, plan_d, status)
             us = med_us(lambda: kvc.decode(cr, hd, state, inp, ape, plan_d, o, status))
+            cold_us = med_us(lambda: kvc.decode(cr, hd, state, inp, ape, plan_d, o, status), cold=True)
             assert int(status.item()) == 0
             nbytes = algorithmic_bytes_decode(cr, hd, 2, seq)
             out["decode"].append({"ratio": cr, "batch": B, "boundaries": int((seq % cr == 0).sum()), "us": us,
-                                  "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)})
+                                  "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "cold_us": cold_us,
+                                  "cold_GBps": round(nbytes / (cold_us * 1e-6) / 1e9, 1)})
             del state, inp
     del flush_buf
+    torch.cuda.empty_cache()
+    return out
+
+
+def time_chain(torch, stream, named, n=50, warm=5):
+    """Times of a chain of launches on `stream`: `named` is a list of (name, fn) run in order.  Each
+    launch alone, bracketed by a pair of events (median over n; a pair adds a few microseconds of
+    stream time, so a launch-bound kernel reads long), and the chain as the time of n chains run
+    back to back divided by n.  Returns ({name: us}, chain_us)."""
+    for _ in range(warm):
+        for _, f in named:
+            f()
+    per = {name: [] for name, _ in named}
+    for _ in range(n):
+        for name, f in named:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            f()
+            b.record(stream)
+            per[name].append((a, b))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(n):
+        for _, f in named:
+            f()
+    b.record(stream)
+    torch.cuda.synchronize()
+    med = lambda pairs: round(float(np.median([x.elapsed_time(y) for x, y in pairs])) * 1e3, 2)  # noqa: E731
+    return {name: med(v) for name, v in per.items()}, round(a.elapsed_time(b) * 1e3 / n, 2)
+
+
+def cold_times(torch, stream, cases, n=20):
+    """Median time of each launch with cold caches: before every timed launch the state it reads or
+    writes is restored from its pristine copy and 1 GiB is written to a scratch buffer, so neither
+    L2 nor the 256 MB last-level cache holds any of its operands (both untimed).  cases: list of
+    (name, fn, restore)."""
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=stream.device)
+    out = {}
+    for name, f, restore in cases:
+        pairs = []
+        for _ in range(n + 2):
+            restore()
+            flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            f()
+            b.record(stream)
+            pairs.append((a, b))
+        torch.cuda.synchronize()
+        out[name] = round(float(np.median([a.elapsed_time(b) for a, b in pairs[2:]])) * 1e3, 2)
+    del flush
     torch.cuda.empty_cache()
     return out
 
@@ -298,8 +363,12 @@ def main():
             self.w = w
             self.s, self.e, self.idx = to_dev(w.seq_lens), to_dev(w.extend_lens), to_dev(w.state_index)
             self.inp, self.ape, self.state = to_dev(w.input), to_dev(w.ape), to_dev(w.state)
+            self.pristine = self.state.clone()
             self.plan_c, self.plan_w, self.counts = kvc.alloc_prefill_plan(w.cr, w.B, w.num_q, dev)
             self.out = torch.empty((self.plan_c.shape[0], w.hd), dtype=torch.float32, device=dev)
+
+        def restore(self):
+            self.state.copy_(self.pristine)
 
         def plan(self):
             kvc.plan_prefill(self.w.cr, self.s, self.e, self.idx, self.w.num_state_rows, self.w.num_q,
@@ -316,6 +385,7 @@ def main():
             self.w = w
             self.s, self.idx = to_dev(w.seq_lens), to_dev(w.state_index)
             self.inp, self.ape, self.state = to_dev(w.input), to_dev(w.ape), to_dev(w.state)
+            self.pristine = self.state.clone()
             self.plan_d = torch.empty((w.B, kvc.D_BYTES), dtype=torch.uint8, device=dev)
             self.status = torch.zeros(1, dtype=torch.int32, device=dev)
             self.out = torch.empty((w.B, w.hd), dtype=torch.float32, device=dev)
@@ -325,6 +395,9 @@ def main():
 
         def decode(self):
             kvc.decode(self.w.cr, self.w.hd, self.state, self.inp, self.ape, self.plan_d, self.out, self.status)
+
+        def restore(self):
+            self.state.copy_(self.pristine)
 
     P4, P128, D4, D128 = Prefill(p4), Prefill(p128), Decode(d4), Decode(d128)
 
@@ -588,6 +661,41 @@ def main():
     torch.cuda.synchronize()
     overlap_ms = oa.elapsed_time(ob) / args.steps
 
+    # the four kernels of the step with cold caches: state restored and 1 GiB written before every
+    # launch (untimed); the headline loop above runs its steps back to back ("warm")
+    cold = cold_times(torch, stream, [("compress_c4", P4.compress, P4.restore),
+                                      ("compress_c128", P128.compress, P128.restore),
+                                      ("decode_c4", D4.decode, D4.restore),
+                                      ("decode_c128", D128.decode, D128.restore)])
+
+    # the other named workloads, each timed as its own chain: the small ratio-4 prefill (1 request,
+    # 64 tokens, fp32, head_dim 128) and the ratio-128 prefill of 4 requests (plan -> compress ->
+    # write), and the two decode batches of the step (plan -> fused decode)
+    configs = {}
+    for name, w in (("c4_prefill_1x64", wl.c4_prefill_1x64()), ("c128_prefill_4req", wl.c128_prefill_4req())):
+        X = Prefill(w)
+        per, chain_us = time_chain(torch, stream, [("plan", X.plan), ("compress", X.compress), ("write", X.write)])
+        c = X.counts.cpu().tolist()
+        assert c[2] == 0 and c[3] == 0, (name, c)
+        seqs = X.plan_c[: c[0]].cpu().numpy().view("<u4").reshape(-1, 4)[:, 0].astype(np.int64)
+        cb = algorithmic_bytes_compress(w.cr, w.hd, w.esize, seqs)
+        wb = algorithmic_bytes_write(w.cr, w.hd, w.esize, c[1])
+        configs[name] = {"tokens": w.num_q, "rows": c[0], "writes": c[1], "dtype": "f32" if w.esize == 4 else "bf16",
+                         "head_dim": w.hd, "plan_us": per["plan"], "compress_us": per["compress"],
+                         "write_us": per["write"], "chain_us": chain_us,
+                         "tokens_per_s": round(w.num_q / (chain_us * 1e-6), 1),
+                         "compress_bytes": cb, "compress_GBps": round(cb / (per["compress"] * 1e-6) / 1e9, 1),
+                         "write_bytes": wb, "bound": "launch"}
+        del X
+    for name, D in (("c4_decode_b256", D4), ("c128_decode_b1024", D128)):
+        per, chain_us = time_chain(torch, stream, [("plan", D.plan), ("decode", D.decode)])
+        db = algorithmic_bytes_decode(D.w.cr, D.w.hd, D.w.esize, D.w.seq_lens)
+        configs[name] = {"tokens": D.w.B, "rows": int((D.w.seq_lens % D.w.cr == 0).sum()), "dtype": "bf16",
+                         "head_dim": D.w.hd, "plan_us": per["plan"], "decode_us": per["decode"],
+                         "chain_us": chain_us, "tokens_per_s": round(D.w.B / (chain_us * 1e-6), 1),
+                         "decode_bytes": db, "decode_GBps": round(db / (per["decode"] * 1e-6) / 1e9, 1),
+                         "bound": "launch"}
+
     # sanity: no device-side errors, plans as sized
     for P in (P4, P128, M4, M128):
         c = P.counts.cpu().tolist()
@@ -627,8 +735,12 @@ def main():
     def row_entry(name, nbytes, bound):
         us = kernels_us[name]
         gbps = nbytes / (us * 1e-6) / 1e9
-        return {"us": us, "bytes": int(nbytes), "GBps": round(gbps, 1), "frac": round(gbps / 8000.0, 4),
-                "bound": bound}
+        r = {"us": us, "bytes": int(nbytes), "GBps": round(gbps, 1), "frac": round(gbps / 8000.0, 4),
+             "bound": bound}
+        if name in cold:
+            r["cold_us"] = cold[name]
+            r["cold_frac"] = round(nbytes / (cold[name] * 1e-6) / 1e9 / 8000.0, 4)
+        return r
 
     step_rows = {}
     for cr, P, w in ((4, P4, p4), (128, P128, p128)):
@@ -724,7 +836,11 @@ def main():
             "traffic": measured_traffic(),
             "bytes_per_launch": dom_bytes,
             "avg_launch_us": round(dom_us, 2),
+            "cache": "warm",
+            "cold_us": cold[dominant],
+            "cold_frac": round(dom_bytes / (cold[dominant] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         },
+        "configs": configs,
         "kernels_us": kernels_us,
         "step_rows": step_rows,
         "f_rows": f_rows,
@@ -746,42 +862,75 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def _slices(n, parts):
+    """[lo, hi) bounds splitting range(n) into at most `parts` nearly equal pieces."""
+    parts = max(1, min(parts, n))
+    cuts = [n * k // parts for k in range(parts + 1)]
+    return [(a, b) for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
+
+
 def cpu_baseline(p4, p128, d4, d128, tokens, reps):
-    """The float64 C oracle over one whole step (same workloads, host copies), one core."""
+    """The float64 C oracle over one whole step (same workloads, host copies), in two legs: all the
+    cores this process may use (up to 16), then one core.  Each leg runs the unchanged oracle calls:
+    the plan on one thread, the pool over slices of C records, the write over slices of W records
+    (after every pool slice), and each decode over slices of requests, the slices on a thread pool
+    (the oracle's C calls release the interpreter lock)."""
+    import concurrent.futures
+
     import oracle
 
     oracle.build(force=False)
+    model = cpu_model()
 
-    def one_step():
+    def one_step(ex, parts):
         """The oracle calls of one step, timed; the state copies that give each run a fresh state
         (the write and the decodes change it in place) are made before the clock starts."""
         fresh = {id(w): w.state.copy() for w in (p4, p128, d4, d128)}
+
+        def run(fn, n, *args):
+            futs = [ex.submit(fn, a, b, *args) for a, b in _slices(n, parts)]
+            for f in futs:
+                f.result()
+
         t = time.perf_counter()
         for w in (p4, p128):
             cap_c, cap_w = oracle.capacities(w.cr, w.B, w.num_q)
             pc, pw, counts = oracle.plan_prefill(w.cr, w.seq_lens, w.extend_lens, w.state_index, w.num_state_rows,
                                                  w.num_q, cap_c, cap_w)
-            oracle.compress(w.cr, w.hd, w.state, w.input, w.ape, pc, counts[0])
-            oracle.write(w.cr, w.hd, fresh[id(w)], w.input, pw, counts[1])
+            run(lambda a, b: oracle.compress(w.cr, w.hd, w.state, w.input, w.ape, pc[a:b], b - a), int(counts[0]))
+            st = fresh[id(w)]
+            run(lambda a, b: oracle.write(w.cr, w.hd, st, w.input, pw[a:b], b - a), int(counts[1]))
         for w in (d4, d128):
             pd, _ = oracle.plan_decode(w.cr, w.seq_lens, w.state_index, w.num_state_rows)
-            oracle.decode(w.cr, w.hd, fresh[id(w)], w.input, w.ape, pd)
+            st = fresh[id(w)]
+            run(lambda a, b: oracle.decode(w.cr, w.hd, st, w.input[a:b], w.ape, pd[a:b]), w.B)
         return time.perf_counter() - t
 
-    times = [one_step() for _ in range(reps)]
-    sec = float(np.median(times))
-    cpu = platform.processor() or ""
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    cpu = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
-    return {"value": round(tokens / sec, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": "the whole step (both prefills, both decodes), median of %d runs, %.2f s each; %s"
-                      % (reps, sec, cpu)}
+    legs = []
+    for threads in (min(len(os.sched_getaffinity(0)), 16), 1):
+        with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
+            times = [one_step(ex, threads) for _ in range(reps)]
+        sec = float(np.median(times))
+        legs.append({"threads": threads, "value": round(tokens / sec, 1), "s_per_step": round(sec, 4),
+                     "runs": reps})
+    best = legs[0]
+    return {"value": best["value"], "unit": "tokens/s", "cores": best["threads"], "kind": "oracle",
+            "model": model, "one_core": legs[1],
+            "sample": "the whole bench step (both mixed prefills, both decode batches), float64 C oracle, "
+                      "median of %d runs per leg: %d threads %.3f s per step, 1 thread %.3f s per step; %s"
+                      % (reps, best["threads"], best["s_per_step"], legs[1]["s_per_step"], model)}
 
 
 if __name__ == "__main__":

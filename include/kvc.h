@@ -81,7 +81,10 @@
  *  in place of the prefill pool (still before kvc_write), and
  *  kvc_decode_c4_norm_rope_store in place of kvc_decode_c4.
  *  Plans depend only on lengths and indices, so one plan serves every layer.
- *  The state indices of one call must be distinct.
+ *  The state slots of one call must be distinct: the prefill planners check
+ *  it (KVC_DERR_DUPLICATE, a plan error); for a decode batch it is the
+ *  caller's precondition (two requests on one slot make the decode's writes
+ *  and pools race).
  */
 #ifndef KVC_H_
 #define KVC_H_
@@ -103,6 +106,7 @@ extern "C" {
 #define KVC_DERR_INDEX 4    /* state_index outside [0, num_state_rows / window) */
 #define KVC_DERR_CAPACITY 8 /* prefill: more C or W records than cap_c or cap_w */
 #define KVC_DERR_RECORD 16  /* a consumer met a record that points outside its buffers */
+#define KVC_DERR_DUPLICATE 32 /* prefill: two requests name the same state slot */
 
 /* limits */
 #define KVC_MAX_PREFILL_BATCH 1024
@@ -166,7 +170,8 @@ typedef struct kvc_plan_d {
  *  num_q           batch .. KVC_MAX_TOKENS-1 rows in the ragged input
  *  seq_lens, extend_lens, state_index   device int32 [batch]
  *  num_state_rows  rows of the state buffer (0 .. INT32_MAX); a state index
- *                  must lie in [0, num_state_rows / W), W = 8 or 128
+ *                  must lie in [0, num_state_rows / W), W = 8 or 128, and no
+ *                  two requests may share one (KVC_DERR_DUPLICATE)
  *  plan_c, cap_c   device output, cap_c >= 0 records (never more than
  *                  min(num_q, num_q/ratio + batch) are needed)
  *  plan_w, cap_w   device output, cap_w >= 0 records (never more than
@@ -216,7 +221,8 @@ int kvc_plan_decode(int compress_ratio, int batch, const int32_t* seq_lens, cons
  * Requirements (else KVC_EINVAL): swa_page_size % ring_size == 0; ratio 4:
  * ring_size a multiple of 8; ratio 128: ring_size == 128.
  * Errors: seq_len > r2t_stride or a request slot outside [0, num_reqs) is a
- * plan error (KVC_DERR_INDEX in counts[2], no records).  A lookup that leaves
+ * plan error (KVC_DERR_INDEX in counts[2], no records), and so are two
+ * requests with one request slot (KVC_DERR_DUPLICATE).  A lookup that leaves
  * its table, a missing SWA slot or a row outside the state buffer makes just
  * that record invalid and ORs KVC_DERR_INDEX into *status (device int32,
  * may be NULL; the caller clears it).
@@ -258,7 +264,8 @@ int kvc_plan_decode_swa(int compress_ratio, int batch, const int32_t* seq_lens, 
  *  - the written positions are those of kvc_plan_prefill; position p goes to
  *    row (p < last_position ? write_first_page : page_index[b]) * 4 + p % 4.
  * A page_index outside [0, num_state_rows / 4) is a plan error
- * (KVC_DERR_INDEX in counts[2], no records).  A bundle page outside that
+ * (KVC_DERR_INDEX in counts[2], no records), and so is a page_index that two
+ * requests share (KVC_DERR_DUPLICATE).  A bundle page outside that
  * range which a record reads or writes makes that record invalid and ORs
  * KVC_DERR_INDEX into *status (may be NULL; the caller clears it); pages that
  * are not read (the first block's masked entries) are not checked.

@@ -57,6 +57,7 @@
 #define ERR_INDEX 4    /* some state_index outside [0, num_state_rows / window) */
 #define ERR_CAPACITY 8 /* more C or W records than cap_c / cap_w */
 #define ERR_RECORD 16  /* a consumer met a record pointing outside its buffers */
+#define ERR_DUPLICATE 32 /* two requests of a prefill chunk name the same state slot */
 
 static void put_u32(uint8_t* p, uint32_t v) {
   p[0] = (uint8_t)(v & 0xFF);
@@ -107,6 +108,20 @@ static double widen(const void* base, int is_bf16, int64_t row, int64_t row_len,
   return (double)((const float*)base)[row * row_len + col];
 }
 
+/* Whether two requests of a chunk name the same in-range slot (request ring
+ * or page, request-pool row, or caller page): both would write the same
+ * state rows.  The pages leave distinct slots unstated; a chunk that breaks
+ * it is refused as a whole.  Out-of-range slots are ERR_INDEX already and
+ * are not compared. */
+static int has_duplicate(const int32_t* idx, int B, int64_t limit) {
+  for (int b = 0; b < B; ++b) {
+    if (idx[b] < 0 || idx[b] >= limit) continue;
+    for (int c = b + 1; c < B; ++c)
+      if (idx[c] == idx[b]) return 1;
+  }
+  return 0;
+}
+
 static int bad_host_args(int cr, int B) {
   if (cr != 4 && cr != 128) return 1;
   if (B < 1 || B > 1024) return 1;
@@ -136,6 +151,7 @@ int oracle_plan_prefill(int cr, int B, int num_q, const int32_t* seq_lens, const
     if (idx < 0 || idx >= num_state_rows / W) err |= ERR_INDEX;
   }
   if (total != num_q) err |= ERR_NUMQ;
+  if (has_duplicate(state_index, B, num_state_rows / W)) err |= ERR_DUPLICATE;
 
   int num_c = 0, num_w = 0;
   uint8_t* tmp_c = NULL;
@@ -485,6 +501,7 @@ int oracle_plan_prefill_swa(int cr, int B, int num_q, const int32_t* seq_lens, c
     if (rid < 0 || rid >= num_reqs || s > r2t_stride) err |= ERR_INDEX;
   }
   if (total != num_q) err |= ERR_NUMQ;
+  if (has_duplicate(req_pool_indices, B, num_reqs)) err |= ERR_DUPLICATE;
 
   int num_c = 0, num_w = 0;
   uint8_t* tmp_c = NULL;
@@ -876,6 +893,7 @@ int oracle_plan_prefill_page4(int B, int num_q, const int32_t* seq_lens, const i
     total += extend_lens[b];
   }
   if (!(err & ERR_EXTEND) && total != num_q) err |= ERR_NUMQ;
+  if (has_duplicate(page_index, B, num_state_rows / 4)) err |= ERR_DUPLICATE;
   int nc = 0, nw = 0;
   if (!err) {
     int64_t ragged_base = 0;

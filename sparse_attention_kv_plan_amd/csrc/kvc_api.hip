@@ -403,6 +403,8 @@ KVC_EXPORT const char* kvc_strerror(int code) {
       return "device data: plan needs more records than cap_c / cap_w";
     case KVC_DERR_RECORD:
       return "device data: record points outside the input or the state";
+    case KVC_DERR_DUPLICATE:
+      return "device data: two requests of a prefill chunk share a state slot";
     default:
       return "unknown kvc code";
   }

@@ -9,7 +9,8 @@
 //
 // Prefill plan, one launch, no host sync, no scratch memory:
 //   stage A  every workgroup loads the <= 1024 requests (4 per thread), checks
-//            them, and forms per request e, num_c = s/r - p0/r and num_w (the
+//            them (two requests on one slot are found with an LDS hash set),
+//            and forms per request e, num_c = s/r - p0/r and num_w (the
 //            chunk's positions the next window needs; in SWA mode also the
 //            last 4 slots of every SWA page, counted in closed form);
 //   stage B  64-lane wavefront scans (shuffles) + a 4-wave combine in LDS
@@ -92,6 +93,27 @@ __device__ __forceinline__ int32_t tail_pos(int64_t lo, int64_t t, int sps) {
 // a 4-row page of the state buffer (page-4 mode)
 __device__ __forceinline__ bool page4_ok(int32_t page, int64_t num_state_rows) {
   return page >= 0 && (int64_t)page < num_state_rows / 4;
+}
+
+// Open-addressing set of the slots of a chunk's requests, in LDS: at most
+// KVC_MAX_PREFILL_BATCH keys in twice as many entries, so a probe sequence
+// always meets an empty entry.  Two requests with the same slot follow the
+// same probe sequence, and entries only go from empty to taken, so exactly
+// one of them inserts the key and the other finds it.
+constexpr int kDupBits = 11;
+constexpr int kDupSlots = 1 << kDupBits;
+static_assert(kDupSlots >= 2 * KVC_MAX_PREFILL_BATCH, "load factor of the slot set");
+
+// Insert slot v (>= 0); true when another request had inserted it already.
+__device__ __forceinline__ bool slot_seen(int32_t* set, int32_t v) {
+  uint32_t h = ((uint32_t)v * 2654435761u) >> (32 - kDupBits);  // multiplicative hash
+  for (int probe = 0; probe < kDupSlots; ++probe) {
+    const int32_t old = atomicCAS(&set[h], -1, v);
+    if (old == -1) return false;
+    if (old == v) return true;
+    h = (h + 1) & (kDupSlots - 1);
+  }
+  return false;  // not reached (an empty entry always exists)
 }
 
 struct RequestTable {
@@ -237,12 +259,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_prefill_kernel(PlanPrefillA
   __shared__ int w_err[kPlanWaves];
   __shared__ uint32_t w_min[kPlanWaves];
   __shared__ uint32_t w_max[kPlanWaves];
+  __shared__ int32_t slot_set[kDupSlots];
 
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1);
   const int wave = t / kWave;
   const int64_t max_idx = MAP == kPlanSwa ? a.swa.num_reqs : a.num_state_rows / (MAP == kPlanPage4 ? 4 : W);
   const int sps = a.swa.swa_page_size;
+  for (int i = t; i < kDupSlots; i += kPlanThreads) slot_set[i] = -1;
+  __syncthreads();
 
   // ---- stage A: this thread's requests t*4 .. t*4+3 ----
   uint32_t ve[kPerThread], vc[kPerThread], vw[kPerThread];
@@ -257,7 +282,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_prefill_kernel(PlanPrefillA
       const int32_t s = a.seq_lens[b], e = a.extend_lens[b], idx = a.state_index[b];
       const bool ok = e >= 1 && e <= s;
       if (!ok) err |= KVC_DERR_EXTEND;
-      if (idx < 0 || (int64_t)idx >= max_idx) err |= KVC_DERR_INDEX;
+      if (idx < 0 || (int64_t)idx >= max_idx) {
+        err |= KVC_DERR_INDEX;
+      } else if (slot_seen(slot_set, idx)) {
+        err |= KVC_DERR_DUPLICATE;  // two requests would write the same state rows
+      }
       if (MAP == kPlanSwa && (int64_t)s > a.swa.stride) err |= KVC_DERR_INDEX;
       esum += e;
       const int32_t p0 = ok ? s - e : 0;

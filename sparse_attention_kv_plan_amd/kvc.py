@@ -25,7 +25,7 @@ HEADER = os.path.join(ROOT, "include", "kvc.h")
 
 KVC_OK, KVC_EINVAL, KVC_EHIP = 0, -1, -2
 KVC_F32, KVC_BF16 = 0, 1
-DERR_EXTEND, DERR_NUMQ, DERR_INDEX, DERR_CAPACITY, DERR_RECORD = 1, 2, 4, 8, 16
+DERR_EXTEND, DERR_NUMQ, DERR_INDEX, DERR_CAPACITY, DERR_RECORD, DERR_DUPLICATE = 1, 2, 4, 8, 16, 32
 WINDOW = {4: 8, 128: 128}
 ROW_MULT = {4: 4, 128: 2}
 C_BYTES, W_BYTES, D_BYTES = 16, 8, 16

@@ -53,7 +53,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_strerror(lib):
     assert kvc.strerror(0) == "ok"
-    for code in (-1, -2, 1, 2, 4, 8, 16):
+    for code in (-1, -2, 1, 2, 4, 8, 16, 32):
         assert kvc.strerror(code) and "unknown" not in kvc.strerror(code)
     assert "unknown" in kvc.strerror(12345)
 

@@ -66,3 +66,17 @@ def test_bench_refuses_more_than_one_gpu():
                        stdout=subprocess.PIPE, stderr=subprocess.PIPE, timeout=300)
     assert r.returncode == 2 and r.stdout == b""
     assert b"one GPU" in r.stderr
+
+
+def test_cpu_baseline_slices_cover_the_work_once():
+    """The all-cores oracle leg hands each thread a slice of records or requests: the slices are
+    disjoint, in order, and cover the whole range (an empty range gives no slice)."""
+    for n in (0, 1, 7, 16, 31448):
+        for parts in (1, 3, 8, 16, 64):
+            sl = bench._slices(n, parts)
+            assert len(sl) <= max(1, parts)
+            covered = [k for a, b in sl for k in range(a, b)] if n < 100 else None
+            if covered is not None:
+                assert covered == list(range(n))
+            assert all(b > a for a, b in sl) and (not sl or (sl[0][0] == 0 and sl[-1][1] == n))
+            assert all(sl[i][1] == sl[i + 1][0] for i in range(len(sl) - 1))

@@ -83,6 +83,13 @@ def test_plan_page4_errors(gpu):
     bad_idx[3] = n_pages
     args = (s, e, bad_idx, bundle, n_pages * 4, num_q, cap_c, cap_w)
     _same(gpu.plan_prefill_page4(*args), oracle.plan_prefill_page4(*args))
+    # two requests on one page: plan error
+    dup_idx = idx.copy()
+    dup_idx[9] = dup_idx[2]
+    args = (s, e, dup_idx, bundle, n_pages * 4, num_q, cap_c, cap_w)
+    o = oracle.plan_prefill_page4(*args)
+    assert o[2][2] == 32
+    _same(gpu.plan_prefill_page4(*args), o)
     # bad bundle pages that records read or write: those records only
     bad = bundle.copy()
     bad[2, 1] = -3          # load_second_page

@@ -114,10 +114,44 @@ def test_plan_prefill_errors(gpu):
         (128, [300, 130], [300, 5], [1, 0], 256, 305, 0, 0),    # zero capacities
         (128, [300, 130], [300, 5], [1, 0], 256, 305, 3, 46),   # exactly enough
         (4, [2 ** 31 - 1], [5], [0], 8, 5, 5, 5),       # very long sequence
+        (4, [8, 8, 8], [4, 4, 4], [2, 0, 2], 24, 12, 9, 12),   # two requests on one ring
+        (128, [130, 5], [2, 5], [1, 1], 256, 7, 4, 7),          # two requests on one page
+        (4, [8, 8], [4, 4], [2, 2], 16, 8, 6, 8),               # repeated index out of range: index error only
+        (4, [6, 6, 6], [2, 2, 2], [1, 0, 1], 24, 6, 6, 6),      # duplicate on the uniform-extend path
     ]
     for c in cases:
         say("plan_prefill errors", c)
         _plans_equal(gpu.plan_prefill(*c), oracle.plan_prefill(*c))
+
+
+@pytest.mark.parametrize("cr", [4, 128])
+def test_plan_prefill_duplicate_slots(gpu, cr):
+    """Batches of up to 1024 requests in which one or several state slots are repeated anywhere in
+    the batch (or not at all): the planner flags exactly the batches the oracle flags, with the
+    same counts and all-invalid records; the uniform-extend path included."""
+    rng = np.random.default_rng(900 + cr)
+    for case in range(24):
+        B = int(rng.choice([2, 3, 64, 1000, 1024]))
+        e = np.full(B, 2) if case % 3 == 0 else rng.integers(1, 40, size=B)
+        s = (rng.integers(0, 400, size=B) + e).astype(np.int32)
+        e = e.astype(np.int32)
+        slots = B + 8
+        idx = rng.permutation(slots)[:B].astype(np.int32)
+        kind = case % 4
+        if kind == 1:    # one repeat, at two random places
+            i, j = rng.choice(B, size=2, replace=False)
+            idx[j] = idx[i]
+        elif kind == 2:  # many repeats
+            k = max(1, B // 10)
+            idx[rng.choice(B, size=k, replace=False)] = idx[rng.choice(B, size=k)]
+        elif kind == 3:  # first and last
+            idx[-1] = idx[0]
+        num_q = int(e.sum())
+        cap_c, cap_w = oracle.capacities(cr, B, num_q)
+        args = (cr, s, e, idx, slots * W[cr], num_q, cap_c, cap_w)
+        o = oracle.plan_prefill(*args)
+        assert bool(o[2][2] & kvc.DERR_DUPLICATE) == (len(set(idx.tolist())) < B)
+        _plans_equal(gpu.plan_prefill(*args), o)
 
 
 @pytest.mark.parametrize("cr", [4, 128])

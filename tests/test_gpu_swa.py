@@ -97,6 +97,7 @@ def test_swa_errors(gpu):
         (4, [12], [12], [0], r2t, bad, 64, 8, 16, 12, 8, 16),         # one failed lookup
         (4, [12, 9], [12, 9], [0, 1], r2t, bad, 64, 8, 16, 21, 8, 24),
         (4, [12, 9], [12, 9], [0, 1], r2t, bad, 64, 8, 16, 21, 2, 24),  # capacity error: no lookups
+        (4, [8, 8], [4, 4], [1, 1], r2t, f2s, 64, 8, 16, 8, 6, 16),   # two requests on one slot
     ]
     for c in cases:
         say("swa errors", c[:4])

@@ -98,6 +98,9 @@ MUTANTS = [
      "        const int64_t row = ragged - 126 + i;\n        const double t"),
     ("online compress accepts buffer_len above 127", "    if (blen > 127 || (blen > 0 && (slot < 0",
      "    if ((blen > 0 && (slot < 0"),
+    ("duplicate state slots accepted", "      if (idx[c] == idx[b]) return 1;", "      if (0) return 1;"),
+    ("duplicate state slots compared with the next request only", "    for (int c = b + 1; c < B; ++c)",
+     "    for (int c = b + 1; c < B && c < b + 2; ++c)"),
     ("page4 overlap entries always from the first load page", "rp0 = blen <= 4 ? lsp : lfp;",
      "rp0 = lfp;"),
     ("page4 overlap threshold off by one", "rp0 = blen <= 4 ? lsp : lfp;",

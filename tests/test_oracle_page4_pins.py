@@ -93,6 +93,9 @@ def test_page4_errors():
     # a page index outside the state is a plan error
     pc, pw, counts, st = oracle.plan_prefill_page4(s, e, [12, 1], [(0, 1, 2, 8), (-1, -1, 3, 8)], rows, 11, 4, 11)
     assert counts.tolist() == [0, 0, ERR_INDEX, 0] and np.all(pc == 0xFF) and np.all(pw == 0xFF)
+    # two requests whose new tokens go to one page: a plan error
+    pc, pw, counts, st = oracle.plan_prefill_page4(s, e, [4, 4], [(0, 1, 2, 8), (-1, -1, 3, 8)], rows, 11, 4, 11)
+    assert counts.tolist() == [0, 0, 32, 0] and np.all(pc == 0xFF) and np.all(pw == 0xFF)
     # a bundle page that a record reads: only that record goes, and the status says so
     pc, pw, counts, st = oracle.plan_prefill_page4(s, e, [5, 1], [(0, 99, 2, 8), (-1, -1, 3, 8)], rows, 11, 4, 11)
     assert counts[2] == 0 and st == ERR_INDEX

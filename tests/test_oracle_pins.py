@@ -145,6 +145,16 @@ def test_plan_errors_and_padding():
     # capacity too small
     _, _, counts = oracle.plan_prefill(4, [64], [64], [0], 8, 64, 15, 8)
     assert counts.tolist() == [0, 0, 8, 0]
+    # two requests on one ring (not neighbours in the batch): both would write its rows
+    pc, pw, counts = oracle.plan_prefill(4, [8, 8, 8], [4, 4, 4], [2, 0, 2], 24, 12, 9, 12)
+    assert counts.tolist() == [0, 0, 32, 0] and np.all(pc == 0xFF) and np.all(pw == 0xFF)
+    _, _, counts = oracle.plan_prefill(128, [130, 5], [2, 5], [1, 1], 256, 7, 4, 7)
+    assert counts.tolist() == [0, 0, 32, 0]
+    # an index repeated outside the buffer is an index error only; distinct indices are fine
+    _, _, counts = oracle.plan_prefill(4, [8, 8], [4, 4], [2, 2], 16, 8, 6, 8)
+    assert counts.tolist() == [0, 0, 4, 0]
+    _, _, counts = oracle.plan_prefill(4, [8, 8, 8], [4, 4, 4], [2, 0, 1], 24, 12, 9, 12)
+    assert counts[2] == 0
     # host-checkable argument errors are rejected outright
     with pytest.raises(oracle.OracleError):
         oracle.plan_prefill(5, [8], [8], [0], 8, 8, 4, 4)

@@ -196,6 +196,9 @@ def test_swa_errors():
     assert counts.tolist() == [0, 0, 4, 0]
     _, _, counts, _ = oracle.plan_prefill_swa(4, [70], [4], [0], r2t, f2s, 64, 8, 16, 4, 6, 16)
     assert counts.tolist() == [0, 0, 4, 0]
+    # two requests on one request-pool row: a plan error
+    pc, pw, counts, _ = oracle.plan_prefill_swa(4, [8, 8], [4, 4], [1, 1], r2t, f2s, 64, 8, 16, 8, 6, 16)
+    assert counts.tolist() == [0, 0, 32, 0] and np.all(pc == 0xFF) and np.all(pw == 0xFF)
     # a full-cache slot with no SWA slot invalidates just the records that need it
     bad = f2s.copy()
     bad[9] = -1  # position 9 is written by this chunk
