@@ -19,8 +19,8 @@ events on the launch stream over the timed region ("cache": "warm"), and its
 cold-cache time beside it.  After the timed region, untimed passes give:
   * every launch's time and algorithmic GB/s (step_rows, f_rows);
   * the four kernels of the step with cold caches: before each launch the
-    state is restored from a pristine copy and 1 GiB is written to a scratch
-    buffer (cold_us, cold_frac);
+    state is restored from a pristine copy and then 1 GiB is read (cold_us,
+    cold_frac);
   * each named workload as its own chain (configs): the ratio-4 prefill of one
     64-token request (fp32, head_dim 128) and the ratio-128 prefill of four
     requests, plan -> compress -> write; the two decode batches, plan ->
@@ -214,15 +214,15 @@ def algorithmic_bytes_online(hd, esize, blen_of_rows, write_runs, decode_seq_len
 def sweep(torch, kvc, dev, P4, P128, to_dev):
     """Extra, labelled results: kernel time and algorithmic GB/s as the work grows (prefill: the first
     k requests of the mixed batch; decode: batches with device-generated inputs), warm and with cold
-    caches (1 GiB written before every launch, untimed)."""
+    caches (1 GiB read before every launch, untimed)."""
     stream = torch.cuda.current_stream()
-    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush_buf = torch.ones(1 << 27, dtype=torch.int64, device=dev)
 
     def med_us(f, n=10, cold=False):
         ts = []
         for _ in range(n + 2):
             if cold:
-                flush_buf.fill_(1)
+                flush_caches(flush_buf)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             f()
@@ -305,18 +305,24 @@ def time_chain(torch, stream, named, n=50, warm=5):
     return {name: med(v) for name, v in per.items()}, round(a.elapsed_time(b) * 1e3 / n, 2)
 
 
+def flush_caches(flush):
+    """Read a 1 GiB buffer (untimed): afterwards L2 and the 256 MB last-level cache hold only its clean
+    lines.  A flush by writing would leave up to 256 MB of dirty lines that the next kernel has to
+    write back to HBM on its own time."""
+    flush.sum(dtype=flush.dtype)
+
+
 def cold_times(torch, stream, cases, n=20):
     """Median time of each launch with cold caches: before every timed launch the state it reads or
-    writes is restored from its pristine copy and 1 GiB is written to a scratch buffer, so neither
-    L2 nor the 256 MB last-level cache holds any of its operands (both untimed).  cases: list of
-    (name, fn, restore)."""
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=stream.device)
+    writes is restored from its pristine copy, then 1 GiB is read, so neither L2 nor the last-level
+    cache holds any of its operands (both untimed).  cases: list of (name, fn, restore)."""
+    flush = torch.ones(1 << 27, dtype=torch.int64, device=stream.device)
     out = {}
     for name, f, restore in cases:
         pairs = []
         for _ in range(n + 2):
             restore()
-            flush.fill_(1)
+            flush_caches(flush)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             f()
@@ -661,7 +667,7 @@ def main():
     torch.cuda.synchronize()
     overlap_ms = oa.elapsed_time(ob) / args.steps
 
-    # the four kernels of the step with cold caches: state restored and 1 GiB written before every
+    # the four kernels of the step with cold caches: state restored and 1 GiB read before every
     # launch (untimed); the headline loop above runs its steps back to back ("warm")
     cold = cold_times(torch, stream, [("compress_c4", P4.compress, P4.restore),
                                       ("compress_c128", P128.compress, P128.restore),

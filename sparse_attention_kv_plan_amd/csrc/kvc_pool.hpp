@@ -31,30 +31,19 @@ struct NoPre {
   __device__ void operator()() const {}
 };
 
-template <typename T, int HD, int FIRST, typename Pre = NoPre>
-__device__ __forceinline__ void c4_pool(const typename Elem<T>::storage* __restrict__ state,
-                                        const typename Elem<T>::storage* __restrict__ input,
-                                        const typename Elem<T>::storage* __restrict__ ape, int64_t ragged, int blen,
-                                        int64_t rp0, int64_t rp1, int c, float* res, const Pre& pre = Pre()) {
+// The pool of one lane's channels [c, c + V) from the window's raw kv and
+// score vectors (entries FIRST..7); ape_of(i) gives entry i's ape vector.
+template <typename T, int FIRST, typename ApeOf>
+__device__ __forceinline__ void c4_pool_math(const u32x4* kv_raw, const u32x4* sc_raw, const ApeOf& ape_of,
+                                             float* res) {
   typedef typename Acc<T>::type A;
   constexpr int V = Elem<T>::kVec;
-  constexpr int64_t R = 4 * HD;
-  // all kv / score loads of the window are issued before any use
-  u32x4 kv_raw[8], sc_raw[8];
-#pragma unroll
-  for (int i = FIRST; i < 8; ++i) {
-    const int64_t srow = (i < 4) ? rp0 * 4 + i : rp1 * 4 + (i - 4);
-    const typename Elem<T>::storage* row = (i < blen) ? state + srow * R : input + (ragged - 7 + i) * R;
-    kv_raw[i] = load16_stream(row + ((i < 4) ? 0 : HD) + c);
-    sc_raw[i] = load16_stream(row + ((i < 4) ? 2 * HD : 3 * HD) + c);
-  }
-  pre();
   A t[8][V];
 #pragma unroll
   for (int i = FIRST; i < 8; ++i) {
     float sc[V], a[V];
     widen16<T>(sc_raw[i], sc);
-    widen16<T>(load16(ape + i * HD + c), a);  // ape is reused by every row: cached load
+    widen16<T>(ape_of(i), a);
 #pragma unroll
     for (int v = 0; v < V; ++v) t[i][v] = (A)sc[v] + (A)a[v];
   }
@@ -74,6 +63,48 @@ __device__ __forceinline__ void c4_pool(const typename Elem<T>::storage* __restr
     }
     res[v] = (float)(num / den);
   }
+}
+
+template <typename T, int HD, int FIRST, typename Pre = NoPre>
+__device__ __forceinline__ void c4_pool(const typename Elem<T>::storage* __restrict__ state,
+                                        const typename Elem<T>::storage* __restrict__ input,
+                                        const typename Elem<T>::storage* __restrict__ ape, int64_t ragged, int blen,
+                                        int64_t rp0, int64_t rp1, int c, float* res, const Pre& pre = Pre()) {
+  constexpr int64_t R = 4 * HD;
+  // all kv / score loads of the window are issued before any use
+  u32x4 kv_raw[8], sc_raw[8];
+#pragma unroll
+  for (int i = FIRST; i < 8; ++i) {
+    const int64_t srow = (i < 4) ? rp0 * 4 + i : rp1 * 4 + (i - 4);
+    const typename Elem<T>::storage* row = (i < blen) ? state + srow * R : input + (ragged - 7 + i) * R;
+    kv_raw[i] = load16_stream(row + ((i < 4) ? 0 : HD) + c);
+    sc_raw[i] = load16_stream(row + ((i < 4) ? 2 * HD : 3 * HD) + c);
+  }
+  pre();
+  // ape is reused by every row: cached loads, issued as the arithmetic needs them
+  c4_pool_math<T, FIRST>(kv_raw, sc_raw, [&](int i) { return load16(ape + i * HD + c); }, res);
+}
+
+// The decode window: entries FIRST..6 from the state (pages rp0, rp1), entry 7
+// (the new token) from the lane's own copy of its input row, q = the row's
+// four quarters |kv overlap|kv|score overlap|score| at channels [c, c + V);
+// the ape rows go out with the window's loads.
+template <typename T, int HD, int FIRST>
+__device__ __forceinline__ void c4_decode_window(const typename Elem<T>::storage* __restrict__ state,
+                                                 const typename Elem<T>::storage* __restrict__ ape, int64_t rp0,
+                                                 int64_t rp1, int c, const u32x4* q, u32x4* kv_raw, u32x4* sc_raw,
+                                                 u32x4* ap_raw) {
+  constexpr int64_t R = 4 * HD;
+#pragma unroll
+  for (int i = FIRST; i < 7; ++i) {
+    const typename Elem<T>::storage* row = state + ((i < 4) ? rp0 * 4 + i : rp1 * 4 + (i - 4)) * R;
+    kv_raw[i] = load16_stream(row + ((i < 4) ? 0 : HD) + c);
+    sc_raw[i] = load16_stream(row + ((i < 4) ? 2 * HD : 3 * HD) + c);
+  }
+#pragma unroll
+  for (int i = FIRST; i < 8; ++i) ap_raw[i] = load16(ape + i * HD + c);
+  kv_raw[7] = q[1];
+  sc_raw[7] = q[3];
 }
 
 // Rows the ratio-4 window of a record reads, checked against the buffers.
@@ -315,16 +346,47 @@ struct C128Pool {
     const A* ll = lds + S * HDW;
     const A* la = lds + 2 * S * HDW;
     A M = lm[d];
-#pragma unroll
+#pragma unroll 8
     for (int s = 1; s < S; ++s) M = amax(M, lm[s * HDW + d]);
     A Lsum = 0, Asum = 0;
-#pragma unroll
+#pragma unroll 8
     for (int s = 0; s < S; ++s) {
       const A f = softmax_exp(lm[s * HDW + d] - M);
       Lsum = afma(ll[s * HDW + d], f, Lsum);
       Asum = afma(la[s * HDW + d], f, Asum);
     }
     return (float)(Asum / Lsum);
+  }
+
+  // The slice's channels into out_row (streaming stores), each channel merged
+  // by P = NT / HDW consecutive lanes over S / P partials apiece and combined
+  // with lane shuffles: with many streams (S >= 16) this keeps every wave of
+  // the workgroup busy instead of one wave running all S steps per channel.
+  __device__ __forceinline__ static void store_merged_par(const A* lds, int cs, float* __restrict__ out_row) {
+    constexpr int P = NT / HDW;
+    static_assert(P >= 1 && (P & (P - 1)) == 0 && P <= kWave && S % P == 0, "parallel merge shape");
+    const A* lm = lds;
+    const A* ll = lds + S * HDW;
+    const A* la = lds + 2 * S * HDW;
+    const int p = threadIdx.x % P, d = threadIdx.x / P;
+    A M = lm[p * HDW + d];
+#pragma unroll
+    for (int s = p + P; s < S; s += P) M = amax(M, lm[s * HDW + d]);
+#pragma unroll
+    for (int o = 1; o < P; o <<= 1) M = amax(M, __shfl_xor(M, o, kWave));
+    A Lsum = 0, Asum = 0;
+#pragma unroll
+    for (int s = p; s < S; s += P) {
+      const A f = softmax_exp(lm[s * HDW + d] - M);
+      Lsum = afma(ll[s * HDW + d], f, Lsum);
+      Asum = afma(la[s * HDW + d], f, Asum);
+    }
+#pragma unroll
+    for (int o = 1; o < P; o <<= 1) {
+      Lsum += __shfl_xor(Lsum, o, kWave);
+      Asum += __shfl_xor(Asum, o, kWave);
+    }
+    if (p == 0) __builtin_nontemporal_store((float)(Asum / Lsum), out_row + cs * HDW + d);
   }
 
   // accumulate, then the slice's channels into out_row (streaming stores)
