@@ -56,16 +56,24 @@ __global__ __launch_bounds__(kCompressThreads) void compress_online_kernel(Onlin
   }
 }
 
-// Workgroup (g, cs) covers W records [16 g, 16 g + 16) and channel slice cs:
+// Workgroup (g, cs) covers W records [32 g, 32 g + 32) and channel slice cs:
 // it folds every run that starts among its records, one after another, each
-// by 16 streams x 8 entries over its slice (at most two rounds of loads), so
-// a request's run is spread over CS workgroups on different CUs.  The
-// records it needs (one before its range to find run heads, 127 after it for
-// run lengths) are staged in LDS with one load per thread, and a run's old
-// slot values are fetched before its window.
+// by 16 streams x 8 entries over its slice (one round of loads), so a
+// request's run is spread over CS workgroups on different CUs.  The records
+// it needs (one before its range to find run heads, 127 after it for run
+// lengths) are staged in LDS (both loads of a thread in flight together), and
+// a run's old slot values go out with its window.  A request has one run per
+// chunk (its positions after the last completed block, at most 127), so most
+// workgroups find no head and leave after the staging.  The launch is
+// latency-bound: a run takes three dependent trips to memory (records; slot
+// and window; the slot's store).  Measured by kernel trace on the mixed
+// prefill (64 runs): 13.3 us with 32 records per workgroup, 14.6 us with 16,
+// 17 and 20 us with 64 and 128 (more runs in sequence per workgroup); 256
+// threads with 4 entries per stream, or the window's loads interleaved with
+// the arithmetic, change nothing.
 constexpr int kWriteThreads = 128;
-constexpr int kWriteGroup = 16;
-constexpr int kWriteRecs = kWriteGroup + 128;  // records k0 - 1 .. k0 + 142
+constexpr int kWriteGroup = 32;
+constexpr int kWriteRecs = kWriteGroup + 128;  // records k0 - 1 .. k0 + 158
 
 template <typename T, int HD>
 struct WriteShape {
@@ -90,9 +98,21 @@ __global__ __launch_bounds__(kWriteThreads) void write_online_kernel(OnlineArgs 
   const int64_t k0 = (int64_t)(blockIdx.x / CS) * kWriteGroup;
   const int cs = blockIdx.x % CS;
   const int64_t n_w = min((int64_t)a.counts[1], (int64_t)a.cap);
-  for (int i = threadIdx.x; i < kWriteRecs; i += kWriteThreads) {
+  if (k0 >= n_w) return;  // uniform: no record of this workgroup's range (n_w >= 1 below)
+  // unconditional loads (indices clamped into [0, n_w), records outside
+  // [0, n_w) replaced afterwards), so both go out before the first wait
+  constexpr int kPerThread = (kWriteRecs + kWriteThreads - 1) / kWriteThreads;
+  uint2 r[kPerThread];
+#pragma unroll
+  for (int u = 0; u < kPerThread; ++u) {
+    const int64_t k = k0 - 1 + threadIdx.x + u * kWriteThreads;
+    r[u] = *reinterpret_cast<const uint2*>(a.plan_w + min(max(k, (int64_t)0), n_w - 1));
+  }
+#pragma unroll
+  for (int u = 0; u < kPerThread; ++u) {
+    const int i = threadIdx.x + u * kWriteThreads;
     const int64_t k = k0 - 1 + i;
-    recs[i] = (k >= 0 && k < n_w) ? *reinterpret_cast<const uint2*>(a.plan_w + k) : make_uint2(0xFFFFFFFFu, 0u);
+    if (i < kWriteRecs) recs[i] = (k >= 0 && k < n_w) ? r[u] : make_uint2(0xFFFFFFFFu, 0u);
   }
   if (threadIdx.x == 0) n_heads = 0;
   __syncthreads();

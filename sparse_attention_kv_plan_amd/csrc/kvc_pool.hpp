@@ -270,6 +270,9 @@ struct C128Pool {
         sc_raw[u] = load16_stream(row + HD + c);
         ap_raw[u] = load16(ape + (int64_t)(ape0 + es) * HD + c);
       }
+      // every load of the chunk goes out before the first use (the scheduler
+      // otherwise interleaves them with the arithmetic of earlier entries)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         A t[U];

@@ -281,6 +281,32 @@ def test_mixed_prefill_fused_store_full_size(gpu, cr):
     assert_store_close(_cache_host(cache), ref, w.name)
 
 
+@pytest.mark.parametrize("cr", [4, 128])
+def test_mixed_prefill_standalone_store_full_size(gpu, cr):
+    """64 requests, 125,792 tokens: GPU plan -> GPU pool into fp32 rows -> standalone store (the
+    launch that gives each lane group several rows), against the oracle's store of the same fp32
+    rows; every other cache row stays untouched."""
+    w = wl.mixed_prefill(cr)
+    say("standalone store workload %s: B=%d num_q=%d" % (w.name, w.B, w.num_q))
+    plan_c, plan_w, counts = kvc.alloc_prefill_plan(cr, w.B, w.num_q)
+    kvc.plan_prefill(cr, dev(w.seq_lens), dev(w.extend_lens), dev(w.state_index), w.num_state_rows, w.num_q,
+                     plan_c, plan_w, counts)
+    rows = torch.full((plan_c.shape[0], w.hd), float("nan"), dtype=torch.float32, device="cuda")
+    kvc.compress(cr, w.hd, dev(w.state), dev(w.input), dev(w.ape), plan_c, counts, rows)
+    rng = np.random.default_rng(2005 + cr)
+    si = wl.store_inputs(rng, w.hd, 64, int(w.seq_lens.max()) + 1, w.num_q)
+    wt, f, loc, cache = _store_tensors(si, w.hd)
+    kvc.norm_rope_store_prefill(cr, rows, plan_c, counts, wt, si.eps, f, loc, cache)
+    torch.cuda.synchronize()
+    c = counts.cpu().numpy()
+    assert c[2] == 0 and c[3] == 0
+    n = int(c[0])
+    ref, err = oracle.store_prefill(cr, rows.cpu().numpy(), plan_c.cpu().numpy(), n, si.norm_weight, si.eps,
+                                    si.freqs_cis, si.out_loc, np.full((si.num_cache_rows, w.hd), np.nan))
+    assert err == 0
+    assert_store_close(_cache_host(cache), ref, w.name)
+
+
 @pytest.mark.parametrize("name", ["c4_decode_b256", "c128_decode_b1024"])
 def test_decode_store_full_size(gpu, name):
     w = wl.c4_decode_b256() if name == "c4_decode_b256" else wl.c128_decode_b1024()
