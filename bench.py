@@ -24,7 +24,7 @@ cold-cache time beside it.  After the timed region, untimed passes give:
   * each named workload as its own chain (configs): the ratio-4 prefill of one
     64-token request (fp32, head_dim 128) and the ratio-128 prefill of four
     requests, plan -> compress -> write; the two decode batches, plan ->
-    decode;
+    decode; launched one by one and as a replayed HIP graph;
   * the decode step as a replayed HIP graph, and the step on four streams.
 cpu_baseline times the float64 C oracle over the same step on the host cores
 (all this process may use, up to 16, then one).
@@ -303,6 +303,29 @@ def time_chain(torch, stream, named, n=50, warm=5):
     torch.cuda.synchronize()
     med = lambda pairs: round(float(np.median([x.elapsed_time(y) for x, y in pairs])) * 1e3, 2)  # noqa: E731
     return {name: med(v) for name, v in per.items()}, round(a.elapsed_time(b) * 1e3 / n, 2)
+
+
+def time_graph(torch, stream, fns, n=100):
+    """The chain `fns` captured once as a HIP graph (on a side stream) and replayed n times back to
+    back on `stream`: the time per replay, without host launch gaps.  The chains hold no memset."""
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for f in fns:
+                f()
+    stream.wait_stream(side)
+    for _ in range(5):
+        graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(n):
+        graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return round(a.elapsed_time(b) * 1e3 / n, 2)
 
 
 def flush_caches(flush):
@@ -627,15 +650,8 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n
 
-    decode_us = {"eager": round(per_call_ms(decode_step) * 1e3, 2)}
-    side = torch.cuda.Stream()
-    side.wait_stream(stream)
-    with torch.cuda.stream(side):
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=side):
-            decode_step()
-    stream.wait_stream(side)
-    decode_us["graph"] = round(per_call_ms(graph.replay) * 1e3, 2)
+    decode_us = {"eager": round(per_call_ms(decode_step) * 1e3, 2),
+                 "graph": time_graph(torch, stream, [f for _, f in launches[6:]], n=200)}
 
     # The same step with its four chains on four streams (default priority).  The chains share no
     # buffer, so they are joined only at the two ends of the loop: a join in every step costs more
@@ -681,6 +697,7 @@ def main():
     for name, w in (("c4_prefill_1x64", wl.c4_prefill_1x64()), ("c128_prefill_4req", wl.c128_prefill_4req())):
         X = Prefill(w)
         per, chain_us = time_chain(torch, stream, [("plan", X.plan), ("compress", X.compress), ("write", X.write)])
+        graph_us = time_graph(torch, stream, [X.plan, X.compress, X.write])
         c = X.counts.cpu().tolist()
         assert c[2] == 0 and c[3] == 0, (name, c)
         seqs = X.plan_c[: c[0]].cpu().numpy().view("<u4").reshape(-1, 4)[:, 0].astype(np.int64)
@@ -688,17 +705,21 @@ def main():
         wb = algorithmic_bytes_write(w.cr, w.hd, w.esize, c[1])
         configs[name] = {"tokens": w.num_q, "rows": c[0], "writes": c[1], "dtype": "f32" if w.esize == 4 else "bf16",
                          "head_dim": w.hd, "plan_us": per["plan"], "compress_us": per["compress"],
-                         "write_us": per["write"], "chain_us": chain_us,
+                         "write_us": per["write"], "chain_us": chain_us, "graph_chain_us": graph_us,
                          "tokens_per_s": round(w.num_q / (chain_us * 1e-6), 1),
+                         "graph_tokens_per_s": round(w.num_q / (graph_us * 1e-6), 1),
                          "compress_bytes": cb, "compress_GBps": round(cb / (per["compress"] * 1e-6) / 1e9, 1),
                          "write_bytes": wb, "bound": "launch"}
         del X
     for name, D in (("c4_decode_b256", D4), ("c128_decode_b1024", D128)):
         per, chain_us = time_chain(torch, stream, [("plan", D.plan), ("decode", D.decode)])
+        graph_us = time_graph(torch, stream, [D.plan, D.decode])
         db = algorithmic_bytes_decode(D.w.cr, D.w.hd, D.w.esize, D.w.seq_lens)
         configs[name] = {"tokens": D.w.B, "rows": int((D.w.seq_lens % D.w.cr == 0).sum()), "dtype": "bf16",
                          "head_dim": D.w.hd, "plan_us": per["plan"], "decode_us": per["decode"],
-                         "chain_us": chain_us, "tokens_per_s": round(D.w.B / (chain_us * 1e-6), 1),
+                         "chain_us": chain_us, "graph_chain_us": graph_us,
+                         "tokens_per_s": round(D.w.B / (chain_us * 1e-6), 1),
+                         "graph_tokens_per_s": round(D.w.B / (graph_us * 1e-6), 1),
                          "decode_bytes": db, "decode_GBps": round(db / (per["decode"] * 1e-6) / 1e9, 1),
                          "bound": "launch"}
 
