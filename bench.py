@@ -65,7 +65,8 @@ def parse():
                     help="also time the compress and decode kernels over growing workloads (reported under "
                          "'sweep')")
     ap.add_argument("--copy-probe", action="store_true",
-                    help="only copy 1 GiB device to device 5 times (calibrates the HBM byte counters)")
+                    help="only copy 1 GiB device to device 5 times (calibrates the HBM byte counters), then "
+                         "time plain one-read-one-write streams of 128 MiB to 1 GiB")
     return ap.parse_args()
 
 
@@ -107,6 +108,11 @@ def measured_traffic():
 
 
 def copy_probe():
+    """A 1 GiB device-to-device copy, 5 times (the byte counters' calibration: every byte is read once
+    and written once), then the plain streams that bound a kernel reading as many bytes as it writes,
+    128 MiB to 1 GiB each way: torch's copy (the runtime's blit kernel) and torch's elementwise negation
+    (a vector kernel, one read and one write per element), warm (back to back) and cold (1 GiB read
+    between launches), medians of 20."""
     import torch
     n = 1 << 30
     src = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -122,6 +128,27 @@ def copy_probe():
     ms = a.elapsed_time(b) / 5
     print(json.dumps({"copy_probe_bytes": n, "copies": 5, "ms_per_copy": round(ms, 4),
                       "GBps_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+    flush = torch.ones(1 << 27, dtype=torch.int64, device="cuda")
+    streams = []
+    for mib in (128, 256, 512, 1024):
+        m = mib << 20
+        s64, d64 = src[:m].view(torch.int64), dst[:m].view(torch.int64)
+        for kind, f in (("copy_", lambda: d64.copy_(s64)), ("neg", lambda: torch.neg(s64, out=d64))):
+            for cold in (False, True):
+                ts = []
+                for _ in range(22):
+                    if cold:
+                        flush_caches(flush)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    f()
+                    e1.record()
+                    ts.append((e0, e1))
+                torch.cuda.synchronize()
+                us = float(np.median([x.elapsed_time(y) for x, y in ts[2:]])) * 1e3
+                streams.append({"MiB_each_way": mib, "kernel": kind, "cache": "cold" if cold else "warm",
+                                "us": round(us, 2), "GBps": round(2 * m / (us * 1e-6) / 1e9, 1)})
+    print(json.dumps({"read1_write1_streams": streams}), flush=True)
 
 
 def algorithmic_bytes_compress(cr, hd, esize, seq_lens_of_rows):
@@ -214,7 +241,9 @@ def algorithmic_bytes_online(hd, esize, blen_of_rows, write_runs, decode_seq_len
 def sweep(torch, kvc, dev, P4, P128, to_dev):
     """Extra, labelled results: kernel time and algorithmic GB/s as the work grows (prefill: the first
     k requests of the mixed batch; decode: batches with device-generated inputs), warm and with cold
-    caches (1 GiB read before every launch, untimed)."""
+    caches (1 GiB read before every launch, untimed).  Each decode batch also times a plain stream of
+    the same algorithmic bytes (torch's elementwise negation, half of them read and half written) under
+    the same two conditions; of_stream is the stream's time over the decode's."""
     stream = torch.cuda.current_stream()
     flush_buf = torch.ones(1 << 27, dtype=torch.int64, device=dev)
 
@@ -269,10 +298,19 @@ def sweep(torch, kvc, dev, P4, P128, to_dev):
             cold_us = med_us(lambda: kvc.decode(cr, hd, state, inp, ape, plan_d, o, status), cold=True)
             assert int(status.item()) == 0
             nbytes = algorithmic_bytes_decode(cr, hd, 2, seq)
+            del state, inp
+            # the ceiling at this size: a plain stream moving the same bytes, half read and half written
+            half = max(nbytes // 16, 1)
+            src = torch.ones(half, dtype=torch.int64, device=dev)
+            dst = torch.empty_like(src)
+            s_us = med_us(lambda: torch.neg(src, out=dst))
+            s_cold = med_us(lambda: torch.neg(src, out=dst), cold=True)
+            del src, dst
             out["decode"].append({"ratio": cr, "batch": B, "boundaries": int((seq % cr == 0).sum()), "us": us,
                                   "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "cold_us": cold_us,
-                                  "cold_GBps": round(nbytes / (cold_us * 1e-6) / 1e9, 1)})
-            del state, inp
+                                  "cold_GBps": round(nbytes / (cold_us * 1e-6) / 1e9, 1),
+                                  "stream_us": s_us, "stream_cold_us": s_cold,
+                                  "of_stream": round(s_us / us, 3), "cold_of_stream": round(s_cold / cold_us, 3)})
     del flush_buf
     torch.cuda.empty_cache()
     return out
