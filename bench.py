@@ -928,15 +928,23 @@ def main():
 
 
 def cpu_model():
-    """The host CPU's model name from /proc/cpuinfo."""
+    """The host CPU from /proc/cpuinfo: its model name, with the family / model / stepping numbers
+    (a virtual machine may show only a generic name) and the logical CPUs the host lists."""
+    fields, n = {}, 0
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                k, _, v = line.partition(":")
+                k = k.strip()
+                if k == "processor":
+                    n += 1
+                elif k in ("model name", "cpu family", "model", "stepping") and k not in fields:
+                    fields[k] = v.strip()
     except OSError:
         pass
-    return platform.processor() or "unknown"
+    name = fields.get("model name") or platform.processor() or "unknown"
+    nums = ", ".join("%s %s" % (k, fields[k]) for k in ("cpu family", "model", "stepping") if k in fields)
+    return "%s (%s%s%d logical CPUs)" % (name, nums, "; " if nums else "", n or (os.cpu_count() or 0))
 
 
 def _slices(n, parts):
