@@ -34,6 +34,15 @@ struct Elem<Bf16> {
   static constexpr int kVec = 8;
 };
 
+// Puts a wave-uniform value (a kernel argument) in scalar registers at this
+// point.  The compiler otherwise loads an argument where it is first used;
+// one first used inside a branch or a loop then costs a trip to memory of its
+// own there, after whatever the kernel waited for before.
+template <typename T>
+__device__ __forceinline__ void in_sgprs(T v) {
+  asm volatile("" ::"s"(v));
+}
+
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ u32x2 load8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }

@@ -70,7 +70,9 @@ __global__ __launch_bounds__(kCompressThreads) void compress_online_kernel(Onlin
 // prefill (64 runs): 13.3 us with 32 records per workgroup, 14.6 us with 16,
 // 17 and 20 us with 64 and 128 (more runs in sequence per workgroup); 256
 // threads with 4 entries per stream, or the window's loads interleaved with
-// the arithmetic, change nothing.
+// the arithmetic, change nothing.  The count is read in the records' round
+// trip and every argument at the start (an argument first read inside the
+// run loop cost a trip of its own there).
 constexpr int kWriteThreads = 128;
 constexpr int kWriteGroup = 32;
 constexpr int kWriteRecs = kWriteGroup + 128;  // records k0 - 1 .. k0 + 158
@@ -94,20 +96,28 @@ __global__ __launch_bounds__(kWriteThreads) void write_online_kernel(OnlineArgs 
   __shared__ typename Pool::A lds[Pool::kLdsElems];
   __shared__ uint2 recs[kWriteRecs];
   __shared__ int heads[kWriteGroup];
-  __shared__ int n_heads, run_end;
+  __shared__ int n_heads, run_end[kWriteThreads / kWave];
   const int64_t k0 = (int64_t)(blockIdx.x / CS) * kWriteGroup;
   const int cs = blockIdx.x % CS;
-  const int64_t n_w = min((int64_t)a.counts[1], (int64_t)a.cap);
-  if (k0 >= n_w) return;  // uniform: no record of this workgroup's range (n_w >= 1 below)
-  // unconditional loads (indices clamped into [0, n_w), records outside
-  // [0, n_w) replaced afterwards), so both go out before the first wait
+  in_sgprs(a.state);  // the arguments a run needs, read with the first ones
+  in_sgprs(a.input);
+  in_sgprs(a.ape);
+  in_sgprs(a.num_slots);
+  in_sgprs(a.num_q);
+  // The count and the records in one round trip: the record loads are
+  // unconditional, their indices clamped into the buffer [0, cap) (cap >= 1),
+  // and records at or past the count are replaced once both are in.
+  const int32_t count = a.counts[1];
   constexpr int kPerThread = (kWriteRecs + kWriteThreads - 1) / kWriteThreads;
   uint2 r[kPerThread];
 #pragma unroll
   for (int u = 0; u < kPerThread; ++u) {
     const int64_t k = k0 - 1 + threadIdx.x + u * kWriteThreads;
-    r[u] = *reinterpret_cast<const uint2*>(a.plan_w + min(max(k, (int64_t)0), n_w - 1));
+    r[u] = *reinterpret_cast<const uint2*>(a.plan_w + min(max(k, (int64_t)0), (int64_t)a.cap - 1));
   }
+  asm volatile("" ::: "memory");  // every load above goes out before the count is tested
+  const int64_t n_w = min((int64_t)count, (int64_t)a.cap);
+  if (k0 >= n_w) return;  // uniform: no record of this workgroup's range (n_w >= 1 below)
 #pragma unroll
   for (int u = 0; u < kPerThread; ++u) {
     const int i = threadIdx.x + u * kWriteThreads;
@@ -133,21 +143,7 @@ __global__ __launch_bounds__(kWriteThreads) void write_online_kernel(OnlineArgs 
       if (cs == 0 && threadIdx.x == 0) atomicOr(a.counts + 3, KVC_DERR_RECORD);
       continue;
     }
-    // run length: records j0 .. j0+n-1 continue the head's slot, rows and positions
-    if (threadIdx.x == 0) run_end = 128 - p0;
-    __syncthreads();
-    if (threadIdx.x > 0 && threadIdx.x < 128 - p0) {
-      const uint2 r = recs[j0 + threadIdx.x];
-      if (!(r.x == (uint32_t)(ragged + threadIdx.x) && (int64_t)(int32_t)r.y == loc + threadIdx.x))
-        atomicMin(&run_end, (int)threadIdx.x);
-    }
-    __syncthreads();
-    const int n = run_end;
-    __syncthreads();  // every thread has read run_end before the next run resets it
-    if (ragged + n > a.num_q) {  // uniform
-      if (cs == 0 && threadIdx.x == 0) atomicOr(a.counts + 3, KVC_DERR_RECORD);
-      continue;
-    }
+    // the slot's old values go out before the run's length is known
     float* st = a.state + slot * 3 * HD + cs * HDW;
     const int d = threadIdx.x;
     const bool cont = p0 > 0;  // the block started before this chunk: continue the slot
@@ -157,7 +153,30 @@ __global__ __launch_bounds__(kWriteThreads) void write_online_kernel(OnlineArgs 
       l0 = st[HD + d];
       a0 = st[2 * HD + d];
     }
-    // entries e in [p0, p0 + n) of the block: input row ragged - p0 + e, ape row e
+    // run length: records j0 .. j0+n-1 continue the head's slot, rows and
+    // positions; n is the first record that breaks the run (or the block's
+    // end), found by a ballot in each wave and the waves' minimum.  (An LDS
+    // atomicMin here became a scalar loop over the active lanes, 1.4 us.)
+    bool brk = false;
+    if (threadIdx.x > 0 && threadIdx.x < 128 - p0) {
+      const uint2 r = recs[j0 + threadIdx.x];
+      brk = !(r.x == (uint32_t)(ragged + threadIdx.x) && (int64_t)(int32_t)r.y == loc + threadIdx.x);
+    }
+    const unsigned long long breaks = __ballot(brk);
+    if (threadIdx.x % kWave == 0)
+      run_end[threadIdx.x / kWave] = breaks ? (int)(threadIdx.x + __ffsll(breaks) - 1) : 128 - p0;
+    __syncthreads();
+    int n = run_end[0];
+#pragma unroll
+    for (int w = 1; w < kWriteThreads / kWave; ++w) n = min(n, run_end[w]);
+    __syncthreads();  // every thread has read run_end before the next run writes it
+    if (ragged + n > a.num_q) {  // uniform
+      if (cs == 0 && threadIdx.x == 0) atomicOr(a.counts + 3, KVC_DERR_RECORD);
+      continue;
+    }
+    // entries e in [p0, p0 + n) of the block: input row ragged - p0 + e, ape
+    // row e.  (Issuing the window before n is known means loading the rows
+    // past the run too, which costs more than the wait it saves.)
     Pool::accumulate_range(static_cast<const E*>(a.input), static_cast<const E*>(a.ape), ragged - p0, 0, p0, p0 + n,
                            cs, lds);
     if (d < HDW) {

@@ -239,16 +239,84 @@ struct C128Pool {
 
   // The online-state form: entry e (0..127) is input row row0 + e with ape row
   // ape0 + e, and only entries lo <= e < hi take part (0 <= lo < hi <= 128).
-  // The others are loaded from row row0 + lo (always in range, so the load
-  // count stays fixed) and weighted 0.  A chunk whose entries are all out of
-  // range leaves its stream's partial untouched.
+  // Every entry is loaded (the load count stays fixed): an entry out of
+  // [lo, hi) loads the nearest entry in range (the same few rows, so cache
+  // hits) and is weighed 0.  A chunk whose entries are all out of range
+  // leaves its stream's partial untouched.
+  struct Chunk {
+    u32x4 kv[U], sc[U], ap[U];
+  };
+
+  // the loads of chunk k0 (entries sid + S * (k0 + u) of this thread's stream)
+  __device__ __forceinline__ static void load_chunk(const typename Elem<T>::storage* __restrict__ input,
+                                                    const typename Elem<T>::storage* __restrict__ ape, int64_t row0,
+                                                    int ape0, int lo, int hi, int k0, int cs, Chunk& ch) {
+    constexpr int64_t R = 2 * HD;
+    const int sid = threadIdx.x / kLanes;
+    const int c = cs * HDW + (threadIdx.x % kLanes) * V;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = min(max(sid + S * (k0 + u), lo), hi - 1);
+      const typename Elem<T>::storage* row = input + (row0 + e) * R;
+      ch.kv[u] = load16_stream(row + c);
+      ch.sc[u] = load16_stream(row + HD + c);
+      ch.ap[u] = load16(ape + (int64_t)(ape0 + e) * HD + c);
+    }
+  }
+
+  // folds chunk k0 into the running (m, l, acc) of this thread's channels
+  __device__ __forceinline__ static void fold_chunk(const Chunk& ch, int lo, int hi, int k0, A* m, A* l, A* acc) {
+    const int sid = threadIdx.x / kLanes;
+    bool in[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = sid + S * (k0 + u);
+      in[u] = e >= lo && e < hi;
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      A t[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float sc[V], ap[V];
+        widen16<T>(ch.sc[u], sc);
+        widen16<T>(ch.ap[u], ap);
+        t[u] = in[u] ? (A)sc[v] + (A)ap[v] : (A)-INFINITY;
+      }
+      A cm = t[0];
+#pragma unroll
+      for (int u = 1; u < U; ++u) cm = amax(cm, t[u]);
+      const A nm = amax(m[v], cm);
+      const A sh = nm == (A)-INFINITY ? (A)0 : nm;  // nothing in range yet: keep the zeros
+      const A scale = softmax_exp(m[v] - sh);
+      A lv = l[v] * scale, av = acc[v] * scale;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float kv[V];
+        widen16<T>(ch.kv[u], kv);
+        const A w = softmax_exp(t[u] - sh);
+        lv += w;
+        av = afma(w, in[u] ? (A)kv[v] : (A)0, av);
+      }
+      m[v] = nm;
+      l[v] = lv;
+      acc[v] = av;
+    }
+  }
+
+  // this thread's partial into lds, then a workgroup barrier
+  __device__ __forceinline__ static void store_partial(const A* m, const A* l, const A* acc, A* lds) {
+    const int sid = threadIdx.x / kLanes;
+    const int cl = (threadIdx.x % kLanes) * V;
+    store_acc<V>(lds + sid * HDW + cl, m);
+    store_acc<V>(lds + S * HDW + sid * HDW + cl, l);
+    store_acc<V>(lds + 2 * S * HDW + sid * HDW + cl, acc);
+    __syncthreads();
+  }
+
   __device__ __forceinline__ static void accumulate_range(const typename Elem<T>::storage* __restrict__ input,
                                                           const typename Elem<T>::storage* __restrict__ ape,
                                                           int64_t row0, int ape0, int lo, int hi, int cs, A* lds) {
-    constexpr int64_t R = 2 * HD;
-    const int sid = threadIdx.x / kLanes;
-    const int cl = (threadIdx.x % kLanes) * V;
-    const int c = cs * HDW + cl;
     A m[V], l[V], acc[V];
 #pragma unroll
     for (int v = 0; v < V; ++v) {
@@ -258,59 +326,15 @@ struct C128Pool {
     }
     for (int k0 = 0; k0 < PER; k0 += U) {
       if constexpr (kPrio) progress_priority(k0 * 4 / PER);
-      u32x4 kv_raw[U], sc_raw[U], ap_raw[U];
-      bool in[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int e = sid + S * (k0 + u);
-        in[u] = e >= lo && e < hi;
-        const int es = in[u] ? e : lo;
-        const typename Elem<T>::storage* row = input + (row0 + es) * R;
-        kv_raw[u] = load16_stream(row + c);
-        sc_raw[u] = load16_stream(row + HD + c);
-        ap_raw[u] = load16(ape + (int64_t)(ape0 + es) * HD + c);
-      }
+      Chunk ch;
+      load_chunk(input, ape, row0, ape0, lo, hi, k0, cs, ch);
       // every load of the chunk goes out before the first use (the scheduler
       // otherwise interleaves them with the arithmetic of earlier entries)
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int v = 0; v < V; ++v) {
-        A t[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          float sc[V], ap[V];
-          widen16<T>(sc_raw[u], sc);
-          widen16<T>(ap_raw[u], ap);
-          t[u] = in[u] ? (A)sc[v] + (A)ap[v] : (A)-INFINITY;
-        }
-        A cm = t[0];
-#pragma unroll
-        for (int u = 1; u < U; ++u) cm = amax(cm, t[u]);
-        const A nm = amax(m[v], cm);
-        const A sh = nm == (A)-INFINITY ? (A)0 : nm;  // nothing in range yet: keep the zeros
-        const A scale = softmax_exp(m[v] - sh);
-        A lv = l[v] * scale, av = acc[v] * scale;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          float kv[V];
-          widen16<T>(kv_raw[u], kv);
-          const A w = softmax_exp(t[u] - sh);
-          lv += w;
-          av = afma(w, in[u] ? (A)kv[v] : (A)0, av);
-        }
-        m[v] = nm;
-        l[v] = lv;
-        acc[v] = av;
-      }
+      fold_chunk(ch, lo, hi, k0, m, l, acc);
     }
     if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
-    A* lm = lds;
-    A* ll = lds + S * HDW;
-    A* la = lds + 2 * S * HDW;
-    store_acc<V>(lm + sid * HDW + cl, m);
-    store_acc<V>(ll + sid * HDW + cl, l);
-    store_acc<V>(la + sid * HDW + cl, acc);
-    __syncthreads();
+    store_partial(m, l, acc, lds);
   }
 
   // The merged (max, sum, weighted sum) of channel d of the slice, with an
