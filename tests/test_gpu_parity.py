@@ -292,7 +292,7 @@ def _scale_all(a, dtype, factor):
 @pytest.mark.parametrize("scale", [3.0, 30.0, 1000.0])
 def test_fp32_bar_at_large_input_scales(gpu, cr, scale):
     """fp32 inputs (kv, scores and ape) 3, 30 and 1000 times the configs' size, prefill and decode,
-    at the spec bar 1e-5 + 1e-5 |ref|.  At these sizes two nearly equal leading weights on
+    at the fp32 bar 1e-5 + 1e-5 |ref|.  At these sizes two nearly equal leading weights on
     kv values of opposite sign leave |ref| small while the terms are large, so the bar asks for
     weights correct to a few parts in 1e8 of the kv spread: the pool's float64 arithmetic for
     fp32 inputs gives that for any finite input with |kv| up to 2^30."""
