@@ -128,6 +128,45 @@ def test_online_decode(gpu, hd, dtype):
         assert_slots_close(st_g, st_o, idx[valid], "decode")
 
 
+@pytest.mark.parametrize("hd,dtype", [(512, "bf16"), (128, "f32")])
+def test_online_write_run_shapes(gpu, hd, dtype):
+    """The state update where runs are short and many (every record a run of its own, so a
+    32-record group holds up to 32 runs), where runs cross group boundaries, where a run fills a
+    block up to its last open position (127 records) and where it continues a block that began
+    in an earlier chunk: slots equal the oracle's, untouched slots stay bit-identical."""
+    rng = np.random.default_rng(900 + hd)
+    cases = {
+        "runs of 1": np.ones(160, np.int64),
+        "runs of 1 to 3": rng.integers(1, 4, size=120),
+        "runs of 2 to 40": rng.integers(2, 41, size=40),
+        "runs of 127": np.full(6, 127),
+    }
+    for name, runs in cases.items():
+        B = len(runs)
+        # a run is the chunk's positions after the block's last completed position: prefix p0 % 128 + run <= 127
+        p0 = np.array([int(rng.integers(0, 128 - r)) if r < 127 else 0 for r in runs]) + 128 * rng.integers(0, 3, B)
+        e = runs.astype(np.int32)
+        s = (p0 + e).astype(np.int32)
+        num_q = int(e.sum())
+        slots_n = B + 5
+        idx = rng.permutation(slots_n)[:B].astype(np.int32)
+        x = rng.standard_normal((num_q, 2 * hd)).astype(np.float32)
+        inp = wl.to_bf16_bits(x) if dtype == "bf16" else x
+        a = (0.1 * rng.standard_normal((128, hd))).astype(np.float32)
+        ape = wl.to_bf16_bits(a) if dtype == "bf16" else a
+        slots = _slots(rng, slots_n, hd)
+        cap_c, cap_w = oracle.capacities(128, B, num_q)
+        pc, pw, counts = oracle.plan_prefill(128, s, e, idx, slots_n * 128, num_q, cap_c, cap_w)
+        assert counts[2] == 0 and counts[1] == num_q, name  # every new token is written: no block closes
+        say("online write %s hd=%d %s B=%d num_w=%d" % (name, hd, dtype, B, counts[1]))
+        st_o, err = oracle.write_online(hd, slots, inp, ape, pw, counts[1])
+        st_g, gerr = gpu.write_online(hd, slots, inp, ape, pw, counts[1])
+        assert err == gerr == 0, name
+        assert_slots_close(st_g, st_o, idx, "write " + name)
+        untouched = np.setdiff1d(np.arange(slots_n), idx)
+        assert np.array_equal(st_g[untouched].view(np.uint32), slots[untouched].view(np.uint32)), name
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_online_chunked_prefill_then_decode(gpu, dtype):
     """Random chunkings and decode steps from NaN slots: the GPU emits the oracle's rows."""
