@@ -381,6 +381,58 @@ def test_decode_maximum_batch(gpu):
     assert np.array_equal(st_g, st_o), "state differs after decode"
 
 
+@pytest.mark.parametrize("B,hd", [(4100, 128), (16384, 512), (40000, 128)])
+def test_decode_c128_large_batches(gpu, B, hd):
+    """Ratio-128 decode past 4096 requests, where the kernel groups 64 (up to 32 768) or 256
+    requests per pool workgroup; 16 384 at hd 512 bf16 is the bench sweep's launch shape.  The
+    whole batch runs on the GPU from device-drawn inputs (a state of up to 4 GiB).  The oracle
+    then pools every closing request and 256 others, each from a copy of its own page, and every
+    state row is checked: each new token's row holds its input row bit for bit, and no other row
+    changes."""
+    cr, Wn = 128, 128
+    R = 2 * hd
+    dev = gpu.device
+    rng = np.random.default_rng(B + hd)
+    s = rng.integers(1, 65537, size=B).astype(np.int64)
+    close = rng.choice(B, size=max(8, B // 64), replace=False)  # more closing requests, the first block among them
+    s[close] = rng.integers(1, 512, size=len(close)) * 128
+    s[close[0]] = 128
+    s = s.astype(np.int32)
+    idx = rng.permutation(B).astype(np.int32)
+    g = torch.Generator(device=dev)
+    g.manual_seed(B * 7 + hd)
+    state = torch.randn((B * Wn, R), generator=g, device=dev).to(torch.bfloat16)
+    inp = torch.randn((B, R), generator=g, device=dev).to(torch.bfloat16)
+    ape = (0.1 * torch.randn((Wn, hd), generator=g, device=dev)).to(torch.bfloat16)
+    pd, status = oracle.plan_decode(cr, s, idx, B * Wn)
+    assert status == 0
+    closing = np.nonzero(s % cr == 0)[0]
+    others = rng.choice(np.nonzero(s % cr != 0)[0], size=256, replace=False)
+    sample = np.concatenate([closing, others])
+    pages = state.view(B, Wn, R)[torch.from_numpy(idx[sample].astype(np.int64)).to(dev)].contiguous()
+    pristine = state.clone()
+    say("decode c128 large batch B=%d hd=%d closing=%d" % (B, hd, len(closing)))
+    out = torch.full((B, hd), float("nan"), dtype=torch.float32, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    kvc.decode(cr, hd, state, inp, ape, torch.from_numpy(pd).to(dev), out, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    loc = torch.from_numpy(idx.astype(np.int64) * Wn + (s.astype(np.int64) - 1) % Wn).to(dev)
+    assert torch.equal(state[loc].view(torch.int16), inp.view(torch.int16)), "new tokens' rows"
+    state[loc] = pristine[loc]
+    assert torch.equal(state.view(torch.int16), pristine.view(torch.int16)), "a row other than a new token's changed"
+    del state, pristine
+    n = len(sample)
+    bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)  # noqa: E731
+    pd_c, status = oracle.plan_decode(cr, s[sample], np.arange(n, dtype=np.int32), n * Wn)
+    ref, err = oracle.decode(cr, hd, bits(pages.view(n * Wn, R)), bits(inp[torch.from_numpy(sample).to(dev)]),
+                             bits(ape), pd_c)
+    assert status == err == 0
+    got = out[torch.from_numpy(sample).to(dev)].cpu().numpy().astype(np.float64)
+    assert_pool_close(got, ref, "bf16", "decode c128 B=%d" % B)
+    assert np.all(got[len(closing):] == 0.0)
+
+
 def test_first_block_never_reads_masked_rows(gpu):
     """Block 0 of ratio 4: the overlap entries precede the sequence and must not be loaded.
     The state is NaN and the ragged rows before the request hold +-inf; a read of either
