@@ -166,14 +166,21 @@ __global__ __launch_bounds__(kThreads) void decode_c4_store_kernel(DecodeArgs a)
 }
 
 // Ratio 128: one launch, two roles chosen by workgroup index.
-//  - Pool workgroups (the first n_pool): workgroup (g, cs) loads the records of
-//    request group g (gp requests, one per thread) and pools each of the
-//    group's boundary requests over channel slice cs: 64 channels, so the
-//    workgroup's 256 threads are 4V streams of 64/V lanes, each stream holding
-//    128/(4V) entries, and the whole 128-entry window of the slice is one
-//    round of loads; the stream partials merge in LDS.  The slices of a row
-//    need no merge (the softmax is per channel), so a boundary request is
-//    spread over HD/64 workgroups on different CUs with no exchange.
+//  - Pool workgroups (the first n_pool): the batch is cut into ranges of
+//    1024 requests, and each range has R rank slots per channel slice.
+//    Workgroup (q, r, cs) loads the range's records (4 per thread, one round
+//    of loads), ranks the range's boundary requests in request order (a
+//    ballot per wave and pass, prefix counts in LDS), and pools those whose
+//    rank is r modulo R over channel slice cs: 64 channels, so the
+//    workgroup's 256 threads are 4V streams of 64/V lanes, each stream
+//    holding 128/(4V) entries, and the whole 128-entry window of the slice is
+//    one round of loads; the stream partials merge in LDS.  Ranking spreads
+//    boundary requests evenly over the slots wherever they sit in the batch,
+//    so a run of neighbouring requests that all close a block is pooled by
+//    many workgroups at once, not one after another by a single one.  The
+//    slices of a row need no merge (the softmax is per channel), so a
+//    boundary request is spread over HD/64 workgroups on different CUs with
+//    no exchange.
 //  - Copy workgroups: 8 requests each.  The 8 input rows are loaded at once
 //    (16-byte vectors, 2*HD/V per row, the vectors of a row on consecutive
 //    lanes; 4 per thread at hd 512 bf16: copies with 8 or more vectors per
@@ -184,12 +191,13 @@ __global__ __launch_bounds__(kThreads) void decode_c4_store_kernel(DecodeArgs a)
 // The pool reads entries 0..126 of the page and takes entry 127, the new
 // token, from the input row; the copy writes only row 127 of the page
 // (write_loc of a boundary request), so the two roles touch disjoint rows.
-// gp (the pool group) is chosen by the host: small batches have few boundary
-// requests and want them spread over many workgroups, large ones want few
-// workgroups that find nothing to pool.
+// R (the rank slots per range) is chosen by the host: with random lengths a
+// range holds about 8 boundary requests, and more slots mean more workgroups
+// that scan the range and find nothing to pool.
 constexpr int kDec128Threads = 256;
 constexpr int kDec128CopyGroup = 8;
-constexpr int kDec128MaxPoolGroup = 1024;
+constexpr int kDec128Range = 1024;  // requests ranked together
+constexpr int kDec128Passes = kDec128Range / kDec128Threads;
 constexpr int kDec128SliceChannels = 64;
 
 template <typename T, int HD>
@@ -209,30 +217,58 @@ __device__ __forceinline__ bool dec128_ok(const kvc_plan_d& rec, int64_t b, cons
 }
 
 template <typename T, int HD>
-__device__ __forceinline__ void dec128_pool_role(const DecodeArgs& a, int64_t g, int cs, int gp) {
+__device__ __forceinline__ void dec128_pool_role(const DecodeArgs& a, int64_t q, int r, int n_slots, int cs) {
   typedef typename Elem<T>::storage E;
   typedef typename Dec128Shape<T, HD>::Pool Pool;
+  constexpr int kWaves = kDec128Threads / kWave;
   __shared__ typename Pool::A lds[Pool::kLdsElems];
-  __shared__ int32_t req[kDec128MaxPoolGroup], page[kDec128MaxPoolGroup];
-  __shared__ int n;
-  if (threadIdx.x == 0) n = 0;
+  __shared__ int32_t req[kDec128Range], page[kDec128Range];
+  __shared__ int cnt[kDec128Passes][kWaves];  // boundary requests per pass and wave
+  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
+  const int64_t base = q * kDec128Range;
+  // the range's records, clamped into the batch (a record past the batch is
+  // loaded from the last request and not counted), all in one round of loads
+  kvc_plan_d rec[kDec128Passes];
+#pragma unroll
+  for (int i = 0; i < kDec128Passes; ++i)
+    rec[i] = load_plan_d(a.plan_d + min(base + i * kDec128Threads + t, (int64_t)a.batch - 1));
+  bool pools[kDec128Passes];
+  unsigned long long mask[kDec128Passes];
+#pragma unroll
+  for (int i = 0; i < kDec128Passes; ++i) {
+    const int64_t b = base + i * kDec128Threads + t;
+    pools[i] = b < a.batch && !plan_d_invalid(rec[i]) && (rec[i].seq_len & 127u) == 0u && dec128_ok(rec[i], b, a);
+    mask[i] = __ballot(pools[i]);
+    if (lane == 0) cnt[i][wave] = __popcll(mask[i]);
+  }
   __syncthreads();
-  for (int k = threadIdx.x; k < gp; k += kDec128Threads) {
-    const int64_t b = g * gp + k;
-    if (b >= a.batch) break;
-    const kvc_plan_d rec = load_plan_d(a.plan_d + b);
-    if (!plan_d_invalid(rec) && (rec.seq_len & 127u) == 0u && dec128_ok(rec, b, a)) {
-      const int j = atomicAdd(&n, 1);  // boundary requests are independent: their order is free
-      req[j] = (int32_t)b;
-      page[j] = rec.read_page_0;
+  // rank = the boundary requests before this one in the range (request order)
+  int total = 0;
+#pragma unroll
+  for (int i = 0; i < kDec128Passes; ++i) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) total += cnt[i][w];
+  }
+#pragma unroll
+  for (int i = 0; i < kDec128Passes; ++i) {
+    int pre = 0;  // boundary requests of the earlier passes and of the earlier waves of this pass
+#pragma unroll
+    for (int i2 = 0; i2 < kDec128Passes; ++i2) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) pre += (i2 < i || (i2 == i && w < wave)) ? cnt[i2][w] : 0;
+    }
+    const int rank = pre + __popcll(mask[i] & __lanemask_lt());
+    if (pools[i] && rank % n_slots == r) {
+      req[rank / n_slots] = (int32_t)(base + i * kDec128Threads + t);
+      page[rank / n_slots] = rec[i].read_page_0;
     }
   }
   __syncthreads();
-  const int cnt = n;
+  const int cnt_mine = total > r ? (total - 1 - r) / n_slots + 1 : 0;
   const E* state = static_cast<const E*>(a.state);
   const E* input = static_cast<const E*>(a.input);
   const E* ape = static_cast<const E*>(a.ape);
-  for (int j = 0; j < cnt; ++j) {  // uniform over the workgroup
+  for (int j = 0; j < cnt_mine; ++j) {  // uniform over the workgroup
     Pool::accumulate(state, input, ape, req[j], 127, page[j], cs, lds);
     Pool::store_merged_par(lds, cs, a.out + (int64_t)req[j] * HD);
     __syncthreads();  // the next pool reuses lds
@@ -307,22 +343,29 @@ __device__ __forceinline__ void dec128_copy_role(const DecodeArgs& a, int64_t b0
 }
 
 template <typename T, int HD>
-__global__ __launch_bounds__(kDec128Threads) void decode_c128_kernel(DecodeArgs a, int gp, int n_pool) {
+__global__ __launch_bounds__(kDec128Threads) void decode_c128_kernel(DecodeArgs a, int n_slots, int n_pool) {
   constexpr int CS = Dec128Shape<T, HD>::CS;
   if ((int)blockIdx.x < n_pool) {
-    dec128_pool_role<T, HD>(a, blockIdx.x / CS, blockIdx.x % CS, gp);
+    const int slot = blockIdx.x / CS;  // (range, rank slot)
+    dec128_pool_role<T, HD>(a, slot / n_slots, slot % n_slots, n_slots, blockIdx.x % CS);
   } else {
     dec128_copy_role<T, HD>(a, (int64_t)(blockIdx.x - n_pool) * kDec128CopyGroup);
   }
 }
 
-// Requests per pool workgroup: 16 up to 4096 requests (boundary requests, one
-// in 128 for random lengths, spread over many workgroups), then 64, and 256
-// beyond 32768 (fewer workgroups that find nothing to pool).  Measured on
-// MI355X with random lengths: at 16384 requests 64 beats 16 and 256 by 3-12%,
-// at 65536 256 beats 64 by 2-3%; below 4096, 16 is 30% faster than 64.
-inline int dec128_pool_group(int batch) {
-  return batch <= 4096 ? 16 : batch <= 32768 ? 64 : 256;
+// Rank slots per range of 1024 requests: 8 up to 32 768 requests, then 4.
+// Measured on MI355X at hd 512 bf16 (HIP events, 1/128 of the requests
+// closing a block) against the previous design, which pooled the boundary
+// requests of each group of 16-256 neighbours in one workgroup:
+//  - boundaries at random places: 24.9 against 29.6 us at 16 384 requests,
+//    49.3 against 47.6 at 32 768, 88.2 against 84.8 at 65 536 (4 slots;
+//    8 slots take 91.2 there);
+//  - all boundaries in the first requests of the batch: 60 against 198 us,
+//    116 against 208, 399 against 754;
+//  - 1024 requests (5 closing): 5.8 against 6.0 us by kernel trace.
+// More slots spread a cluster wider but make more workgroups scan each range.
+inline int dec128_rank_slots(int batch) {
+  return batch <= 32768 ? 8 : 4;
 }
 
 template <typename T, int HD>
@@ -337,10 +380,10 @@ struct C4Go {
 template <typename T, int HD>
 struct C128Go {
   static hipError_t go(const DecodeArgs& a, hipStream_t s) {
-    const int gp = dec128_pool_group(a.batch);
-    const int n_pool = (a.batch + gp - 1) / gp * Dec128Shape<T, HD>::CS;
+    const int n_slots = dec128_rank_slots(a.batch);
+    const int n_pool = (a.batch + kDec128Range - 1) / kDec128Range * n_slots * Dec128Shape<T, HD>::CS;
     const int n_copy = (a.batch + kDec128CopyGroup - 1) / kDec128CopyGroup;
-    decode_c128_kernel<T, HD><<<(unsigned)(n_pool + n_copy), kDec128Threads, 0, s>>>(a, gp, n_pool);
+    decode_c128_kernel<T, HD><<<(unsigned)(n_pool + n_copy), kDec128Threads, 0, s>>>(a, n_slots, n_pool);
     return hipGetLastError();
   }
 };

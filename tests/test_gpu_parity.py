@@ -381,20 +381,26 @@ def test_decode_maximum_batch(gpu):
     assert np.array_equal(st_g, st_o), "state differs after decode"
 
 
-@pytest.mark.parametrize("B,hd", [(4100, 128), (16384, 512), (40000, 128)])
-def test_decode_c128_large_batches(gpu, B, hd):
-    """Ratio-128 decode past 4096 requests, where the kernel groups 64 (up to 32 768) or 256
-    requests per pool workgroup; 16 384 at hd 512 bf16 is the bench sweep's launch shape.  The
-    whole batch runs on the GPU from device-drawn inputs (a state of up to 4 GiB).  The oracle
-    then pools every closing request and 256 others, each from a copy of its own page, and every
-    state row is checked: each new token's row holds its input row bit for bit, and no other row
-    changes."""
+@pytest.mark.parametrize("B,hd,layout", [(4100, 128, "random"), (16384, 512, "random"), (40000, 128, "random"),
+                                         (16384, 128, "clustered"), (40000, 128, "clustered")])
+def test_decode_c128_large_batches(gpu, B, hd, layout):
+    """Ratio-128 decode at large batches, where the pool workgroups rank the closing requests of
+    each range of 1024 requests over 8 (up to 32 768 requests) or 4 slots; 16 384 at hd 512 bf16
+    is the bench sweep's launch shape.  Closing requests sit at random places, or in one
+    contiguous run across several ranges (every slot then pools many).  The whole batch runs on
+    the GPU from device-drawn inputs (a state of up to 4 GiB).  The oracle then pools every
+    closing request and 256 others, each from a copy of its own page, and every state row is
+    checked: each new token's row holds its input row bit for bit, and no other row changes."""
     cr, Wn = 128, 128
     R = 2 * hd
     dev = gpu.device
-    rng = np.random.default_rng(B + hd)
+    rng = np.random.default_rng(B + hd + (layout == "clustered"))
     s = rng.integers(1, 65537, size=B).astype(np.int64)
-    close = rng.choice(B, size=max(8, B // 64), replace=False)  # more closing requests, the first block among them
+    if layout == "clustered":  # a run of 1500 neighbours all closing a block, across range edges
+        s[s % cr == 0] += 1
+        close = np.arange(700, 2200)
+    else:  # more closing requests at random places
+        close = rng.choice(B, size=max(8, B // 64), replace=False)  # the first block among them
     s[close] = rng.integers(1, 512, size=len(close)) * 128
     s[close[0]] = 128
     s = s.astype(np.int32)
