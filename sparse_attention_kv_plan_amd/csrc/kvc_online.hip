@@ -56,26 +56,28 @@ __global__ __launch_bounds__(kCompressThreads) void compress_online_kernel(Onlin
   }
 }
 
-// Workgroup (g, cs) covers W records [32 g, 32 g + 32) and channel slice cs:
-// it folds every run that starts among its records, one after another, each
-// by 16 streams x 8 entries over its slice (one round of loads), so a
-// request's run is spread over CS workgroups on different CUs.  The records
-// it needs (one before its range to find run heads, 127 after it for run
-// lengths) are staged in LDS (both loads of a thread in flight together), and
-// a run's old slot values go out with its window.  A request has one run per
-// chunk (its positions after the last completed block, at most 127), so most
-// workgroups find no head and leave after the staging.  The launch is
-// latency-bound: a run takes three dependent trips to memory (records; slot
-// and window; the slot's store).  Measured by kernel trace on the mixed
-// prefill (64 runs): 13.3 us with 32 records per workgroup, 14.6 us with 16,
-// 17 and 20 us with 64 and 128 (more runs in sequence per workgroup); 256
-// threads with 4 entries per stream, or the window's loads interleaved with
-// the arithmetic, change nothing.  The count is read in the records' round
-// trip and every argument at the start (an argument first read inside the
-// run loop cost a trip of its own there).
+// Workgroup (g, cs) covers W records [32 g, 32 g + 32) and channel slice cs,
+// and folds every run that starts among its records.  The records it needs
+// (one before its range to find run heads, 127 after it for run lengths) are
+// staged in LDS together with the count (one round trip); a ballot per wave
+// marks the records that continue no run, and each head's length is the
+// distance to the next such record.  Runs of up to 8 records (a few tokens
+// per request per chunk, as when several tokens are verified at once) are
+// folded side by side, 8 threads each (one 16-byte vector of the slice per
+// thread, the run's entries in turn); longer runs one after another, each by
+// 16 streams x 8 entries over the slice (one round of loads) merged in LDS,
+// so a long run is spread over CS workgroups on different CUs.  A request has
+// one run per chunk (its positions after the last completed block, at most
+// 127), so most workgroups find no head and leave after the staging.
+// Measured by kernel trace on the mixed prefill (64 runs of 1-127 records):
+// 13.3 us with 32 records per workgroup, 14.6 us with 16, 17 and 20 us with
+// 64 and 128; 256 threads with 4 entries per stream, or the window's loads
+// interleaved with the arithmetic, change nothing.
 constexpr int kWriteThreads = 128;
 constexpr int kWriteGroup = 32;
 constexpr int kWriteRecs = kWriteGroup + 128;  // records k0 - 1 .. k0 + 158
+constexpr int kShortRun = 8;                   // runs folded side by side
+constexpr int kShortChunk = 4;                 // entries per round of loads in a short run
 
 template <typename T, int HD>
 struct WriteShape {
@@ -86,19 +88,109 @@ __device__ __forceinline__ int64_t slot_of(uint2 r) {
   return (r.x == 0xFFFFFFFFu || (int32_t)r.y < 0) ? -1 : (int32_t)r.y / 128;
 }
 
+// Whether record r continues the run of the record q before it: the next
+// ragged row and the next state row of the same block.
+__device__ __forceinline__ bool continues(uint2 q, uint2 r) {
+  return r.x != 0xFFFFFFFFu && r.x == q.x + 1u && (int32_t)r.y == (int32_t)q.y + 1 && ((int32_t)r.y & 127) != 0;
+}
+
+// A run of n <= kShortRun records folded by one thread over V channels [c, c + V)
+// of its slot: the block's entries p0 .. p0 + n - 1 (input rows ragged ..,
+// ape rows p0 ..), onto the slot's partial when the block began earlier.
+template <typename T, int HD>
+__device__ __forceinline__ void fold_short_run(const OnlineArgs& a, int64_t ragged, int64_t slot, int p0, int n,
+                                               int c) {
+  typedef typename Elem<T>::storage E;
+  typedef typename Acc<T>::type A;
+  constexpr int V = Elem<T>::kVec;
+  constexpr int64_t R = 2 * HD;
+  const E* input = static_cast<const E*>(a.input);
+  const E* ape = static_cast<const E*>(a.ape);
+  float* st = a.state + slot * 3 * HD + c;
+  A m[V], l[V], acc[V];
+  if (p0 > 0) {  // continue the slot
+    float m0[V], l0[V], a0[V];
+#pragma unroll
+    for (int v = 0; v < V; v += 4) {
+      widen16<float>(load16(st + v), m0 + v);
+      widen16<float>(load16(st + HD + v), l0 + v);
+      widen16<float>(load16(st + 2 * HD + v), a0 + v);
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      m[v] = m0[v];
+      l[v] = l0[v];
+      acc[v] = a0[v];
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      m[v] = -INFINITY;
+      l[v] = 0;
+      acc[v] = 0;
+    }
+  }
+  for (int e0 = 0; e0 < n; e0 += kShortChunk) {
+    u32x4 kv_raw[kShortChunk], sc_raw[kShortChunk], ap_raw[kShortChunk];
+#pragma unroll
+    for (int u = 0; u < kShortChunk; ++u) {  // entries past the run load its last one (not used)
+      const int e = min(e0 + u, n - 1);
+      kv_raw[u] = load16_stream(input + (ragged + e) * R + c);
+      sc_raw[u] = load16_stream(input + (ragged + e) * R + HD + c);
+      ap_raw[u] = load16(ape + (int64_t)(p0 + e) * HD + c);
+    }
+#pragma unroll
+    for (int u = 0; u < kShortChunk; ++u) {
+      if (e0 + u >= n) break;
+      float kv[V], sc[V], ap[V];
+      widen16<T>(kv_raw[u], kv);
+      widen16<T>(sc_raw[u], sc);
+      widen16<T>(ap_raw[u], ap);
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const A t = (A)sc[v] + (A)ap[v];
+        const A nm = amax(m[v], t);
+        const A f = softmax_exp(m[v] - nm), w = softmax_exp(t - nm);  // f = 0 on a fresh block
+        l[v] = afma(l[v], f, w);
+        acc[v] = afma(acc[v], f, w * (A)kv[v]);
+        m[v] = nm;
+      }
+    }
+  }
+  // stored relative to the fp32 value the slot keeps as its maximum
+  float mo[V], lo[V], ao[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const A M = slot_shift(m[v]);
+    const A f = softmax_exp(m[v] - M);
+    mo[v] = (float)M;
+    lo[v] = (float)(l[v] * f);
+    ao[v] = (float)(acc[v] * f);
+  }
+  store_floats<V>(st, mo);
+  store_floats<V>(st + HD, lo);
+  store_floats<V>(st + 2 * HD, ao);
+}
+
 template <typename T, int HD>
 __global__ __launch_bounds__(kWriteThreads) void write_online_kernel(OnlineArgs a) {
   typedef typename Elem<T>::storage E;
+  constexpr int V = Elem<T>::kVec;
   constexpr int CS = WriteShape<T, HD>::CS;
   constexpr int HDW = HD / CS;
-  static_assert(HDW <= kWriteThreads, "one channel of the slice per thread");
+  constexpr int kVecs = HDW / V;                      // vectors of a slice (8)
+  constexpr int kSide = kWriteThreads / kVecs;        // short runs folded at once (16)
+  constexpr int kWords = 2 * kWriteThreads / kWave;   // break-mask words over 256 record places
+  static_assert(HDW <= kWriteThreads && kWriteRecs <= 2 * kWriteThreads, "write shape");
   typedef C128Pool<T, HD, kWriteThreads, CS, 8> Pool;  // a stream's 8 entries in one round of loads
   __shared__ typename Pool::A lds[Pool::kLdsElems];
   __shared__ uint2 recs[kWriteRecs];
-  __shared__ int heads[kWriteGroup];
-  __shared__ int n_heads, run_end[kWriteThreads / kWave];
+  __shared__ unsigned long long stop[kWords];  // bit k of word w: record 64 w + k continues no run
+  __shared__ int run_j[2][kWriteGroup], run_n[2][kWriteGroup];  // [0] short runs, [1] long: head in recs, length
+  __shared__ int n_runs[2];
   const int64_t k0 = (int64_t)(blockIdx.x / CS) * kWriteGroup;
   const int cs = blockIdx.x % CS;
+  const int t = threadIdx.x;
   in_sgprs(a.state);  // the arguments a run needs, read with the first ones
   in_sgprs(a.input);
   in_sgprs(a.ape);
@@ -112,7 +204,7 @@ __global__ __launch_bounds__(kWriteThreads) void write_online_kernel(OnlineArgs 
   uint2 r[kPerThread];
 #pragma unroll
   for (int u = 0; u < kPerThread; ++u) {
-    const int64_t k = k0 - 1 + threadIdx.x + u * kWriteThreads;
+    const int64_t k = k0 - 1 + t + u * kWriteThreads;
     r[u] = *reinterpret_cast<const uint2*>(a.plan_w + min(max(k, (int64_t)0), (int64_t)a.cap - 1));
   }
   asm volatile("" ::: "memory");  // every load above goes out before the count is tested
@@ -120,32 +212,68 @@ __global__ __launch_bounds__(kWriteThreads) void write_online_kernel(OnlineArgs 
   if (k0 >= n_w) return;  // uniform: no record of this workgroup's range (n_w >= 1 below)
 #pragma unroll
   for (int u = 0; u < kPerThread; ++u) {
-    const int i = threadIdx.x + u * kWriteThreads;
+    const int i = t + u * kWriteThreads;
     const int64_t k = k0 - 1 + i;
     if (i < kWriteRecs) recs[i] = (k >= 0 && k < n_w) ? r[u] : make_uint2(0xFFFFFFFFu, 0u);
   }
-  if (threadIdx.x == 0) n_heads = 0;
+  if (t < 2) n_runs[t] = 0;
   __syncthreads();
-  if (threadIdx.x < kWriteGroup) {
-    const uint2 r = recs[threadIdx.x + 1];
-    if (r.x != 0xFFFFFFFFu && (slot_of(recs[threadIdx.x]) != slot_of(r) || slot_of(r) < 0))
-      heads[atomicAdd(&n_heads, 1)] = (int)threadIdx.x;  // runs touch distinct slots: their order is free
+  // which records continue no run (a ballot per wave; places past the staged records count as stops)
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int k = p * kWriteThreads + t;
+    const bool cont = k >= 1 && k < kWriteRecs && continues(recs[k - 1], recs[k]);
+    const unsigned long long m = __ballot(!cont);
+    if (t % kWave == 0) stop[p * (kWriteThreads / kWave) + t / kWave] = m;
   }
   __syncthreads();
-  const int nh = n_heads;
-  for (int h = 0; h < nh; ++h) {
-    const int j0 = heads[h] + 1;  // the head's index in recs
+  if (t < kWriteGroup) {
+    const int j0 = t + 1;  // a head is a record whose slot differs from the one before
+    const uint2 head = recs[j0];
+    if (head.x != 0xFFFFFFFFu && (slot_of(recs[t]) != slot_of(head) || slot_of(head) < 0)) {
+      // its run: records j0 .. j0+n-1, up to the next record that continues no run
+      int k = j0 + 1;
+      while (k < kWords * kWave) {  // ends by the staged records' end: every place past it stops
+        const unsigned long long m = stop[k >> 6] >> (k & 63);
+        if (m) {
+          k += __ffsll(m) - 1;
+          break;
+        }
+        k = ((k >> 6) + 1) << 6;
+      }
+      const int n = k - j0;
+      const int64_t loc = (int32_t)head.y, ragged = head.x;
+      if (loc < 0 || loc / 128 >= a.num_slots || ragged + n > a.num_q) {
+        if (cs == 0) atomicOr(a.counts + 3, KVC_DERR_RECORD);
+      } else {
+        const int kind = n > kShortRun;
+        const int i = atomicAdd(&n_runs[kind], 1);  // runs touch distinct slots: their order is free
+        run_j[kind][i] = j0;
+        run_n[kind][i] = n;
+      }
+    }
+  }
+  __syncthreads();
+  // short runs side by side: thread t folds vector t % kVecs of run t / kVecs
+  const int ns = n_runs[0];
+  for (int i0 = 0; i0 < ns; i0 += kSide) {
+    const int i = i0 + t / kVecs;
+    if (i < ns) {
+      const uint2 head = recs[run_j[0][i]];
+      const int64_t loc = (int32_t)head.y;
+      fold_short_run<T, HD>(a, head.x, loc / 128, (int)(loc % 128), run_n[0][i], cs * HDW + (t % kVecs) * V);
+    }
+  }
+  // long runs one after another, each by the whole workgroup
+  const int nl = n_runs[1];
+  for (int h = 0; h < nl; ++h) {
+    const int j0 = run_j[1][h], n = run_n[1][h];
     const uint2 head = recs[j0];
     const int64_t loc = (int32_t)head.y, ragged = head.x;
-    const int64_t slot = loc >= 0 ? loc / 128 : -1;
-    const int p0 = loc >= 0 ? (int)(loc % 128) : 0;
-    if (loc < 0 || slot >= a.num_slots || ragged >= a.num_q) {  // uniform over the workgroup
-      if (cs == 0 && threadIdx.x == 0) atomicOr(a.counts + 3, KVC_DERR_RECORD);
-      continue;
-    }
-    // the slot's old values go out before the run's length is known
+    const int64_t slot = loc / 128;
+    const int p0 = (int)(loc % 128);
     float* st = a.state + slot * 3 * HD + cs * HDW;
-    const int d = threadIdx.x;
+    const int d = t;
     const bool cont = p0 > 0;  // the block started before this chunk: continue the slot
     float m0 = 0.f, l0 = 0.f, a0 = 0.f;
     if (cont && d < HDW) {
@@ -153,30 +281,7 @@ __global__ __launch_bounds__(kWriteThreads) void write_online_kernel(OnlineArgs 
       l0 = st[HD + d];
       a0 = st[2 * HD + d];
     }
-    // run length: records j0 .. j0+n-1 continue the head's slot, rows and
-    // positions; n is the first record that breaks the run (or the block's
-    // end), found by a ballot in each wave and the waves' minimum.  (An LDS
-    // atomicMin here became a scalar loop over the active lanes, 1.4 us.)
-    bool brk = false;
-    if (threadIdx.x > 0 && threadIdx.x < 128 - p0) {
-      const uint2 r = recs[j0 + threadIdx.x];
-      brk = !(r.x == (uint32_t)(ragged + threadIdx.x) && (int64_t)(int32_t)r.y == loc + threadIdx.x);
-    }
-    const unsigned long long breaks = __ballot(brk);
-    if (threadIdx.x % kWave == 0)
-      run_end[threadIdx.x / kWave] = breaks ? (int)(threadIdx.x + __ffsll(breaks) - 1) : 128 - p0;
-    __syncthreads();
-    int n = run_end[0];
-#pragma unroll
-    for (int w = 1; w < kWriteThreads / kWave; ++w) n = min(n, run_end[w]);
-    __syncthreads();  // every thread has read run_end before the next run writes it
-    if (ragged + n > a.num_q) {  // uniform
-      if (cs == 0 && threadIdx.x == 0) atomicOr(a.counts + 3, KVC_DERR_RECORD);
-      continue;
-    }
-    // entries e in [p0, p0 + n) of the block: input row ragged - p0 + e, ape
-    // row e.  (Issuing the window before n is known means loading the rows
-    // past the run too, which costs more than the wait it saves.)
+    // entries e in [p0, p0 + n) of the block: input row ragged - p0 + e, ape row e
     Pool::accumulate_range(static_cast<const E*>(a.input), static_cast<const E*>(a.ape), ragged - p0, 0, p0, p0 + n,
                            cs, lds);
     if (d < HDW) {
