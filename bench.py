@@ -605,9 +605,10 @@ def main():
     # the uniform-extend variant of the mixed batch (every extend 2, the multi-token-prediction shape):
     # the planner's equal-extend path, timed in the breakdown pass only
     M4, M128 = Prefill(wl.mixed_prefill(4, uniform_extend=2)), Prefill(wl.mixed_prefill(128, uniform_extend=2))
+    OM128 = Online(M128, M128.w.B, 4130)  # the online state after the same chunk: 64 runs of 2 tokens
     mtp_launches = [("plan_prefill c4 e=2", M4.plan), ("compress_c4 e=2", M4.compress), ("write c4 e=2", M4.write),
                     ("plan_prefill c128 e=2", M128.plan), ("compress_c128 e=2", M128.compress),
-                    ("write c128 e=2", M128.write)]
+                    ("write c128 e=2", M128.write), ("write_c128_online e=2", OM128.write)]
 
     ST4, ST128 = Store(P4, p4.num_q, 3004), Store(P128, p128.num_q, 3128)
     SD4S, SD128S = Store(D4, d4.B, 3003), Store(D128, d128.B, 3129)
