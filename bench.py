@@ -192,9 +192,10 @@ def algorithmic_bytes_plan_prefill(B, cap_c, cap_w):
     return 12 * B + 16 * cap_c + 8 * cap_w + 16
 
 
-def algorithmic_bytes_plan_decode(B):
-    """Bytes a decode planner must move: two int32 per request in, one 16-byte record out."""
-    return 8 * B + 16 * B
+def algorithmic_bytes_plan_decode(B, n_list=None):
+    """Bytes a decode planner must move: two int32 per request in, one 16-byte record out, and with
+    a ratio-128 boundary list its n_list entries and the count (8 bytes each)."""
+    return 8 * B + 16 * B + (0 if n_list is None else 8 * n_list + 8)
 
 
 def algorithmic_bytes_write(cr, hd, esize, num_w):
@@ -293,9 +294,12 @@ def sweep(torch, kvc, dev, P4, P128, to_dev):
             plan_d = torch.empty((B, kvc.D_BYTES), dtype=torch.uint8, device=dev)
             status = torch.zeros(1, dtype=torch.int32, device=dev)
             o = torch.empty((B, hd), dtype=torch.float32, device=dev)
-            kvc.plan_decode(cr, to_dev(seq), to_dev(idx), B * W, plan_d, status)
-            us = med_us(lambda: kvc.decode(cr, hd, state, inp, ape, plan_d, o, status))
-            cold_us = med_us(lambda: kvc.decode(cr, hd, state, inp, ape, plan_d, o, status), cold=True)
+            bl = kvc.boundary_list(B, dev) if cr == 128 else None
+            kvc.plan_decode(cr, to_dev(seq), to_dev(idx), B * W, plan_d, status, boundaries=bl)
+            us = med_us(lambda: kvc.decode(cr, hd, state, inp, ape, plan_d, o, status, boundaries=bl))
+            cold_us = med_us(lambda: kvc.decode(cr, hd, state, inp, ape, plan_d, o, status, boundaries=bl), cold=True)
+            # ratio 128 without the list: the pool workgroups rank the closing requests themselves
+            scan_us = med_us(lambda: kvc.decode(cr, hd, state, inp, ape, plan_d, o, status)) if cr == 128 else None
             assert int(status.item()) == 0
             nbytes = algorithmic_bytes_decode(cr, hd, 2, seq)
             del state, inp
@@ -310,7 +314,8 @@ def sweep(torch, kvc, dev, P4, P128, to_dev):
                                   "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "cold_us": cold_us,
                                   "cold_GBps": round(nbytes / (cold_us * 1e-6) / 1e9, 1),
                                   "stream_us": s_us, "stream_cold_us": s_cold,
-                                  "of_stream": round(s_us / us, 3), "cold_of_stream": round(s_cold / cold_us, 3)})
+                                  "of_stream": round(s_us / us, 3), "cold_of_stream": round(s_cold / cold_us, 3),
+                                  "no_list_us": scan_us})
     del flush_buf
     torch.cuda.empty_cache()
     return out
@@ -456,12 +461,16 @@ def main():
             self.plan_d = torch.empty((w.B, kvc.D_BYTES), dtype=torch.uint8, device=dev)
             self.status = torch.zeros(1, dtype=torch.int32, device=dev)
             self.out = torch.empty((w.B, w.hd), dtype=torch.float32, device=dev)
+            # ratio 128: the planner's boundary list feeds the decode's pool workgroups
+            self.bl = kvc.boundary_list(w.B, dev) if w.cr == 128 else None
 
         def plan(self):
-            kvc.plan_decode(self.w.cr, self.s, self.idx, self.w.num_state_rows, self.plan_d, self.status)
+            kvc.plan_decode(self.w.cr, self.s, self.idx, self.w.num_state_rows, self.plan_d, self.status,
+                            boundaries=self.bl)
 
         def decode(self):
-            kvc.decode(self.w.cr, self.w.hd, self.state, self.inp, self.ape, self.plan_d, self.out, self.status)
+            kvc.decode(self.w.cr, self.w.hd, self.state, self.inp, self.ape, self.plan_d, self.out, self.status,
+                       boundaries=self.bl)
 
         def restore(self):
             self.state.copy_(self.pristine)
@@ -820,8 +829,9 @@ def main():
         step_rows["write c%d" % cr] = row_entry(
             "write c%d" % cr, algorithmic_bytes_write(cr, w.hd, w.esize, c[1]), "latency")
     for cr, D, w in ((4, D4, d4), (128, D128, d128)):
-        step_rows["plan_decode c%d" % cr] = row_entry("plan_decode c%d" % cr, algorithmic_bytes_plan_decode(w.B),
-                                                      "latency")
+        n_list = int((w.seq_lens % 128 == 0).sum()) if cr == 128 else None
+        step_rows["plan_decode c%d" % cr] = row_entry(
+            "plan_decode c%d" % cr, algorithmic_bytes_plan_decode(w.B, n_list), "latency")
         step_rows["decode_c%d" % cr] = row_entry(
             "decode_c%d" % cr, algorithmic_bytes_decode(cr, w.hd, w.esize, w.seq_lens), "latency")
 

@@ -74,7 +74,9 @@
  *                 kvc_write (compress must read the state as it was before
  *                 this chunk's writes: c4.cuh, flash_c4_prefill launches the
  *                 compress kernel before the write kernel);
- *  decode step:   kvc_plan_decode -> kvc_decode_c4 | kvc_decode_c128.
+ *  decode step:   kvc_plan_decode -> kvc_decode_c4 | kvc_decode_c128 (for
+ *                 ratio 128 the planner can also write a boundary list that
+ *                 the decode then takes: the same results, fewer loads).
  *  The compressed rows then go through norm + rotary embedding into a bf16
  *  cache: kvc_norm_rope_store_prefill / kvc_norm_rope_store_decode after the
  *  pool, or kvc_compress_c4_norm_rope_store / kvc_compress_c128_norm_rope_store
@@ -193,9 +195,20 @@ int kvc_plan_prefill(int compress_ratio, int batch, int num_q, const int32_t* se
  * out of range gets an invalid record; `status` (device int32 [1], may be
  * NULL) receives the OR of the error bits.
  *  batch 1 .. KVC_MAX_DECODE_BATCH.
+ *
+ * boundaries (ratio 128 only, else NULL; may be NULL): device int32
+ * [2 * batch + 2], 8-byte aligned, owned by the caller.  The planner fills
+ * it with the boundary list, an index of the records for kvc_decode_c128:
+ * for the n requests whose record is valid and whose seq_len % 128 == 0 (the
+ * new token closes a block), in request order, entry k is the pair
+ * (request b, read_page_0 of its record) at [2k], [2k + 1]; n is at
+ * [2 * batch] and [2 * batch + 1] is 0.  Entries past n are left as they
+ * were.  The list is not part of the method: it lets the decode find its
+ * pooling requests without scanning the records.
  */
 int kvc_plan_decode(int compress_ratio, int batch, const int32_t* seq_lens, const int32_t* state_index,
-                    int64_t num_state_rows, kvc_plan_d* plan_d, int32_t* status, void* stream);
+                    int64_t num_state_rows, kvc_plan_d* plan_d, int32_t* boundaries, int32_t* status,
+                    void* stream);
 
 /*
  * SWA-paged state mapping (c_plan.cuh page: plan_compress_prefill_kernel0,
@@ -239,11 +252,12 @@ int kvc_plan_prefill_swa(int compress_ratio, int batch, int num_q, const int32_t
  * positions max(seq_len - 1 - ratio, 0) and seq_len - 1 divided by the ratio.
  * A request with seq_len <= 0, a bad slot or a failed lookup gets an invalid
  * record; *status (may be NULL) receives the OR of the error bits.
+ * boundaries: as for kvc_plan_decode (ratio 128 only, may be NULL).
  */
 int kvc_plan_decode_swa(int compress_ratio, int batch, const int32_t* seq_lens, const int32_t* req_pool_indices,
                         const int32_t* req_to_token, int64_t r2t_stride, int64_t num_reqs, const int32_t* full_to_swa,
                         int64_t num_full, int swa_page_size, int ring_size, int64_t num_state_rows,
-                        kvc_plan_d* plan_d, int32_t* status, void* stream);
+                        kvc_plan_d* plan_d, int32_t* boundaries, int32_t* status, void* stream);
 
 /*
  * Ratio 4 over caller-allocated 4-row pages (c4.cuh page, PageMode::Page4Align
@@ -340,10 +354,18 @@ int kvc_decode_c4(kvc_dtype dtype, int head_dim, void* state, int64_t num_state_
  * kvc_decode_c128 - fused decode step for ratio 128 (compressor_v2.py,
  * _c128_compress_decode_kernel): as kvc_decode_c4 with the 128-entry window
  * of page read_page_0, pooled when seq_len % 128 == 0.
+ * boundaries (may be NULL; 8-byte aligned): the boundary list that
+ * kvc_plan_decode or kvc_plan_decode_swa wrote in the same call as plan_d.
+ * With it, the pooled rows are those of its entries; without it, the decode
+ * finds the pooling requests in plan_d itself.  The results are the same,
+ * bit for bit.  A list that does not match plan_d is the caller's error:
+ * the count is clamped to [0, batch], an entry outside the batch or the
+ * state is skipped with KVC_DERR_RECORD in *status, and other mismatches
+ * leave the pooled rows undefined (never an access outside the buffers).
  */
 int kvc_decode_c128(kvc_dtype dtype, int head_dim, void* state, int64_t num_state_rows, const void* input,
-                    const void* ape, const kvc_plan_d* plan_d, int batch, int32_t* status, float* out,
-                    void* stream);
+                    const void* ape, const kvc_plan_d* plan_d, const int32_t* boundaries, int batch,
+                    int32_t* status, float* out, void* stream);
 
 /*
  * Norm, rotary embedding and store of the compressed rows (compressor_v2.py

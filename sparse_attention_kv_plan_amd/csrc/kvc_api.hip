@@ -21,6 +21,8 @@ bool hd_ok(int hd) { return hd == 128 || hd == 256 || hd == 512; }
 bool rows_ok(int64_t rows) { return rows >= 0 && rows <= INT32_MAX; }
 int status_of(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_EHIP; }
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+// the ratio-128 boundary list: optional, 8-byte aligned; ratio 4 has none
+bool boundaries_ok(int cr, const int32_t* list) { return list == nullptr || (cr == 128 && aligned8(list)); }
 
 }  // namespace
 
@@ -51,10 +53,12 @@ KVC_EXPORT int kvc_plan_prefill(int compress_ratio, int batch, int num_q, const 
 }
 
 KVC_EXPORT int kvc_plan_decode(int compress_ratio, int batch, const int32_t* seq_lens, const int32_t* state_index,
-                               int64_t num_state_rows, kvc_plan_d* plan_d, int32_t* status, void* stream) {
+                               int64_t num_state_rows, kvc_plan_d* plan_d, int32_t* boundaries, int32_t* status,
+                               void* stream) {
   if (!ratio_ok(compress_ratio) || batch < 1 || batch > KVC_MAX_DECODE_BATCH || !rows_ok(num_state_rows))
     return KVC_EINVAL;
   if (!aligned4(seq_lens) || !aligned4(state_index) || !aligned16(plan_d)) return KVC_EINVAL;
+  if (!boundaries_ok(compress_ratio, boundaries)) return KVC_EINVAL;
   if (status != nullptr && !aligned4(status)) return KVC_EINVAL;
   kvc::PlanDecodeArgs a{};
   a.seq_lens = seq_lens;
@@ -63,6 +67,7 @@ KVC_EXPORT int kvc_plan_decode(int compress_ratio, int batch, const int32_t* seq
   a.plan_d = plan_d;
   a.status = status;
   a.batch = batch;
+  a.boundaries = boundaries;
   return status_of(kvc::launch_plan_decode(compress_ratio, kvc::kPlanRing, a, as_stream(stream)));
 }
 
@@ -119,11 +124,12 @@ KVC_EXPORT int kvc_plan_prefill_swa(int compress_ratio, int batch, int num_q, co
 KVC_EXPORT int kvc_plan_decode_swa(int compress_ratio, int batch, const int32_t* seq_lens,
                                    const int32_t* req_pool_indices, const int32_t* req_to_token, int64_t r2t_stride,
                                    int64_t num_reqs, const int32_t* full_to_swa, int64_t num_full, int swa_page_size,
-                                   int ring_size, int64_t num_state_rows, kvc_plan_d* plan_d, int32_t* status,
-                                   void* stream) {
+                                   int ring_size, int64_t num_state_rows, kvc_plan_d* plan_d, int32_t* boundaries,
+                                   int32_t* status, void* stream) {
   if (!ratio_ok(compress_ratio) || batch < 1 || batch > KVC_MAX_DECODE_BATCH || !rows_ok(num_state_rows))
     return KVC_EINVAL;
   if (!aligned4(seq_lens) || !aligned4(req_pool_indices) || !aligned16(plan_d)) return KVC_EINVAL;
+  if (!boundaries_ok(compress_ratio, boundaries)) return KVC_EINVAL;
   if (status != nullptr && !aligned4(status)) return KVC_EINVAL;
   kvc::PlanDecodeArgs a{};
   if (!swa_args_ok(compress_ratio, req_to_token, r2t_stride, num_reqs, full_to_swa, num_full, swa_page_size,
@@ -135,6 +141,7 @@ KVC_EXPORT int kvc_plan_decode_swa(int compress_ratio, int batch, const int32_t*
   a.plan_d = plan_d;
   a.status = status;
   a.batch = batch;
+  a.boundaries = boundaries;
   return status_of(kvc::launch_plan_decode(compress_ratio, kvc::kPlanSwa, a, as_stream(stream)));
 }
 
@@ -242,15 +249,16 @@ int compress_common(bool c4, kvc_dtype dtype, int head_dim, const void* state, i
 
 // out != nullptr: pooled rows to float32; st != nullptr (ratio 4): pool + norm + rotary + store
 int decode_common(bool c4, kvc_dtype dtype, int head_dim, void* state, int64_t num_state_rows, const void* input,
-                  const void* ape, const kvc_plan_d* plan_d, int batch, int32_t* status, float* out,
-                  const kvc_store_args* st, void* stream) {
+                  const void* ape, const kvc_plan_d* plan_d, const int32_t* boundaries, int batch, int32_t* status,
+                  float* out, const kvc_store_args* st, void* stream) {
   if (!dtype_ok(dtype) || !hd_ok(head_dim) || !rows_ok(num_state_rows)) return KVC_EINVAL;
   if (batch < 1 || batch > KVC_MAX_DECODE_BATCH) return KVC_EINVAL;
   if (!aligned16(input) || !aligned16(ape) || !aligned16(plan_d)) return KVC_EINVAL;
   if (st == nullptr ? !aligned16(out) : !store_args_ok(head_dim, st)) return KVC_EINVAL;
   if (num_state_rows > 0 && !aligned16(state)) return KVC_EINVAL;
   if (status != nullptr && !aligned4(status)) return KVC_EINVAL;
-  kvc::DecodeArgs a{state, input, ape, plan_d, status, out, num_state_rows, batch, {}};
+  if (!boundaries_ok(c4 ? 4 : 128, boundaries)) return KVC_EINVAL;
+  kvc::DecodeArgs a{state, input, ape, plan_d, status, out, num_state_rows, batch, {}, boundaries};
   hipError_t e;
   if (st != nullptr) {
     a.st = *st;
@@ -322,23 +330,23 @@ KVC_EXPORT int kvc_norm_rope_store_decode(int compress_ratio, int head_dim, cons
 KVC_EXPORT int kvc_decode_c4(kvc_dtype dtype, int head_dim, void* state, int64_t num_state_rows, const void* input,
                              const void* ape, const kvc_plan_d* plan_d, int batch, int32_t* status, float* out,
                              void* stream) {
-  return decode_common(true, dtype, head_dim, state, num_state_rows, input, ape, plan_d, batch, status, out, nullptr,
-                       stream);
+  return decode_common(true, dtype, head_dim, state, num_state_rows, input, ape, plan_d, nullptr, batch, status, out,
+                       nullptr, stream);
 }
 
 KVC_EXPORT int kvc_decode_c128(kvc_dtype dtype, int head_dim, void* state, int64_t num_state_rows, const void* input,
-                               const void* ape, const kvc_plan_d* plan_d, int batch, int32_t* status, float* out,
-                               void* stream) {
-  return decode_common(false, dtype, head_dim, state, num_state_rows, input, ape, plan_d, batch, status, out,
-                       nullptr, stream);
+                               const void* ape, const kvc_plan_d* plan_d, const int32_t* boundaries, int batch,
+                               int32_t* status, float* out, void* stream) {
+  return decode_common(false, dtype, head_dim, state, num_state_rows, input, ape, plan_d, boundaries, batch, status,
+                       out, nullptr, stream);
 }
 
 KVC_EXPORT int kvc_decode_c4_norm_rope_store(kvc_dtype dtype, int head_dim, void* state, int64_t num_state_rows,
                                              const void* input, const void* ape, const kvc_plan_d* plan_d, int batch,
                                              int32_t* status, const kvc_store_args* args, void* stream) {
   if (args == nullptr) return KVC_EINVAL;
-  return decode_common(true, dtype, head_dim, state, num_state_rows, input, ape, plan_d, batch, status, nullptr,
-                       args, stream);
+  return decode_common(true, dtype, head_dim, state, num_state_rows, input, ape, plan_d, nullptr, batch, status,
+                       nullptr, args, stream);
 }
 
 namespace {

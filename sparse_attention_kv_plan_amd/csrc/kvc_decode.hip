@@ -15,6 +15,8 @@
 //  - ratio 4 with the store step (compressor_v2.py, compress_norm_rope_store):
 //    the pooled row is normalised, rotated and stored as bf16 into the
 //    compressed cache straight from registers; nothing else is written for it.
+#include <algorithm>
+
 #include "kvc_device.hpp"
 #include "kvc_launch.hpp"
 #include "kvc_pool.hpp"
@@ -166,21 +168,25 @@ __global__ __launch_bounds__(kThreads) void decode_c4_store_kernel(DecodeArgs a)
 }
 
 // Ratio 128: one launch, two roles chosen by workgroup index.
-//  - Pool workgroups (the first n_pool): the batch is cut into ranges of
-//    1024 requests, and each range has R rank slots per channel slice.
-//    Workgroup (q, r, cs) loads the range's records (4 per thread, one round
-//    of loads), ranks the range's boundary requests in request order (a
-//    ballot per wave and pass, prefix counts in LDS), and pools those whose
-//    rank is r modulo R over channel slice cs: 64 channels, so the
-//    workgroup's 256 threads are 4V streams of 64/V lanes, each stream
-//    holding 128/(4V) entries, and the whole 128-entry window of the slice is
-//    one round of loads; the stream partials merge in LDS.  Ranking spreads
-//    boundary requests evenly over the slots wherever they sit in the batch,
-//    so a run of neighbouring requests that all close a block is pooled by
-//    many workgroups at once, not one after another by a single one.  The
-//    slices of a row need no merge (the softmax is per channel), so a
-//    boundary request is spread over HD/64 workgroups on different CUs with
-//    no exchange.
+//  - Pool workgroups (the first n_pool) pool the boundary requests (those
+//    whose new token closes a block), each over one channel slice of SL
+//    channels: the workgroup's 256 threads are streams of SL/V lanes, each
+//    stream holding every S-th entry of the 128-entry window, and the stream
+//    partials merge in LDS.  The slices of a row need no merge (the softmax
+//    is per channel), so a boundary request is spread over HD/SL workgroups
+//    on different CUs with no exchange.  Which boundary requests a pool
+//    workgroup takes:
+//    - with the planner's boundary list (the boundary requests in request
+//      order, with their pages, and their count): slot p of P takes list
+//      entries p, p + P, p + 2P, ...; it loads the count and its first entry
+//      in one round, so it goes straight to the window, and the requests are
+//      spread evenly over the slots wherever they sit in the batch;
+//    - without it: the batch is cut into ranges of 1024 requests with R rank
+//      slots each.  Workgroup (q, r, cs) loads the range's records (4 per
+//      thread, one round of loads), ranks the range's boundary requests in
+//      request order (a ballot per wave and pass, prefix counts in LDS), and
+//      pools those whose rank is r modulo R.  Every slot scans the whole
+//      range, so more slots cost more scanning.
 //  - Copy workgroups: 8 requests each.  The 8 input rows are loaded at once
 //    (16-byte vectors, 2*HD/V per row, the vectors of a row on consecutive
 //    lanes; 4 per thread at hd 512 bf16: copies with 8 or more vectors per
@@ -191,21 +197,24 @@ __global__ __launch_bounds__(kThreads) void decode_c4_store_kernel(DecodeArgs a)
 // The pool reads entries 0..126 of the page and takes entry 127, the new
 // token, from the input row; the copy writes only row 127 of the page
 // (write_loc of a boundary request), so the two roles touch disjoint rows.
-// R (the rank slots per range) is chosen by the host: with random lengths a
-// range holds about 8 boundary requests, and more slots mean more workgroups
-// that scan the range and find nothing to pool.
+// SL (the slice width) is chosen by the host: a slice reads a 2*SL*sizeof(T)
+// byte piece of each of the window's rows (kv and score halves), and wider
+// pieces stream better from HBM, while narrower slices finish a single
+// boundary request sooner.
 constexpr int kDec128Threads = 256;
 constexpr int kDec128CopyGroup = 8;
 constexpr int kDec128Range = 1024;  // requests ranked together
 constexpr int kDec128Passes = kDec128Range / kDec128Threads;
-constexpr int kDec128SliceChannels = 64;
 
-template <typename T, int HD>
+template <typename T, int HD, int SL>
 struct Dec128Shape {
   static constexpr int V = Elem<T>::kVec;
-  static constexpr int CS = HD / kDec128SliceChannels;      // channel slices per request
-  static constexpr int S = kDec128Threads / (kDec128SliceChannels / V);  // streams of a pool workgroup
-  typedef C128Pool<T, HD, kDec128Threads, CS, 128 / S> Pool;  // one round of loads per stream
+  static constexpr int CS = HD / SL;                    // channel slices per request
+  static constexpr int S = kDec128Threads / (SL / V);  // streams of a pool workgroup
+  // entries per stream and round of loads: the whole window in one round at
+  // 64 channels, rounds of 4 entries in wider slices (register budget)
+  static constexpr int U = SL == 64 || 128 / S < 4 ? 128 / S : 4;
+  typedef C128Pool<T, HD, kDec128Threads, CS, U> Pool;
 };
 
 // Whether decode record rec (request b) can run, and whether it pools.
@@ -216,12 +225,12 @@ __device__ __forceinline__ bool dec128_ok(const kvc_plan_d& rec, int64_t b, cons
   return ok;
 }
 
-template <typename T, int HD>
-__device__ __forceinline__ void dec128_pool_role(const DecodeArgs& a, int64_t q, int r, int n_slots, int cs) {
+template <typename T, int HD, int SL>
+__device__ __forceinline__ void dec128_pool_role(const DecodeArgs& a, int64_t q, int r, int n_slots, int cs,
+                                                 typename Dec128Shape<T, HD, SL>::Pool::A* lds) {
   typedef typename Elem<T>::storage E;
-  typedef typename Dec128Shape<T, HD>::Pool Pool;
+  typedef typename Dec128Shape<T, HD, SL>::Pool Pool;
   constexpr int kWaves = kDec128Threads / kWave;
-  __shared__ typename Pool::A lds[Pool::kLdsElems];
   __shared__ int32_t req[kDec128Range], page[kDec128Range];
   __shared__ int cnt[kDec128Passes][kWaves];  // boundary requests per pass and wave
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
@@ -272,6 +281,36 @@ __device__ __forceinline__ void dec128_pool_role(const DecodeArgs& a, int64_t q,
     Pool::accumulate(state, input, ape, req[j], 127, page[j], cs, lds);
     Pool::store_merged_par(lds, cs, a.out + (int64_t)req[j] * HD);
     __syncthreads();  // the next pool reuses lds
+  }
+}
+
+// Slot p of n_slots with the planner's boundary list: entries p, p + n_slots,
+// ... below the count (clamped to [0, batch]).  An entry outside the batch
+// or the state is skipped and reported.
+template <typename T, int HD, int SL>
+__device__ __forceinline__ void dec128_list_role(const DecodeArgs& a, int p, int n_slots, int cs,
+                                                 typename Dec128Shape<T, HD, SL>::Pool::A* lds) {
+  typedef typename Elem<T>::storage E;
+  typedef typename Dec128Shape<T, HD, SL>::Pool Pool;
+  const int32_t* list = a.boundaries;
+  // the count and the first entry in one round of loads (p < n_slots <= batch:
+  // the entry lies inside the list whatever the count)
+  const int32_t raw = list[2 * (int64_t)a.batch];
+  int2 e = *reinterpret_cast<const int2*>(list + 2 * p);
+  const int n = raw < 0 ? 0 : (raw > a.batch ? a.batch : raw);
+  const E* state = static_cast<const E*>(a.state);
+  const E* input = static_cast<const E*>(a.input);
+  const E* ape = static_cast<const E*>(a.ape);
+  for (int j = p; j < n; j += n_slots) {  // uniform over the workgroup
+    if (j != p) e = *reinterpret_cast<const int2*>(list + 2 * (int64_t)j);
+    const int64_t b = e.x;
+    if (b >= 0 && b < a.batch && c128_record_ok(b, 127, e.y, a.batch, a.num_state_rows)) {
+      Pool::accumulate(state, input, ape, b, 127, e.y, cs, lds);
+      Pool::store_merged_par(lds, cs, a.out + b * HD);
+      __syncthreads();  // the next pool reuses lds
+    } else if (threadIdx.x == 0 && a.status) {
+      atomicOr(a.status, KVC_DERR_RECORD);
+    }
   }
 }
 
@@ -342,21 +381,27 @@ __device__ __forceinline__ void dec128_copy_role(const DecodeArgs& a, int64_t b0
   }
 }
 
-template <typename T, int HD>
+template <typename T, int HD, int SL>
 __global__ __launch_bounds__(kDec128Threads) void decode_c128_kernel(DecodeArgs a, int n_slots, int n_pool) {
-  constexpr int CS = Dec128Shape<T, HD>::CS;
+  typedef typename Dec128Shape<T, HD, SL>::Pool Pool;
+  constexpr int CS = Dec128Shape<T, HD, SL>::CS;
   if ((int)blockIdx.x < n_pool) {
-    const int slot = blockIdx.x / CS;  // (range, rank slot)
-    dec128_pool_role<T, HD>(a, slot / n_slots, slot % n_slots, n_slots, blockIdx.x % CS);
+    __shared__ typename Pool::A lds[Pool::kLdsElems];  // the stream partials, either way of choosing requests
+    const int slot = blockIdx.x / CS;
+    if (a.boundaries != nullptr) {
+      dec128_list_role<T, HD, SL>(a, slot, n_slots, blockIdx.x % CS, lds);
+    } else {  // slot = (range, rank slot)
+      dec128_pool_role<T, HD, SL>(a, slot / n_slots, slot % n_slots, n_slots, blockIdx.x % CS, lds);
+    }
   } else {
     dec128_copy_role<T, HD>(a, (int64_t)(blockIdx.x - n_pool) * kDec128CopyGroup);
   }
 }
 
-// Rank slots per range of 1024 requests: 8 up to 32 768 requests, then 4.
-// Measured on MI355X at hd 512 bf16 (HIP events, 1/128 of the requests
-// closing a block) against the previous design, which pooled the boundary
-// requests of each group of 16-256 neighbours in one workgroup:
+// Rank slots per range of 1024 requests (no boundary list): 8 up to 32 768
+// requests, then 4.  Measured on MI355X at hd 512 bf16 (HIP events, 1/128 of
+// the requests closing a block) against the previous design, which pooled the
+// boundary requests of each group of 16-256 neighbours in one workgroup:
 //  - boundaries at random places: 24.9 against 29.6 us at 16 384 requests,
 //    49.3 against 47.6 at 32 768, 88.2 against 84.8 at 65 536 (4 slots;
 //    8 slots take 91.2 there);
@@ -366,6 +411,38 @@ __global__ __launch_bounds__(kDec128Threads) void decode_c128_kernel(DecodeArgs 
 // More slots spread a cluster wider but make more workgroups scan each range.
 inline int dec128_rank_slots(int batch) {
   return batch <= 32768 ? 8 : 4;
+}
+
+// List slots: one per 64 requests, about twice the boundary requests of a
+// batch with random lengths, so that a slot rarely pools two.
+inline int dec128_list_slots(int batch) {
+  return std::max(1, std::min(batch, (batch + 63) / 64));
+}
+
+// Slice width: 64 channels, and 256-byte pieces (128 bf16 channels) above
+// 16 384 requests.  Measured on MI355X at hd 512 bf16 (kernel trace, rank
+// slots): 47.7 against 50.7 us at 32 768 requests and 83.0 against 91.7 at
+// 65 536, but 26.0 against 23.9 at 16 384 and 7.3 against 6.2 at 1024.
+constexpr int kDec128WideBatch = 16384;
+template <typename T>
+constexpr int dec128_wide_slice() {
+  return 256 / (int)sizeof(typename Elem<T>::storage) > 64 ? 256 / (int)sizeof(typename Elem<T>::storage) : 64;
+}
+
+template <typename T, int HD, int SL>
+hipError_t dec128_go(const DecodeArgs& a, hipStream_t s) {
+  constexpr int CS = Dec128Shape<T, HD, SL>::CS;
+  int n_slots, n_pool;
+  if (a.boundaries != nullptr) {
+    n_slots = dec128_list_slots(a.batch);
+    n_pool = n_slots * CS;
+  } else {
+    n_slots = dec128_rank_slots(a.batch);
+    n_pool = (a.batch + kDec128Range - 1) / kDec128Range * n_slots * CS;
+  }
+  const int n_copy = (a.batch + kDec128CopyGroup - 1) / kDec128CopyGroup;
+  decode_c128_kernel<T, HD, SL><<<(unsigned)(n_pool + n_copy), kDec128Threads, 0, s>>>(a, n_slots, n_pool);
+  return hipGetLastError();
 }
 
 template <typename T, int HD>
@@ -380,11 +457,10 @@ struct C4Go {
 template <typename T, int HD>
 struct C128Go {
   static hipError_t go(const DecodeArgs& a, hipStream_t s) {
-    const int n_slots = dec128_rank_slots(a.batch);
-    const int n_pool = (a.batch + kDec128Range - 1) / kDec128Range * n_slots * Dec128Shape<T, HD>::CS;
-    const int n_copy = (a.batch + kDec128CopyGroup - 1) / kDec128CopyGroup;
-    decode_c128_kernel<T, HD><<<(unsigned)(n_pool + n_copy), kDec128Threads, 0, s>>>(a, n_slots, n_pool);
-    return hipGetLastError();
+    constexpr int kNarrow = HD < 64 ? HD : 64;
+    constexpr int kWide = HD < dec128_wide_slice<T>() ? HD : dec128_wide_slice<T>();
+    if (kWide != kNarrow && a.batch > kDec128WideBatch) return dec128_go<T, HD, kWide>(a, s);
+    return dec128_go<T, HD, kNarrow>(a, s);
   }
 };
 

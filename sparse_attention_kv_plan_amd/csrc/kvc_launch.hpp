@@ -51,6 +51,7 @@ struct PlanDecodeArgs {
   int batch;
   SwaTables swa;
   const int32_t* prev_page;  // page-4 mode: [batch] page of the block before the new token's
+  int32_t* boundaries;       // ratio 128, may be null: the boundary list (int32 [2 * batch + 2])
 };
 
 struct WriteArgs {
@@ -86,7 +87,8 @@ struct DecodeArgs {
   float* out;  // decode only
   int64_t num_state_rows;
   int batch;
-  kvc_store_args st;  // decode + norm + rotary + store only
+  kvc_store_args st;               // decode + norm + rotary + store only
+  const int32_t* boundaries;       // ratio 128, may be null: the planner's boundary list
 };
 
 // norm + rotary + store of float32 rows (prefill: plan_c / counts; decode: plan_d / status)

@@ -51,14 +51,14 @@ def load(build_if_missing: bool = False):
     P, I, L = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     sig = {
         "kvc_plan_prefill": [I, I, I, P, P, P, L, P, I, P, I, P, P],
-        "kvc_plan_decode": [I, I, P, P, L, P, P, P],
+        "kvc_plan_decode": [I, I, P, P, L, P, P, P, P],
         "kvc_write": [I, I, I, P, L, P, I, P, I, P, P],
         "kvc_compress_c4": [I, I, P, L, P, I, P, P, I, P, P, P],
         "kvc_compress_c128": [I, I, P, L, P, I, P, P, I, P, P, P],
         "kvc_decode_c4": [I, I, P, L, P, P, P, I, P, P, P],
-        "kvc_decode_c128": [I, I, P, L, P, P, P, I, P, P, P],
+        "kvc_decode_c128": [I, I, P, L, P, P, P, P, I, P, P, P],
         "kvc_plan_prefill_swa": [I, I, I, P, P, P, P, L, L, P, L, I, I, L, P, I, P, I, P, P, P],
-        "kvc_plan_decode_swa": [I, I, P, P, P, L, L, P, L, I, I, L, P, P, P],
+        "kvc_plan_decode_swa": [I, I, P, P, P, L, L, P, L, I, I, L, P, P, P, P],
         "kvc_norm_rope_store_prefill": [I, I, P, P, I, P, P, P],
         "kvc_norm_rope_store_decode": [I, I, P, P, I, P, P, P],
         "kvc_compress_c4_norm_rope_store": [I, I, P, L, P, I, P, P, I, P, P, P],
@@ -178,14 +178,27 @@ def plan_prefill(cr, seq_lens, extend_lens, state_index, num_state_rows, num_q, 
     _check(rc, "kvc_plan_prefill")
 
 
-def plan_decode(cr, seq_lens, state_index, num_state_rows, plan_d, status=None, stream=None):
+def boundary_list(batch, device):
+    """An int32 buffer for the ratio-128 boundary list of a decode batch (see kvc_plan_decode)."""
+    return torch.empty(2 * batch + 2, dtype=torch.int32, device=device)
+
+
+def _boundaries(cr, boundaries, batch):
+    _i32(boundaries)
+    _dev(boundaries)
+    if boundaries is not None and (cr != 128 or boundaries.numel() < 2 * batch + 2):
+        raise KvcError("the boundary list is for ratio 128 and needs 2 * batch + 2 int32 entries")
+
+
+def plan_decode(cr, seq_lens, state_index, num_state_rows, plan_d, status=None, stream=None, boundaries=None):
     _i32(seq_lens, state_index, status)
     _dev(seq_lens, state_index, plan_d, status)
     if state_index.numel() != seq_lens.numel():
         raise KvcError("seq_lens and state_index must have one entry per request")
     _shape(plan_d, seq_lens.numel(), D_BYTES, "plan_d")
+    _boundaries(cr, boundaries, seq_lens.numel())
     rc = load().kvc_plan_decode(cr, seq_lens.numel(), _p(seq_lens), _p(state_index), num_state_rows, _p(plan_d),
-                                _p(status), _stream(stream))
+                                _p(boundaries), _p(status), _stream(stream))
     _check(rc, "kvc_plan_decode")
 
 
@@ -215,16 +228,17 @@ def plan_prefill_swa(cr, seq_lens, extend_lens, req_pool_indices, req_to_token, 
 
 
 def plan_decode_swa(cr, seq_lens, req_pool_indices, req_to_token, full_to_swa, swa_page_size, ring_size,
-                    num_state_rows, plan_d, status=None, stream=None):
+                    num_state_rows, plan_d, status=None, stream=None, boundaries=None):
     _i32(seq_lens, req_pool_indices, req_to_token, full_to_swa, status)
     _dev(seq_lens, req_pool_indices, req_to_token, full_to_swa, plan_d, status)
     if req_pool_indices.numel() != seq_lens.numel() or req_to_token.dim() != 2:
         raise KvcError("one request slot per request, req_to_token 2-D")
     _shape(plan_d, seq_lens.numel(), D_BYTES, "plan_d")
+    _boundaries(cr, boundaries, seq_lens.numel())
     rc = load().kvc_plan_decode_swa(cr, seq_lens.numel(), _p(seq_lens), _p(req_pool_indices), _p(req_to_token),
                                     req_to_token.shape[1], req_to_token.shape[0], _p(full_to_swa),
                                     full_to_swa.numel(), swa_page_size, ring_size, num_state_rows, _p(plan_d),
-                                    _p(status), _stream(stream))
+                                    _p(boundaries), _p(status), _stream(stream))
     _check(rc, "kvc_plan_decode_swa")
 
 
@@ -466,7 +480,8 @@ def decode_c4(head_dim, state, inp, ape, plan_d, out, status=None, stream=None):
     _check(rc, "kvc_decode_c4")
 
 
-def decode_c128(head_dim, state, inp, ape, plan_d, out, status=None, stream=None):
+def decode_c128(head_dim, state, inp, ape, plan_d, out, status=None, stream=None, boundaries=None):
+    """boundaries: the list kvc_plan_decode (or _swa) wrote with plan_d, or None."""
     _i32(status)
     _dev(state, inp, ape, plan_d, out, status)
     _rows(128, head_dim, state, inp)
@@ -475,12 +490,18 @@ def decode_c128(head_dim, state, inp, ape, plan_d, out, status=None, stream=None
     _shape(inp, B, ROW_MULT[128] * head_dim, "input")
     _shape(ape, WINDOW[128], head_dim, "ape")
     _shape(out, B, head_dim, "out")
+    _boundaries(128, boundaries, B)
     if out.dtype != torch.float32 or ape.element_size() != inp.element_size():
         raise KvcError("out must be float32 and ape share the input dtype")
     rc = load().kvc_decode_c128(_dtype(inp), head_dim, _p(state), state.shape[0], _p(inp), _p(ape), _p(plan_d),
-                                plan_d.shape[0], _p(status), _p(out), _stream(stream))
+                                _p(boundaries), plan_d.shape[0], _p(status), _p(out), _stream(stream))
     _check(rc, "kvc_decode_c128")
 
 
-def decode(cr, head_dim, state, inp, ape, plan_d, out, status=None, stream=None):
-    (decode_c4 if cr == 4 else decode_c128)(head_dim, state, inp, ape, plan_d, out, status, stream)
+def decode(cr, head_dim, state, inp, ape, plan_d, out, status=None, stream=None, boundaries=None):
+    if cr == 4:
+        if boundaries is not None:
+            raise KvcError("the boundary list is for ratio 128")
+        decode_c4(head_dim, state, inp, ape, plan_d, out, status, stream)
+    else:
+        decode_c128(head_dim, state, inp, ape, plan_d, out, status, stream, boundaries)

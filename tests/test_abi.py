@@ -73,9 +73,12 @@ def test_host_argument_checks_reject_without_enqueueing(lib):
     assert lib.kvc_plan_prefill(4, 1, 1, None, p, p, 8, p, 1, p, 1, p, None) == E
     misaligned = ctypes.c_void_p(p.value + 4)
     assert lib.kvc_plan_prefill(4, 1, 1, p, p, p, 8, misaligned, 1, p, 1, p, None) == E
-    assert lib.kvc_plan_decode(3, 1, p, p, 8, p, None, None) == E
-    assert lib.kvc_plan_decode(4, 0, p, p, 8, p, None, None) == E
-    assert lib.kvc_plan_decode(4, 65537, p, p, 8, p, None, None) == E
+    assert lib.kvc_plan_decode(3, 1, p, p, 8, p, None, None, None) == E
+    assert lib.kvc_plan_decode(4, 0, p, p, 8, p, None, None, None) == E
+    assert lib.kvc_plan_decode(4, 65537, p, p, 8, p, None, None, None) == E
+    # the boundary list: ratio 128 only, 8-byte aligned
+    assert lib.kvc_plan_decode(4, 1, p, p, 8, p, p, None, None) == E
+    assert lib.kvc_plan_decode(128, 1, p, p, 128, p, misaligned, None, None) == E
     # dtype and head_dim
     assert lib.kvc_write(4, 2, 128, p, 8, p, 1, p, 1, p, None) == E
     assert lib.kvc_write(4, 1, 64, p, 8, p, 1, p, 1, p, None) == E
@@ -83,15 +86,18 @@ def test_host_argument_checks_reject_without_enqueueing(lib):
     assert lib.kvc_compress_c128(3, 128, p, 8, p, 1, p, p, 1, p, p, None) == E
     assert lib.kvc_compress_c4(1, 128, p, 8, p, 1, misaligned, p, 1, p, p, None) == E
     assert lib.kvc_decode_c4(1, 128, p, 8, p, p, p, 0, None, p, None) == E
-    assert lib.kvc_decode_c128(1, 128, p, 8, p, p, None, 1, None, p, None) == E
+    assert lib.kvc_decode_c128(1, 128, p, 8, p, p, None, None, 1, None, p, None) == E
+    assert lib.kvc_decode_c128(1, 128, p, 128, p, p, p, misaligned, 1, None, p, None) == E
     # SWA planners: page size not a multiple of the ring, ratio-4 ring of 4, ratio-128 ring of 256
     L = ctypes.c_int64
     assert lib.kvc_plan_prefill_swa(4, 1, 8, p, p, p, p, L(64), L(1), p, L(64), 12, 8, L(8), p, 4, p, 8, p,
                                     None, None) == E
     assert lib.kvc_plan_prefill_swa(4, 1, 8, p, p, p, p, L(64), L(1), p, L(64), 16, 4, L(8), p, 4, p, 8, p,
                                     None, None) == E
-    assert lib.kvc_plan_decode_swa(128, 1, p, p, p, L(64), L(1), p, L(64), 256, 256, L(256), p, None, None) == E
-    assert lib.kvc_plan_decode_swa(4, 1, p, p, p, L(0), L(1), p, L(64), 16, 8, L(8), p, None, None) == E
+    assert lib.kvc_plan_decode_swa(128, 1, p, p, p, L(64), L(1), p, L(64), 256, 256, L(256), p, None, None,
+                                   None) == E
+    assert lib.kvc_plan_decode_swa(4, 1, p, p, p, L(0), L(1), p, L(64), 16, 8, L(8), p, None, None, None) == E
+    assert lib.kvc_plan_decode_swa(4, 1, p, p, p, L(64), L(1), p, L(64), 16, 8, L(8), p, p, None, None) == E
     # norm / rotary / store parameters
     def st(**kw):
         a = dict(norm_weight=p.value, freqs_cis=p.value, out_loc=p.value, cache=p.value, num_loc=4, max_position=8,

@@ -381,16 +381,22 @@ def test_decode_maximum_batch(gpu):
     assert np.array_equal(st_g, st_o), "state differs after decode"
 
 
-@pytest.mark.parametrize("B,hd,layout", [(4100, 128, "random"), (16384, 512, "random"), (40000, 128, "random"),
-                                         (16384, 128, "clustered"), (40000, 128, "clustered")])
-def test_decode_c128_large_batches(gpu, B, hd, layout):
-    """Ratio-128 decode at large batches, where the pool workgroups rank the closing requests of
-    each range of 1024 requests over 8 (up to 32 768 requests) or 4 slots; 16 384 at hd 512 bf16
-    is the bench sweep's launch shape.  Closing requests sit at random places, or in one
-    contiguous run across several ranges (every slot then pools many).  The whole batch runs on
-    the GPU from device-drawn inputs (a state of up to 4 GiB).  The oracle then pools every
-    closing request and 256 others, each from a copy of its own page, and every state row is
-    checked: each new token's row holds its input row bit for bit, and no other row changes."""
+@pytest.mark.parametrize("B,hd,layout,listed", [
+    (4100, 128, "random", False), (16384, 512, "random", False), (40000, 128, "random", False),
+    (16384, 128, "clustered", False), (40000, 128, "clustered", False),
+    (16384, 512, "random", True), (32768, 512, "random", True), (65536, 128, "random", True),
+    (16384, 128, "clustered", True), (40000, 128, "clustered", True)])
+def test_decode_c128_large_batches(gpu, B, hd, layout, listed):
+    """Ratio-128 decode at large batches.  Without the planner's boundary list the pool workgroups
+    rank the closing requests of each range of 1024 requests over 8 (up to 32 768 requests) or 4
+    slots; with it (planned on the GPU, records checked against the oracle's) they take every
+    P-th entry.  Above 16 384 requests the slices are 128 channels wide at bf16.  16 384 and
+    32 768 at hd 512 bf16 are the bench sweep's launch shapes.  Closing requests sit at random
+    places, or in one contiguous run across several ranges (every rank slot then pools many).
+    The whole batch runs on the GPU from device-drawn inputs (a state of up to 8 GiB).  The
+    oracle then pools every closing request and 256 others, each from a copy of its own page, and
+    every state row is checked: each new token's row holds its input row bit for bit, and no
+    other row changes."""
     cr, Wn = 128, 128
     R = 2 * hd
     dev = gpu.device
@@ -417,10 +423,21 @@ def test_decode_c128_large_batches(gpu, B, hd, layout):
     sample = np.concatenate([closing, others])
     pages = state.view(B, Wn, R)[torch.from_numpy(idx[sample].astype(np.int64)).to(dev)].contiguous()
     pristine = state.clone()
-    say("decode c128 large batch B=%d hd=%d closing=%d" % (B, hd, len(closing)))
+    say("decode c128 large batch B=%d hd=%d %s closing=%d list=%s" % (B, hd, layout, len(closing), listed))
     out = torch.full((B, hd), float("nan"), dtype=torch.float32, device=dev)
     st = torch.zeros(1, dtype=torch.int32, device=dev)
-    kvc.decode(cr, hd, state, inp, ape, torch.from_numpy(pd).to(dev), out, st)
+    bl = None
+    pd_dev = torch.from_numpy(pd).to(dev)
+    if listed:
+        pd_dev = torch.zeros_like(pd_dev)
+        bl = kvc.boundary_list(B, dev)
+        kvc.plan_decode(cr, torch.from_numpy(s).to(dev), torch.from_numpy(idx).to(dev), B * Wn, pd_dev, st,
+                        boundaries=bl)
+        assert int(st.item()) == 0 and np.array_equal(pd_dev.cpu().numpy(), pd)
+        lst = bl.cpu().numpy()
+        assert lst[2 * B] == len(closing) and np.array_equal(lst[0:2 * len(closing):2], closing)
+        assert np.array_equal(lst[1:2 * len(closing):2], oracle.unpack_d(pd)[closing, 2])
+    kvc.decode(cr, hd, state, inp, ape, pd_dev, out, st, boundaries=bl)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     loc = torch.from_numpy(idx.astype(np.int64) * Wn + (s.astype(np.int64) - 1) % Wn).to(dev)
