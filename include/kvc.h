@@ -199,10 +199,11 @@ int kvc_plan_prefill(int compress_ratio, int batch, int num_q, const int32_t* se
  * boundaries (ratio 128 only, else NULL; may be NULL): device int32
  * [2 * batch + 2], 8-byte aligned, owned by the caller.  The planner fills
  * it with the boundary list, an index of the records for kvc_decode_c128:
- * for the n requests whose record is valid and whose seq_len % 128 == 0 (the
- * new token closes a block), in request order, entry k is the pair
- * (request b, read_page_0 of its record) at [2k], [2k + 1]; n is at
- * [2 * batch] and [2 * batch + 1] is 0.  Entries past n are left as they
+ * each of the n requests whose record is valid and whose seq_len % 128 == 0
+ * (the new token closes a block) has one entry, the pair (request b,
+ * read_page_0 of its record) at [2k], [2k + 1] for some k < n; the order of
+ * the entries is not fixed and may differ between calls.  n is at
+ * [2 * batch] and [2 * batch + 1] is 0; entries past n are left as they
  * were.  The list is not part of the method: it lets the decode find its
  * pooling requests without scanning the records.
  */

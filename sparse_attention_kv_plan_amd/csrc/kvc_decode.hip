@@ -176,11 +176,12 @@ __global__ __launch_bounds__(kThreads) void decode_c4_store_kernel(DecodeArgs a)
 //    is per channel), so a boundary request is spread over HD/SL workgroups
 //    on different CUs with no exchange.  Which boundary requests a pool
 //    workgroup takes:
-//    - with the planner's boundary list (the boundary requests in request
-//      order, with their pages, and their count): slot p of P takes list
-//      entries p, p + P, p + 2P, ...; it loads the count and its first entry
-//      in one round, so it goes straight to the window, and the requests are
-//      spread evenly over the slots wherever they sit in the batch;
+//    - with the planner's boundary list (the boundary requests, each once
+//      with its page, and their count): slot p of P takes list entries p,
+//      p + P, p + 2P, ...; it loads the count and its first entry in one
+//      round, so it goes straight to the window, and the requests are spread
+//      evenly over the slots wherever they sit in the batch (a request's row
+//      is the same whichever slot pools it);
 //    - without it: the batch is cut into ranges of 1024 requests with R rank
 //      slots each.  Workgroup (q, r, cs) loads the range's records (4 per
 //      thread, one round of loads), ranks the range's boundary requests in

@@ -436,123 +436,30 @@ __global__ __launch_bounds__(kPlanThreads) void plan_prefill_kernel(PlanPrefillA
 }
 
 // Ratio 128's boundary list: the requests whose valid record closes a block,
-// in request order, as (request, read_page_0) pairs, then their count at
-// [2 * batch].  In the record loop each wave's ballot of its closing
-// requests in each pass goes to LDS (mask, with its count in cnt), and each
-// thread marks its own (bit i of `mine` for pass i).  A request's rank is the
-// closing requests of the earlier (pass, wave) pairs plus those of the
-// earlier lanes of its ballot: with one pass each wave adds the counts of the
-// waves before it, otherwise an exclusive scan of the counts in (pass, wave)
-// order gives every pair its first rank.  A thread keeps the pages of its first 4 closing requests in
-// registers and reads later ones back from its own records, 16 loads at a
-// time, so a batch with one request in 128 closing writes its list with no
-// further loads.
+// as (request, read_page_0) pairs, then their count at [2 * batch].  In the
+// record loop a wave with closing requests in a pass takes that many entries
+// from a workgroup counter in LDS (one atomic add by its first lane) and its
+// closing lanes write theirs in lane order, so the list needs no pass of its
+// own; the entries of different waves and passes land in the order the waves
+// reach the counter.
 constexpr int kDecodePlanThreads = 1024;
-constexpr int kDecodePlanWaves = kDecodePlanThreads / kWave;
-constexpr int kDecodePlanPasses = KVC_MAX_DECODE_BATCH / kDecodePlanThreads;  // at most 64: one bit each
-static_assert(kDecodePlanPasses <= 64 && kDecodePlanPasses * kDecodePlanWaves <= kDecodePlanThreads,
-              "boundary ranks: one bit per pass, one (pass, wave) entry per thread");
-
-struct BoundaryLds {
-  int cnt[kDecodePlanThreads];        // closing requests of (pass, wave), later its first rank
-  uint64_t mask[kDecodePlanThreads];  // their lanes
-  int wave_sum[kDecodePlanWaves];
-};
-
-// Pages of a thread's first closing requests, in registers (no dynamic indexing).
-struct FirstPages {
-  int32_t p0 = 0, p1 = 0, p2 = 0, p3 = 0;
-  __device__ __forceinline__ void put(int j, int32_t v) {
-    if (j == 0) p0 = v;
-    if (j == 1) p1 = v;
-    if (j == 2) p2 = v;
-    if (j == 3) p3 = v;
-  }
-  __device__ __forceinline__ int32_t get(int j) const { return j == 0 ? p0 : j == 1 ? p1 : j == 2 ? p2 : p3; }
-};
-
-// Called by every thread after the record loop and a barrier.
-__device__ __forceinline__ void boundary_list(const PlanDecodeArgs& a, BoundaryLds& L, uint64_t mine,
-                                              const FirstPages& pages) {
-  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
-  const int n_pass = (a.batch + kDecodePlanThreads - 1) / kDecodePlanThreads;
-  int total = 0, first = 0;  // one pass: first = the closing requests of the earlier waves
-  if (n_pass == 1) {
-#pragma unroll
-    for (int w = 0; w < kDecodePlanWaves; ++w) {
-      const int c = L.cnt[w];  // the same address in every lane
-      first += w < wave ? c : 0;
-      total += c;
-    }
-  } else {
-    const int c = t < n_pass * kDecodePlanWaves ? L.cnt[t] : 0;
-    int incl = c;  // inclusive scan over the wave's lanes
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int y = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += y;
-    }
-    if (lane == kWave - 1) L.wave_sum[wave] = incl;
-    __syncthreads();  // every count read, every wave's sum written
-    int before = 0;
-#pragma unroll
-    for (int w = 0; w < kDecodePlanWaves; ++w) {
-      before += w < wave ? L.wave_sum[w] : 0;
-      total += L.wave_sum[w];
-    }
-    L.cnt[t] = before + incl - c;  // exclusive: the first rank of (pass, wave) pair t
-    __syncthreads();
-  }
-  // the lanes below this one, written out: __lanemask_lt() also masks by the
-  // lanes active at the call, and the loops below diverge
-  const uint64_t below = (1ull << lane) - 1ull;
-  auto emit = [&](int i, int32_t page) {
-    const int k = i * kDecodePlanWaves + wave;
-    const int rank = (n_pass == 1 ? first : L.cnt[k]) + __popcll(L.mask[k] & below);
-    *reinterpret_cast<int2*>(a.boundaries + 2 * (int64_t)rank) = make_int2(i * kDecodePlanThreads + t, page);
-  };
-  uint64_t rest = mine;
-  for (int j = 0; j < 4 && rest != 0; ++j, rest &= rest - 1)
-    emit(__ffsll((unsigned long long)rest) - 1, pages.get(j));
-  while (rest != 0) {  // more than 4: the pages read back from this thread's own records, 16 in flight
-    constexpr int kQ = 16;
-    int is[kQ];
-    int32_t pg[kQ];
-#pragma unroll
-    for (int q = 0; q < kQ; ++q) {
-      is[q] = rest != 0 ? __ffsll((unsigned long long)rest) - 1 : -1;
-      rest &= rest - 1;  // 0 stays 0
-    }
-#pragma unroll
-    for (int q = 0; q < kQ; ++q)
-      pg[q] = is[q] >= 0 ? (int32_t)a.plan_d[is[q] * kDecodePlanThreads + t].read_page_0 : 0;
-#pragma unroll
-    for (int q = 0; q < kQ; ++q)
-      if (is[q] >= 0) emit(is[q], pg[q]);
-  }
-  if (t == 0) *reinterpret_cast<int2*>(a.boundaries + 2 * (int64_t)a.batch) = make_int2(total, 0);
-}
 
 // One workgroup; requests are independent, the error word needs the whole batch.
 template <int CR, int MAP>
 __global__ __launch_bounds__(kDecodePlanThreads) void plan_decode_kernel(PlanDecodeArgs a) {
   constexpr int32_t W = CR == 4 ? 8 : 128;
   __shared__ int s_err;
-  __shared__ BoundaryLds s_bl;  // ratio 128 with a boundary list only
+  __shared__ int s_listed;  // ratio 128 with a boundary list: entries taken so far
   const bool listed = CR == 128 && a.boundaries != nullptr;
-  if (threadIdx.x == 0) s_err = 0;
-  if (listed) {  // (pass, wave) pairs past the batch keep count 0
-    s_bl.cnt[threadIdx.x] = 0;
-    s_bl.mask[threadIdx.x] = 0;
+  if (threadIdx.x == 0) {
+    s_err = 0;
+    s_listed = 0;
   }
   __syncthreads();
   const int64_t max_idx = MAP == kPlanSwa ? a.swa.num_reqs : a.num_state_rows / (MAP == kPlanPage4 ? 4 : W);
   int err = 0;
-  uint64_t mine = 0;  // listed: bit i set when this thread's request of pass i closes a block
-  FirstPages pages;
-  int n_mine = 0;
   // one request: its record, its error bits, and whether it joins the boundary list
-  auto one = [&](int b, int i, int32_t s, int32_t idx, int32_t prev) {
+  auto one = [&](int b, int32_t s, int32_t idx, int32_t prev) {
     int bad = 0;
     if (s <= 0) bad |= KVC_DERR_EXTEND;
     if (idx < 0 || (int64_t)idx >= max_idx) bad |= KVC_DERR_INDEX;
@@ -596,25 +503,28 @@ __global__ __launch_bounds__(kDecodePlanThreads) void plan_decode_kernel(PlanDec
       if (listed) {  // uniform; the wave's active lanes ballot (lane 0 is active whenever any is)
         const bool f = !bad && (s & 127) == 0;
         const uint64_t m = __ballot(f);
-        if (threadIdx.x % kWave == 0) {
-          s_bl.mask[i * kDecodePlanWaves + threadIdx.x / kWave] = m;
-          s_bl.cnt[i * kDecodePlanWaves + threadIdx.x / kWave] = __popcll(m);
-        }
-        if (f) {
-          pages.put(n_mine++, (int32_t)v.z);  // kept for the first 4 only
-          mine |= 1ull << i;
+        if (m != 0) {  // uniform over the wave
+          const int lane = threadIdx.x % kWave;
+          int base = 0;
+          if (lane == 0) base = atomicAdd(&s_listed, __popcll(m));
+          base = __builtin_amdgcn_readfirstlane(base);  // lane 0's
+          if (f) {
+            // the lanes below this one, written out (__lanemask_lt() also masks by the active lanes)
+            const int k = base + __popcll(m & ((1ull << lane) - 1ull));
+            *reinterpret_cast<int2*>(a.boundaries + 2 * (int64_t)k) = make_int2(b, (int32_t)v.z);
+          }
         }
       }
     }
   };
-  for (int b = threadIdx.x, i = 0; b < a.batch; b += kDecodePlanThreads, ++i)
-    one(b, i, a.seq_lens[b], a.state_index[b], MAP == kPlanPage4 ? a.prev_page[b] : 0);
+  for (int b = threadIdx.x; b < a.batch; b += kDecodePlanThreads)
+    one(b, a.seq_lens[b], a.state_index[b], MAP == kPlanPage4 ? a.prev_page[b] : 0);
   if (err) atomicOr(&s_err, err);
   __syncthreads();
-  if constexpr (CR == 128) {
-    if (listed) boundary_list(a, s_bl, mine, pages);
+  if (threadIdx.x == 0) {
+    if (a.status) a.status[0] = s_err;
+    if (listed) *reinterpret_cast<int2*>(a.boundaries + 2 * (int64_t)a.batch) = make_int2(s_listed, 0);
   }
-  if (threadIdx.x == 0 && a.status) a.status[0] = s_err;
 }
 
 template <int CR, int MAP>
