@@ -210,3 +210,55 @@ def test_decode_c128_list_errors(dev):
             # the fill the planner left, a request outside the batch, and are reported too
             assert int(status.item()) == expect, what
             assert np.array_equal(got.view(np.uint64), ref.view(np.uint64)), what
+
+
+def test_random_boundary_lists(dev):
+    """60 random batches (up to 8192 requests, hd 128-512, bf16 or fp32): closing requests at random,
+    in one cluster or strided, at fractions from none to all, with invalid records among them.  The
+    list against the oracle's records, and the decode with and without it bit for bit."""
+    for case in range(60):
+        rng = np.random.default_rng([41, case])
+        B = int(np.exp(rng.uniform(0, np.log(8192))))
+        hd = int(rng.choice([128, 256, 512]))
+        dtype = str(rng.choice(["bf16", "f32"]))
+        s = rng.integers(1, 65537, size=B)
+        s[s % 128 == 0] += 1
+        nb = int(round(float(rng.choice([0.0, 1 / 128, 1 / 16, 0.5, 1.0])) * B))
+        if nb:
+            kind = int(rng.integers(0, 3))
+            if kind == 0:
+                close = rng.choice(B, size=nb, replace=False)
+            elif kind == 1:
+                first = int(rng.integers(0, B - nb + 1))
+                close = np.arange(first, first + nb)
+            else:
+                close = (np.arange(nb) * max(1, B // nb)) % B
+            s[close] = rng.integers(1, 512, size=len(close)) * 128
+        slots = B + 2
+        idx = rng.permutation(slots)[:B]
+        if B > 8:
+            bad = rng.choice(B, size=B // 8, replace=False)
+            s[bad[::2]] = 0
+            idx[bad[1::2]] = slots + 5
+        say("random boundary list case %d B=%d hd=%d %s closing=%d" % (case, B, hd, dtype, nb))
+        pd, bl, status = gpu_plan(dev, s, idx, slots * 128)
+        opd, ostatus = oracle.plan_decode(128, s, idx, slots * 128)
+        assert status == ostatus and np.array_equal(pd.cpu().numpy(), opd)
+        check_list(bl.cpu().numpy(), opd, "case %d" % case)
+        R = 2 * hd
+        g = torch.Generator(device=dev)
+        g.manual_seed(case)
+        tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        state0 = torch.randn((slots * 128, R), generator=g, device=dev).to(tdt)
+        inp = torch.randn((B, R), generator=g, device=dev).to(tdt)
+        ape = (0.1 * torch.randn((128, hd), generator=g, device=dev)).to(tdt)
+        res = []
+        for lst in (None, bl):
+            state = state0.clone()
+            out = torch.full((B, hd), float("nan"), dtype=torch.float32, device=dev)
+            st = torch.zeros(1, dtype=torch.int32, device=dev)
+            kvc.decode_c128(hd, state, inp, ape, pd, out, st, boundaries=lst)
+            res.append((out.view(torch.int32).cpu(), state.view(torch.int16).cpu(), int(st.item())))
+        assert res[0][2] == res[1][2]
+        assert torch.equal(res[0][0], res[1][0]), "case %d: rows differ with the list" % case
+        assert torch.equal(res[0][1], res[1][1]), "case %d: state differs with the list" % case
