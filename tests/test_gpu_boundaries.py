@@ -262,3 +262,38 @@ def test_random_boundary_lists(dev):
         assert res[0][2] == res[1][2]
         assert torch.equal(res[0][0], res[1][0]), "case %d: rows differ with the list" % case
         assert torch.equal(res[0][1], res[1][1]), "case %d: state differs with the list" % case
+
+
+def test_decode_c128_with_swa_list(dev):
+    """The list from kvc_plan_decode_swa feeds kvc_decode_c128: rows and state equal bit for bit to the
+    decode without it, and the rows match the oracle's decode of the oracle's SWA records."""
+    rng = np.random.default_rng(655)
+    hd, B, stride = 256, 600, 1024
+    r2t, f2s, _ = wl.swa_tables(rng, stride, B + 3, 128, stride=stride)
+    rows = (B + 3) * 128
+    s = rng.integers(1, stride + 1, size=B)
+    close = rng.random(B) < 1 / 4
+    s[close] = rng.integers(1, stride // 128 + 1, size=int(close.sum())) * 128
+    rid = rng.permutation(B + 3)[:B]
+    pd = torch.empty((B, kvc.D_BYTES), dtype=torch.uint8, device=dev)
+    bl = torch.full((2 * B + 2,), SENT, dtype=torch.int32, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    kvc.plan_decode_swa(128, to_dev(np.asarray(s, np.int32)), to_dev(np.asarray(rid, np.int32)),
+                        to_dev(np.asarray(r2t, np.int32)), to_dev(np.asarray(f2s, np.int32)), 128, 128, rows,
+                        pd, st, boundaries=bl)
+    opd, ostatus = oracle.plan_decode_swa(128, s, rid, r2t, f2s, 128, 128, rows)
+    assert int(st.item()) == ostatus == 0 and np.array_equal(pd.cpu().numpy(), opd)
+    n = check_list(bl.cpu().numpy(), opd, "swa")
+    say("decode c128 with an SWA list B=%d boundaries=%d" % (B, n))
+    R = 2 * hd
+    state = wl.to_bf16_bits(rng.standard_normal((rows, R)).astype(np.float32))
+    inp = wl.to_bf16_bits(rng.standard_normal((B, R)).astype(np.float32))
+    ape = wl.to_bf16_bits((0.1 * rng.standard_normal((128, hd))).astype(np.float32))
+    (g0, s0, e0), (g1, s1, e1) = decode_pair(dev, hd, state, inp, ape, pd, bl)
+    st_o = state.copy()
+    ref, err = oracle.decode(128, hd, st_o, inp, ape, opd)
+    assert err == e0 == e1 == 0
+    assert np.array_equal(g0.view(np.uint64), g1.view(np.uint64)), "rows differ with the list"
+    assert np.array_equal(s0.view(np.uint8), s1.view(np.uint8)), "state differs with the list"
+    assert_pool_close(g1, ref, "bf16", "SWA decode with the list")
+    assert np.array_equal(s1.view(np.uint8), st_o.view(np.uint8)), "state differs from the oracle's"
