@@ -297,3 +297,48 @@ def test_decode_c128_with_swa_list(dev):
     assert np.array_equal(s0.view(np.uint8), s1.view(np.uint8)), "state differs with the list"
     assert_pool_close(g1, ref, "bf16", "SWA decode with the list")
     assert np.array_equal(s1.view(np.uint8), st_o.view(np.uint8)), "state differs from the oracle's"
+
+
+def test_decode_step_with_list_under_graph_capture(dev):
+    """plan_decode with the boundary list, then decode_c128 from it, captured in a HIP graph and
+    replayed: every replay matches the eager run (the list's count word included).  The planner
+    takes its entries from an LDS counter, so nothing needs clearing between steps."""
+    rng = np.random.default_rng(23)
+    hd, B = 512, 3000
+    w = wl.random_decode(rng, 128, hd, "bf16", B, prefix_hi=3 * 128, num_slots=B + 2)
+    w.seq_lens[rng.choice(B, size=B // 10, replace=False)] = 128 * 2
+    s_d, i_d = to_dev(w.seq_lens), to_dev(w.state_index)
+    inp, ape, state0 = to_dev(w.input), to_dev(w.ape), to_dev(w.state)
+    pd = torch.empty((B, kvc.D_BYTES), dtype=torch.uint8, device=dev)
+    bl = kvc.boundary_list(B, dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = torch.zeros((B, hd), dtype=torch.float32, device=dev)
+    state = state0.clone()
+
+    def step():
+        kvc.plan_decode(128, s_d, i_d, w.num_state_rows, pd, st, boundaries=bl)
+        kvc.decode_c128(hd, state, inp, ape, pd, out, st, boundaries=bl)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (out.clone(), state.clone(), int(bl[2 * B].item()), int(st.item()))
+    assert ref[3] == 0 and ref[2] == int((w.seq_lens % 128 == 0).sum())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g = torch.cuda.CUDAGraph()
+        state.copy_(state0)
+        with torch.cuda.graph(g, stream=side):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(4):
+        say("decode step graph replay", rep)
+        state.copy_(state0)
+        out.fill_(float("nan"))
+        bl.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(bl[2 * B].item()) == ref[2] and int(st.item()) == 0
+        assert torch.equal(out.view(torch.int32), ref[0].view(torch.int32))
+        assert torch.equal(state.view(torch.int16), ref[1].view(torch.int16))
