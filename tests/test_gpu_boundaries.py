@@ -342,3 +342,25 @@ def test_decode_step_with_list_under_graph_capture(dev):
         assert int(bl[2 * B].item()) == ref[2] and int(st.item()) == 0
         assert torch.equal(out.view(torch.int32), ref[0].view(torch.int32))
         assert torch.equal(state.view(torch.int16), ref[1].view(torch.int16))
+
+
+def test_binding_rejects_bad_lists(dev):
+    """The binding refuses a boundary list for ratio 4, one shorter than 2 * batch + 2 entries, and one
+    that is not int32, before anything is enqueued."""
+    B = 16
+    s = to_dev(np.full(B, 128, np.int32))
+    idx = to_dev(np.arange(B, dtype=np.int32))
+    pd = torch.empty((B, kvc.D_BYTES), dtype=torch.uint8, device=dev)
+    for cr, bl in ((4, kvc.boundary_list(B, dev)), (128, torch.zeros(2 * B + 1, dtype=torch.int32, device=dev)),
+                   (128, torch.zeros(2 * B + 2, dtype=torch.int64, device=dev))):
+        with pytest.raises(kvc.KvcError):
+            kvc.plan_decode(cr, s, idx, B * 128, pd, None, boundaries=bl)
+    state = torch.zeros((B * 128, 256), dtype=torch.bfloat16, device=dev)
+    inp = torch.zeros((B, 256), dtype=torch.bfloat16, device=dev)
+    ape = torch.zeros((128, 128), dtype=torch.bfloat16, device=dev)
+    out = torch.zeros((B, 128), dtype=torch.float32, device=dev)
+    with pytest.raises(kvc.KvcError):
+        kvc.decode(4, 128, state, inp, ape, pd, out, None, boundaries=kvc.boundary_list(B, dev))
+    with pytest.raises(kvc.KvcError):
+        kvc.decode_c128(128, state, inp, ape, pd, out, None, boundaries=torch.zeros(2 * B, dtype=torch.int32,
+                                                                                     device=dev))
