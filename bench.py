@@ -25,7 +25,10 @@ cold-cache time beside it.  After the timed region, untimed passes give:
     64-token request (fp32, head_dim 128) and the ratio-128 prefill of four
     requests, plan -> compress -> write; the two decode batches, plan ->
     decode; launched one by one and as a replayed HIP graph;
-  * the decode step as a replayed HIP graph, and the step on four streams.
+  * the decode step as a replayed HIP graph, and the step on four streams;
+  * same-box bandwidth ceilings: 16-byte-vector streams over 1 GiB (a copy,
+    8 reads per write, reads only) from probe/libstream_probe.so, and the
+    dominant kernel's GB/s as a fraction of the copy and of the 8:1 stream.
 cpu_baseline times the float64 C oracle over the same step on the host cores
 (all this process may use, up to 16, then one).
 
@@ -376,6 +379,67 @@ def flush_caches(flush):
     lines.  A flush by writing would leave up to 256 MB of dirty lines that the next kernel has to
     write back to HBM on its own time."""
     flush.sum(dtype=flush.dtype)
+
+
+PROBE_KINDS = (("copy", 0, 2.0), ("read8_write1", 1, 1.125), ("read", 2, 1.0))  # name, kind, bytes moved per src byte
+
+
+def load_stream_probe():
+    """probe/libstream_probe.so: plain 16-byte-vector streams (copy, 8 reads per write, read only) that
+    give the same-box bandwidth ceilings.  Built by the package's build step beside libkvc.so."""
+    import ctypes
+
+    import torch  # noqa: F401  (first: the library then binds to the HIP runtime torch has loaded)
+    from sparse_attention_kv_plan_amd import build as hip_build
+    if not os.path.exists(hip_build.PROBE_LIB):
+        raise RuntimeError("%s is not built (python -m sparse_attention_kv_plan_amd.build)" % hip_build.PROBE_LIB)
+    lib = ctypes.CDLL(hip_build.PROBE_LIB)
+    lib.stream_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                 ctypes.c_int64, ctypes.c_void_p]
+    lib.stream_probe.restype = ctypes.c_int
+    return lib
+
+
+def stream_ceilings(torch, stream, n=10):
+    """Same-box bandwidth ceilings, measured beside the kernels (outside the timed step): 16-byte-vector
+    streams over a 1 GiB source, with ordinary and with streaming (non-temporal) loads, warm (back to
+    back) and cold (1 GiB read before each launch, untimed), medians of n launches on `stream`.  "copy"
+    reads and writes every byte; "read8_write1" writes one vector per 8 read (the ratio-4 pool's mix of
+    about 8 bytes in per byte out); "read" writes nothing.  GB/s count read plus written bytes.
+    Back-to-back copies run slower than cold ones (each inherits the previous one's dirty lines in the
+    last-level cache), so the ceiling of a stream is its best over both load kinds and both cache states.
+    Returns (all entries, {name: that best GB/s})."""
+    lib = load_stream_probe()
+    m = 1 << 30
+    src = torch.full((m // 8,), 0x0101010101010101, dtype=torch.int64, device=stream.device)
+    dst = torch.empty_like(src)
+    flush = torch.ones(1 << 27, dtype=torch.int64, device=stream.device)
+    entries, best = [], {}
+    for name, kind, per_byte in PROBE_KINDS:
+        for nt in (0, 1):
+            def launch():
+                rc = lib.stream_probe(kind, nt, src.data_ptr(), m, dst.data_ptr(), m, stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError("stream_probe(%d, %d) returned %d" % (kind, nt, rc))
+            launch()
+            for cold in (False, True):
+                ts = []
+                for _ in range(n + 2):
+                    if cold:
+                        flush_caches(flush)
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    launch()
+                    b.record(stream)
+                    ts.append((a, b))
+                torch.cuda.synchronize()
+                us = float(np.median([a.elapsed_time(b) for a, b in ts[2:]])) * 1e3
+                gbps = round(per_byte * m / (us * 1e-6) / 1e9, 1)
+                entries.append({"stream": name, "loads": "nontemporal" if nt else "ordinary",
+                                "cache": "cold" if cold else "warm", "us": round(us, 2), "GBps": gbps})
+                best[name] = max(best.get(name, 0.0), gbps)
+    del src, dst, flush
+    return entries, best
 
 
 def cold_times(torch, stream, cases, n=20):
@@ -737,6 +801,7 @@ def main():
                                       ("compress_c128", P128.compress, P128.restore),
                                       ("decode_c4", D4.decode, D4.restore),
                                       ("decode_c128", D128.decode, D128.restore)])
+    ceil_all, ceil = stream_ceilings(torch, stream)
 
     # the other named workloads, each timed as its own chain: the small ratio-4 prefill (1 request,
     # 64 tokens, fp32, head_dim 128) and the ratio-128 prefill of 4 requests (plan -> compress ->
@@ -915,7 +980,14 @@ def main():
             "cache": "warm",
             "cold_us": cold[dominant],
             "cold_frac": round(dom_bytes / (cold[dominant] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            # same-box ceilings (16-byte-vector streams over 1 GiB, the best of their four timings): a
+            # copy moves as many bytes in as out, the pool's mix about 8 in per 1 out
+            "copy_ceiling": ceil["copy"],
+            "of_copy_ceiling": round(achieved / ceil["copy"], 4),
+            "mix_ceiling": ceil["read8_write1"],
+            "of_mix_ceiling": round(achieved / ceil["read8_write1"], 4),
         },
+        "stream_ceilings": ceil_all,
         "configs": configs,
         "kernels_us": kernels_us,
         "step_rows": step_rows,

@@ -5,6 +5,9 @@
 Each csrc/*.hip file is compiled to an object in _build/ (in parallel), then
 linked into sparse_attention_kv_plan_amd/libkvc.so.  Only the symbols of
 include/kvc.h are exported.
+
+probe/stream_probe.hip (plain bandwidth streams that the benchmark times beside
+the kernels; no part of libkvc.so) becomes probe/libstream_probe.so.
 """
 from __future__ import annotations
 
@@ -19,6 +22,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvc.so")
+PROBE_SRC = os.path.join(PKG, "probe", "stream_probe.hip")
+PROBE_LIB = os.path.join(PKG, "probe", "libstream_probe.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -46,22 +51,30 @@ def _compile(src):
     return obj, out
 
 
-def build(verbose=False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        results = list(ex.map(_compile, srcs))
-    if verbose:
-        for _, out in results:
-            if out.strip():
-                print(out)
-    objs = [o for o, _ in results]
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib):
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout.decode(errors="replace"))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs) + 1)) as ex:
+        probe = ex.submit(_compile, PROBE_SRC)
+        results = list(ex.map(_compile, srcs))
+        probe_obj, probe_out = probe.result()
+    if verbose:
+        for _, out in results:
+            if out.strip():
+                print(out)
+        if probe_out.strip():
+            print(probe_out)
+    _link([o for o, _ in results], LIB)
+    _link([probe_obj], PROBE_LIB)
     return LIB
 
 
