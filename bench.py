@@ -658,12 +658,25 @@ def main():
             gen.manual_seed(seed)
             self.slots = torch.randn((n, 3, w.hd), generator=gen, device=dev, dtype=torch.float32)
             self.slots[:, 1].abs_().add_(1.0)  # running sums are positive
+            self.runs = None
+            if hasattr(X, "plan_w"):  # a prefill chunk: plan it once more with the run list for the write
+                self.runs = kvc.run_list(w.B, dev)
+                self.plan_runs()
+
+        def plan_runs(self):
+            X, w = self.X, self.X.w
+            kvc.plan_prefill(128, X.s, X.e, X.idx, w.num_state_rows, w.num_q, X.plan_c, X.plan_w, X.counts,
+                             runs=self.runs)
 
         def compress(self):
             X, w = self.X, self.X.w
             kvc.compress_c128_online(w.hd, self.slots, X.inp, X.ape, X.plan_c, X.counts, X.out)
 
         def write(self):
+            X, w = self.X, self.X.w
+            kvc.write_c128_online(w.hd, self.slots, X.inp, X.ape, X.plan_w, X.counts, runs=self.runs)
+
+        def write_scan(self):
             X, w = self.X, self.X.w
             kvc.write_c128_online(w.hd, self.slots, X.inp, X.ape, X.plan_w, X.counts)
 
@@ -672,7 +685,8 @@ def main():
             kvc.decode_c128_online(w.hd, self.slots, X.inp, X.ape, X.plan_d, X.out, X.status)
 
     OP128, OD128 = Online(P128, p128.B, 4128), Online(D128, d128.B, 4129)
-    online_launches = [("compress_c128_online", OP128.compress), ("write_c128_online", OP128.write),
+    online_launches = [("plan_prefill c128 runs", OP128.plan_runs), ("compress_c128_online", OP128.compress),
+                       ("write_c128_online", OP128.write), ("write_c128_online scan", OP128.write_scan),
                        ("decode_c128_online", OD128.decode)]
 
     # the uniform-extend variant of the mixed batch (every extend 2, the multi-token-prediction shape):
@@ -681,7 +695,8 @@ def main():
     OM128 = Online(M128, M128.w.B, 4130)  # the online state after the same chunk: 64 runs of 2 tokens
     mtp_launches = [("plan_prefill c4 e=2", M4.plan), ("compress_c4 e=2", M4.compress), ("write c4 e=2", M4.write),
                     ("plan_prefill c128 e=2", M128.plan), ("compress_c128 e=2", M128.compress),
-                    ("write c128 e=2", M128.write), ("write_c128_online e=2", OM128.write)]
+                    ("write c128 e=2", M128.write), ("write_c128_online e=2", OM128.write),
+                    ("write_c128_online scan e=2", OM128.write_scan)]
 
     ST4, ST128 = Store(P4, p4.num_q, 3004), Store(P128, p128.num_q, 3128)
     SD4S, SD128S = Store(D4, d4.B, 3003), Store(D128, d128.B, 3129)
@@ -930,7 +945,12 @@ def main():
         k = j
     ob = algorithmic_bytes_online(p128.hd, p128.esize, blen, runs, d128.seq_lens)
     f_rows["compress_c128_online"] = row_entry("compress_c128_online", ob[0], "hbm")
-    f_rows["write_c128_online"] = row_entry("write_c128_online", ob[1], "latency")
+    f_rows["plan_prefill c128 runs"] = row_entry(
+        "plan_prefill c128 runs", algorithmic_bytes_plan_prefill(p128.B, P128.plan_c.shape[0], P128.plan_w.shape[0])
+        + 16 * p128.B, "latency")
+    # with the run list the write reads one 16-byte entry per request instead of the 8-byte W records
+    f_rows["write_c128_online"] = row_entry("write_c128_online", ob[1] - 8 * c[1] + 16 * p128.B, "latency")
+    f_rows["write_c128_online scan"] = row_entry("write_c128_online scan", ob[1], "latency")
     f_rows["decode_c128_online"] = row_entry("decode_c128_online", ob[2], "latency")
     for name, P, w in (("plan_prefill_swa c4", SP4, p4), ("plan_prefill_swa c128", SP128, p128),
                        ("plan_prefill_page4", PG4, p4)):

@@ -182,11 +182,20 @@ typedef struct kvc_plan_d {
  *                  bits of the plan, 0 (consumers OR their errors into
  *                  counts[3]).  On any plan error num_c = num_w = 0 and every
  *                  record is invalid, so the consumers do nothing.
+ *  runs            NULL, or (ratio 128 only) device int32 [batch, 4], 16-byte
+ *                  aligned, written: for request b its run of W records as
+ *                  (ragged_id of the first, write_loc of the first, n, 0); the
+ *                  run's records are positions write_loc % 128 .. + n - 1 of
+ *                  one page with consecutive ragged rows.  A request without
+ *                  W records, and every request of a plan with an error, gets
+ *                  (0, 0, 0, 0).
+ *                  kvc_write_c128_online takes it in place of a scan of the W
+ *                  records.  NULL for ratio 4 (else KVC_EINVAL).
  */
 int kvc_plan_prefill(int compress_ratio, int batch, int num_q, const int32_t* seq_lens,
                      const int32_t* extend_lens, const int32_t* state_index, int64_t num_state_rows,
                      kvc_plan_c* plan_c, int cap_c, kvc_plan_w* plan_w, int cap_w, int32_t* counts,
-                     void* stream);
+                     int32_t* runs, void* stream);
 
 /*
  * kvc_plan_decode - plan one decode step, one record per request
@@ -482,10 +491,16 @@ int kvc_compress_c128_online(kvc_dtype dtype, int head_dim, const float* state, 
  * its first position is a multiple of 128, else it continues the slot.  Must
  * run after the chunk's kvc_compress_c128_online.  A run whose rows or slot
  * are out of range is skipped and sets KVC_DERR_RECORD in counts[3].
+ *  runs, batch     NULL (batch unused): the runs are found by scanning
+ *                  plan_w.  Else the run list that kvc_plan_prefill wrote
+ *                  for the same chunk (int32 [batch, 4], 16-byte aligned,
+ *                  1 <= batch <= KVC_MAX_PREFILL_BATCH): one run per entry
+ *                  with n > 0, nothing when counts[1] == 0.  The slots end
+ *                  bit for bit as with the scan.
  */
 int kvc_write_c128_online(kvc_dtype dtype, int head_dim, float* state, int64_t num_slots, const void* input,
                           int num_q, const void* ape, const kvc_plan_w* plan_w, int cap_w, int32_t* counts,
-                          void* stream);
+                          const int32_t* runs, int batch, void* stream);
 
 /*
  * kvc_decode_c128_online - for each request b: fold input row b at position

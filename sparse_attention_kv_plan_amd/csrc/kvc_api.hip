@@ -29,8 +29,9 @@ bool boundaries_ok(int cr, const int32_t* list) { return list == nullptr || (cr 
 KVC_EXPORT int kvc_plan_prefill(int compress_ratio, int batch, int num_q, const int32_t* seq_lens,
                                 const int32_t* extend_lens, const int32_t* state_index, int64_t num_state_rows,
                                 kvc_plan_c* plan_c, int cap_c, kvc_plan_w* plan_w, int cap_w, int32_t* counts,
-                                void* stream) {
+                                int32_t* runs, void* stream) {
   if (!ratio_ok(compress_ratio) || batch < 1 || batch > KVC_MAX_PREFILL_BATCH) return KVC_EINVAL;
+  if (runs != nullptr && (compress_ratio != 128 || !aligned16(runs))) return KVC_EINVAL;
   if (num_q < batch || num_q >= KVC_MAX_TOKENS || cap_c < 0 || cap_w < 0 || !rows_ok(num_state_rows))
     return KVC_EINVAL;
   if (!aligned4(seq_lens) || !aligned4(extend_lens) || !aligned4(state_index) || !aligned4(counts))
@@ -49,6 +50,7 @@ KVC_EXPORT int kvc_plan_prefill(int compress_ratio, int batch, int num_q, const 
   a.num_q = num_q;
   a.cap_c = cap_c;
   a.cap_w = cap_w;
+  a.runs = runs;
   return status_of(kvc::launch_plan_prefill(compress_ratio, kvc::kPlanRing, a, as_stream(stream)));
 }
 
@@ -367,19 +369,38 @@ KVC_EXPORT int kvc_compress_c128_online(kvc_dtype dtype, int head_dim, const flo
   if (num_q < 0 || num_q >= KVC_MAX_TOKENS || cap_c < 0 || !aligned4(counts)) return KVC_EINVAL;
   if (cap_c == 0) return KVC_OK;
   if (!aligned16(plan_c) || !aligned16(out)) return KVC_EINVAL;
-  kvc::OnlineArgs a{const_cast<float*>(state), input, ape, plan_c, nullptr, nullptr, counts, nullptr, out,
-                    num_slots, num_q, cap_c};
+  kvc::OnlineArgs a{};
+  a.state = const_cast<float*>(state);
+  a.input = input;
+  a.ape = ape;
+  a.plan_c = plan_c;
+  a.counts = counts;
+  a.out = out;
+  a.num_slots = num_slots;
+  a.num_q = num_q;
+  a.cap = cap_c;
   return status_of(kvc::launch_compress_online(dtype, head_dim, a, as_stream(stream)));
 }
 
 KVC_EXPORT int kvc_write_c128_online(kvc_dtype dtype, int head_dim, float* state, int64_t num_slots,
                                      const void* input, int num_q, const void* ape, const kvc_plan_w* plan_w,
-                                     int cap_w, int32_t* counts, void* stream) {
+                                     int cap_w, int32_t* counts, const int32_t* runs, int batch, void* stream) {
   if (!online_common_ok(dtype, head_dim, state, num_slots, input, ape)) return KVC_EINVAL;
   if (num_q < 0 || num_q >= KVC_MAX_TOKENS || cap_w < 0 || !aligned4(counts)) return KVC_EINVAL;
+  if (runs != nullptr && (!aligned16(runs) || batch < 1 || batch > KVC_MAX_PREFILL_BATCH)) return KVC_EINVAL;
   if (cap_w == 0) return KVC_OK;
   if (!aligned8(plan_w)) return KVC_EINVAL;
-  kvc::OnlineArgs a{state, input, ape, nullptr, plan_w, nullptr, counts, nullptr, nullptr, num_slots, num_q, cap_w};
+  kvc::OnlineArgs a{};
+  a.state = state;
+  a.input = input;
+  a.ape = ape;
+  a.plan_w = plan_w;
+  a.counts = counts;
+  a.runs = runs;
+  a.num_slots = num_slots;
+  a.num_q = num_q;
+  a.cap = cap_w;
+  a.batch = batch;
   return status_of(kvc::launch_write_online(dtype, head_dim, a, as_stream(stream)));
 }
 
@@ -389,7 +410,15 @@ KVC_EXPORT int kvc_decode_c128_online(kvc_dtype dtype, int head_dim, float* stat
   if (!online_common_ok(dtype, head_dim, state, num_slots, input, ape)) return KVC_EINVAL;
   if (batch < 1 || batch > KVC_MAX_DECODE_BATCH || !aligned16(plan_d) || !aligned16(out)) return KVC_EINVAL;
   if (status != nullptr && !aligned4(status)) return KVC_EINVAL;
-  kvc::OnlineArgs a{state, input, ape, nullptr, nullptr, plan_d, nullptr, status, out, num_slots, 0, batch};
+  kvc::OnlineArgs a{};
+  a.state = state;
+  a.input = input;
+  a.ape = ape;
+  a.plan_d = plan_d;
+  a.status = status;
+  a.out = out;
+  a.num_slots = num_slots;
+  a.cap = batch;
   return status_of(kvc::launch_decode_online(dtype, head_dim, a, as_stream(stream)));
 }
 

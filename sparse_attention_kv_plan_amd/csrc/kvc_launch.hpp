@@ -40,6 +40,7 @@ struct PlanPrefillArgs {
   int cap_w;
   SwaTables swa;
   const int32_t* bundle;  // page-4 mode: [batch, 4] load_first, load_second, write_first page, last position
+  int32_t* runs;          // ratio 128, per-request pages, may be null: each request's W run (int32 [batch, 4])
 };
 
 struct PlanDecodeArgs {
@@ -114,9 +115,11 @@ struct OnlineArgs {
   int32_t* counts;           // compress (counts[0], [3]) and write (counts[1], [3])
   int32_t* status;           // decode (may be null)
   float* out;                // compress and decode
+  const int32_t* runs;       // write, may be null: the planner's run list (int32 [batch, 4])
   int64_t num_slots;
   int num_q;
   int cap;  // cap_c, cap_w or batch
+  int batch;  // write with a run list: its entries
 };
 
 hipError_t launch_plan_prefill(int compress_ratio, int map, const PlanPrefillArgs& a, hipStream_t stream);

@@ -9,8 +9,9 @@
 //    before the chunk); out = acc / l;
 //  - write: each request's run of W records (its positions after the last
 //    completed block, consecutive records of one slot) is folded into the
-//    slot, continuing it unless the run starts a block; a workgroup covers 16
-//    records and one channel slice and folds the runs that start there;
+//    slot, continuing it unless the run starts a block; a workgroup covers 32
+//    records and one channel slice and folds the runs that start there, or,
+//    given the prefill planner's run list, one request's run;
 //  - decode: one token folded per request; a request that closes a block
 //    emits acc / l, the others a zero row.
 // HBM-bound like the paged pool; a slot is 6 KiB at hd 512 instead of a
@@ -295,6 +296,59 @@ __global__ __launch_bounds__(kWriteThreads) void write_online_kernel(OnlineArgs 
   }
 }
 
+// The same fold driven by the planner's run list: workgroup (b, cs) folds
+// request b's run (input rows ragged .., positions p0 .. p0 + n - 1 of slot
+// loc / 128, p0 = loc % 128) over channel slice cs, by the same two paths as
+// above (a run of up to kShortRun records by one thread per vector of the
+// slice, a longer one by the whole workgroup), so the slots come out bit for
+// bit as with the scan.  One round trip for the entry and the W count (0
+// after a planner error), then the run's entries and the slot's partial; no
+// staging or search.
+template <typename T, int HD>
+__global__ __launch_bounds__(kWriteThreads) void write_online_runs_kernel(OnlineArgs a) {
+  typedef typename Elem<T>::storage E;
+  constexpr int CS = WriteShape<T, HD>::CS;
+  constexpr int HDW = HD / CS;
+  typedef C128Pool<T, HD, kWriteThreads, CS, 8> Pool;
+  __shared__ typename Pool::A lds[Pool::kLdsElems];
+  const int64_t b = blockIdx.x / CS;
+  const int cs = blockIdx.x % CS;
+  const int d = threadIdx.x;
+  const int4 run = *reinterpret_cast<const int4*>(a.runs + 4 * b);
+  const int32_t n_w = a.counts[1];
+  const int n = run.z;
+  if (n == 0 || n_w <= 0) return;  // uniform over the workgroup
+  const int64_t ragged = run.x, loc = run.y;
+  const int64_t slot = loc / 128;
+  const int p0 = (int)(loc % 128);
+  if (loc < 0 || slot >= a.num_slots || n < 0 || p0 + n > 128 || ragged < 0 || ragged + n > a.num_q) {
+    if (cs == 0 && d == 0) atomicOr(a.counts + 3, KVC_DERR_RECORD);
+    return;
+  }
+  if (n <= kShortRun) {
+    constexpr int kVecs = HDW / Elem<T>::kVec;
+    if (d < kVecs) fold_short_run<T, HD>(a, ragged, slot, p0, n, cs * HDW + d * Elem<T>::kVec);
+    return;
+  }
+  float* st = a.state + slot * 3 * HD + cs * HDW;
+  const bool cont = p0 > 0;  // the block started before this chunk: continue the slot
+  float m0 = 0.f, l0 = 0.f, a0 = 0.f;
+  if (cont && d < HDW) {
+    m0 = st[d];
+    l0 = st[HD + d];
+    a0 = st[2 * HD + d];
+  }
+  Pool::accumulate_range(static_cast<const E*>(a.input), static_cast<const E*>(a.ape), ragged - p0, 0, p0, p0 + n, cs,
+                         lds);
+  if (d < HDW) {
+    typename Pool::A M, L, Acc;
+    Pool::merged_partial(lds, d, cont, m0, l0, a0, &M, &L, &Acc);
+    st[d] = (float)M;
+    st[HD + d] = (float)L;
+    st[2 * HD + d] = (float)Acc;
+  }
+}
+
 // one thread per V channels of one request
 template <typename T, int HD>
 __global__ __launch_bounds__(kThreads) void decode_online_kernel(OnlineArgs a) {
@@ -389,7 +443,11 @@ KVC_ONLINE_KERNEL(CompressK, compress_online_kernel, kCompressThreads)
 template <typename T, int HD>
 struct WriteK {
   static void launch(const OnlineArgs& a, int64_t grid, hipStream_t s) {
-    write_online_kernel<T, HD><<<(unsigned)(grid * WriteShape<T, HD>::CS), kWriteThreads, 0, s>>>(a);
+    if (a.runs != nullptr) {
+      write_online_runs_kernel<T, HD><<<(unsigned)(a.batch * WriteShape<T, HD>::CS), kWriteThreads, 0, s>>>(a);
+    } else {
+      write_online_kernel<T, HD><<<(unsigned)(grid * WriteShape<T, HD>::CS), kWriteThreads, 0, s>>>(a);
+    }
   }
 };
 KVC_ONLINE_KERNEL(DecodeK, decode_online_kernel, kThreads)

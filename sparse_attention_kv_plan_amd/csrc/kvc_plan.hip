@@ -386,6 +386,26 @@ __global__ __launch_bounds__(kPlanThreads) void plan_prefill_kernel(PlanPrefillA
   // ---- stage C: records ----
   const int gtid = blockIdx.x * kPlanThreads + t;
   const int gstride = gridDim.x * kPlanThreads;
+  if constexpr (CR == 128 && MAP == kPlanRing) {
+    // the run list: request b's W records are positions first .. s - 1 of its page, consecutive
+    // input rows from roff + (first - p0); a request without W records, and every request of a
+    // plan with an error, gets an all-zero entry
+    if (a.runs != nullptr) {
+      for (int b = gtid; b < a.batch; b += gstride) {
+        const int32_t s = T.s[b], p0 = T.p0[b];
+        const int32_t fw = first_write<CR, MAP>(s, a.swa);
+        const int32_t first = p0 > fw ? p0 : fw;
+        const int32_t n = tot_err ? 0 : s - first;
+        int4 v = {0, 0, 0, 0};
+        if (n > 0) {
+          v.x = T.roff[b] + (first - p0);
+          v.y = loc_of<CR>(T.idx[b], first);
+          v.z = n;
+        }
+        *reinterpret_cast<int4*>(a.runs + 4 * (int64_t)b) = v;
+      }
+    }
+  }
   const bool uniform = !tot_err && tmin == tmax && tmax <= (uint32_t)kUniformMaxExtend;
   if (uniform) {
     const int E = (int)tmax;  // num_q == batch * E

@@ -50,7 +50,7 @@ def load(build_if_missing: bool = False):
     lib = ctypes.CDLL(LIB_PATH)
     P, I, L = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     sig = {
-        "kvc_plan_prefill": [I, I, I, P, P, P, L, P, I, P, I, P, P],
+        "kvc_plan_prefill": [I, I, I, P, P, P, L, P, I, P, I, P, P, P],
         "kvc_plan_decode": [I, I, P, P, L, P, P, P, P],
         "kvc_write": [I, I, I, P, L, P, I, P, I, P, P],
         "kvc_compress_c4": [I, I, P, L, P, I, P, P, I, P, P, P],
@@ -67,7 +67,7 @@ def load(build_if_missing: bool = False):
         "kvc_compress_c128_online": [I, I, P, L, P, I, P, P, I, P, P, P],
         "kvc_plan_prefill_page4": [I, I, P, P, P, P, L, P, I, P, I, P, P, P],
         "kvc_plan_decode_page4": [I, P, P, P, L, P, P, P],
-        "kvc_write_c128_online": [I, I, P, L, P, I, P, P, I, P, P],
+        "kvc_write_c128_online": [I, I, P, L, P, I, P, P, I, P, P, I, P],
         "kvc_decode_c128_online": [I, I, P, L, P, P, P, I, P, P, P],
     }
     for name, args in sig.items():
@@ -164,18 +164,31 @@ def alloc_prefill_plan(cr: int, batch: int, num_q: int, device="cuda", cap_c=Non
 # --------------------------------------------------------------------------
 
 def plan_prefill(cr, seq_lens, extend_lens, state_index, num_state_rows, num_q, plan_c, plan_w, counts,
-                 stream=None):
-    _i32(seq_lens, extend_lens, state_index, counts)
-    _dev(seq_lens, extend_lens, state_index, plan_c, plan_w, counts)
+                 stream=None, runs=None):
+    """runs: None, or for ratio 128 an int32 [batch, 4] tensor (run_list()) that receives each
+    request's run of W records for kvc_write_c128_online."""
+    _i32(seq_lens, extend_lens, state_index, counts, runs)
+    _dev(seq_lens, extend_lens, state_index, plan_c, plan_w, counts, runs)
     B = seq_lens.numel()
     if extend_lens.numel() != B or state_index.numel() != B or counts.numel() < 4:
         raise KvcError("seq_lens, extend_lens, state_index must have one entry per request; counts 4")
     _shape(plan_c, 0, C_BYTES, "plan_c")
     _shape(plan_w, 0, W_BYTES, "plan_w")
+    _runs(cr, runs, B)
     rc = load().kvc_plan_prefill(cr, seq_lens.numel(), num_q, _p(seq_lens), _p(extend_lens), _p(state_index),
                                  num_state_rows, _p(plan_c), plan_c.shape[0], _p(plan_w), plan_w.shape[0],
-                                 _p(counts), _stream(stream))
+                                 _p(counts), _p(runs), _stream(stream))
     _check(rc, "kvc_plan_prefill")
+
+
+def run_list(batch, device):
+    """An int32 [batch, 4] buffer for the ratio-128 run list of a prefill chunk (see kvc_plan_prefill)."""
+    return torch.empty((batch, 4), dtype=torch.int32, device=device)
+
+
+def _runs(cr, runs, batch):
+    if runs is not None and (cr != 128 or tuple(runs.shape) != (batch, 4) or not runs.is_contiguous()):
+        raise KvcError("the run list is for ratio 128 and must be a contiguous int32 [batch, 4] tensor")
 
 
 def boundary_list(batch, device):
@@ -435,17 +448,23 @@ def compress_c128_online(head_dim, state, inp, ape, plan_c, counts, out, stream=
     _check(rc, "kvc_compress_c128_online")
 
 
-def write_c128_online(head_dim, state, inp, ape, plan_w, counts, stream=None):
-    _i32(counts)
-    _dev(state, inp, ape, plan_w, counts)
+def write_c128_online(head_dim, state, inp, ape, plan_w, counts, stream=None, runs=None):
+    """runs: None (the runs are found in plan_w), or the run list the chunk's plan_prefill wrote."""
+    _i32(counts, runs)
+    _dev(state, inp, ape, plan_w, counts, runs)
     _online_state(state, head_dim)
     _shape(inp, 0, 2 * head_dim, "input")
     _shape(ape, WINDOW[128], head_dim, "ape")
     _shape(plan_w, 0, W_BYTES, "plan_w")
     if ape.element_size() != inp.element_size():
         raise KvcError("ape must share the input dtype")
+    batch = 0
+    if runs is not None:
+        batch = runs.shape[0] if runs.dim() == 2 else -1
+        _runs(128, runs, batch)
     rc = load().kvc_write_c128_online(_dtype(inp), head_dim, _p(state), state.shape[0], _p(inp), inp.shape[0],
-                                      _p(ape), _p(plan_w), plan_w.shape[0], _p(counts), _stream(stream))
+                                      _p(ape), _p(plan_w), plan_w.shape[0], _p(counts), _p(runs), batch,
+                                      _stream(stream))
     _check(rc, "kvc_write_c128_online")
 
 

@@ -63,16 +63,19 @@ def test_host_argument_checks_reject_without_enqueueing(lib):
     p = ctypes.c_void_p((ctypes.addressof(buf) + 15) // 16 * 16)
     E = kvc.KVC_EINVAL
     # ratio, batch, num_q, capacities, row count
-    assert lib.kvc_plan_prefill(5, 1, 1, p, p, p, 8, p, 1, p, 1, p, None) == E
-    assert lib.kvc_plan_prefill(4, 0, 1, p, p, p, 8, p, 1, p, 1, p, None) == E
-    assert lib.kvc_plan_prefill(4, 1025, 2000, p, p, p, 8, p, 1, p, 1, p, None) == E
-    assert lib.kvc_plan_prefill(4, 2, 1, p, p, p, 8, p, 1, p, 1, p, None) == E
-    assert lib.kvc_plan_prefill(4, 1, 1 << 24, p, p, p, 8, p, 1, p, 1, p, None) == E
-    assert lib.kvc_plan_prefill(4, 1, 1, p, p, p, 8, p, -1, p, 1, p, None) == E
-    assert lib.kvc_plan_prefill(4, 1, 1, p, p, p, -8, p, 1, p, 1, p, None) == E
-    assert lib.kvc_plan_prefill(4, 1, 1, None, p, p, 8, p, 1, p, 1, p, None) == E
+    assert lib.kvc_plan_prefill(5, 1, 1, p, p, p, 8, p, 1, p, 1, p, None, None) == E
+    assert lib.kvc_plan_prefill(4, 0, 1, p, p, p, 8, p, 1, p, 1, p, None, None) == E
+    assert lib.kvc_plan_prefill(4, 1025, 2000, p, p, p, 8, p, 1, p, 1, p, None, None) == E
+    assert lib.kvc_plan_prefill(4, 2, 1, p, p, p, 8, p, 1, p, 1, p, None, None) == E
+    assert lib.kvc_plan_prefill(4, 1, 1 << 24, p, p, p, 8, p, 1, p, 1, p, None, None) == E
+    assert lib.kvc_plan_prefill(4, 1, 1, p, p, p, 8, p, -1, p, 1, p, None, None) == E
+    assert lib.kvc_plan_prefill(4, 1, 1, p, p, p, -8, p, 1, p, 1, p, None, None) == E
+    assert lib.kvc_plan_prefill(4, 1, 1, None, p, p, 8, p, 1, p, 1, p, None, None) == E
     misaligned = ctypes.c_void_p(p.value + 4)
-    assert lib.kvc_plan_prefill(4, 1, 1, p, p, p, 8, misaligned, 1, p, 1, p, None) == E
+    assert lib.kvc_plan_prefill(4, 1, 1, p, p, p, 8, misaligned, 1, p, 1, p, None, None) == E
+    # the run list: ratio 128 only, 16-byte aligned
+    assert lib.kvc_plan_prefill(4, 1, 1, p, p, p, 8, p, 1, p, 1, p, p, None) == E
+    assert lib.kvc_plan_prefill(128, 1, 1, p, p, p, 128, p, 1, p, 1, p, misaligned, None) == E
     assert lib.kvc_plan_decode(3, 1, p, p, 8, p, None, None, None) == E
     assert lib.kvc_plan_decode(4, 0, p, p, 8, p, None, None, None) == E
     assert lib.kvc_plan_decode(4, 65537, p, p, 8, p, None, None, None) == E
@@ -130,10 +133,15 @@ def test_host_argument_checks_reject_without_enqueueing(lib):
     assert lib.kvc_compress_c128_online(1, 96, p, 2, p, 1, p, p, 1, p, p, None) == E
     assert lib.kvc_compress_c128_online(1, 128, p, -1, p, 1, p, p, 1, p, p, None) == E
     assert lib.kvc_compress_c128_online(1, 128, misaligned, 2, p, 1, p, p, 1, p, p, None) == E
-    assert lib.kvc_write_c128_online(1, 128, p, 2, p, 1, p, misaligned, 1, p, None) == E
+    assert lib.kvc_write_c128_online(1, 128, p, 2, p, 1, p, misaligned, 1, p, None, 0, None) == E
+    # with a run list: 16-byte aligned, 1 <= batch <= 1024 (checked before the empty-plan shortcut)
+    assert lib.kvc_write_c128_online(1, 128, p, 2, p, 1, p, p, 1, p, misaligned, 1, None) == E
+    assert lib.kvc_write_c128_online(1, 128, p, 2, p, 1, p, p, 0, p, p, 0, None) == E
+    assert lib.kvc_write_c128_online(1, 128, p, 2, p, 1, p, p, 0, p, p, 1025, None) == E
     assert lib.kvc_decode_c128_online(1, 128, p, 2, p, p, p, 0, None, p, None) == E
     assert lib.kvc_compress_c128_online(1, 128, p, 2, p, 1, p, p, 0, p, p, None) == kvc.KVC_OK
-    assert lib.kvc_write_c128_online(1, 128, p, 2, p, 1, p, p, 0, p, None) == kvc.KVC_OK
+    assert lib.kvc_write_c128_online(1, 128, p, 2, p, 1, p, p, 0, p, None, 0, None) == kvc.KVC_OK
+    assert lib.kvc_write_c128_online(1, 128, p, 2, p, 1, p, p, 0, p, p, 1, None) == kvc.KVC_OK
     # empty work is a no-op that needs no device
     assert lib.kvc_compress_c4(1, 128, p, 8, p, 1, p, p, 0, p, p, None) == kvc.KVC_OK
     assert lib.kvc_write(128, 1, 512, p, 8, p, 1, p, 0, p, None) == kvc.KVC_OK
