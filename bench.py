@@ -727,9 +727,9 @@ def main():
     torch.cuda.synchronize()
 
     # ---- timed region: exactly K steps ----
-    # the dominant kernel is bracketed by events on every EVENT_EVERY-th step (each pair of events
-    # costs a few microseconds of stream time)
-    EVENT_EVERY = 4
+    # the dominant kernel is bracketed by events on every EVENT_EVERY-th step (a bracketed step runs
+    # about 13 us longer, so the pairs are kept few: 20 samples at K = 200)
+    EVENT_EVERY = 10
     kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range((args.steps + EVENT_EVERY - 1) // EVENT_EVERY)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
